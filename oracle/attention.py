@@ -1,0 +1,94 @@
+"""Dense softmax attention over a segment's key set, in fp64 (oracle, test-only).
+
+Source: "Hy-Nomas: an 8.6B world model whose memory is a KV cache"
+(ai.thesatyajit.com), sections "How one segment is made" (the current
+segment's text and video tokens meet in joint attention; attention is
+segment-wise causal, reading earlier segments from the KV cache; 16 heads of
+128) and "What 'world memory' stores" (the cache holds, per layer, the keys and
+values of earlier segments' tokens).
+
+At inference only the newest segment has queries, so the segment-wise causal
+mask reduces to: every query of the current segment sees every cached key and
+every key of its own segment, with no mask inside the segment.
+
+Readings where the pages are silent: softmax scale 1/sqrt(head_dim), no
+query/key normalisation; query rows are the video tokens in (t, h, w) raster
+order followed by the text tokens; keys are the kept history frames in list
+order, then the current segment's frames, then its text tokens (the order of
+keys does not change the result).
+"""
+
+import numpy as np
+
+from .rope import rope3d
+
+
+def attention(q, k, v, scale):
+    """Plain softmax attention for one head: softmax(scale * q k^T) v.
+
+    q [M, D], k [N, D], v [N, D], all float64. Returns (out [M, D], lse [M]),
+    lse = natural log of sum_j exp(scale * q.k_j). Exact row max first, then
+    the sums (two passes). N == 0 is rejected: softmax over nothing is
+    undefined.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if k.shape[0] == 0:
+        raise ValueError("attention over an empty key set is undefined")
+    s = (q @ k.T) * scale
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    lsum = p.sum(axis=1, keepdims=True)
+    out = (p @ v) / lsum
+    lse = (m + np.log(lsum))[:, 0]
+    return out, lse
+
+
+def segment_attention(q, q_pos, k, k_pos, v, split=(16, 56, 56), theta=10000.0,
+                      scale=None, rows=None, chunk=1024):
+    """Joint attention of one session over its key set, every head.
+
+    q     [Lq, H, D]  raw (unrotated) queries, float64 (exact bf16 values)
+    q_pos [Lq, 3]     (t, h, w) of each query row (text rows at 0, 0, 0)
+    k, v  [Lk, H, D]  raw keys / values of the whole key set (kept history
+                      frames, the own segment, the own text), float64
+    k_pos [Lk, 3]     positions of the keys
+    rows  optional index array of query rows to evaluate (sampling)
+    Returns (out [len(rows), H, D], lse [len(rows), H]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    D = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if rows is None:
+        rows = np.arange(q.shape[0])
+    rows = np.asarray(rows, dtype=np.int64)
+    qr = rope3d(q[rows], np.asarray(q_pos)[rows], split, theta)
+    kr = rope3d(k, k_pos, split, theta)
+    v = np.asarray(v, dtype=np.float64)
+    H = q.shape[1]
+    out = np.zeros((len(rows), H, D))
+    lse = np.zeros((len(rows), H))
+    for h in range(H):
+        kh = np.ascontiguousarray(kr[:, h, :])
+        vh = np.ascontiguousarray(v[:, h, :])
+        for c0 in range(0, len(rows), chunk):
+            o, l = attention(qr[c0:c0 + chunk, h, :], kh, vh, scale)
+            out[c0:c0 + chunk, h, :] = o
+            lse[c0:c0 + chunk, h] = l
+    return out, lse
+
+
+def merge_partials(o_a, lse_a, o_b, lse_b):
+    """Combine attention over disjoint key sets A and B from their (out, lse).
+
+    The identity the split/merge check relies on: with weights exp(lse_x - lse),
+    lse = log(exp(lse_a) + exp(lse_b)), out = sum_x w_x * out_x.
+    """
+    m = np.maximum(lse_a, lse_b)
+    wa = np.exp(lse_a - m)
+    wb = np.exp(lse_b - m)
+    lse = m + np.log(wa + wb)
+    out = (o_a * wa[..., None] + o_b * wb[..., None]) / (wa + wb)[..., None]
+    return out, lse

@@ -1,0 +1,181 @@
+"""Cache planes: layout, byte counts and expected contents (oracle, test-only).
+
+Sources: "Hy-Nomas: an 8.6B world model whose memory is a KV cache"
+(ai.thesatyajit.com), sections "What 'world memory' stores" (K and V are each
+2,048 wide per token and layer; BF16 costs 8,192 bytes per token per layer,
+389 MB per 880-token latent frame over 54 layers) and "The 4090 preset" (the
+INT8 cache stores one byte per value plus an FP32 scale per token and head,
+4,224 bytes per token per layer; 18 kept frames are about 3.6 GB); section
+"How one segment is made" (3D RoPE on keys; 880 tokens per latent frame).
+
+Plane layout (the library's own design; the pages fix no layout). Per layer,
+with H heads, D = head_dim, P = lat_h * lat_w tokens per latent frame:
+
+* K plane  [frame_capacity][H][P][D]  element ((f*H + h)*P + p)*D + c
+* V plane  [frame_capacity][H][D][P]  element ((f*H + h)*D + c)*P + p
+  (V is stored transposed per (frame, head): the P.V contraction runs over
+  tokens, so tokens are the contiguous axis)
+* text K   [H][text_capacity][D]      element (h*TC + i)*D + c
+* text V   [H][D][text_capacity]      element (h*D + c)*TC + i
+* fp8 (e4m3fn) planes use the same shapes with one byte per element, plus
+  fp32 scales k_scale/v_scale [frame_capacity][H] and k_text_scale /
+  v_text_scale [H].
+
+Stored values. K is rotated by the 3D RoPE at its absolute position (frame f
+for video token p of frame f; (0, 0, 0) for text) and rounded to the cache
+format; V is stored unrotated. fp8 scale per (frame, head) plane (per head for
+the text slot) = amax / 448 over that plane's values, computed in fp32
+(amax == 0 gives scale 1); codes = e4m3 round-nearest-even of
+x * (448 / amax) evaluated in fp32 and saturated, so that the quantisation
+decision is taken in the same precision as the kernel's.
+"""
+
+import numpy as np
+
+from . import numerics
+from .rope import rope3d, video_positions, text_positions
+
+E4M3_MAX = 448.0
+
+
+# ---------------------------------------------------------------- byte counts
+def bytes_per_token_per_layer(fmt, heads=16, head_dim=128):
+    """K + V bytes of one token in one layer for a cache format.
+
+    'bf16'            : 2 bytes per value
+    'int8_token_head' : the pages' single-GPU format, 1 byte per value plus an
+                        fp32 scale per token and head
+    """
+    width = heads * head_dim
+    if fmt == "bf16":
+        return 2 * width * 2
+    if fmt == "int8_token_head":
+        return 2 * (width + heads * 4)
+    raise ValueError(fmt)
+
+
+def plane_bytes(dtype, heads, head_dim, P, frame_capacity, text_capacity):
+    """Bytes of one layer's cache planes in this library's layout.
+
+    dtype 'bf16' or 'fp8' (fp8 adds fp32 scales per (frame, head) and per
+    head for the text slot, for K and V).
+    """
+    elems = 2 * heads * head_dim * (frame_capacity * P + text_capacity)
+    if dtype == "bf16":
+        return 2 * elems
+    if dtype == "fp8":
+        return elems + 2 * 4 * heads * (frame_capacity + 1)
+    raise ValueError(dtype)
+
+
+# --------------------------------------------------------------- layout maps
+def k_offset(f, h, p, c, H, P, D):
+    return ((f * H + h) * P + p) * D + c
+
+
+def v_offset(f, h, p, c, H, P, D):
+    return ((f * H + h) * D + c) * P + p
+
+
+def text_k_offset(h, i, c, TC, D):
+    return (h * TC + i) * D + c
+
+
+def text_v_offset(h, i, c, TC, D):
+    return (h * D + c) * TC + i
+
+
+# ------------------------------------------------------ expected append (bf16)
+def append_bf16(k_in, v_in, frame0, lat_h, lat_w, split, theta):
+    """Expected bf16 plane contents for frames [frame0, frame0+F) of a segment.
+
+    k_in, v_in: float64 [F*P, H, D] raw values (exact bf16 inputs), token
+    order (t, h, w) raster. Returns (K [F, H, P, D], V [F, H, D, P]) as float64
+    values that are exactly bf16: K = bf16(RoPE(k) in exact arithmetic), V a copy.
+    """
+    k_in = np.asarray(k_in, dtype=np.float64)
+    v_in = np.asarray(v_in, dtype=np.float64)
+    P = lat_h * lat_w
+    n, H, D = k_in.shape
+    F = n // P
+    pos = video_positions(frame0, F, lat_h, lat_w)
+    kr = numerics.bf16_round(rope3d(k_in, pos, split, theta))
+    K = kr.reshape(F, P, H, D).transpose(0, 2, 1, 3)
+    V = v_in.reshape(F, P, H, D).transpose(0, 2, 3, 1)
+    return K, V
+
+
+def append_text_bf16(k_in, v_in):
+    """Expected text slot (bf16): K [H, n, D] (identity rotation), V [H, D, n]."""
+    k_in = np.asarray(k_in, dtype=np.float64)
+    v_in = np.asarray(v_in, dtype=np.float64)
+    kr = numerics.bf16_round(rope3d(k_in, text_positions(k_in.shape[0])))
+    return kr.transpose(1, 0, 2), v_in.transpose(1, 2, 0)
+
+
+# ------------------------------------------------------- expected append (fp8)
+def quantize_plane_fp8(x):
+    """Quantise one plane (any shape) of fp32-valued reals to e4m3 codes.
+
+    Returns (codes uint8 same shape, scale float32). The decision path is
+    float32: amax is the fp32 maximum magnitude, inv = fp32(448 / amax),
+    y = fp32(x * inv), code = e4m3 nearest-even of y, saturated.
+    """
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
+    if amax == 0:
+        return np.zeros(x32.shape, np.uint8), np.float32(1.0)
+    inv = np.float32(E4M3_MAX) / amax
+    scale = amax / np.float32(E4M3_MAX)
+    y = (x32 * inv).astype(np.float32)
+    return numerics.e4m3_encode(y.astype(np.float64)), np.float32(scale)
+
+
+def append_fp8(k_in, v_in, frame0, lat_h, lat_w, split, theta):
+    """Expected fp8 planes and scales for frames [frame0, frame0+F).
+
+    K is rotated in exact arithmetic here and then quantised from its float32
+    rounding; the kernel rotates in float32, so its K codes may differ from
+    these by one code step near a rounding boundary. V is an exact input, so
+    its codes and scales are fully determined.
+    Returns (Kc [F,H,P,D] u8, Ks [F,H] f32, Vc [F,H,D,P] u8, Vs [F,H] f32).
+    """
+    k_in = np.asarray(k_in, dtype=np.float64)
+    v_in = np.asarray(v_in, dtype=np.float64)
+    P = lat_h * lat_w
+    n, H, D = k_in.shape
+    F = n // P
+    pos = video_positions(frame0, F, lat_h, lat_w)
+    kr = rope3d(k_in, pos, split, theta).reshape(F, P, H, D).transpose(0, 2, 1, 3)
+    vv = v_in.reshape(F, P, H, D).transpose(0, 2, 3, 1)
+    Kc = np.zeros(kr.shape, np.uint8)
+    Vc = np.zeros(vv.shape, np.uint8)
+    Ks = np.zeros((F, H), np.float32)
+    Vs = np.zeros((F, H), np.float32)
+    for f in range(F):
+        for h in range(H):
+            Kc[f, h], Ks[f, h] = quantize_plane_fp8(kr[f, h])
+            Vc[f, h], Vs[f, h] = quantize_plane_fp8(vv[f, h])
+    return Kc, Ks, Vc, Vs
+
+
+def append_text_fp8(k_in, v_in):
+    """Expected fp8 text slot: (Kc [H,n,D], Ks [H], Vc [H,D,n], Vs [H])."""
+    k_in = np.asarray(k_in, dtype=np.float64)
+    v_in = np.asarray(v_in, dtype=np.float64)
+    n, H, D = k_in.shape
+    kt = k_in.transpose(1, 0, 2)
+    vt = v_in.transpose(1, 2, 0)
+    Kc = np.zeros(kt.shape, np.uint8)
+    Vc = np.zeros(vt.shape, np.uint8)
+    Ks = np.zeros(H, np.float32)
+    Vs = np.zeros(H, np.float32)
+    for h in range(H):
+        Kc[h], Ks[h] = quantize_plane_fp8(kt[h])
+        Vc[h], Vs[h] = quantize_plane_fp8(vt[h])
+    return Kc, Ks, Vc, Vs
+
+
+def dequant(codes, scale):
+    """Real value of fp8 codes times their plane scale (float64)."""
+    return numerics.e4m3_decode(codes) * np.float64(scale)

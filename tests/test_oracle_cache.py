@@ -1,0 +1,145 @@
+"""Pins for oracle.cache (byte counts, plane layout, expected append contents).
+
+Byte counts are pinned by the figures printed on the page ("Hy-Nomas: an 8.6B
+world model ...", sections "What 'world memory' stores" and "The 4090 preset",
+stored in tests/golden/page_figures.json). Layout maps are pinned by brute
+force (bijection onto the plane; agreement with numpy's own transposes).
+Append contents are pinned by exact cases (V is a copy; position (0,0,0) is the
+identity rotation) and by the explicit per-row rotation.
+"""
+
+import json
+import os
+
+import numpy as np
+
+from oracle import cache, numerics, rope
+
+FIG = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+
+
+def test_token_grid_figures():
+    g = FIG["token_grid"]
+    assert g["frame_h_px"] // g["spatial_factor"] == g["lat_h"]
+    assert g["frame_w_px"] // g["spatial_factor"] == g["lat_w"]
+    assert g["lat_h"] * g["lat_w"] == g["tokens_per_frame"]
+    assert g["tokens_per_frame"] * g["latent_frames_per_segment"] == g["tokens_per_segment"]
+    assert g["heads"] * g["head_dim"] == g["hidden"]
+    assert sum(g["rope_split"]) == g["head_dim"]
+
+
+def test_bf16_bytes_match_page():
+    f = FIG["bf16_cache"]
+    g = FIG["token_grid"]
+    b = cache.bytes_per_token_per_layer("bf16", g["heads"], g["head_dim"])
+    assert b == f["bytes_per_token_per_layer"]
+    assert b * g["layers"] == f["bytes_per_token_54_layers"]
+    per_frame = b * g["layers"] * g["tokens_per_frame"]
+    assert round(per_frame / 1e6) == f["mb_per_frame"]
+    per_s = per_frame * f["latent_fps"]
+    assert round(per_s / 1e9, 2) == f["gb_per_second"]
+    assert round(per_s * 60 / 1e9) == f["gb_per_minute"]
+    assert round(per_s * 60 / 8 / 1e9, 1) == f["gb_per_gpu_sp8"]
+
+
+def test_int8_bytes_match_page():
+    f = FIG["int8_cache"]
+    g = FIG["token_grid"]
+    b = cache.bytes_per_token_per_layer("int8_token_head", g["heads"], g["head_dim"])
+    assert b == f["bytes_per_token_per_layer"]
+    per_frame = b * g["layers"] * g["tokens_per_frame"]
+    assert round(per_frame * f["kept_frames"] / 1e9, 1) == f["gb_kept"]
+    assert round(per_frame / 1e6, -2) == f["mb_per_frame"]
+    assert round(per_frame * 6 / 1e9, 1) == f["gb_per_second"]
+    assert round(per_frame * 6 * 60 / 1e9) == f["gb_per_minute"]
+
+
+def test_plane_bytes():
+    assert cache.plane_bytes("bf16", 16, 128, 880, 60, 256) == 2 * 2 * 2048 * (60 * 880 + 256)
+    assert cache.plane_bytes("fp8", 16, 128, 880, 60, 256) == 2 * 2048 * (60 * 880 + 256) + 8 * 16 * 61
+
+
+def test_layout_is_bijection_and_matches_numpy_transposes():
+    F, H, P, D, TC = 3, 2, 6, 4, 5
+    n = F * H * P * D
+    ko = np.array([cache.k_offset(f, h, p, c, H, P, D) for f in range(F) for h in range(H)
+                   for p in range(P) for c in range(D)])
+    vo = np.array([cache.v_offset(f, h, p, c, H, P, D) for f in range(F) for h in range(H)
+                   for p in range(P) for c in range(D)])
+    assert sorted(ko.tolist()) == list(range(n)) and sorted(vo.tolist()) == list(range(n))
+    x = np.arange(n).reshape(F, H, P, D)              # value = k-plane offset
+    flatK = np.empty(n, dtype=np.int64)
+    flatK[ko] = x.reshape(-1)
+    assert np.array_equal(flatK, x.reshape(-1))
+    flatV = np.empty(n, dtype=np.int64)
+    flatV[vo] = x.reshape(-1)
+    assert np.array_equal(flatV, x.transpose(0, 1, 3, 2).reshape(-1))
+    tk = [cache.text_k_offset(h, i, c, TC, D) for h in range(H) for i in range(TC) for c in range(D)]
+    tv = [cache.text_v_offset(h, i, c, TC, D) for h in range(H) for i in range(TC) for c in range(D)]
+    assert sorted(tk) == list(range(H * TC * D)) and sorted(tv) == list(range(H * TC * D))
+
+
+def _bf16_inputs(shape, seed):
+    return numerics.bf16_round(np.random.default_rng(seed).standard_normal(shape))
+
+
+def test_append_bf16_v_copy_and_k_rotation():
+    lat_h, lat_w, H, D, F = 4, 6, 2, 128, 2
+    P = lat_h * lat_w
+    k = _bf16_inputs((F * P, H, D), 0)
+    v = _bf16_inputs((F * P, H, D), 1)
+    for frame0 in (0, 7):
+        K, V = cache.append_bf16(k, v, frame0, lat_h, lat_w, (16, 56, 56), 10000.0)
+        assert K.shape == (F, H, P, D) and V.shape == (F, H, D, P)
+        for f in range(F):
+            for p in range(P):
+                tok = f * P + p
+                assert np.array_equal(V[f, :, :, p], v[tok])
+                pos = np.array([[frame0 + f, p // lat_w, p % lat_w]])
+                want = numerics.bf16_round(rope.rope3d(k[tok], pos))
+                assert np.array_equal(K[f, :, p, :], want)
+        if frame0 == 0:
+            assert np.array_equal(K[0, :, 0, :], k[0])          # position (0,0,0)
+
+
+def test_append_text_is_identity_layout():
+    k = _bf16_inputs((9, 3, 128), 2)
+    v = _bf16_inputs((9, 3, 128), 3)
+    K, V = cache.append_text_bf16(k, v)
+    assert np.array_equal(K, k.transpose(1, 0, 2)) and np.array_equal(V, v.transpose(1, 2, 0))
+
+
+def test_quantize_plane_fp8_properties():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((24, 128)) * 1.7).astype(np.float32).astype(np.float64)
+    codes, scale = cache.quantize_plane_fp8(x)
+    amax = np.float32(np.abs(x).max())
+    assert scale == np.float32(amax / np.float32(448.0))
+    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert codes[i] & 0x7F == 0x7E                          # amax maps to 448
+    dq = cache.dequant(codes, scale)
+    # relative error of e4m3 (3 mantissa bits) is at most 2**-4 for normals
+    normal = np.abs(x) / scale >= 2.0 ** -6
+    assert np.all(np.abs(dq - x)[normal] <= np.abs(x)[normal] * 2.0 ** -4 * 1.0001)
+    assert np.all(np.abs(dq - x)[~normal] <= 2.0 ** -10 * scale * 1.0001)
+    z, s0 = cache.quantize_plane_fp8(np.zeros((3, 4)))
+    assert s0 == 1.0 and not z.any()
+
+
+def test_append_fp8_v_codes_follow_fp32_decision():
+    lat_h, lat_w, H, F = 4, 6, 2, 2
+    P = lat_h * lat_w
+    k = _bf16_inputs((F * P, H, 128), 5)
+    v = _bf16_inputs((F * P, H, 128), 6) * 3
+    Kc, Ks, Vc, Vs = cache.append_fp8(k, v, 3, lat_h, lat_w, (16, 56, 56), 10000.0)
+    for f in range(F):
+        for h in range(H):
+            plane = v[f * P:(f + 1) * P, h, :].T.astype(np.float32)    # [D, P]
+            amax = np.float32(np.abs(plane).max())
+            inv = np.float32(448.0) / amax
+            y = (plane * inv).astype(np.float32)
+            assert np.array_equal(Vc[f, h], numerics.e4m3_encode(y.astype(np.float64)))
+            assert Vs[f, h] == amax / np.float32(448.0)
+    dk = cache.dequant(Kc[0, 0], Ks[0, 0])
+    kr = rope.rope3d(k[:P], rope.video_positions(3, 1, lat_h, lat_w))[:, 0, :]
+    assert np.max(np.abs(dk - kr)) <= np.abs(kr).max() * 2.0 ** -4
