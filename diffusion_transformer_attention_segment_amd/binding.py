@@ -1,0 +1,257 @@
+"""ctypes binding of the segment-attention C ABI (include/segattn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library. PyTorch supplies device memory (tensor.data_ptr()) and the current
+stream. If libsegattn.so has not been built, loading raises -- there is no
+fallback implementation.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsegattn.so")
+
+SA_OK = 0
+STATUS_NAMES = {0: "SA_OK", 1: "SA_E_ARG", 2: "SA_E_SHAPE", 3: "SA_E_ALIGN",
+                4: "SA_E_UNSUPPORTED", 5: "SA_E_RANGE", 6: "SA_E_CAPACITY", 7: "SA_E_HIP"}
+KV_BF16, KV_FP8 = 0, 1
+SEL_ALL, SEL_RECENT, SEL_POWER, SEL_ANCHOR_RECENT = 0, 1, 2, 3
+MAX_ITEMS = 8
+HEAD_DIM = 128
+
+
+class SegAttnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class sa_geom(ctypes.Structure):
+    _fields_ = [("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("lat_h", ctypes.c_int32), ("lat_w", ctypes.c_int32),
+                ("rope_split", ctypes.c_int32 * 3), ("rope_theta", ctypes.c_float),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class sa_kv_layer(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("frame_capacity", ctypes.c_int32),
+                ("text_capacity", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("k_text", ctypes.c_void_p), ("v_text", ctypes.c_void_p),
+                ("k_text_scale", ctypes.c_void_p), ("v_text_scale", ctypes.c_void_p)]
+
+
+class sa_attn_item(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("frame0_q", ctypes.c_int32),
+                ("n_frames_q", ctypes.c_int32), ("n_text_q", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32), ("kv", ctypes.POINTER(sa_kv_layer)),
+                ("frames", ctypes.c_void_p), ("n_frames_kv", ctypes.c_int32),
+                ("n_text_kv", ctypes.c_int32), ("out", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p)]
+
+
+# exported symbol -> (restype, argtypes); also the list of ABI entry points
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+SIGNATURES = {
+    "sa_abi_version": (ctypes.c_int, []),
+    "sa_last_error": (ctypes.c_char_p, []),
+    "sa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sa_cache_bytes": (ctypes.c_size_t, [ctypes.POINTER(sa_geom), _I, _I, _I]),
+    "sa_kv_append": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_kv_layer), _P, _P,
+                                    _I, _I, _P]),
+    "sa_text_append": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_kv_layer), _P, _P,
+                                      _I, _P]),
+    "sa_history_select": (ctypes.c_int, [_I, _I, _I, ctypes.c_double, _I, _I,
+                                         ctypes.POINTER(ctypes.c_int32), _I,
+                                         ctypes.POINTER(ctypes.c_int32)]),
+    "sa_history_gather": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_kv_layer), _P,
+                                         _I, ctypes.POINTER(sa_kv_layer), _P]),
+    "sa_segment_attention": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_attn_item),
+                                            _I, _P]),
+    "sa_kv_dequant": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_kv_layer), _P, _I,
+                                     _I, ctypes.POINTER(sa_kv_layer), _P]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if libsegattn.so is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m diffusion_transformer_attention_segment_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != SA_OK:
+        raise SegAttnError(status, lib().sa_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+class Geom:
+    """Attention geometry (sa_geom)."""
+
+    def __init__(self, heads=16, lat_h=22, lat_w=40, rope_split=(16, 56, 56),
+                 rope_theta=10000.0, softmax_scale=0.0, head_dim=HEAD_DIM):
+        self.heads, self.lat_h, self.lat_w = heads, lat_h, lat_w
+        self.rope_split = tuple(rope_split)
+        self.rope_theta, self.softmax_scale, self.head_dim = rope_theta, softmax_scale, head_dim
+
+    @property
+    def P(self):
+        return self.lat_h * self.lat_w
+
+    def c(self):
+        g = sa_geom()
+        g.heads, g.head_dim, g.lat_h, g.lat_w = self.heads, self.head_dim, self.lat_h, self.lat_w
+        for i in range(3):
+            g.rope_split[i] = self.rope_split[i]
+        g.rope_theta, g.softmax_scale = self.rope_theta, self.softmax_scale
+        return g
+
+
+class KVLayer:
+    """One layer's cache planes as torch tensors (caller-owned device memory)."""
+
+    def __init__(self, dtype, k, v, k_text, v_text, k_scale=None, v_scale=None,
+                 k_text_scale=None, v_text_scale=None):
+        self.dtype = dtype
+        self.k, self.v, self.k_text, self.v_text = k, v, k_text, v_text
+        self.k_scale, self.v_scale = k_scale, v_scale
+        self.k_text_scale, self.v_text_scale = k_text_scale, v_text_scale
+        self.frame_capacity = k.shape[0] if k is not None else 0
+        self.text_capacity = k_text.shape[1] if k_text is not None else 0
+        self._c = None
+
+    @classmethod
+    def allocate(cls, geom, dtype, frame_capacity, text_capacity, device="cuda"):
+        H, P, D = geom.heads, geom.P, geom.head_dim
+        et = torch.bfloat16 if dtype == KV_BF16 else torch.uint8
+        kw = dict(device=device, dtype=et)
+        k = torch.empty((frame_capacity, H, P, D), **kw)
+        v = torch.empty((frame_capacity, H, D, P), **kw)
+        kt = torch.empty((H, text_capacity, D), **kw)
+        vt = torch.zeros((H, D, text_capacity), **kw)
+        sc = {}
+        if dtype == KV_FP8:
+            f32 = dict(device=device, dtype=torch.float32)
+            sc = dict(k_scale=torch.ones((frame_capacity, H), **f32),
+                      v_scale=torch.ones((frame_capacity, H), **f32),
+                      k_text_scale=torch.ones((H,), **f32), v_text_scale=torch.ones((H,), **f32))
+        return cls(dtype, k, v, kt, vt, **sc)
+
+    def c(self):
+        if self._c is None:
+            L = sa_kv_layer()
+            L.dtype, L.frame_capacity, L.text_capacity = self.dtype, self.frame_capacity, self.text_capacity
+            L.k, L.v = _ptr(self.k).value, _ptr(self.v).value
+            L.k_text, L.v_text = _ptr(self.k_text).value, _ptr(self.v_text).value
+            L.k_scale, L.v_scale = _ptr(self.k_scale).value, _ptr(self.v_scale).value
+            L.k_text_scale = _ptr(self.k_text_scale).value
+            L.v_text_scale = _ptr(self.v_text_scale).value
+            self._c = L
+        return self._c
+
+
+def abi_version():
+    return lib().sa_abi_version()
+
+
+def last_error():
+    return lib().sa_last_error().decode()
+
+
+def cache_bytes(geom, dtype, frame_capacity, text_capacity):
+    g = geom.c()
+    n = lib().sa_cache_bytes(ctypes.byref(g), dtype, frame_capacity, text_capacity)
+    if n == 0 and last_error():
+        raise SegAttnError(1, last_error())
+    return n
+
+
+def kv_append(geom, layer, k_in, v_in, frame0, n_frames, stream=None):
+    g = geom.c()
+    _check(lib().sa_kv_append(ctypes.byref(g), ctypes.byref(layer.c()), _ptr(k_in), _ptr(v_in),
+                              frame0, n_frames, _stream(stream)))
+
+
+def text_append(geom, layer, k_in, v_in, n_text, stream=None):
+    g = geom.c()
+    _check(lib().sa_text_append(ctypes.byref(g), ctypes.byref(layer.c()), _ptr(k_in), _ptr(v_in),
+                                n_text, _stream(stream)))
+
+
+def history_select(policy, t_past, budget=0, gamma=2.0, frames_per_segment=1,
+                   recent_segments=0, cap=None):
+    """Host-only selection; returns a list of frame indices (ascending)."""
+    if cap is None:
+        cap = max(t_past, 1)
+    buf = (ctypes.c_int32 * max(cap, 1))()
+    n = ctypes.c_int32(0)
+    _check(lib().sa_history_select(policy, t_past, budget, gamma, frames_per_segment,
+                                   recent_segments, buf, cap, ctypes.byref(n)))
+    return list(buf[:n.value])
+
+
+def history_gather(geom, src, d_frames, n, dst, stream=None):
+    g = geom.c()
+    _check(lib().sa_history_gather(ctypes.byref(g), ctypes.byref(src.c()), _ptr(d_frames), n,
+                                   ctypes.byref(dst.c()), _stream(stream)))
+
+
+class AttnItem:
+    """One session's attention call (sa_attn_item)."""
+
+    def __init__(self, q, layer, frames, n_frames_kv, n_text_kv, out, frame0_q, n_frames_q,
+                 n_text_q, lse=None):
+        self.q, self.layer, self.frames, self.out, self.lse = q, layer, frames, out, lse
+        self.n_frames_kv, self.n_text_kv = n_frames_kv, n_text_kv
+        self.frame0_q, self.n_frames_q, self.n_text_q = frame0_q, n_frames_q, n_text_q
+
+    def c(self):
+        it = sa_attn_item()
+        it.q = _ptr(self.q).value
+        it.frame0_q, it.n_frames_q, it.n_text_q = self.frame0_q, self.n_frames_q, self.n_text_q
+        it.kv = ctypes.pointer(self.layer.c())
+        it.frames = _ptr(self.frames).value
+        it.n_frames_kv, it.n_text_kv = self.n_frames_kv, self.n_text_kv
+        it.out = _ptr(self.out).value
+        it.lse = _ptr(self.lse).value
+        return it
+
+
+def segment_attention(geom, items, stream=None):
+    g = geom.c()
+    arr = (sa_attn_item * max(len(items), 1))()
+    for i, it in enumerate(items):
+        arr[i] = it.c()
+    _check(lib().sa_segment_attention(ctypes.byref(g), arr, len(items), _stream(stream)))
+
+
+def kv_dequant(geom, src, d_frames, n_frames, n_text, dst, stream=None):
+    g = geom.c()
+    _check(lib().sa_kv_dequant(ctypes.byref(g), ctypes.byref(src.c()), _ptr(d_frames), n_frames,
+                               n_text, ctypes.byref(dst.c()), _stream(stream)))

@@ -1,0 +1,127 @@
+// history_gather (materialising frame gather) and kv_dequant (e4m3 -> bf16).
+//
+// Source: "Hy-Nomas: an 8.6B world model whose memory is a KV cache",
+// section "The 4090 preset": before each segment the picked past frames are
+// restored from the archive to the GPU; "Hy-Nomas en una RTX 4090",
+// section "El preset de una GPU": the cache is stored in a narrow format and
+// computed in BF16.
+//
+// Both kernels are HBM-bound copies: gather moves 2 * plane_bytes per frame in
+// and out; dequant reads 1 byte and writes 2 bytes per element.
+#include "device_common.h"
+
+namespace segattn {
+namespace {
+
+constexpr int kGatherThreads = 256;
+constexpr int kChunksPerThread = 4;   // 16-byte chunks in flight per thread
+
+// grid: (chunks of a frame's plane / (256 * 4), n frames, 2 planes (K, V))
+__global__ __launch_bounds__(kGatherThreads) void gather_kernel(const GatherArgs a) {
+  const int i = blockIdx.y;
+  const int which = blockIdx.z;
+  const int frame = a.frames[i];
+  const char* src = static_cast<const char*>(which ? a.src_v : a.src_k) + frame * a.plane_bytes;
+  char* dst = static_cast<char*>(which ? a.dst_v : a.dst_k) + static_cast<int64_t>(i) * a.plane_bytes;
+  const int64_t n16 = a.plane_bytes >> 4;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kGatherThreads * kChunksPerThread;
+  u32x4 x[kChunksPerThread];
+#pragma unroll
+  for (int j = 0; j < kChunksPerThread; ++j) {
+    const int64_t c = base + threadIdx.x + j * kGatherThreads;
+    if (c < n16) x[j] = reinterpret_cast<const u32x4*>(src)[c];
+  }
+#pragma unroll
+  for (int j = 0; j < kChunksPerThread; ++j) {
+    const int64_t c = base + threadIdx.x + j * kGatherThreads;
+    if (c < n16) reinterpret_cast<u32x4*>(dst)[c] = x[j];
+  }
+  if (a.src_ks != nullptr && blockIdx.x == 0 && threadIdx.x < a.heads) {
+    const float* ss = which ? a.src_vs : a.src_ks;
+    float* ds = which ? a.dst_vs : a.dst_ks;
+    ds[static_cast<int64_t>(i) * a.heads + threadIdx.x] =
+        ss[static_cast<int64_t>(frame) * a.heads + threadIdx.x];
+  }
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t sign = (c & 0x80u) << 24;
+  const uint32_t e = (c >> 3) & 0xFu;
+  const uint32_t m = c & 0x7u;
+  float v;
+  if (e == 0) {
+    v = static_cast<float>(m) * 0.001953125f;          // m * 2^-9
+  } else if (e == 15 && m == 7) {
+    v = __uint_as_float(0x7FC00000u);
+  } else {
+    v = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) * 2^(e-7)
+  }
+  return __uint_as_float(__float_as_uint(v) | sign);
+}
+
+// grid: (ceil(n_tok * 128 / (256 * 16)), n planes (frames or 1), H * 2)
+// Each thread converts 16 consecutive bytes of one (frame, head) plane.
+__global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
+  const int i = blockIdx.y;
+  const int h = blockIdx.z >> 1;
+  const int which = blockIdx.z & 1;        // 0: K [tok][128], 1: V^T [128][tok]
+  const int frame = a.frames != nullptr ? a.frames[i] : 0;
+  const float scale = (which ? a.src_vs : a.src_ks)[static_cast<int64_t>(frame) * a.heads + h];
+  const uint8_t* src = (which ? a.src_v : a.src_k) +
+                       (static_cast<int64_t>(frame) * a.heads + h) * a.src_len * kD;
+  uint16_t* dst = (which ? a.dst_v : a.dst_k) +
+                  (static_cast<int64_t>(i) * a.heads + h) * a.dst_len * kD;
+  const int c = blockIdx.x * 256 + threadIdx.x;   // 16-element chunk index
+  int row, col, src_row_len, dst_row_len, row_valid, rows;
+  if (which == 0) {          // K: rows = tokens, 128 elements each (8 chunks)
+    rows = a.n_tok; row = c >> 3; col = (c & 7) * 16;
+    src_row_len = kD; dst_row_len = kD; row_valid = kD;
+  } else {                   // V^T: rows = dims, tokens along the row
+    const int cpr = (a.n_tok + 15) / 16;
+    rows = kD; row = c / cpr; col = (c - row * cpr) * 16;
+    src_row_len = a.src_len; dst_row_len = a.dst_len; row_valid = a.n_tok;
+  }
+  if (row >= rows) return;
+  const uint8_t* s = src + static_cast<int64_t>(row) * src_row_len + col;
+  uint16_t* d = dst + static_cast<int64_t>(row) * dst_row_len + col;
+  const int n = min(16, row_valid - col);
+  if (n == 16 && (reinterpret_cast<uintptr_t>(s) & 15) == 0) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(s);
+    u32x4 lo, hi;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t wv = x[m];
+      const uint32_t p0 = pack_bf16x2(e4m3_to_f32(wv & 0xFF) * scale, e4m3_to_f32((wv >> 8) & 0xFF) * scale);
+      const uint32_t p1 = pack_bf16x2(e4m3_to_f32((wv >> 16) & 0xFF) * scale, e4m3_to_f32(wv >> 24) * scale);
+      if (m < 2) { lo[2 * m] = p0; lo[2 * m + 1] = p1; } else { hi[2 * m - 4] = p0; hi[2 * m - 3] = p1; }
+    }
+    reinterpret_cast<u32x4*>(d)[0] = lo;
+    reinterpret_cast<u32x4*>(d)[1] = hi;
+  } else {
+    for (int j = 0; j < n; ++j) {
+      const float v = e4m3_to_f32(s[j]) * scale;
+      d[j] = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xFFFFu);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
+  const int64_t n16 = a.plane_bytes >> 4;
+  const int64_t per_block = kGatherThreads * kChunksPerThread;
+  dim3 grid(static_cast<unsigned>((n16 + per_block - 1) / per_block), a.n, 2);
+  hipLaunchKernelGGL(gather_kernel, grid, dim3(kGatherThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {
+  const int chunks_k = a.n_tok * (kD / 16);
+  const int chunks_v = kD * ((a.n_tok + 15) / 16);
+  const int chunks = chunks_k > chunks_v ? chunks_k : chunks_v;
+  dim3 grid((chunks + 255) / 256, a.n, a.heads * 2);
+  hipLaunchKernelGGL(dequant_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace segattn

@@ -1,0 +1,430 @@
+// Host side of the C ABI: argument validation, launch configuration and the
+// host-only history selection. Every entry point validates before any HIP
+// call and reports failures through a status code plus a thread-local message.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+using namespace segattn;
+
+namespace {
+
+thread_local std::string g_err;
+
+sa_status fail(sa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+sa_status ok() {
+  g_err.clear();
+  return SA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+sa_status check_geom(const sa_geom* g) {
+  if (g == nullptr) return fail(SA_E_ARG, "geom is NULL");
+  if (g->head_dim != SA_HEAD_DIM)
+    return fail(SA_E_SHAPE, "head_dim %d unsupported (only %d)", g->head_dim, SA_HEAD_DIM);
+  if (g->heads < 1 || g->heads > 1024) return fail(SA_E_SHAPE, "heads %d out of range", g->heads);
+  if (g->lat_h < 1 || g->lat_w < 1) return fail(SA_E_SHAPE, "latent grid %dx%d", g->lat_h, g->lat_w);
+  const int64_t P = static_cast<int64_t>(g->lat_h) * g->lat_w;
+  if (P % 8 != 0 || P > (1 << 20))
+    return fail(SA_E_SHAPE, "tokens per frame P=%lld must be a multiple of 8 (and <= 2^20)",
+                static_cast<long long>(P));
+  int sum = 0;
+  for (int i = 0; i < 3; ++i) {
+    if (g->rope_split[i] < 0 || g->rope_split[i] % 2 != 0)
+      return fail(SA_E_SHAPE, "rope_split[%d]=%d must be even and >= 0", i, g->rope_split[i]);
+    sum += g->rope_split[i];
+  }
+  if (sum != g->head_dim) return fail(SA_E_SHAPE, "rope_split sums to %d, not head_dim", sum);
+  if (!(g->rope_theta > 1.0f) || !std::isfinite(g->rope_theta))
+    return fail(SA_E_SHAPE, "rope_theta must be finite and > 1");
+  if (!(g->softmax_scale >= 0.0f) || !std::isfinite(g->softmax_scale))
+    return fail(SA_E_SHAPE, "softmax_scale must be finite and >= 0");
+  return SA_OK;
+}
+
+int32_t tokens_per_frame(const sa_geom* g) { return g->lat_h * g->lat_w; }
+
+sa_status check_layer(const sa_geom* g, const sa_kv_layer* L, const char* name) {
+  if (L == nullptr) return fail(SA_E_ARG, "%s layer is NULL", name);
+  if (L->dtype != SA_KV_BF16 && L->dtype != SA_KV_FP8_E4M3)
+    return fail(SA_E_UNSUPPORTED, "%s: unknown dtype %d", name, L->dtype);
+  if (L->frame_capacity < 0 || L->text_capacity < 0)
+    return fail(SA_E_ARG, "%s: negative capacity", name);
+  if (L->text_capacity % 16 != 0)
+    return fail(SA_E_SHAPE, "%s: text_capacity %d must be a multiple of 16", name, L->text_capacity);
+  if (L->dtype == SA_KV_FP8_E4M3 && tokens_per_frame(g) % 16 != 0)
+    return fail(SA_E_SHAPE, "%s: fp8 planes need P %% 16 == 0 (P=%d)", name, tokens_per_frame(g));
+  if (L->frame_capacity > 0) {
+    if (L->k == nullptr || L->v == nullptr) return fail(SA_E_ARG, "%s: k/v plane is NULL", name);
+    if (!aligned16(L->k) || !aligned16(L->v)) return fail(SA_E_ALIGN, "%s: k/v not 16-byte aligned", name);
+    if (L->dtype == SA_KV_FP8_E4M3 && (L->k_scale == nullptr || L->v_scale == nullptr))
+      return fail(SA_E_ARG, "%s: fp8 layer needs k_scale and v_scale", name);
+  }
+  if (L->text_capacity > 0) {
+    if (L->k_text == nullptr || L->v_text == nullptr)
+      return fail(SA_E_ARG, "%s: text slot pointers are NULL", name);
+    if (!aligned16(L->k_text) || !aligned16(L->v_text))
+      return fail(SA_E_ALIGN, "%s: text slot not 16-byte aligned", name);
+    if (L->dtype == SA_KV_FP8_E4M3 && (L->k_text_scale == nullptr || L->v_text_scale == nullptr))
+      return fail(SA_E_ARG, "%s: fp8 text slot needs scales", name);
+  }
+  return SA_OK;
+}
+
+RopeParams rope_params(const sa_geom* g) {
+  RopeParams r;
+  r.split0 = g->rope_split[0];
+  r.split1 = g->rope_split[1];
+  r.split2 = g->rope_split[2];
+  r.lat_w = g->lat_w;
+  r.P = tokens_per_frame(g);
+  r.log2_theta = std::log2(static_cast<double>(g->rope_theta));
+  return r;
+}
+
+sa_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sa_abi_version(void) { return SA_ABI_VERSION; }
+
+const char* sa_last_error(void) { return g_err.c_str(); }
+
+const char* sa_status_string(int status) {
+  switch (status) {
+    case SA_OK: return "SA_OK";
+    case SA_E_ARG: return "SA_E_ARG";
+    case SA_E_SHAPE: return "SA_E_SHAPE";
+    case SA_E_ALIGN: return "SA_E_ALIGN";
+    case SA_E_UNSUPPORTED: return "SA_E_UNSUPPORTED";
+    case SA_E_RANGE: return "SA_E_RANGE";
+    case SA_E_CAPACITY: return "SA_E_CAPACITY";
+    case SA_E_HIP: return "SA_E_HIP";
+    default: return "unknown status";
+  }
+}
+
+size_t sa_cache_bytes(const sa_geom* geom, int32_t dtype, int32_t frame_capacity,
+                      int32_t text_capacity) {
+  if (check_geom(geom) != SA_OK) return 0;
+  if (dtype != SA_KV_BF16 && dtype != SA_KV_FP8_E4M3) {
+    fail(SA_E_UNSUPPORTED, "unknown dtype %d", dtype);
+    return 0;
+  }
+  if (frame_capacity < 0 || text_capacity < 0) {
+    fail(SA_E_ARG, "negative capacity");
+    return 0;
+  }
+  const size_t H = geom->heads, D = geom->head_dim, P = tokens_per_frame(geom);
+  const size_t elems = 2 * H * D * (static_cast<size_t>(frame_capacity) * P + text_capacity);
+  ok();
+  if (dtype == SA_KV_BF16) return 2 * elems;
+  return elems + 2 * sizeof(float) * H * (static_cast<size_t>(frame_capacity) + 1);
+}
+
+sa_status sa_kv_append(const sa_geom* geom, const sa_kv_layer* layer, const void* k_in,
+                       const void* v_in, int32_t frame0, int32_t n_frames, void* stream) {
+  sa_status st = check_geom(geom);
+  if (st != SA_OK) return st;
+  if ((st = check_layer(geom, layer, "kv_append")) != SA_OK) return st;
+  if (n_frames < 0) return fail(SA_E_ARG, "n_frames %d < 0", n_frames);
+  if (frame0 < 0 || static_cast<int64_t>(frame0) + n_frames > layer->frame_capacity)
+    return fail(SA_E_RANGE, "frames [%d, %lld) outside capacity %d", frame0,
+                static_cast<long long>(frame0) + n_frames, layer->frame_capacity);
+  if (n_frames == 0) return ok();
+  if (k_in == nullptr || v_in == nullptr) return fail(SA_E_ARG, "k_in/v_in is NULL");
+  if (!aligned16(k_in) || !aligned16(v_in)) return fail(SA_E_ALIGN, "k_in/v_in not 16-byte aligned");
+  AppendArgs a{};
+  a.k_in = static_cast<const uint16_t*>(k_in);
+  a.v_in = static_cast<const uint16_t*>(v_in);
+  a.k = layer->k;
+  a.v = layer->v;
+  a.k_scale = layer->k_scale;
+  a.v_scale = layer->v_scale;
+  a.heads = geom->heads;
+  a.frame0 = frame0;
+  a.n_frames = n_frames;
+  a.plane_len = tokens_per_frame(geom);
+  a.n_tok = a.plane_len;
+  a.is_text = 0;
+  a.rope = rope_params(geom);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = layer->dtype == SA_KV_BF16 ? launch_append_bf16(a, s) : launch_append_fp8(a, s);
+  return hip_status(e, "kv_append launch");
+}
+
+sa_status sa_text_append(const sa_geom* geom, const sa_kv_layer* layer, const void* k_in,
+                         const void* v_in, int32_t n_text, void* stream) {
+  sa_status st = check_geom(geom);
+  if (st != SA_OK) return st;
+  if ((st = check_layer(geom, layer, "text_append")) != SA_OK) return st;
+  if (n_text < 0) return fail(SA_E_ARG, "n_text %d < 0", n_text);
+  if (n_text > layer->text_capacity)
+    return fail(SA_E_CAPACITY, "n_text %d > text_capacity %d", n_text, layer->text_capacity);
+  if (layer->text_capacity == 0) return ok();
+  if (n_text > 0 && (k_in == nullptr || v_in == nullptr)) return fail(SA_E_ARG, "k_in/v_in is NULL");
+  if (n_text > 0 && (!aligned16(k_in) || !aligned16(v_in)))
+    return fail(SA_E_ALIGN, "k_in/v_in not 16-byte aligned");
+  AppendArgs a{};
+  a.k_in = static_cast<const uint16_t*>(k_in);
+  a.v_in = static_cast<const uint16_t*>(v_in);
+  a.k = layer->k_text;
+  a.v = layer->v_text;
+  a.k_scale = layer->k_text_scale;
+  a.v_scale = layer->v_text_scale;
+  a.heads = geom->heads;
+  a.frame0 = 0;
+  a.n_frames = 1;
+  a.plane_len = layer->text_capacity;
+  a.n_tok = n_text;
+  a.is_text = 1;
+  a.rope = rope_params(geom);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = layer->dtype == SA_KV_BF16 ? launch_append_bf16(a, s) : launch_append_fp8(a, s);
+  return hip_status(e, "text_append launch");
+}
+
+sa_status sa_history_select(int32_t policy, int32_t t_past, int32_t budget, double gamma,
+                            int32_t frames_per_segment, int32_t recent_segments,
+                            int32_t* out_frames, int32_t cap, int32_t* out_n) {
+  if (out_n == nullptr) return fail(SA_E_ARG, "out_n is NULL");
+  *out_n = 0;
+  if (t_past < 0) return fail(SA_E_ARG, "t_past %d < 0", t_past);
+  if (cap < 0 || (cap > 0 && out_frames == nullptr)) return fail(SA_E_ARG, "bad output buffer");
+  std::vector<int32_t> sel;
+  switch (policy) {
+    case SA_SEL_ALL:
+      for (int32_t f = 0; f < t_past; ++f) sel.push_back(f);
+      break;
+    case SA_SEL_RECENT: {
+      if (budget < 0) return fail(SA_E_ARG, "budget %d < 0", budget);
+      const int32_t n = budget < t_past ? budget : t_past;
+      for (int32_t f = t_past - n; f < t_past; ++f) sel.push_back(f);
+      break;
+    }
+    case SA_SEL_POWER: {
+      if (budget < 0) return fail(SA_E_ARG, "budget %d < 0", budget);
+      if (!(gamma > 0.0) || !std::isfinite(gamma)) return fail(SA_E_ARG, "gamma must be > 0");
+      const int32_t N = budget < t_past ? budget : t_past;
+      if (N == t_past) {
+        for (int32_t f = 0; f < t_past; ++f) sel.push_back(f);
+      } else if (N == 1) {
+        sel.push_back(t_past - 1);
+      } else if (N > 1) {
+        // d_i = i + rint((T - N) * u_i^gamma), u_i = i / (N - 1); kept = T - 1 - d_i
+        for (int32_t i = 0; i < N; ++i) {
+          const double u = static_cast<double>(i) / static_cast<double>(N - 1);
+          const double d = static_cast<double>(i) +
+                           std::rint(static_cast<double>(t_past - N) * std::pow(u, gamma));
+          sel.push_back(t_past - 1 - static_cast<int32_t>(d));
+        }
+        std::vector<int32_t> sorted(sel.rbegin(), sel.rend());
+        sel.swap(sorted);
+      }
+      break;
+    }
+    case SA_SEL_ANCHOR_RECENT: {
+      if (frames_per_segment < 1) return fail(SA_E_ARG, "frames_per_segment must be >= 1");
+      if (recent_segments < 0) return fail(SA_E_ARG, "recent_segments < 0");
+      const int64_t F = frames_per_segment;
+      const int64_t n_seg = (t_past + F - 1) / F;
+      const int64_t first_recent = n_seg - recent_segments > 0 ? n_seg - recent_segments : 0;
+      for (int64_t f = 0; f < t_past; ++f)
+        if (f % F == 0 || f / F >= first_recent) sel.push_back(static_cast<int32_t>(f));
+      break;
+    }
+    default:
+      return fail(SA_E_ARG, "unknown policy %d", policy);
+  }
+  if (static_cast<int64_t>(sel.size()) > cap)
+    return fail(SA_E_CAPACITY, "selection has %zu frames, buffer holds %d", sel.size(), cap);
+  if (!sel.empty()) std::memcpy(out_frames, sel.data(), sel.size() * sizeof(int32_t));
+  *out_n = static_cast<int32_t>(sel.size());
+  return ok();
+}
+
+sa_status sa_history_gather(const sa_geom* geom, const sa_kv_layer* src, const int32_t* d_frames,
+                            int32_t n, const sa_kv_layer* dst, void* stream) {
+  sa_status st = check_geom(geom);
+  if (st != SA_OK) return st;
+  if ((st = check_layer(geom, src, "gather src")) != SA_OK) return st;
+  if ((st = check_layer(geom, dst, "gather dst")) != SA_OK) return st;
+  if (src->dtype != dst->dtype) return fail(SA_E_UNSUPPORTED, "gather: src and dst dtypes differ");
+  if (n < 0) return fail(SA_E_ARG, "n %d < 0", n);
+  if (n > dst->frame_capacity)
+    return fail(SA_E_CAPACITY, "gather: %d frames > dst capacity %d", n, dst->frame_capacity);
+  if (n == 0) return ok();
+  if (d_frames == nullptr) return fail(SA_E_ARG, "frames is NULL");
+  if (src->frame_capacity == 0) return fail(SA_E_RANGE, "gather: src has no frames");
+  GatherArgs a{};
+  a.src_k = src->k;
+  a.src_v = src->v;
+  a.dst_k = dst->k;
+  a.dst_v = dst->v;
+  const int64_t elt = src->dtype == SA_KV_BF16 ? 2 : 1;
+  a.plane_bytes = elt * geom->heads * static_cast<int64_t>(tokens_per_frame(geom)) * geom->head_dim;
+  if (src->dtype == SA_KV_FP8_E4M3) {
+    a.src_ks = src->k_scale;
+    a.src_vs = src->v_scale;
+    a.dst_ks = dst->k_scale;
+    a.dst_vs = dst->v_scale;
+  }
+  a.frames = d_frames;
+  a.n = n;
+  a.heads = geom->heads;
+  if (geom->heads > 256) return fail(SA_E_SHAPE, "gather: more than 256 heads");
+  return hip_status(launch_gather(a, static_cast<hipStream_t>(stream)), "history_gather launch");
+}
+
+sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
+                               void* stream) {
+  sa_status st = check_geom(geom);
+  if (st != SA_OK) return st;
+  if (items == nullptr) return fail(SA_E_ARG, "items is NULL");
+  if (n_items < 1 || n_items > SA_MAX_ITEMS)
+    return fail(SA_E_ARG, "n_items %d outside [1, %d]", n_items, SA_MAX_ITEMS);
+  const int32_t P = tokens_per_frame(geom);
+  int32_t dtype = -1;
+  for (int i = 0; i < n_items; ++i) {
+    const sa_attn_item& it = items[i];
+    if ((st = check_layer(geom, it.kv, "attention kv")) != SA_OK) return st;
+    if (dtype == -1) dtype = it.kv->dtype;
+    if (it.kv->dtype != dtype) return fail(SA_E_UNSUPPORTED, "items mix cache dtypes");
+    if (it.n_frames_q < 0 || it.n_text_q < 0) return fail(SA_E_ARG, "item %d: negative query counts", i);
+    if (it.frame0_q < 0) return fail(SA_E_ARG, "item %d: frame0_q < 0", i);
+    if (it.n_frames_kv < 0 || it.n_text_kv < 0) return fail(SA_E_ARG, "item %d: negative key counts", i);
+    if (it.n_frames_kv > SA_MAX_FRAMES_KV)
+      return fail(SA_E_RANGE, "item %d: n_frames_kv %d > %d", i, it.n_frames_kv, SA_MAX_FRAMES_KV);
+    if (it.n_frames_kv > 0 && it.kv->frame_capacity == 0)
+      return fail(SA_E_RANGE, "item %d: frames given but the layer has no frame planes", i);
+    if (it.n_text_kv > it.kv->text_capacity)
+      return fail(SA_E_RANGE, "item %d: n_text_kv %d > text_capacity %d", i, it.n_text_kv,
+                  it.kv->text_capacity);
+    const int64_t lk = static_cast<int64_t>(it.n_frames_kv) * P + it.n_text_kv;
+    if (lk < 1) return fail(SA_E_ARG, "item %d: empty key set", i);
+    if (it.n_frames_kv > 0 && it.frames == nullptr) return fail(SA_E_ARG, "item %d: frames is NULL", i);
+    const int64_t rows = static_cast<int64_t>(it.n_frames_q) * P + it.n_text_q;
+    if (rows > (int64_t(1) << 30)) return fail(SA_E_SHAPE, "item %d: too many query rows", i);
+    if (rows > 0) {
+      if (it.q == nullptr || it.out == nullptr) return fail(SA_E_ARG, "item %d: q/out is NULL", i);
+      if (!aligned16(it.q) || !aligned16(it.out)) return fail(SA_E_ALIGN, "item %d: q/out not aligned", i);
+    }
+  }
+  if (dtype != SA_KV_BF16)
+    return fail(SA_E_UNSUPPORTED, "segment_attention: fp8 cache path is not built yet");
+  AttnArgs a{};
+  const int bm = attention_block_m_bf16();
+  int64_t tiles = 0;
+  for (int i = 0; i < n_items; ++i) {
+    const sa_attn_item& it = items[i];
+    AttnItemDev& d = a.items[i];
+    d.q = static_cast<const uint16_t*>(it.q);
+    d.out = static_cast<uint16_t*>(it.out);
+    d.lse = it.lse;
+    d.k = it.kv->k;
+    d.v = it.kv->v;
+    d.k_text = it.kv->k_text;
+    d.v_text = it.kv->v_text;
+    d.k_scale = it.kv->k_scale;
+    d.v_scale = it.kv->v_scale;
+    d.k_text_scale = it.kv->k_text_scale;
+    d.v_text_scale = it.kv->v_text_scale;
+    d.frames = it.frames;
+    d.frame0_q = it.frame0_q;
+    d.n_q_video = it.n_frames_q * P;
+    d.n_q = d.n_q_video + it.n_text_q;
+    d.n_frames_kv = it.n_frames_kv;
+    d.n_text_kv = it.n_text_kv;
+    d.text_cap = it.kv->text_capacity;
+    d.q_tiles = (d.n_q + bm - 1) / bm;
+    d.tile_begin = static_cast<int32_t>(tiles);
+    tiles += static_cast<int64_t>(d.q_tiles) * geom->heads;
+  }
+  if (tiles == 0) return ok();
+  if (tiles > (int64_t(1) << 31) - 1) return fail(SA_E_SHAPE, "too many tiles");
+  a.n_items = n_items;
+  a.heads = geom->heads;
+  a.total_tiles = static_cast<int32_t>(tiles);
+  const double scale = geom->softmax_scale > 0.f ? geom->softmax_scale : 1.0 / std::sqrt(128.0);
+  a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
+  a.rope = rope_params(geom);
+  // items with no query rows own no tiles; point them past the end
+  for (int i = n_items; i < SA_MAX_ITEMS; ++i) a.items[i].tile_begin = a.total_tiles;
+  return hip_status(launch_attention_bf16(a, static_cast<hipStream_t>(stream)),
+                    "segment_attention launch");
+}
+
+sa_status sa_kv_dequant(const sa_geom* geom, const sa_kv_layer* src, const int32_t* d_frames,
+                        int32_t n_frames, int32_t n_text, const sa_kv_layer* dst, void* stream) {
+  sa_status st = check_geom(geom);
+  if (st != SA_OK) return st;
+  if ((st = check_layer(geom, src, "dequant src")) != SA_OK) return st;
+  if ((st = check_layer(geom, dst, "dequant dst")) != SA_OK) return st;
+  if (src->dtype != SA_KV_FP8_E4M3) return fail(SA_E_UNSUPPORTED, "dequant: src must be fp8");
+  if (dst->dtype != SA_KV_BF16) return fail(SA_E_UNSUPPORTED, "dequant: dst must be bf16");
+  if (n_frames < 0 || n_text < 0) return fail(SA_E_ARG, "negative counts");
+  if (n_frames > dst->frame_capacity)
+    return fail(SA_E_CAPACITY, "dequant: %d frames > dst capacity %d", n_frames, dst->frame_capacity);
+  if (n_text > src->text_capacity || n_text > dst->text_capacity)
+    return fail(SA_E_CAPACITY, "dequant: n_text %d exceeds a text capacity", n_text);
+  if (n_frames > 0 && d_frames == nullptr) return fail(SA_E_ARG, "frames is NULL");
+  if (n_frames > 0 && src->frame_capacity == 0) return fail(SA_E_RANGE, "dequant: src has no frames");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_frames > 0) {
+    DequantArgs a{};
+    a.src_k = static_cast<const uint8_t*>(src->k);
+    a.src_v = static_cast<const uint8_t*>(src->v);
+    a.src_ks = src->k_scale;
+    a.src_vs = src->v_scale;
+    a.dst_k = static_cast<uint16_t*>(dst->k);
+    a.dst_v = static_cast<uint16_t*>(dst->v);
+    a.frames = d_frames;
+    a.n = n_frames;
+    a.heads = geom->heads;
+    a.src_len = a.dst_len = a.n_tok = tokens_per_frame(geom);
+    if ((st = hip_status(launch_dequant(a, s), "kv_dequant launch")) != SA_OK) return st;
+  }
+  if (n_text > 0) {
+    DequantArgs a{};
+    a.src_k = static_cast<const uint8_t*>(src->k_text);
+    a.src_v = static_cast<const uint8_t*>(src->v_text);
+    a.src_ks = src->k_text_scale;
+    a.src_vs = src->v_text_scale;
+    a.dst_k = static_cast<uint16_t*>(dst->k_text);
+    a.dst_v = static_cast<uint16_t*>(dst->v_text);
+    a.frames = nullptr;
+    a.n = 1;
+    a.heads = geom->heads;
+    a.src_len = src->text_capacity;
+    a.dst_len = dst->text_capacity;
+    a.n_tok = n_text;
+    if ((st = hip_status(launch_dequant(a, s), "kv_dequant text launch")) != SA_OK) return st;
+  }
+  return ok();
+}
+
+}  // extern "C"

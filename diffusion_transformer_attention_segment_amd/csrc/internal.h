@@ -1,0 +1,113 @@
+// Internal declarations shared by the host layer and the HIP kernel files.
+// Not part of the public ABI (include/segattn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/segattn.h"
+
+namespace segattn {
+
+constexpr int kD = SA_HEAD_DIM;   // head dim (128)
+
+// Per-call RoPE description shared by the append and attention kernels.
+struct RopeParams {
+  int32_t split0, split1, split2;  // t, h, w band widths (even, sum 128)
+  int32_t lat_w;                   // tokens per latent row
+  int32_t P;                       // tokens per latent frame
+  double log2_theta;               // log2(theta), for the fp64 frequencies
+};
+
+// ---- kv_append / text_append ------------------------------------------------
+struct AppendArgs {
+  const uint16_t* k_in;     // bf16 [n_tokens][H][128]
+  const uint16_t* v_in;
+  void* k;                  // plane base (frame 0 / text slot base)
+  void* v;
+  float* k_scale;           // fp8: [frames][H] or [H] for text
+  float* v_scale;
+  int32_t heads;
+  int32_t frame0;           // first frame written (video); unused for text
+  int32_t n_frames;         // video frames (video) / 1 (text)
+  int32_t plane_len;        // P for video, text_capacity for text
+  int32_t n_tok;            // valid tokens per plane (P for video, n_text)
+  int32_t is_text;          // 1: text slot (no rotation, zero-fill V tail)
+  RopeParams rope;
+};
+
+hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s);
+hipError_t launch_append_fp8(const AppendArgs& a, hipStream_t s);
+
+// ---- attention ----------------------------------------------------------------
+struct AttnItemDev {
+  const uint16_t* q;
+  uint16_t* out;
+  float* lse;
+  const void* k;
+  const void* v;
+  const void* k_text;
+  const void* v_text;
+  const float* k_scale;
+  const float* v_scale;
+  const float* k_text_scale;
+  const float* v_text_scale;
+  const int32_t* frames;
+  int32_t frame0_q;
+  int32_t n_q_video;     // video query rows
+  int32_t n_q;           // all query rows (video + text)
+  int32_t n_frames_kv;
+  int32_t n_text_kv;
+  int32_t text_cap;
+  int32_t q_tiles;       // ceil(n_q / BLOCK_M)
+  int32_t tile_begin;    // first logical tile of this item (over heads * q_tiles)
+};
+
+struct AttnArgs {
+  AttnItemDev items[SA_MAX_ITEMS];
+  int32_t n_items;
+  int32_t heads;
+  int32_t total_tiles;
+  float scale_log2;       // softmax scale * log2(e)
+  RopeParams rope;
+};
+
+hipError_t launch_attention_bf16(AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_fp8(AttnArgs& a, hipStream_t s);
+int attention_block_m_bf16();
+int attention_block_m_fp8();
+
+// ---- gather / dequant -----------------------------------------------------------
+struct GatherArgs {
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
+  const float* src_ks;
+  const float* src_vs;
+  float* dst_ks;
+  float* dst_vs;
+  const int32_t* frames;
+  int32_t n;
+  int64_t plane_bytes;     // bytes of one frame's K (= V) plane over all heads
+  int32_t heads;
+};
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+
+struct DequantArgs {
+  const uint8_t* src_k;    // fp8 plane base
+  const uint8_t* src_v;
+  const float* src_ks;     // [frames][H] or [H]
+  const float* src_vs;
+  uint16_t* dst_k;         // bf16 plane base
+  uint16_t* dst_v;
+  const int32_t* frames;   // NULL for the text slot
+  int32_t n;               // frames (or 1 for text)
+  int32_t heads;
+  int32_t src_len;         // tokens per source plane (P or text_capacity)
+  int32_t dst_len;         // tokens per destination plane
+  int32_t n_tok;           // tokens to convert per plane
+};
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
+
+}  // namespace segattn

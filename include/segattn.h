@@ -1,0 +1,224 @@
+/*
+ * segattn.h -- C ABI of the segment-attention library (HIP, gfx950 / MI355X).
+ *
+ * What it computes. In a segment-autoregressive MMDiT world model, the joint
+ * attention of each dual-stream block takes as queries the current segment's
+ * latent video tokens followed by its text tokens, and as keys/values the
+ * per-layer KV cache of earlier segments plus the segment itself, with no mask
+ * inside the segment, 3D rotary position embedding over (t, h, w) and 16 heads
+ * of 128 dimensions.
+ *   Source: "Hy-Nomas: an 8.6B world model whose memory is a KV cache"
+ *   (ai.thesatyajit.com), sections "How one segment is made" (token grid,
+ *   heads, RoPE split [16, 56, 56] with theta 256, segment-wise causal joint
+ *   attention reading history from a KV cache), "Writing the segment into
+ *   memory" (a finished segment's K/V are written to the cache),
+ *   "What 'world memory' stores" (per-layer K/V of past video and text
+ *   tokens) and "The 4090 preset" (a power-spaced pick of past frames is
+ *   restored before each segment; the cache is stored quantised and
+ *   computed in BF16).
+ *
+ * Conventions shared by every call.
+ *  - Device pointers are raw HIP device addresses owned by the caller; the
+ *    library allocates no memory and keeps no pointer after a call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Device calls are asynchronous: buffers must stay alive until the stream
+ *    has passed the call.
+ *  - Every call validates its arguments on the host before any HIP call and
+ *    returns an sa_status; on failure nothing is launched and
+ *    sa_last_error() describes the problem (thread-local, valid until the
+ *    next sa_* call on the same thread). Launch failures return SA_E_HIP.
+ *  - Device-side index lists (frame lists) are trusted: entries must lie in
+ *    [0, frame_capacity) of the layer they index; sa_history_select only
+ *    produces such lists.
+ *  - bf16 = bfloat16 (raw 16-bit patterns); e4m3 = OCP 8-bit float e4m3fn
+ *    (bias 7, max 448, no infinities).
+ *  - Results are bitwise reproducible run to run (no atomics, fixed
+ *    reduction orders).
+ */
+#ifndef SEGATTN_H
+#define SEGATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_ABI_VERSION 1
+#define SA_HEAD_DIM 128       /* the only head dim the kernels are built for */
+#define SA_MAX_ITEMS 8        /* sessions per sa_segment_attention call     */
+#define SA_MAX_FRAMES_KV 65536
+
+typedef enum {
+  SA_OK = 0,
+  SA_E_ARG = 1,          /* null pointer, negative count, bad enum        */
+  SA_E_SHAPE = 2,        /* geometry not supported (head_dim, split, P)   */
+  SA_E_ALIGN = 3,        /* pointer not 16-byte aligned                   */
+  SA_E_UNSUPPORTED = 4,  /* dtype / feature combination not built         */
+  SA_E_RANGE = 5,        /* frame index or count outside the layer        */
+  SA_E_CAPACITY = 6,     /* output buffer too small                       */
+  SA_E_HIP = 7           /* a HIP runtime call or launch failed           */
+} sa_status;
+
+typedef enum { SA_KV_BF16 = 0, SA_KV_FP8_E4M3 = 1 } sa_kv_dtype;
+
+typedef enum {
+  SA_SEL_ALL = 0,            /* every past frame                              */
+  SA_SEL_RECENT = 1,         /* the newest `budget` frames                    */
+  SA_SEL_POWER = 2,          /* power-spaced pick ("The 4090 preset")         */
+  SA_SEL_ANCHOR_RECENT = 3   /* first frame of each segment + newest segments */
+} sa_sel_policy;
+
+/* Attention geometry, identical for every layer of a model.
+ *   heads          number of heads H (16 in the pages' model)
+ *   head_dim       must be SA_HEAD_DIM (128)
+ *   lat_h, lat_w   latent frame grid; P = lat_h * lat_w tokens per frame
+ *                  (22 x 40 = 880 in the pages' model). P % 8 == 0 is required.
+ *   rope_split     dims of the t, h, w bands; each even, sum == head_dim
+ *   rope_theta     RoPE base (> 1); band a, pair j rotates by
+ *                  pos_a * theta^(-2j / rope_split[a]); pairs are (2j, 2j+1)
+ *   softmax_scale  logit scale; 0 selects 1/sqrt(head_dim)                 */
+typedef struct sa_geom {
+  int32_t heads;
+  int32_t head_dim;
+  int32_t lat_h;
+  int32_t lat_w;
+  int32_t rope_split[3];
+  float rope_theta;
+  float softmax_scale;
+} sa_geom;
+
+/* One layer's cache planes (device memory, caller-allocated; sizes from
+ * sa_cache_bytes / the shapes below). Frames are addressed by their absolute
+ * latent-frame index since the world started, which is also their RoPE t.
+ *   k        [frame_capacity][H][P][128]         rotated keys
+ *   v        [frame_capacity][H][128][P]         values, transposed per
+ *                                                (frame, head)
+ *   k_text   [H][text_capacity][128]             text keys (no rotation)
+ *   v_text   [H][128][text_capacity]             text values, transposed
+ *   k_scale, v_scale            [frame_capacity][H] fp32, fp8 only
+ *   k_text_scale, v_text_scale  [H] fp32, fp8 only (NULL for bf16)
+ * Element type: bf16 (2 bytes) or e4m3 (1 byte) per `dtype`.
+ * text_capacity must be a multiple of 16; it may be 0 (no text slot).      */
+typedef struct sa_kv_layer {
+  int32_t dtype;
+  int32_t frame_capacity;
+  int32_t text_capacity;
+  int32_t reserved0;
+  void* k;
+  void* v;
+  float* k_scale;
+  float* v_scale;
+  void* k_text;
+  void* v_text;
+  float* k_text_scale;
+  float* v_text_scale;
+} sa_kv_layer;
+
+/* One session's attention call.
+ *   q          bf16 [n_frames_q * P + n_text_q][H][128]: raw (unrotated)
+ *              queries, video tokens in (t, h, w) raster order, then text
+ *   frame0_q   absolute frame index (RoPE t) of the first query frame
+ *   kv         that session's cache layer
+ *   frames     device int32 [n_frames_kv]: the frames whose keys are
+ *              attended, in order (kept history, then the current segment,
+ *              which must already have been appended)
+ *   n_text_kv  number of text keys taken from the layer's text slot
+ *   out        bf16, same shape as q
+ *   lse        optional fp32 [rows][H] natural-log sum of exp of the scaled
+ *              logits per row and head (NULL to skip)
+ * At least one key is required (n_frames_kv * P + n_text_kv >= 1).         */
+typedef struct sa_attn_item {
+  const void* q;
+  int32_t frame0_q;
+  int32_t n_frames_q;
+  int32_t n_text_q;
+  int32_t reserved0;
+  const sa_kv_layer* kv;
+  const int32_t* frames;
+  int32_t n_frames_kv;
+  int32_t n_text_kv;
+  void* out;
+  float* lse;
+} sa_attn_item;
+
+int sa_abi_version(void);
+const char* sa_last_error(void);
+const char* sa_status_string(int status);
+
+/* Bytes of one layer's cache planes in this layout (K + V planes, text slot,
+ * and for fp8 the fp32 scales). Returns 0 and sets the error on bad input.  */
+size_t sa_cache_bytes(const sa_geom* geom, int32_t dtype, int32_t frame_capacity,
+                      int32_t text_capacity);
+
+/* kv_append: write frames [frame0, frame0 + n_frames) of one segment into the
+ * layer. k_in, v_in: bf16 [n_frames * P][H][128], raw projections in raster
+ * order. K is rotated by the 3D RoPE at (frame, row, column) in fp32 with an
+ * fp64-reduced angle, then rounded to the cache type; V is stored unrotated
+ * and transposed. fp8: per (frame, head) plane, scale = amax / 448 (fp32),
+ * code = round-nearest-even(x * (448 / amax)) saturated; amax 0 gives scale
+ * 1. Source: "Writing the segment into memory" and "How one segment is made"
+ * (RoPE). Errors: SA_E_RANGE if frame0 < 0 or frame0 + n_frames >
+ * frame_capacity.                                                           */
+sa_status sa_kv_append(const sa_geom* geom, const sa_kv_layer* layer, const void* k_in,
+                       const void* v_in, int32_t frame0, int32_t n_frames, void* stream);
+
+/* text_append: write n_text text tokens into the layer's text slot (no
+ * rotation: text sits at position (0,0,0)). k_in, v_in: bf16 [n_text][H][128].
+ * fp8: one scale per head over the n_text tokens. Slots [n_text, capacity)
+ * of the value plane are zeroed so that a partial last key chunk reads finite
+ * values. Errors: SA_E_CAPACITY if n_text > text_capacity.                  */
+sa_status sa_text_append(const sa_geom* geom, const sa_kv_layer* layer, const void* k_in,
+                         const void* v_in, int32_t n_text, void* stream);
+
+/* history_select (host only, pure): the kept past frames for a history of
+ * t_past latent frames, sorted ascending, written to out_frames[0..*out_n).
+ *   SA_SEL_ALL            every frame (budget, gamma ignored)
+ *   SA_SEL_RECENT         the newest min(budget, t_past) frames
+ *   SA_SEL_POWER          N = min(budget, t_past); kept = t_past-1-d_i with
+ *                         d_i = i + rint((t_past-N) * (i/(N-1))^gamma)
+ *                         ("The 4090 preset"); N == t_past keeps all, N == 1
+ *                         keeps the newest
+ *   SA_SEL_ANCHOR_RECENT  frame s*F of every F-frame segment plus all frames
+ *                         of the newest `recent_segments` segments
+ *                         (F = frames_per_segment)
+ * Errors: SA_E_CAPACITY if the result does not fit in cap entries.         */
+sa_status sa_history_select(int32_t policy, int32_t t_past, int32_t budget, double gamma,
+                            int32_t frames_per_segment, int32_t recent_segments,
+                            int32_t* out_frames, int32_t cap, int32_t* out_n);
+
+/* history_gather: materialise frames[i] of src into frame slot i of dst
+ * (i < n), K and V planes and, for fp8, their scales; a byte copy. dst must
+ * have the same dtype and frame_capacity >= n. d_frames is a device array.
+ * This is the pages' "restore the picked frames" step for callers that want
+ * a compact buffer; sa_segment_attention reads through a frame list instead. */
+sa_status sa_history_gather(const sa_geom* geom, const sa_kv_layer* src, const int32_t* d_frames,
+                            int32_t n, const sa_kv_layer* dst, void* stream);
+
+/* segment_attention: for every item, head and query row,
+ *   out = softmax(scale * rope(q) . K^T) V over the item's key set
+ * (frames list in order, then n_text_kv text keys), fp32 accumulation, bf16
+ * output. bf16 layers use bf16 MFMA; fp8 layers use fp8 MFMA with queries
+ * quantised per (row, head) and the per-(frame, head) scales applied to the
+ * logits and folded into the probabilities. All items must share one dtype.
+ * Source: "How one segment is made" and "What 'world memory' stores".
+ * Errors: SA_E_ARG (n_items outside [1, SA_MAX_ITEMS], empty key set),
+ * SA_E_RANGE (n_frames_kv > SA_MAX_FRAMES_KV, n_text_kv > text_capacity).   */
+sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
+                               void* stream);
+
+/* kv_dequant: fp8 frames[i] of src -> bf16 frame slot i of dst (K and V
+ * planes: value = code * scale, rounded to bf16), and, when n_text > 0, the
+ * first n_text tokens of the text slot. The pages' "stored low precision,
+ * computed in BF16" route ("El preset de una GPU", inferencekey.com).
+ * dst must be a bf16 layer with frame_capacity >= n_frames and
+ * text_capacity >= n_text.                                                  */
+sa_status sa_kv_dequant(const sa_geom* geom, const sa_kv_layer* src, const int32_t* d_frames,
+                        int32_t n_frames, int32_t n_text, const sa_kv_layer* dst, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEGATTN_H */

@@ -1,0 +1,200 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, validates arguments before any HIP call, and its host-only
+history selection agrees bit-exactly with the oracle.
+
+No call here reaches a kernel launch: every case either runs host-only code
+(history_select, cache_bytes) or fails validation first.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import diffusion_transformer_attention_segment_amd as sa
+from diffusion_transformer_attention_segment_amd import binding as B
+from oracle import cache as ocache
+from oracle import select as osel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "segattn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sa.LIB_PATH):
+        from diffusion_transformer_attention_segment_amd import build
+        build.build()
+    return sa.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(B.SIGNATURES) == declared
+
+
+def test_abi_version(lib):
+    assert sa.abi_version() == 1
+
+
+def test_status_strings(lib):
+    assert lib.sa_status_string(0) == b"SA_OK"
+    assert lib.sa_status_string(7) == b"SA_E_HIP"
+
+
+@pytest.mark.parametrize("policy", ["all", "recent", "power", "anchor"])
+def test_history_select_matches_oracle(lib, policy):
+    for T in range(0, 400, 7):
+        for budget in (1, 2, 3, 7, 18, 40):
+            if policy == "all":
+                got = sa.history_select(sa.SEL_ALL, T)
+                want = osel.select_all(T)
+            elif policy == "recent":
+                got = sa.history_select(sa.SEL_RECENT, T, budget)
+                want = osel.select_recent(T, budget)
+            elif policy == "power":
+                got = sa.history_select(sa.SEL_POWER, T, budget, 2.0)
+                want = osel.select_power(T, budget, 2.0)
+            else:
+                got = sa.history_select(sa.SEL_ANCHOR_RECENT, T, 0, 2.0, frames_per_segment=budget,
+                                        recent_segments=3)
+                want = osel.select_anchor_recent(T, budget, 3)
+            assert got == want.tolist(), (policy, T, budget)
+
+
+def test_history_select_power_printed_example(lib):
+    got = sa.history_select(sa.SEL_POWER, 360, 18, 2.0)
+    assert got == [0, 40, 78, 113, 146, 177, 205, 231, 254, 275, 294, 310, 324, 336, 345, 352,
+                   357, 359]
+
+
+def test_history_select_power_other_gamma(lib):
+    for T in (50, 100, 361):
+        for g in (1.0, 1.5, 3.0):
+            assert sa.history_select(sa.SEL_POWER, T, 10, g) == osel.select_power(T, 10, g).tolist()
+
+
+def test_history_select_errors(lib):
+    with pytest.raises(sa.SegAttnError) as e:
+        sa.history_select(sa.SEL_ALL, 10, cap=5)
+    assert e.value.status == 6
+    with pytest.raises(sa.SegAttnError) as e:
+        sa.history_select(99, 10)
+    assert e.value.status == 1
+    with pytest.raises(sa.SegAttnError):
+        sa.history_select(sa.SEL_ALL, -1)
+
+
+def test_cache_bytes_matches_oracle(lib):
+    g = sa.Geom()
+    for dt, name in ((sa.KV_BF16, "bf16"), (sa.KV_FP8, "fp8")):
+        for fc, tc in ((60, 256), (390, 256), (0, 16), (1, 0)):
+            assert sa.cache_bytes(g, dt, fc, tc) == ocache.plane_bytes(name, 16, 128, 880, fc, tc)
+    # the page's figure: 8,192 bytes per token per layer in bf16
+    assert sa.cache_bytes(g, sa.KV_BF16, 1, 0) == 880 * 8192
+
+
+# --------------------------------------------------------------- validation
+FAKE = 0x100000     # never dereferenced: validation must fail before any launch
+
+
+def _layer(dtype=0, fc=4, tc=16, k=FAKE, v=FAKE, kt=FAKE, vt=FAKE, ks=FAKE, vs=FAKE):
+    L = B.sa_kv_layer()
+    L.dtype, L.frame_capacity, L.text_capacity = dtype, fc, tc
+    L.k, L.v, L.k_text, L.v_text = k, v, kt, vt
+    L.k_scale, L.v_scale, L.k_text_scale, L.v_text_scale = ks, vs, ks, vs
+    return L
+
+
+def _geom(**kw):
+    g = sa.Geom(heads=2, lat_h=4, lat_w=6)
+    for k, v in kw.items():
+        setattr(g, k, v)
+    return g.c()
+
+
+def _append(g, L, k=FAKE, v=FAKE, f0=0, n=1):
+    return sa.lib().sa_kv_append(ctypes.byref(g), ctypes.byref(L), ctypes.c_void_p(k),
+                                 ctypes.c_void_p(v), f0, n, None)
+
+
+def test_validation_errors(lib):
+    assert _append(_geom(head_dim=64), _layer()) == 2
+    assert _append(_geom(rope_split=(16, 56, 54)), _layer()) == 2
+    assert _append(_geom(rope_split=(15, 57, 56)), _layer()) == 2
+    assert _append(_geom(lat_w=5), _layer()) == 2                 # P = 20 not a multiple of 8
+    assert _append(_geom(rope_theta=1.0), _layer()) == 2
+    assert _append(_geom(), _layer(dtype=5)) == 4
+    assert _append(_geom(), _layer(k=0)) == 1
+    assert _append(_geom(), _layer(k=FAKE + 4)) == 3
+    assert _append(_geom(), _layer(tc=8)) == 2                    # text capacity % 16
+    assert _append(_geom(), _layer(dtype=1)) == 2                 # fp8 needs P % 16 (P=24)
+    assert _append(_geom(), _layer(), f0=3, n=2) == 5             # frames 3..4 > capacity 4
+    assert _append(_geom(), _layer(), f0=-1) == 5
+    assert _append(_geom(), _layer(), k=FAKE + 2) == 3
+    assert _append(_geom(), _layer(), n=-1) == 1
+    assert b"n_frames" in lib.sa_last_error()
+    # the message is cleared by the next successful call
+    assert _append(_geom(), _layer(), n=0) == 0
+    assert lib.sa_last_error() == b""
+    g = _geom()
+    assert lib.sa_text_append(ctypes.byref(g), ctypes.byref(_layer()), ctypes.c_void_p(FAKE),
+                              ctypes.c_void_p(FAKE), 17, None) == 6
+    assert lib.sa_kv_append(None, ctypes.byref(_layer()), None, None, 0, 1, None) == 1
+
+
+def _item(L, rows=True, n_frames_kv=2, n_text_kv=3, frames=FAKE):
+    it = B.sa_attn_item()
+    it.q, it.out = FAKE, FAKE
+    it.frame0_q, it.n_frames_q, it.n_text_q = 0, 1 if rows else 0, 0
+    it.kv = ctypes.pointer(L)
+    it.frames = frames
+    it.n_frames_kv, it.n_text_kv = n_frames_kv, n_text_kv
+    return it
+
+
+def _attn(items, n=None):
+    g = _geom()
+    arr = (B.sa_attn_item * max(len(items), 1))(*items)
+    return sa.lib().sa_segment_attention(ctypes.byref(g), arr, len(items) if n is None else n, None)
+
+
+def test_attention_validation(lib):
+    L = _layer()
+    assert _attn([_item(L)], n=0) == 1
+    assert _attn([_item(L)] * 9) == 1
+    assert _attn([_item(L, n_frames_kv=0, n_text_kv=0)]) == 1     # empty key set
+    assert _attn([_item(L, n_text_kv=17)]) == 5                   # > text capacity 16
+    assert _attn([_item(L, frames=0)]) == 1
+    assert _attn([_item(L, n_frames_kv=70000)]) == 5
+    L8 = _layer(dtype=1)
+    assert _attn([_item(L), _item(L8)]) in (2, 4)                 # mixed dtypes / fp8 P=24
+    bad = _item(L)
+    bad.q = FAKE + 8
+    assert _attn([bad]) == 3
+
+
+def test_gather_and_dequant_validation(lib):
+    g = _geom()
+    src, dst = _layer(), _layer(fc=2)
+    f = lib.sa_history_gather
+    assert f(ctypes.byref(g), ctypes.byref(src), ctypes.c_void_p(FAKE), 3, ctypes.byref(dst), None) == 6
+    assert f(ctypes.byref(g), ctypes.byref(src), None, 1, ctypes.byref(dst), None) == 1
+    dst8 = _layer(dtype=1, fc=2)
+    g16 = sa.Geom(heads=2, lat_h=4, lat_w=8).c()
+    assert f(ctypes.byref(g16), ctypes.byref(src), ctypes.c_void_p(FAKE), 1, ctypes.byref(dst8), None) == 4
+    d = lib.sa_kv_dequant
+    assert d(ctypes.byref(g16), ctypes.byref(src), ctypes.c_void_p(FAKE), 1, 0, ctypes.byref(dst), None) == 4
+    assert d(ctypes.byref(g16), ctypes.byref(_layer(dtype=1)), ctypes.c_void_p(FAKE), 3, 0,
+             ctypes.byref(dst), None) == 6

@@ -1,0 +1,148 @@
+"""GPU parity of kv_append / text_append against the oracle (through the C ABI).
+
+Gates: V planes bit-exact (a pure transposed copy); K planes: at least 99.9 %
+of elements bit-identical to the oracle's exactly rotated, correctly rounded
+keys, and every element within one bf16 ulp of the exact rotation plus the
+fp32 rotation error, 1e-6 times the magnitude of the rotated pair (a rotated
+value near zero is the difference of two products, so its own ulp is no
+bound); K at position (0, 0, 0) bit-exact; frames outside the written range
+untouched. fp8: V codes and all scales follow the fp32 decision
+exactly; K codes within one code step.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_attention_segment_amd as sa
+import seeded_inputs as si
+from oracle import cache as ocache
+from oracle import numerics
+from oracle import rope as orope
+
+pytestmark = pytest.mark.gpu
+
+SPLIT = (16, 56, 56)
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _ordered(bits):
+    b = bits.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def _ulp_diff(a_bits, b_bits):
+    return np.abs(_ordered(a_bits) - _ordered(b_bits))
+
+
+@pytest.mark.parametrize("shape", [(3, 4, 6, 3, 5, 10000.0), (2, 4, 8, 2, 0, 256.0),
+                                   (16, 22, 40, 30, 30, 10000.0)])
+def test_kv_append_bf16(shape):
+    H, lh, lw, F, frame0, theta = shape
+    print(f"kv_append bf16 H={H} grid={lh}x{lw} F={F} frame0={frame0}", flush=True)
+    P = lh * lw
+    geom = sa.Geom(heads=H, lat_h=lh, lat_w=lw, rope_theta=theta)
+    cap = frame0 + F + 2
+    layer = sa.KVLayer.allocate(geom, sa.KV_BF16, cap, 16)
+    sentinel = torch.tensor(0x7FC0, dtype=torch.int16).view(torch.bfloat16)   # bf16 NaN
+    layer.k.fill_(sentinel.item())
+    layer.v.fill_(sentinel.item())
+    k = si.normal_bf16((F * P, H, 128), 11, "cuda")
+    v = si.normal_bf16((F * P, H, 128), 12, "cuda")
+    sa.kv_append(geom, layer, k, v, frame0, F)
+    torch.cuda.synchronize()
+    K, V = ocache.append_bf16(k.float().cpu().double().numpy(), v.float().cpu().double().numpy(),
+                              frame0, lh, lw, SPLIT, theta)
+    gotV = _bits(layer.v[frame0:frame0 + F])
+    assert np.array_equal(gotV, numerics.bf16_bits(V))
+    gotK = _bits(layer.k[frame0:frame0 + F])
+    wantK = numerics.bf16_bits(K)
+    ulp = _ulp_diff(gotK, wantK)
+    frac = float(np.mean(ulp == 0))
+    print(f"  K bitwise fraction {frac:.6f}, max ulp {ulp.max()}", flush=True)
+    assert frac >= 0.999
+    kin = k.float().cpu().double().numpy()
+    exact = orope.rope3d(kin, orope.video_positions(frame0, F, lh, lw), SPLIT, theta)
+    exact = exact.reshape(F, P, H, 128).transpose(0, 2, 1, 3)
+    pair = np.sqrt(exact[..., 0::2] ** 2 + exact[..., 1::2] ** 2).repeat(2, axis=-1)
+    _, e = np.frexp(np.maximum(np.abs(exact), 2.0 ** -126))
+    ulp_exact = np.ldexp(1.0, e - 1 - 7)
+    err = np.abs(numerics.bf16_from_bits(gotK) - exact)
+    assert np.all(err <= ulp_exact + 1e-6 * pair)
+    if frame0 == 0:
+        assert np.array_equal(gotK[0, :, 0, :], _bits(k[0]))
+    untouched = torch.cat([layer.k[:frame0].flatten(), layer.k[frame0 + F:].flatten()])
+    assert torch.isnan(untouched.float()).all()
+    untouched = torch.cat([layer.v[:frame0].flatten(), layer.v[frame0 + F:].flatten()])
+    assert torch.isnan(untouched.float()).all()
+
+
+@pytest.mark.parametrize("n_text,cap", [(16, 16), (37, 48), (256, 256), (0, 16)])
+def test_text_append_bf16(n_text, cap):
+    H = 3
+    geom = sa.Geom(heads=H, lat_h=4, lat_w=6)
+    layer = sa.KVLayer.allocate(geom, sa.KV_BF16, 1, cap)
+    layer.v_text.fill_(float("nan"))
+    k = si.normal_bf16((max(n_text, 1), H, 128), 21, "cuda")
+    v = si.normal_bf16((max(n_text, 1), H, 128), 22, "cuda")
+    sa.text_append(geom, layer, k, v, n_text)
+    torch.cuda.synchronize()
+    if n_text:
+        assert torch.equal(layer.k_text[:, :n_text].view(torch.int16),
+                           k[:n_text].transpose(0, 1).contiguous().view(torch.int16))
+        assert torch.equal(layer.v_text[:, :, :n_text].view(torch.int16),
+                           v[:n_text].permute(1, 2, 0).contiguous().view(torch.int16))
+    # value columns past n_text are zeroed (finite for masked key chunks)
+    assert torch.all(layer.v_text[:, :, n_text:] == 0)
+
+
+@pytest.mark.parametrize("shape", [(2, 4, 8, 3, 2), (16, 22, 40, 2, 7)])
+def test_kv_append_fp8(shape):
+    H, lh, lw, F, frame0 = shape
+    print(f"kv_append fp8 H={H} grid={lh}x{lw} F={F}", flush=True)
+    P = lh * lw
+    geom = sa.Geom(heads=H, lat_h=lh, lat_w=lw)
+    layer = sa.KVLayer.allocate(geom, sa.KV_FP8, frame0 + F, 16)
+    wl = si.Workload("t", heads=H, lat_t=F, lat_h=lh, lat_w=lw, n_text=16, prior_segments=(0,),
+                     kv_dtype="fp8", scale_factors=True)
+    k, v = si.segment_kv(wl, 3, 0, 0, 0, "cuda")
+    sa.kv_append(geom, layer, k, v, frame0, F)
+    torch.cuda.synchronize()
+    Kc, Ks, Vc, Vs = ocache.append_fp8(k.float().cpu().double().numpy(),
+                                       v.float().cpu().double().numpy(), frame0, lh, lw, SPLIT, 10000.0)
+    gotVc = layer.v[frame0:].cpu().numpy()
+    gotVs = layer.v_scale[frame0:].cpu().numpy()
+    assert np.array_equal(gotVs, Vs)
+    assert np.array_equal(gotVc, Vc)
+    gotKs = layer.k_scale[frame0:].cpu().numpy()
+    np.testing.assert_allclose(gotKs, Ks, rtol=2e-6)
+    gotKc = layer.k[frame0:].cpu().numpy()
+    step = np.abs(_e4m3_ordered(gotKc) - _e4m3_ordered(Kc))
+    print(f"  K code agreement {np.mean(step == 0):.6f}", flush=True)
+    assert step.max() <= 1
+    assert np.mean(step == 0) >= 0.99
+
+
+def _e4m3_ordered(c):
+    c = c.astype(np.int32)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
+def test_text_append_fp8():
+    H, n = 4, 40
+    geom = sa.Geom(heads=H, lat_h=4, lat_w=8)
+    layer = sa.KVLayer.allocate(geom, sa.KV_FP8, 1, 48)
+    k = si.normal_bf16((n, H, 128), 31, "cuda")
+    v = si.normal_bf16((n, H, 128), 32, "cuda")
+    sa.text_append(geom, layer, k, v, n)
+    torch.cuda.synchronize()
+    Kc, Ks, Vc, Vs = ocache.append_text_fp8(k.float().cpu().double().numpy(),
+                                            v.float().cpu().double().numpy())
+    assert np.array_equal(layer.k_text_scale.cpu().numpy(), Ks)
+    assert np.array_equal(layer.v_text_scale.cpu().numpy(), Vs)
+    assert np.array_equal(layer.k_text[:, :n].cpu().numpy(), Kc)
+    assert np.array_equal(layer.v_text[:, :, :n].cpu().numpy(), Vc)
+    assert np.all(layer.v_text[:, :, n:].cpu().numpy() == 0)

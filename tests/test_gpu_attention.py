@@ -1,0 +1,208 @@
+"""GPU parity of segment_attention (bf16 cache) against the fp64 oracle.
+
+Small geometries that span several query tiles, ragged query and key tails,
+frames that are not a multiple of the key tile, gathered (non-contiguous)
+history frames, empty history, empty text, theta 256 (the pages' value) and
+sharpened logits. Gate: max-abs <= 2e-2 and mean-abs <= 2e-3 (the bf16 bar);
+relative L2 is also bounded (1e-2) so that a wrong kernel cannot hide under
+the absolute bar. Closed forms: a single key copies its value bitwise; Q = 0
+with one-hot values counts every key exactly once; uniform V gives V within
+one bf16 ulp. Determinism: two runs are bitwise identical.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_attention_segment_amd as sa
+import seeded_inputs as si
+from helpers import Session, compare
+from oracle import select as osel
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS, REL_L2 = 2e-2, 2e-3, 1e-2
+
+
+def _wl(name, H, F, lh, lw, n_text, prior, theta=10000.0):
+    return si.Workload(name, heads=H, lat_t=F, lat_h=lh, lat_w=lw, n_text=n_text,
+                       prior_segments=(prior,), theta=theta)
+
+
+CASES = [
+    # name, H, F, lat_h, lat_w, n_text, prior segments
+    ("tiny", 2, 2, 4, 6, 16, 2),            # the tiny workload (P=24 < key tile)
+    ("ragged", 3, 5, 4, 8, 37, 3),          # Lq=197 (2 q tiles), ragged text
+    ("p80", 2, 4, 8, 10, 64, 2),            # frame = 64 + 16 keys
+    ("p136", 2, 3, 8, 17, 100, 1),          # frame = 64 + 64 + 8 keys
+    ("nohist", 2, 3, 4, 8, 20, 0),          # only the own segment
+    ("notext", 2, 2, 8, 8, 0, 2),           # no text tokens
+    ("big", 4, 6, 8, 16, 256, 2),           # Lq = 1024, Lk = 2560
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_parity_small(case):
+    name, H, F, lh, lw, nt, prior = case
+    print(f"attention parity case={name}", flush=True)
+    wl = _wl(name, H, F, lh, lw, nt, prior)
+    s = Session(wl, seed=7, layer=0, session=0)
+    sa.segment_attention(s.geom, [s.item()])
+    torch.cuda.synchronize()
+    want, want_lse = s.oracle()
+    got, got_lse = s.gpu_out()
+    _, _, rel = compare(got, want, MAX_ABS, MEAN_ABS, name)
+    assert rel <= REL_L2
+    np.testing.assert_allclose(got_lse, want_lse, atol=2e-3, rtol=0)
+
+
+@pytest.mark.parametrize("theta", [256.0, 10000.0])
+@pytest.mark.parametrize("q_scale", [1.0, 4.0])
+def test_parity_theta_and_sharpened(theta, q_scale):
+    """theta 256 is the pages' RoPE base. Q x 4 sharpens the logits 4-fold:
+    the bf16 rounding of the rotated Q and K then moves logits by up to about
+    4 * 2^-8, which alone exceeds the absolute bar on the largest outputs, so
+    the sharpened case is gated on relative L2 against the exact oracle and on
+    the full bar against the oracle that rounds rotated Q and K to bf16."""
+    print(f"attention parity theta={theta} q_scale={q_scale}", flush=True)
+    wl = _wl("sharp", 3, 4, 6, 8, 24, 2, theta=theta)
+    s = Session(wl, seed=9, layer=1, session=0, theta=theta, q_scale=q_scale)
+    sa.segment_attention(s.geom, [s.item()])
+    torch.cuda.synchronize()
+    want, want_lse = s.oracle()
+    got, got_lse = s.gpu_out()
+    label = f"theta={theta} q*{q_scale}"
+    if q_scale == 1.0:
+        _, _, rel = compare(got, want, MAX_ABS, MEAN_ABS, label)
+        np.testing.assert_allclose(got_lse, want_lse, atol=5e-3, rtol=0)
+    else:
+        _, _, rel = compare(got, want, 8e-2, 4e-3, label + " vs exact")
+        wr, wr_lse = s.oracle(round_rotated=True)
+        compare(got, wr, MAX_ABS, MEAN_ABS, label + " vs bf16-rounded Q/K")
+        np.testing.assert_allclose(got_lse, wr_lse, atol=5e-3, rtol=0)
+    assert rel <= REL_L2
+
+
+@pytest.mark.parametrize("case", CASES[:3], ids=[c[0] for c in CASES[:3]])
+def test_kernel_error_against_rounded_inputs(case):
+    """Against the oracle that rounds rotated Q and K to bf16, the kernel's own
+    error (bf16 probabilities, fp32 accumulation) is an order below the bar."""
+    name, H, F, lh, lw, nt, prior = case
+    wl = _wl(name, H, F, lh, lw, nt, prior)
+    s = Session(wl, seed=17, layer=0, session=0)
+    sa.segment_attention(s.geom, [s.item()])
+    torch.cuda.synchronize()
+    got, _ = s.gpu_out()
+    want, _ = s.oracle(round_rotated=True)
+    compare(got, want, 4e-3, 4e-4, name + " vs bf16-rounded Q/K")
+
+
+def test_parity_gathered_power_history_two_sessions():
+    """Two sessions in one call with different, non-contiguous kept-frame lists."""
+    wl = si.Workload("sel", heads=2, lat_t=3, lat_h=4, lat_w=8, n_text=16, prior_segments=(6, 4),
+                     capacity_segments=7)
+    s0 = Session(wl, seed=5, layer=0, session=0, history=osel.select_power(18, 5).tolist())
+    s1 = Session(wl, seed=5, layer=0, session=1, history=osel.select_power(12, 7).tolist()[::-1])
+    sa.segment_attention(s0.geom, [s0.item(), s1.item(with_lse=False)])
+    torch.cuda.synchronize()
+    for s in (s0, s1):
+        want, _ = s.oracle()
+        got, _ = s.gpu_out()
+        _, _, rel = compare(got, want, MAX_ABS, MEAN_ABS, f"session {s.session}")
+        assert rel <= REL_L2
+
+
+def test_single_key_copies_value_bitwise():
+    H = 2
+    geom = sa.Geom(heads=H, lat_h=4, lat_w=6)
+    layer = sa.KVLayer.allocate(geom, sa.KV_BF16, 1, 16)
+    k = si.normal_bf16((1, H, 128), 41, "cuda")
+    v = si.normal_bf16((1, H, 128), 42, "cuda")
+    sa.text_append(geom, layer, k, v, 1)
+    q = si.normal_bf16((2 * 24 + 5, H, 128), 43, "cuda")
+    out = torch.empty_like(q)
+    frames = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sa.segment_attention(geom, [sa.AttnItem(q, layer, frames, 0, 1, out, 0, 2, 5)])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), v.expand(q.shape[0], H, 128).contiguous().view(torch.int16))
+
+
+def test_zero_query_counts_every_key_once():
+    """Q = 0 makes every weight equal: out = mean of V. With V one-hot on
+    (frame index mod 127) for video keys and on dim 127 for text keys, the
+    output counts how many keys of each frame were visited."""
+    H, lh, lw, F = 2, 8, 17, 3           # P = 136: tiles of 64, 64, 8
+    P = lh * lw
+    geom = sa.Geom(heads=H, lat_h=lh, lat_w=lw)
+    n_text = 37
+    cap = 12
+    layer = sa.KVLayer.allocate(geom, sa.KV_BF16, cap, 48)
+    for seg in range(cap // F):
+        k = si.normal_bf16((F * P, H, 128), 50 + seg, "cuda")
+        v = torch.zeros((F * P, H, 128), dtype=torch.bfloat16, device="cuda")
+        for fo in range(F):
+            v[fo * P:(fo + 1) * P, :, (seg * F + fo) % 127] = 1.0
+        sa.kv_append(geom, layer, k, v, seg * F, F)
+    kt = si.normal_bf16((n_text, H, 128), 60, "cuda")
+    vt = torch.zeros((n_text, H, 128), dtype=torch.bfloat16, device="cuda")
+    vt[:, :, 127] = 1.0
+    sa.text_append(geom, layer, kt, vt, n_text)
+    frames = [11, 0, 5, 6, 9]
+    d_frames = torch.tensor(frames, dtype=torch.int32, device="cuda")
+    q = torch.zeros((F * P + n_text, H, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    sa.segment_attention(geom, [sa.AttnItem(q, layer, d_frames, len(frames), n_text, out, 9, F, n_text)])
+    torch.cuda.synchronize()
+    Lk = len(frames) * P + n_text
+    want = np.zeros(128)
+    for f in frames:
+        want[f % 127] += P / Lk
+    want[127] += n_text / Lk
+    got = out.float().cpu().numpy()
+    bf = np.array(torch.tensor(want).to(torch.bfloat16).float())
+    assert np.all(np.abs(got - bf[None, None, :]) <= np.abs(bf)[None, None, :] * 2 ** -7 + 1e-7)
+
+
+def test_uniform_values_give_value():
+    H, lh, lw, F = 2, 4, 8, 2
+    P = lh * lw
+    geom = sa.Geom(heads=H, lat_h=lh, lat_w=lw)
+    layer = sa.KVLayer.allocate(geom, sa.KV_BF16, 4, 16)
+    row = si.normal_bf16((1, H, 128), 70, "cuda")
+    for seg in range(2):
+        k = si.normal_bf16((F * P, H, 128), 71 + seg, "cuda")
+        sa.kv_append(geom, layer, k, row.expand(F * P, H, 128).contiguous(), seg * F, F)
+    sa.text_append(geom, layer, si.normal_bf16((16, H, 128), 73, "cuda"),
+                   row.expand(16, H, 128).contiguous(), 16)
+    q = si.normal_bf16((F * P + 16, H, 128), 74, "cuda") * 3
+    out = torch.empty_like(q)
+    d_frames = torch.arange(4, dtype=torch.int32, device="cuda")
+    sa.segment_attention(geom, [sa.AttnItem(q, layer, d_frames, 4, 16, out, 2, F, 16)])
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().astype(np.int32)
+    want = row.expand_as(out).contiguous().view(torch.int16).cpu().numpy().astype(np.int32)
+    ordered = lambda b: np.where(b < 0, -(b & 0x7FFF), b)
+    assert np.abs(ordered(got) - ordered(want)).max() <= 1
+
+
+def test_deterministic_bitwise():
+    wl = _wl("det", 4, 4, 8, 10, 40, 2)
+    s = Session(wl, seed=3, layer=0, session=0)
+    sa.segment_attention(s.geom, [s.item()])
+    a = s.out.clone()
+    la = s.lse.clone()
+    sa.segment_attention(s.geom, [s.item()])
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), s.out.view(torch.int16))
+    assert torch.equal(la, s.lse)
+
+
+def test_no_query_rows_is_a_noop():
+    wl = _wl("empty", 2, 2, 4, 6, 16, 1)
+    s = Session(wl, seed=3, layer=0, session=0)
+    it = s.item()
+    it.n_frames_q, it.n_text_q = 0, 0
+    sa.segment_attention(s.geom, [it])
+    torch.cuda.synchronize()

@@ -1,0 +1,90 @@
+"""GPU checks of history_gather (bit-exact byte copy of the picked frames) and
+kv_dequant (e4m3 code times fp32 scale, rounded to bf16, against the oracle's
+decode taken in the same fp32 precision).
+
+Source planes are filled with random bytes by torch, not by the library, so
+the expected values never come from the HIP path.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_attention_segment_amd as sa
+from oracle import numerics
+
+pytestmark = pytest.mark.gpu
+
+
+def _fill_random(layer, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    for t in (layer.k, layer.v, layer.k_text, layer.v_text):
+        b = t.view(torch.uint8)
+        b.copy_(torch.randint(0, 256, b.shape, generator=g, device="cuda", dtype=torch.uint8))
+        if layer.dtype == sa.KV_FP8:
+            b[(b & 0x7F) == 0x7F] = 0x3C           # keep codes finite
+        else:
+            t.view(torch.int16)[torch.isnan(t.float())] = 0
+    if layer.dtype == sa.KV_FP8:
+        for t in (layer.k_scale, layer.v_scale, layer.k_text_scale, layer.v_text_scale):
+            t.copy_(torch.rand(t.shape, generator=g, device="cuda") * 0.05 + 0.001)
+
+
+@pytest.mark.parametrize("dtype,grid", [(sa.KV_BF16, (4, 6)), (sa.KV_FP8, (4, 8)),
+                                        (sa.KV_BF16, (22, 40))])
+def test_gather_bit_exact(dtype, grid):
+    H = 16 if grid == (22, 40) else 3
+    geom = sa.Geom(heads=H, lat_h=grid[0], lat_w=grid[1])
+    src = sa.KVLayer.allocate(geom, dtype, 40, 16)
+    _fill_random(src, 1)
+    frames = [39, 0, 17, 18, 5, 33]
+    dst = sa.KVLayer.allocate(geom, dtype, len(frames) + 1, 16)
+    d_frames = torch.tensor(frames, dtype=torch.int32, device="cuda")
+    sa.history_gather(geom, src, d_frames, len(frames), dst)
+    torch.cuda.synchronize()
+    idx = torch.tensor(frames, device="cuda")
+    assert torch.equal(dst.k[:len(frames)].view(torch.uint8), src.k[idx].view(torch.uint8))
+    assert torch.equal(dst.v[:len(frames)].view(torch.uint8), src.v[idx].view(torch.uint8))
+    if dtype == sa.KV_FP8:
+        assert torch.equal(dst.k_scale[:len(frames)], src.k_scale[idx])
+        assert torch.equal(dst.v_scale[:len(frames)], src.v_scale[idx])
+
+
+def _dequant_ref(codes, scale):
+    """Oracle decode, product taken in fp32, then bf16 nearest-even (as bits)."""
+    val = numerics.e4m3_decode(codes).astype(np.float32) * np.float32(scale)
+    return numerics.bf16_bits(numerics.bf16_round(val.astype(np.float32).astype(np.float64)))
+
+
+@pytest.mark.parametrize("n_text", [0, 16, 29])
+def test_dequant_matches_oracle(n_text):
+    H = 3
+    geom = sa.Geom(heads=H, lat_h=4, lat_w=8)
+    src = sa.KVLayer.allocate(geom, sa.KV_FP8, 10, 32)
+    _fill_random(src, 2)
+    frames = [9, 2, 4]
+    dst = sa.KVLayer.allocate(geom, sa.KV_BF16, 3, 32)
+    dst.k.zero_()
+    dst.v.zero_()
+    dst.k_text.zero_()
+    dst.v_text.zero_()
+    d_frames = torch.tensor(frames, dtype=torch.int32, device="cuda")
+    sa.kv_dequant(geom, src, d_frames, len(frames), n_text, dst)
+    torch.cuda.synchronize()
+    sk, sv = src.k.cpu().numpy(), src.v.cpu().numpy()
+    ks, vs = src.k_scale.cpu().numpy(), src.v_scale.cpu().numpy()
+    gk = dst.k.view(torch.int16).cpu().numpy().view(np.uint16)
+    gv = dst.v.view(torch.int16).cpu().numpy().view(np.uint16)
+    for i, f in enumerate(frames):
+        for h in range(H):
+            assert np.array_equal(gk[i, h], _dequant_ref(sk[f, h], ks[f, h]))
+            assert np.array_equal(gv[i, h], _dequant_ref(sv[f, h], vs[f, h]))
+    if n_text:
+        tk = dst.k_text.view(torch.int16).cpu().numpy().view(np.uint16)
+        tv = dst.v_text.view(torch.int16).cpu().numpy().view(np.uint16)
+        sk, sv = src.k_text.cpu().numpy(), src.v_text.cpu().numpy()
+        kts, vts = src.k_text_scale.cpu().numpy(), src.v_text_scale.cpu().numpy()
+        for h in range(H):
+            assert np.array_equal(tk[h, :n_text], _dequant_ref(sk[h, :n_text], kts[h]))
+            assert np.array_equal(tv[h, :, :n_text], _dequant_ref(sv[h, :, :n_text], vts[h]))
+            assert np.all(tk[h, n_text:] == 0) and np.all(tv[h, :, n_text:] == 0)
