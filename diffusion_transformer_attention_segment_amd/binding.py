@@ -12,7 +12,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsegattn.so")
+# SEGATTN_LIBRARY may name another build of the same library (same ABI)
+LIB_PATH = os.environ.get("SEGATTN_LIBRARY", os.path.join(_PKG, "libsegattn.so"))
 
 SA_OK = 0
 STATUS_NAMES = {0: "SA_OK", 1: "SA_E_ARG", 2: "SA_E_SHAPE", 3: "SA_E_ALIGN",

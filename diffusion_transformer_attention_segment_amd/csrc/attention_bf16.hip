@@ -7,30 +7,44 @@
 // and text tokens, 16 heads of 128, 3D RoPE, reading history from a KV cache)
 // and "The 4090 preset" (a picked subset of past frames is attended).
 //
-// Work decomposition. One workgroup = 4 waves = 128 query rows of one head of
-// one session; each wave owns 32 rows. Key tiles of 64 keys never straddle a
-// frame (a frame of P tokens is ceil(P/64) tiles), so a tile's address is one
-// frame-plane base plus a row offset and the frame list is read once per tile.
+// Work decomposition. One workgroup = 8 waves = 256 query rows of one head of
+// one session (two waves per SIMD); each wave owns 32 rows. Key tiles of 64
+// keys never straddle a frame (a frame of P tokens is ceil(P/64) tiles), so a
+// tile's address is one frame-plane base plus a row offset and the frame list
+// is read once per tile. K/V tiles go HBM -> registers -> a 4-stage LDS ring
+// (one barrier per tile); loads for tile t+3 are in flight while tile t is
+// computed.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, 32x32 output, K = 16):
 //   S^T = K . Q^T   A = K rows (keys), B = Q^T (queries = lanes % 32)
 //   O^T = V^T . P^T A = V^T rows (dims), B = P^T (queries = lanes % 32)
-// The S^T accumulator of lane l holds, for query l % 32, keys
-//   8*(r/4) + 4*(l/32) + r%4 of the A rows (register r). Loading K row
-//   pi(r) = r with bits 2 and 3 swapped into A row r makes lane-group g hold the
-//   contiguous keys 16c + 8g .. 16c + 8g + 7 in registers 8c .. 8c + 7, which
-//   is exactly the B-operand layout P^T needs -- so P never leaves registers,
-//   and V^T (stored transposed in the cache) is read as contiguous 16 bytes.
+// The S^T accumulator of lane l holds, for query l % 32, A rows
+// 8*(r/4) + 4*(l/32) + r%4 (register r). Loading K row pi(r) = r with bits 2
+// and 3 swapped into A row r makes lane-group g hold the contiguous keys
+// 16c + 8g .. 16c + 8g + 7 in registers 8c .. 8c + 7, exactly the B-operand
+// layout P^T needs -- so P never leaves registers, and V^T (stored transposed
+// in the cache) is read from LDS as contiguous 16 bytes.
+//
+// In-wave pipeline over 32-key blocks: the QK^T MFMAs of block j+1 are issued
+// next to the softmax VALU work of block j, and the PV MFMAs of block j next
+// to the softmax of block j+1, so the matrix pipe has work while the wave
+// computes exponentials (two waves per SIMD fill the remaining gaps).
 #include "device_common.h"
 
 namespace segattn {
 namespace {
 
-constexpr int BM = 128;          // query rows per workgroup
+constexpr int BM = 256;          // query rows per workgroup
 constexpr int BN = 64;           // keys per tile
-constexpr int kThreads = 256;
-constexpr int KS = kD + 8;       // LDS row stride of the K tile (elements)
-constexpr int VS = BN + 8;       // LDS row stride of the V^T tile (elements)
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStages = 4;        // LDS ring depth (power of two)
+constexpr int KS = kD + 8;       // LDS row stride of the K tile (elements): 272 B
+constexpr int VS = BN + 8;       // LDS row stride of the V^T tile (elements): 144 B
+constexpr int KT = BN * KS;      // elements of one K stage
+constexpr int VT = kD * VS;      // elements of one V^T stage
+constexpr int kKChunks = BN * kD / 8 / kThreads;   // 16-byte K chunks per thread (2)
+constexpr int kVChunks = kD * BN / 8 / kThreads;   // 16-byte V chunks per thread (2)
 constexpr float kRescaleSlack = 8.0f;   // log2 headroom before O is rescaled
 
 struct TileDesc {
@@ -63,9 +77,17 @@ __device__ __forceinline__ TileDesc tile_at(const AttnItemDev& I, int t, int tpf
   return d;
 }
 
+__device__ __forceinline__ int tile_nvalid(const AttnItemDev& I, int t, int tpf, int nvid, int P) {
+  if (t < nvid) {
+    const int fi = t / tpf;
+    return min(BN, P - (t - fi * tpf) * BN);
+  }
+  return min(BN, I.n_text_kv - (t - nvid) * BN);
+}
+
 __device__ __forceinline__ void load_tile(const TileDesc& d, int tid, u32x4* kr, u32x4* vr) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kKChunks; ++i) {
     const int c = tid + kThreads * i;
     const int row = c >> 4, col = c & 15;
     kr[i] = row < d.nvalid
@@ -73,7 +95,7 @@ __device__ __forceinline__ void load_tile(const TileDesc& d, int tid, u32x4* kr,
                 : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kVChunks; ++i) {
     const int c = tid + kThreads * i;
     const int dd = c >> 3, kc = c & 7;
     vr[i] = 8 * kc < d.nvalid
@@ -85,22 +107,129 @@ __device__ __forceinline__ void load_tile(const TileDesc& d, int tid, u32x4* kr,
 __device__ __forceinline__ void store_tile(uint16_t* Ks, uint16_t* Vs, int tid, const u32x4* kr,
                                            const u32x4* vr) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kKChunks; ++i) {
     const int c = tid + kThreads * i;
     const int row = c >> 4, col = c & 15;
     *reinterpret_cast<u32x4*>(&Ks[row * KS + col * 8]) = kr[i];
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kVChunks; ++i) {
     const int c = tid + kThreads * i;
     const int dd = c >> 3, kc = c & 7;
     *reinterpret_cast<u32x4*>(&Vs[dd * VS + kc * 8]) = vr[i];
   }
 }
 
-__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kD * VS];
+// S^T of one 32-key block: kp points at this lane's K row (pi(r32)) and its
+// 8-dim group; eight dependent 16-dim MFMA steps.
+__device__ __forceinline__ f32x16 qk_block(const uint16_t* kp, const bf16x8* qf) {
+  f32x16 s = {};
+#pragma unroll
+  for (int cd = 0; cd < 8; ++cd)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kp + 16 * cd),
+                                                qf[cd], s, 0, 0, 0);
+  return s;
+}
+
+// O^T += V^T P^T for one 16-key chunk: vp points at this lane's V^T row r32
+// and the chunk's 8-key group; four independent 32-dim blocks.
+__device__ __forceinline__ void pv_chunk(const uint16_t* vp, const bf16x8& p, f32x16* o) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        *reinterpret_cast<const bf16x8*>(vp + 32 * db * VS), p, o[db], 0, 0, 0);
+}
+
+__device__ __forceinline__ float max_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// exp2(s * c2 - m) for the 16 keys of a block, packed as two bf16 B operands,
+// with their fp32 sum folded into l. (The sum uses plain adds: this compiler
+// emits v_dot2c_f32_bf16 sequences that read the same source word each time.)
+__device__ __forceinline__ void block_probs(const f32x16& s, float c2, float m, float& l,
+                                            bf16x8* p) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    u32x4 pw;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * c + 2 * k], c2, -m));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * c + 2 * k + 1], c2, -m));
+      pw[k] = pack_bf16x2(p0, p1);
+      l += p0 + p1;
+    }
+    p[c] = __builtin_bit_cast(bf16x8, pw);
+  }
+}
+
+// Keys of a 32-key block at or beyond `nvalid` (relative to the block) get -inf.
+__device__ __forceinline__ void mask_block(f32x16& s, int nvalid, int g) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = 16 * (r >> 3) + 8 * g + (r & 7);
+    if (key >= nvalid) s[r] = -INFINITY;
+  }
+}
+
+// Block max of S^T over the 32 keys (both lane halves), scaled to log2 units.
+__device__ __forceinline__ float block_max(const f32x16& s, float c2) {
+  float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+  for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
+  return max_other_half(fmaxf(mx, s[15])) * c2;
+}
+
+// Lazy online-softmax update for a block whose max is mt (log2 units): the
+// running max moves only when the block max exceeds it by the slack; then O,
+// the running sum and the probabilities of the block still waiting for its
+// P.V step (pending) are rescaled by exp2(m_old - m_new). Called once per
+// block, outside the MFMA/exp basic blocks; the branch is wave-uniform.
+__device__ __forceinline__ void update_max(float mt, float& m_run, float& l_run, f32x16* o,
+                                           bf16x8* pending) {
+  const bool need = mt > m_run + kRescaleSlack;
+  if (__any(need)) {
+    const float mn = need ? mt : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] *= alpha;
+    l_run *= alpha;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      u32x4 pw = __builtin_bit_cast(u32x4, pending[c]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        pw[k] = pack_bf16x2(__uint_as_float(pw[k] << 16) * alpha,
+                            __uint_as_float(pw[k] & 0xFFFF0000u) * alpha);
+      pending[c] = __builtin_bit_cast(bf16x8, pw);
+    }
+    m_run = mn;
+  }
+}
+
+// One pipeline step (one basic block): PV of the previous block (its P^T in
+// p_prev, V^T rows at vp) and QK^T of the next block (K rows at kp) on the
+// matrix pipe, next to the exponentials of the current block s_cur.
+__device__ __forceinline__ void fused_step(const uint16_t* vp, const bf16x8* p_prev, f32x16* o,
+                                           const uint16_t* kp, const bf16x8* qf, f32x16& s_next,
+                                           const f32x16& s_cur, float c2, float m_run,
+                                           float& l_run, bf16x8* p_cur) {
+  pv_chunk(vp, p_prev[0], o);
+  pv_chunk(vp + 16, p_prev[1], o);
+  s_next = qk_block(kp, qf);
+  block_probs(s_cur, c2, m_run, l_run, p_cur);
+  // materialise the probabilities here, so that they are not sunk past the
+  // branches that follow (they must share this block with the MFMAs)
+#ifndef SEGATTN_NO_PIN
+  asm volatile("" : "+v"(p_cur[0]), "+v"(p_cur[1]), "+v"(l_run));
+#endif
+}
+
+__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kStages * KT];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[kStages * VT];
   __shared__ double om[kD / 2];
   __shared__ int ax[kD / 2];
 
@@ -126,11 +255,23 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, r32 = lane & 31;
 
+  const int tpf = (P + BN - 1) / BN;
+  const int nvid = I.n_frames_kv * tpf;
+  const int ntiles = nvid + (I.n_text_kv + BN - 1) / BN;
+
+  // start the first K/V loads before the RoPE prologue
+  u32x4 kr[kKChunks], vr[kVChunks];
+  load_tile(tile_at(I, 0, tpf, nvid, h, H, P), tid, kr, vr);
+
   if (tid < kD / 2) {
     int axis;
     om[tid] = rope_omega(tid, a.rope, &axis);
     ax[tid] = axis;
   }
+  // the last V stage is read once with zero probabilities before it is first
+  // written: give it finite contents
+  for (int i = tid; i < VT / 8; i += kThreads)
+    reinterpret_cast<u32x4*>(Vs + (kStages - 1) * VT)[i] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
   // ---- Q fragments (B operand of S^T = K Q^T), rotated in fp32 -------------
@@ -168,100 +309,79 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const AttnArgs a) {
     }
   }
 
+  // ---- prologue: tiles 0, 1 into LDS stages 0, 1; tile 2 in flight ----------
+  store_tile(Ks, Vs, tid, kr, vr);
+  if (ntiles > 1) {
+    load_tile(tile_at(I, 1, tpf, nvid, h, H, P), tid, kr, vr);
+    store_tile(Ks + KT, Vs + VT, tid, kr, vr);
+  }
+  if (ntiles > 2) load_tile(tile_at(I, 2, tpf, nvid, h, H, P), tid, kr, vr);
+  __syncthreads();
+
+  const int pi_row = (r32 & ~0xC) | ((r32 & 4) << 1) | ((r32 & 8) >> 1);
+  const int koff0 = pi_row * KS + 8 * g;          // block 0 K row of this lane
+  const int koff1 = (32 + pi_row) * KS + 8 * g;   // block 1
+  const int voff = r32 * VS + 8 * g;
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY;
   float l_run = 0.f;
   const float c2 = a.scale_log2;
 
-  const int tpf = (P + BN - 1) / BN;
-  const int nvid = I.n_frames_kv * tpf;
-  const int ntiles = nvid + (I.n_text_kv + BN - 1) / BN;
-
-  // K row this lane feeds into A row r32 (bits 2 and 3 swapped)
-  const int pi_row = (r32 & ~0xC) | ((r32 & 4) << 1) | ((r32 & 8) >> 1);
-
-  u32x4 kr[4], vr[4];
-  TileDesc cur = tile_at(I, 0, tpf, nvid, h, H, P);
-  load_tile(cur, tid, kr, vr);
+  // Blocks 2t and 2t+1 are the halves of tile t (stage t % 4). Step j runs
+  // PV(j-1) + QK(j+1) on the matrix pipe next to the exponentials of block j,
+  // then the max of block j+1 decides the (rare) rescale. Step 2t still reads
+  // V of tile t-1, so tile t+2 goes to stage (t+2) % 4, last read two steps
+  // before the barrier that precedes the store.
+  f32x16 sa = qk_block(Ks + koff0, qf);     // S of the current block
+  f32x16 sb;                                // S of the next block
+  {
+    const int nv0 = tile_nvalid(I, 0, tpf, nvid, P);
+    if (nv0 < 32) mask_block(sa, nv0, g);
+  }
+  float m_run = block_max(sa, c2);          // block 0 always has a valid key
+  bf16x8 pprev[2], pcur[2];
+  pprev[0] = pprev[1] = bf16x8{};
 
 #pragma unroll 1
   for (int t = 0; t < ntiles; ++t) {
+    const int st = t & (kStages - 1);
+    const uint16_t* Kst = Ks + st * KT;
+    const uint16_t* Vst = Vs + st * VT;
+    const uint16_t* Vprev = Vs + ((t + kStages - 1) & (kStages - 1)) * VT;
+    const uint16_t* Knext = Ks + ((t + 1) & (kStages - 1)) * KT;
+    const int nvalid = tile_nvalid(I, t, tpf, nvid, P);
     __syncthreads();
-    store_tile(Ks, Vs, tid, kr, vr);
-    __syncthreads();
-    const int nvalid = cur.nvalid;
+    // tile t+2: registers -> LDS stage (t+2) % 4; start loading tile t+3
+    if (t + 2 < ntiles) {
+      const int s2 = (t + 2) & (kStages - 1);
+      store_tile(Ks + s2 * KT, Vs + s2 * VT, tid, kr, vr);
+      if (t + 3 < ntiles) load_tile(tile_at(I, t + 3, tpf, nvid, h, H, P), tid, kr, vr);
+    }
+
+    // step 2t: PV(2t-1) + QK(2t+1) | exp(2t)
+    fused_step(Vprev + voff + 32, pprev, o, Kst + koff1, qf, sb, sa, c2, m_run, l_run, pcur);
+    if (nvalid < BN) mask_block(sb, nvalid - 32, g);
+    update_max(block_max(sb, c2), m_run, l_run, o, pcur);
+    pprev[0] = pcur[0];
+    pprev[1] = pcur[1];
+    sa = sb;
+
+    // step 2t+1: PV(2t) + QK(2t+2) | exp(2t+1)
+    fused_step(Vst + voff, pprev, o, Knext + koff0, qf, sb, sa, c2, m_run, l_run, pcur);
     if (t + 1 < ntiles) {
-      cur = tile_at(I, t + 1, tpf, nvid, h, H, P);
-      load_tile(cur, tid, kr, vr);
+      const int nv1 = tile_nvalid(I, t + 1, tpf, nvid, P);
+      if (nv1 < 32) mask_block(sb, nv1, g);
+      update_max(block_max(sb, c2), m_run, l_run, o, pcur);
     }
-
-    // ---- S^T = K Q^T for two 32-key blocks --------------------------------
-    f32x16 s[2];
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk) {
-      s[bk] = f32x16{};
-      const uint16_t* krow = &Ks[(32 * bk + pi_row) * KS + 8 * g];
-#pragma unroll
-      for (int cd = 0; cd < 8; ++cd) {
-        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(krow + 16 * cd);
-        s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[cd], s[bk], 0, 0, 0);
-      }
-    }
-    if (nvalid < BN) {
-#pragma unroll
-      for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * bk + 16 * (r >> 3) + 8 * g + (r & 7);
-          if (key >= nvalid) s[bk][r] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax (log2 domain, lazy rescale) ------------------------
-    float mx = s[0][0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mt = mx * c2;
-    const bool need = mt > m_run + kRescaleSlack;
-    if (__any(need)) {
-      const float mn = need ? mt : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] *= alpha;
-      l_run *= alpha;
-      m_run = mn;
-    }
-    float lsum = 0.f;
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[bk][r], c2, -m_run));
-        s[bk][r] = p;
-        lsum += p;
-      }
-    l_run += lsum;
-
-    // ---- O^T += V^T P^T ------------------------------------------------------
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const int bk = cc >> 1, hh = (cc & 1) * 8;
-      u32x4 pw;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) pw[m] = pack_bf16x2(s[bk][hh + 2 * m], s[bk][hh + 2 * m + 1]);
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x8 av =
-            *reinterpret_cast<const bf16x8*>(&Vs[(32 * db + r32) * VS + 16 * cc + 8 * g]);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf, o[db], 0, 0, 0);
-      }
-    }
+    pprev[0] = pcur[0];
+    pprev[1] = pcur[1];
+    sa = sb;
+  }
+  {
+    const uint16_t* Vlast = Vs + ((ntiles - 1) & (kStages - 1)) * VT;
+    pv_chunk(Vlast + voff + 32, pprev[0], o);
+    pv_chunk(Vlast + voff + 48, pprev[1], o);
   }
 
   // ---- epilogue ----------------------------------------------------------------
