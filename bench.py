@@ -125,6 +125,29 @@ class LayerState:
             ev[1].record()
 
 
+def measure_gather(sa, geom, n_frames=99, capacity=128, reps=5):
+    """history_gather of n_frames picked out of a capacity-frame bf16 layer:
+    a plain copy of 2 planes x n_frames x H x P x 128 x 2 bytes, read and written."""
+    src = sa.KVLayer.allocate(geom, sa.KV_BF16, capacity, 16)
+    dst = sa.KVLayer.allocate(geom, sa.KV_BF16, n_frames, 16)
+    g = torch.Generator().manual_seed(1234)
+    frames = torch.randperm(capacity, generator=g)[:n_frames].sort().values.to(torch.int32)
+    d_frames = frames.cuda()
+    sa.history_gather(geom, src, d_frames, n_frames, dst)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        sa.history_gather(geom, src, d_frames, n_frames, dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    plane = geom.heads * geom.P * 128 * 2
+    moved = 2 * 2 * n_frames * plane          # K and V, read + write
+    return {"frames": n_frames, "ms": round(ms, 4), "bytes_read_plus_written": moved,
+            "GB_per_s": round(moved / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(state, rows_wanted, seed):
     """Time the fp64 oracle on a bounded sample of the first session of the workload."""
     import numpy as np
@@ -264,6 +287,7 @@ def main():
                       "GB_per_s": round(app_bytes / (app_ms * 1e-3) / 1e9, 1),
                       "frac_of_hbm_peak": round(app_bytes / (app_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
     }
+    line["history_gather"] = measure_gather(sa, state.geom)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(state, args.cpu_rows, args.seed)
     print(json.dumps(line), flush=True)

@@ -10,10 +10,11 @@
 // Work decomposition. One workgroup = 8 waves = 256 query rows of one head of
 // one session (two waves per SIMD); each wave owns 32 rows. Key tiles of 64
 // keys never straddle a frame (a frame of P tokens is ceil(P/64) tiles), so a
-// tile's address is one frame-plane base plus a row offset and the frame list
-// is read once per tile. K/V tiles go HBM -> registers -> a 4-stage LDS ring
-// (one barrier per tile); loads for tile t+3 are in flight while tile t is
-// computed.
+// tile is one frame-plane base plus a row offset: tiles are fetched with
+// buffer loads whose resource bounds zero-fill the rows past the frame end,
+// and the frame list is read once per frame by a scalar cursor. K/V tiles go
+// HBM -> registers -> a 4-stage LDS ring (one barrier per tile); the loads of
+// tile t+3 are in flight while tile t is computed.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, 32x32 output, K = 16):
 //   S^T = K . Q^T   A = K rows (keys), B = Q^T (queries = lanes % 32)
@@ -25,10 +26,13 @@
 // layout P^T needs -- so P never leaves registers, and V^T (stored transposed
 // in the cache) is read from LDS as contiguous 16 bytes.
 //
-// In-wave pipeline over 32-key blocks: the QK^T MFMAs of block j+1 are issued
-// next to the softmax VALU work of block j, and the PV MFMAs of block j next
-// to the softmax of block j+1, so the matrix pipe has work while the wave
-// computes exponentials (two waves per SIMD fill the remaining gaps).
+// In-wave pipeline over 32-key blocks: step j issues, in one basic block,
+// PV of block j-1 and QK^T of block j+1 (alternating, so the dependent QK^T
+// chain is interleaved with independent PV work) next to the softmax VALU work
+// of block j (its max and its exponentials against the running max). When the
+// block max exceeds the running max by more than the slack -- rare after the
+// first blocks -- a wave-uniform branch rescales O and the sum and recomputes
+// the block's probabilities.
 #include "device_common.h"
 
 namespace segattn {
@@ -38,7 +42,7 @@ constexpr int BM = 256;          // query rows per workgroup
 constexpr int BN = 64;           // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStages = 4;        // LDS ring depth (power of two)
+constexpr int kStages = 4;       // LDS ring depth (power of two)
 constexpr int KS = kD + 8;       // LDS row stride of the K tile (elements): 272 B
 constexpr int VS = BN + 8;       // LDS row stride of the V^T tile (elements): 144 B
 constexpr int KT = BN * KS;      // elements of one K stage
@@ -46,62 +50,80 @@ constexpr int VT = kD * VS;      // elements of one V^T stage
 constexpr int kKChunks = BN * kD / 8 / kThreads;   // 16-byte K chunks per thread (2)
 constexpr int kVChunks = kD * BN / 8 / kThreads;   // 16-byte V chunks per thread (2)
 constexpr float kRescaleSlack = 8.0f;   // log2 headroom before O is rescaled
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer resource, 32-bit data format
 
-struct TileDesc {
-  const uint16_t* kb;   // K row 0 of the tile
-  const uint16_t* vb;   // V^T column 0 of the tile (row stride vstride)
-  int vstride;
-  int nvalid;           // valid keys in the tile (1..64)
+// Scalar walk over the key tiles of one (item, head): video frames in list
+// order (ceil(P / 64) tiles each), then the text slot. Everything here is
+// wave-uniform.
+struct TileCursor {
+  int fi;               // segment: frame-list index, or n_frames (the text slot)
+  int p0;               // first key of the tile within its segment
+  int len;              // keys in the segment (P or n_text)
+  const char* kplane;   // K plane of the segment
+  const char* vplane;   // V^T plane of the segment
+  int vstride;          // tokens per V^T row of the plane (P or text capacity)
 };
 
-__device__ __forceinline__ TileDesc tile_at(const AttnItemDev& I, int t, int tpf, int nvid,
-                                            int h, int H, int P) {
-  TileDesc d;
-  if (t < nvid) {
-    const int fi = t / tpf;
-    const int p0 = (t - fi * tpf) * BN;
-    const int frame = I.frames[fi];
-    const size_t plane = (static_cast<size_t>(frame) * H + h) * static_cast<size_t>(P) * kD;
-    d.kb = static_cast<const uint16_t*>(I.k) + plane + static_cast<size_t>(p0) * kD;
-    d.vb = static_cast<const uint16_t*>(I.v) + plane + p0;
-    d.vstride = P;
-    d.nvalid = min(BN, P - p0);
+__device__ __forceinline__ void cursor_enter(TileCursor& c, const AttnItemDev& I, int h, int H,
+                                             int P) {
+  c.p0 = 0;
+  if (c.fi < I.n_frames_kv) {
+    const int frame = I.frames[c.fi];
+    const size_t plane = (static_cast<size_t>(frame) * H + h) * static_cast<size_t>(P) * kD * 2;
+    c.kplane = static_cast<const char*>(I.k) + plane;
+    c.vplane = static_cast<const char*>(I.v) + plane;
+    c.len = P;
+    c.vstride = P;
   } else {
-    const int p0 = (t - nvid) * BN;
-    const size_t plane = static_cast<size_t>(h) * I.text_cap * kD;
-    d.kb = static_cast<const uint16_t*>(I.k_text) + plane + static_cast<size_t>(p0) * kD;
-    d.vb = static_cast<const uint16_t*>(I.v_text) + plane + p0;
-    d.vstride = I.text_cap;
-    d.nvalid = min(BN, I.n_text_kv - p0);
+    const size_t plane = static_cast<size_t>(h) * I.text_cap * kD * 2;
+    c.kplane = static_cast<const char*>(I.k_text) + plane;
+    c.vplane = static_cast<const char*>(I.v_text) + plane;
+    c.len = I.n_text_kv;
+    c.vstride = I.text_cap;
   }
-  return d;
 }
 
-__device__ __forceinline__ int tile_nvalid(const AttnItemDev& I, int t, int tpf, int nvid, int P) {
-  if (t < nvid) {
-    const int fi = t / tpf;
-    return min(BN, P - (t - fi * tpf) * BN);
+__device__ __forceinline__ void cursor_next(TileCursor& c, const AttnItemDev& I, int h, int H,
+                                            int P) {
+  c.p0 += BN;
+  if (c.p0 >= c.len) {
+    ++c.fi;
+    if (c.fi <= I.n_frames_kv) cursor_enter(c, I, h, H, P);
   }
-  return min(BN, I.n_text_kv - (t - nvid) * BN);
 }
 
-__device__ __forceinline__ void load_tile(const TileDesc& d, int tid, u32x4* kr, u32x4* vr) {
+__device__ __forceinline__ int cursor_nvalid(const TileCursor& c) { return min(BN, c.len - c.p0); }
+
+// Per-thread byte offsets of this thread's 16-byte chunks inside a tile (K) or
+// a V^T plane (V, for the two row strides in use).
+struct ChunkOffsets {
+  uint32_t k[kKChunks];
+  uint32_t v_video[kVChunks];
+  uint32_t v_text[kVChunks];
+};
+
+// Load tile c: K rows past the valid count and V^T bytes past the plane end
+// read as zero through the buffer bounds; V^T columns past the valid count
+// inside the plane are finite cache values that meet zero probabilities.
+__device__ __forceinline__ void load_tile(const TileCursor& c, const ChunkOffsets& off,
+                                          bool video, u32x4* kr, u32x4* vr) {
+  const int nv = cursor_nvalid(c);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(c.kplane + static_cast<size_t>(c.p0) * kD * 2), static_cast<short>(0),
+      nv * kD * 2, kRsrcFlags);
+  // the V^T resource starts at the tile's first column and ends at the plane
+  // end, so the bounds check alone keeps every read inside the plane
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(c.vplane + c.p0 * 2), static_cast<short>(0),
+      c.vstride * kD * 2 - c.p0 * 2, kRsrcFlags);
 #pragma unroll
-  for (int i = 0; i < kKChunks; ++i) {
-    const int c = tid + kThreads * i;
-    const int row = c >> 4, col = c & 15;
-    kr[i] = row < d.nvalid
-                ? *reinterpret_cast<const u32x4*>(d.kb + static_cast<size_t>(row) * kD + col * 8)
-                : u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int i = 0; i < kKChunks; ++i)
+    kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off.k[i], 0, 0));
 #pragma unroll
-  for (int i = 0; i < kVChunks; ++i) {
-    const int c = tid + kThreads * i;
-    const int dd = c >> 3, kc = c & 7;
-    vr[i] = 8 * kc < d.nvalid
-                ? *reinterpret_cast<const u32x4*>(d.vb + static_cast<size_t>(dd) * d.vstride + kc * 8)
-                : u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int i = 0; i < kVChunks; ++i)
+    vr[i] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, video ? off.v_video[i] : off.v_text[i],
+                                                     0, 0));
 }
 
 __device__ __forceinline__ void store_tile(uint16_t* Ks, uint16_t* Vs, int tid, const u32x4* kr,
@@ -118,26 +140,6 @@ __device__ __forceinline__ void store_tile(uint16_t* Ks, uint16_t* Vs, int tid, 
     const int dd = c >> 3, kc = c & 7;
     *reinterpret_cast<u32x4*>(&Vs[dd * VS + kc * 8]) = vr[i];
   }
-}
-
-// S^T of one 32-key block: kp points at this lane's K row (pi(r32)) and its
-// 8-dim group; eight dependent 16-dim MFMA steps.
-__device__ __forceinline__ f32x16 qk_block(const uint16_t* kp, const bf16x8* qf) {
-  f32x16 s = {};
-#pragma unroll
-  for (int cd = 0; cd < 8; ++cd)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kp + 16 * cd),
-                                                qf[cd], s, 0, 0, 0);
-  return s;
-}
-
-// O^T += V^T P^T for one 16-key chunk: vp points at this lane's V^T row r32
-// and the chunk's 8-key group; four independent 32-dim blocks.
-__device__ __forceinline__ void pv_chunk(const uint16_t* vp, const bf16x8& p, f32x16* o) {
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        *reinterpret_cast<const bf16x8*>(vp + 32 * db * VS), p, o[db], 0, 0, 0);
 }
 
 __device__ __forceinline__ float max_other_half(float x) {
@@ -174,7 +176,7 @@ __device__ __forceinline__ void mask_block(f32x16& s, int nvalid, int g) {
   }
 }
 
-// Block max of S^T over the 32 keys (both lane halves), scaled to log2 units.
+// Block max of S^T over its 32 keys (both lane halves), in log2 units.
 __device__ __forceinline__ float block_max(const f32x16& s, float c2) {
   float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
@@ -182,49 +184,56 @@ __device__ __forceinline__ float block_max(const f32x16& s, float c2) {
   return max_other_half(fmaxf(mx, s[15])) * c2;
 }
 
-// Lazy online-softmax update for a block whose max is mt (log2 units): the
-// running max moves only when the block max exceeds it by the slack; then O,
-// the running sum and the probabilities of the block still waiting for its
-// P.V step (pending) are rescaled by exp2(m_old - m_new). Called once per
-// block, outside the MFMA/exp basic blocks; the branch is wave-uniform.
-__device__ __forceinline__ void update_max(float mt, float& m_run, float& l_run, f32x16* o,
-                                           bf16x8* pending) {
-  const bool need = mt > m_run + kRescaleSlack;
-  if (__any(need)) {
-    const float mn = need ? mt : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+// One pipeline step, one basic block: PV of the previous block (P^T in p_prev,
+// V^T rows at vp) and QK^T of the next block (K rows at kp) on the matrix
+// pipe, alternating; next to them the max and the exponentials of the current
+// block s_cur against the running max m_run. Returns the block max (log2).
+__device__ __forceinline__ float fused_step(const uint16_t* vp, const bf16x8* p_prev, f32x16* o,
+                                            const uint16_t* kp, const bf16x8* qf, f32x16& s_next,
+                                            const f32x16& s_cur, float c2, float m_run,
+                                            float& l_run, bf16x8* p_cur) {
+  f32x16 s = {};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] *= alpha;
-    l_run *= alpha;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      u32x4 pw = __builtin_bit_cast(u32x4, pending[c]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        pw[k] = pack_bf16x2(__uint_as_float(pw[k] << 16) * alpha,
-                            __uint_as_float(pw[k] & 0xFFFF0000u) * alpha);
-      pending[c] = __builtin_bit_cast(bf16x8, pw);
-    }
-    m_run = mn;
+  for (int i = 0; i < 8; ++i) {
+    const int c = i >> 2, db = i & 3;
+    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        *reinterpret_cast<const bf16x8*>(vp + 16 * c + 32 * db * VS), p_prev[c], o[db], 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kp + 16 * i),
+                                                qf[i], s, 0, 0, 0);
   }
-}
-
-// One pipeline step (one basic block): PV of the previous block (its P^T in
-// p_prev, V^T rows at vp) and QK^T of the next block (K rows at kp) on the
-// matrix pipe, next to the exponentials of the current block s_cur.
-__device__ __forceinline__ void fused_step(const uint16_t* vp, const bf16x8* p_prev, f32x16* o,
-                                           const uint16_t* kp, const bf16x8* qf, f32x16& s_next,
-                                           const f32x16& s_cur, float c2, float m_run,
-                                           float& l_run, bf16x8* p_cur) {
-  pv_chunk(vp, p_prev[0], o);
-  pv_chunk(vp + 16, p_prev[1], o);
-  s_next = qk_block(kp, qf);
+  s_next = s;
+  const float mt = block_max(s_cur, c2);
   block_probs(s_cur, c2, m_run, l_run, p_cur);
   // materialise the probabilities here, so that they are not sunk past the
-  // branches that follow (they must share this block with the MFMAs)
-#ifndef SEGATTN_NO_PIN
+  // branch that follows (they must share this block with the MFMAs)
   asm volatile("" : "+v"(p_cur[0]), "+v"(p_cur[1]), "+v"(l_run));
-#endif
+  return mt;
+}
+
+// Rare path of a step: move the running max to the block max where it ran
+// ahead by more than the slack, rescale O (which holds every block before this
+// one) and the sum accumulated before this block, and recompute the block's
+// probabilities against the new max.
+__device__ __forceinline__ void rescale_step(float mt, float& m_run, float l_before, float& l_run,
+                                             f32x16* o, const f32x16& s_cur, float c2,
+                                             bf16x8* p_cur) {
+  const bool need = mt > m_run + kRescaleSlack;
+  const float mn = need ? mt : m_run;
+  const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] *= alpha;
+  m_run = mn;
+  l_run = l_before * alpha;
+  block_probs(s_cur, c2, m_run, l_run, p_cur);
+}
+
+__device__ __forceinline__ f32x16 qk_block(const uint16_t* kp, const bf16x8* qf) {
+  f32x16 s = {};
+#pragma unroll
+  for (int cd = 0; cd < 8; ++cd)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kp + 16 * cd),
+                                                qf[cd], s, 0, 0, 0);
+  return s;
 }
 
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a) {
@@ -255,13 +264,30 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, r32 = lane & 31;
 
-  const int tpf = (P + BN - 1) / BN;
-  const int nvid = I.n_frames_kv * tpf;
-  const int ntiles = nvid + (I.n_text_kv + BN - 1) / BN;
+  ChunkOffsets off;
+#pragma unroll
+  for (int i = 0; i < kKChunks; ++i) {
+    const int c = tid + kThreads * i;
+    off.k[i] = static_cast<uint32_t>((c >> 4) * kD * 2 + (c & 15) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < kVChunks; ++i) {
+    const int c = tid + kThreads * i;
+    off.v_video[i] = static_cast<uint32_t>((c >> 3) * P * 2 + (c & 7) * 16);
+    off.v_text[i] = static_cast<uint32_t>((c >> 3) * I.text_cap * 2 + (c & 7) * 16);
+  }
 
-  // start the first K/V loads before the RoPE prologue
+  const int tpf = (P + BN - 1) / BN;
+  const int ntiles = I.n_frames_kv * tpf + (I.n_text_kv + BN - 1) / BN;
+
+  // the load cursor runs three tiles ahead of the compute tile; nv0..nv2 keep
+  // the valid-key counts of the tiles in between
+  TileCursor lc;
+  lc.fi = 0;
+  cursor_enter(lc, I, h, H, P);
   u32x4 kr[kKChunks], vr[kVChunks];
-  load_tile(tile_at(I, 0, tpf, nvid, h, H, P), tid, kr, vr);
+  int nv0 = cursor_nvalid(lc);
+  load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
 
   if (tid < kD / 2) {
     int axis;
@@ -311,11 +337,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
 
   // ---- prologue: tiles 0, 1 into LDS stages 0, 1; tile 2 in flight ----------
   store_tile(Ks, Vs, tid, kr, vr);
+  int nv1 = 0, nv2 = 0;
   if (ntiles > 1) {
-    load_tile(tile_at(I, 1, tpf, nvid, h, H, P), tid, kr, vr);
+    cursor_next(lc, I, h, H, P);
+    nv1 = cursor_nvalid(lc);
+    load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
     store_tile(Ks + KT, Vs + VT, tid, kr, vr);
   }
-  if (ntiles > 2) load_tile(tile_at(I, 2, tpf, nvid, h, H, P), tid, kr, vr);
+  if (ntiles > 2) {
+    cursor_next(lc, I, h, H, P);
+    nv2 = cursor_nvalid(lc);
+    load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
+  }
   __syncthreads();
 
   const int pi_row = (r32 & ~0xC) | ((r32 & 4) << 1) | ((r32 & 8) >> 1);
@@ -328,20 +361,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   float l_run = 0.f;
   const float c2 = a.scale_log2;
 
-  // Blocks 2t and 2t+1 are the halves of tile t (stage t % 4). Step j runs
-  // PV(j-1) + QK(j+1) on the matrix pipe next to the exponentials of block j,
-  // then the max of block j+1 decides the (rare) rescale. Step 2t still reads
-  // V of tile t-1, so tile t+2 goes to stage (t+2) % 4, last read two steps
-  // before the barrier that precedes the store.
-  f32x16 sa = qk_block(Ks + koff0, qf);     // S of the current block
-  f32x16 sb;                                // S of the next block
-  {
-    const int nv0 = tile_nvalid(I, 0, tpf, nvid, P);
-    if (nv0 < 32) mask_block(sa, nv0, g);
-  }
+  // Blocks 2t and 2t+1 are the halves of tile t (stage t % 4). Step 2t still
+  // reads V of tile t-1, so tile t+2 goes to stage (t+2) % 4, last read before
+  // the barrier that precedes the store.
+  // Each tile has two steps, so the two S buffers and the two P buffers swap
+  // roles between the steps and the loop carries no register copies.
+  f32x16 sa = qk_block(Ks + koff0, qf);     // S of block 2t at the top of the loop
+  f32x16 sb;                                // S of block 2t+1
+  if (nv0 < 32) mask_block(sa, nv0, g);
   float m_run = block_max(sa, c2);          // block 0 always has a valid key
-  bf16x8 pprev[2], pcur[2];
-  pprev[0] = pprev[1] = bf16x8{};
+  bf16x8 pa[2], pb[2];                      // P of block 2t-1 at the top; of 2t
+  pa[0] = pa[1] = bf16x8{};
 
 #pragma unroll 1
   for (int t = 0; t < ntiles; ++t) {
@@ -350,38 +380,47 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     const uint16_t* Vst = Vs + st * VT;
     const uint16_t* Vprev = Vs + ((t + kStages - 1) & (kStages - 1)) * VT;
     const uint16_t* Knext = Ks + ((t + 1) & (kStages - 1)) * KT;
-    const int nvalid = tile_nvalid(I, t, tpf, nvid, P);
+    const int nvalid = nv0;
     __syncthreads();
     // tile t+2: registers -> LDS stage (t+2) % 4; start loading tile t+3
+    int nv3 = 0;
     if (t + 2 < ntiles) {
       const int s2 = (t + 2) & (kStages - 1);
       store_tile(Ks + s2 * KT, Vs + s2 * VT, tid, kr, vr);
-      if (t + 3 < ntiles) load_tile(tile_at(I, t + 3, tpf, nvid, h, H, P), tid, kr, vr);
+      if (t + 3 < ntiles) {
+        cursor_next(lc, I, h, H, P);
+        nv3 = cursor_nvalid(lc);
+        load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
+      }
     }
 
-    // step 2t: PV(2t-1) + QK(2t+1) | exp(2t)
-    fused_step(Vprev + voff + 32, pprev, o, Kst + koff1, qf, sb, sa, c2, m_run, l_run, pcur);
+    // step 2t: PV(2t-1) [pa] + QK(2t+1) [-> sb] | softmax(2t) [sa -> pb]
+    if (nvalid < 32) mask_block(sa, nvalid, g);
+    float l_before = l_run;
+    float mt = fused_step(Vprev + voff + 32, pa, o, Kst + koff1, qf, sb, sa, c2, m_run, l_run, pb);
+    if (__any(mt > m_run + kRescaleSlack))
+      rescale_step(mt, m_run, l_before, l_run, o, sa, c2, pb);
+
+    // step 2t+1: PV(2t) [pb] + QK(2t+2) [-> sa] | softmax(2t+1) [sb -> pa]
     if (nvalid < BN) mask_block(sb, nvalid - 32, g);
-    update_max(block_max(sb, c2), m_run, l_run, o, pcur);
-    pprev[0] = pcur[0];
-    pprev[1] = pcur[1];
-    sa = sb;
+    l_before = l_run;
+    mt = fused_step(Vst + voff, pb, o, Knext + koff0, qf, sa, sb, c2, m_run, l_run, pa);
+    if (__any(mt > m_run + kRescaleSlack))
+      rescale_step(mt, m_run, l_before, l_run, o, sb, c2, pa);
 
-    // step 2t+1: PV(2t) + QK(2t+2) | exp(2t+1)
-    fused_step(Vst + voff, pprev, o, Knext + koff0, qf, sb, sa, c2, m_run, l_run, pcur);
-    if (t + 1 < ntiles) {
-      const int nv1 = tile_nvalid(I, t + 1, tpf, nvid, P);
-      if (nv1 < 32) mask_block(sb, nv1, g);
-      update_max(block_max(sb, c2), m_run, l_run, o, pcur);
-    }
-    pprev[0] = pcur[0];
-    pprev[1] = pcur[1];
-    sa = sb;
+    nv0 = nv1;
+    nv1 = nv2;
+    nv2 = nv3;
   }
   {
     const uint16_t* Vlast = Vs + ((ntiles - 1) & (kStages - 1)) * VT;
-    pv_chunk(Vlast + voff + 32, pprev[0], o);
-    pv_chunk(Vlast + voff + 48, pprev[1], o);
+    const uint16_t* vp = Vlast + voff + 32;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = i >> 2, db = i & 3;
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const bf16x8*>(vp + 16 * c + 32 * db * VS), pa[c], o[db], 0, 0, 0);
+    }
   }
 
   // ---- epilogue ----------------------------------------------------------------
