@@ -33,13 +33,13 @@
 // block max exceeds the running max by more than the slack -- rare after the
 // first blocks -- a wave-uniform branch rescales O and the sum and recomputes
 // the block's probabilities.
-#include "device_common.h"
+#include "attention_common.h"
 
 namespace segattn {
 namespace {
 
 constexpr int BM = 256;          // query rows per workgroup
-constexpr int BN = 64;           // keys per tile
+constexpr int BN = kKeyTile;     // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStages = 4;       // LDS ring depth (power of two)
@@ -50,49 +50,6 @@ constexpr int VT = kD * VS;      // elements of one V^T stage
 constexpr int kKChunks = BN * kD / 8 / kThreads;   // 16-byte K chunks per thread (2)
 constexpr int kVChunks = kD * BN / 8 / kThreads;   // 16-byte V chunks per thread (2)
 constexpr float kRescaleSlack = 8.0f;   // log2 headroom before O is rescaled
-constexpr int kRsrcFlags = 0x00020000;  // raw buffer resource, 32-bit data format
-
-// Scalar walk over the key tiles of one (item, head): video frames in list
-// order (ceil(P / 64) tiles each), then the text slot. Everything here is
-// wave-uniform.
-struct TileCursor {
-  int fi;               // segment: frame-list index, or n_frames (the text slot)
-  int p0;               // first key of the tile within its segment
-  int len;              // keys in the segment (P or n_text)
-  const char* kplane;   // K plane of the segment
-  const char* vplane;   // V^T plane of the segment
-  int vstride;          // tokens per V^T row of the plane (P or text capacity)
-};
-
-__device__ __forceinline__ void cursor_enter(TileCursor& c, const AttnItemDev& I, int h, int H,
-                                             int P) {
-  c.p0 = 0;
-  if (c.fi < I.n_frames_kv) {
-    const int frame = I.frames[c.fi];
-    const size_t plane = (static_cast<size_t>(frame) * H + h) * static_cast<size_t>(P) * kD * 2;
-    c.kplane = static_cast<const char*>(I.k) + plane;
-    c.vplane = static_cast<const char*>(I.v) + plane;
-    c.len = P;
-    c.vstride = P;
-  } else {
-    const size_t plane = static_cast<size_t>(h) * I.text_cap * kD * 2;
-    c.kplane = static_cast<const char*>(I.k_text) + plane;
-    c.vplane = static_cast<const char*>(I.v_text) + plane;
-    c.len = I.n_text_kv;
-    c.vstride = I.text_cap;
-  }
-}
-
-__device__ __forceinline__ void cursor_next(TileCursor& c, const AttnItemDev& I, int h, int H,
-                                            int P) {
-  c.p0 += BN;
-  if (c.p0 >= c.len) {
-    ++c.fi;
-    if (c.fi <= I.n_frames_kv) cursor_enter(c, I, h, H, P);
-  }
-}
-
-__device__ __forceinline__ int cursor_nvalid(const TileCursor& c) { return min(BN, c.len - c.p0); }
 
 // Per-thread byte offsets of this thread's 16-byte chunks inside a tile (K) or
 // a V^T plane (V, for the two row strides in use).
@@ -107,15 +64,8 @@ struct ChunkOffsets {
 // inside the plane are finite cache values that meet zero probabilities.
 __device__ __forceinline__ void load_tile(const TileCursor& c, const ChunkOffsets& off,
                                           bool video, u32x4* kr, u32x4* vr) {
-  const int nv = cursor_nvalid(c);
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(c.kplane + static_cast<size_t>(c.p0) * kD * 2), static_cast<short>(0),
-      nv * kD * 2, kRsrcFlags);
-  // the V^T resource starts at the tile's first column and ends at the plane
-  // end, so the bounds check alone keeps every read inside the plane
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(c.vplane + c.p0 * 2), static_cast<short>(0),
-      c.vstride * kD * 2 - c.p0 * 2, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rk = tile_k_rsrc<2>(c);
+  const __amdgpu_buffer_rsrc_t rv = tile_v_rsrc<2>(c);
 #pragma unroll
   for (int i = 0; i < kKChunks; ++i)
     kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off.k[i], 0, 0));
@@ -140,12 +90,6 @@ __device__ __forceinline__ void store_tile(uint16_t* Ks, uint16_t* Vs, int tid, 
     const int dd = c >> 3, kc = c & 7;
     *reinterpret_cast<u32x4*>(&Vs[dd * VS + kc * 8]) = vr[i];
   }
-}
-
-__device__ __forceinline__ float max_other_half(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // exp2(s * c2 - m) for the 16 keys of a block, packed as two bf16 B operands,
@@ -242,23 +186,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   __shared__ double om[kD / 2];
   __shared__ int ax[kD / 2];
 
-  // XCD-aware order: workgroups go round-robin over the 8 XCDs, so give each
-  // XCD a contiguous run of logical tiles (same head => shared K/V in its L2).
-  const int nb = gridDim.x;
-  const int b = blockIdx.x;
-  const int xcd = b & 7, idx = b >> 3;
-  const int per = nb >> 3, rem = nb & 7;
-  const int logical = xcd * per + min(xcd, rem) + idx;
-
-  int it = 0;
-#pragma unroll 1
-  for (int j = 1; j < a.n_items; ++j)
-    if (logical >= a.items[j].tile_begin) it = j;
-  const AttnItemDev& I = a.items[it];
-  const int local = logical - I.tile_begin;
+  const WorkTile wt = map_workgroup(a, BM);
+  const AttnItemDev& I = a.items[wt.item];
   const int H = a.heads;
-  const int h = local / I.q_tiles;
-  const int q0 = (local - h * I.q_tiles) * BM;
+  const int h = wt.head;
+  const int q0 = wt.q0;
   const int P = a.rope.P;
 
   const int tid = threadIdx.x;
@@ -284,7 +216,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   // the valid-key counts of the tiles in between
   TileCursor lc;
   lc.fi = 0;
-  cursor_enter(lc, I, h, H, P);
+  cursor_enter<2>(lc, I, h, H, P);
   u32x4 kr[kKChunks], vr[kVChunks];
   int nv0 = cursor_nvalid(lc);
   load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
@@ -304,14 +236,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   const int qrow = q0 + 32 * w + r32;
   bf16x8 qf[8];
   {
-    int tpos = 0, hpos = 0, wpos = 0;
-    const bool video = qrow < I.n_q_video;
-    if (video) {
-      const int f = qrow / P, p = qrow - (qrow / P) * P;
-      tpos = I.frame0_q + f;
-      hpos = p / a.rope.lat_w;
-      wpos = p - hpos * a.rope.lat_w;
-    }
+    bool video;
+    int tpos, hpos, wpos;
+    query_position(I, a.rope, qrow, &video, &tpos, &hpos, &wpos);
 #pragma unroll
     for (int cd = 0; cd < 8; ++cd) {
       u32x4 x = {0u, 0u, 0u, 0u};
@@ -339,13 +266,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   store_tile(Ks, Vs, tid, kr, vr);
   int nv1 = 0, nv2 = 0;
   if (ntiles > 1) {
-    cursor_next(lc, I, h, H, P);
+    cursor_next<2>(lc, I, h, H, P);
     nv1 = cursor_nvalid(lc);
     load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
     store_tile(Ks + KT, Vs + VT, tid, kr, vr);
   }
   if (ntiles > 2) {
-    cursor_next(lc, I, h, H, P);
+    cursor_next<2>(lc, I, h, H, P);
     nv2 = cursor_nvalid(lc);
     load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
   }
@@ -388,7 +315,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
       const int s2 = (t + 2) & (kStages - 1);
       store_tile(Ks + s2 * KT, Vs + s2 * VT, tid, kr, vr);
       if (t + 3 < ntiles) {
-        cursor_next(lc, I, h, H, P);
+        cursor_next<2>(lc, I, h, H, P);
         nv3 = cursor_nvalid(lc);
         load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
       }
@@ -422,6 +349,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
           *reinterpret_cast<const bf16x8*>(vp + 16 * c + 32 * db * VS), pa[c], o[db], 0, 0, 0);
     }
   }
+
+  // The output MFMAs compute across all lanes of the wave: keep them (and
+  // everything feeding them) ahead of the per-row store branch below, where
+  // lanes past the last query row are switched off.
+  asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
 
   // ---- epilogue ----------------------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);

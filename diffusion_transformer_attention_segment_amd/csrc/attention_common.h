@@ -1,0 +1,136 @@
+// Pieces shared by the bf16 and fp8 segment-attention kernels: the
+// workgroup -> (session, head, query tile) mapping, the scalar walk over a
+// session's key tiles, and small cross-lane helpers.
+#pragma once
+
+#include "device_common.h"
+
+namespace segattn {
+
+constexpr int kKeyTile = 64;               // keys per tile (both kernels)
+constexpr int kRsrcFlags = 0x00020000;     // raw buffer resource, 32-bit data format
+
+// Workgroups go round-robin over the 8 XCDs; give each XCD a contiguous run
+// of logical tiles (same head => shared K/V in that XCD's L2). Logical tiles
+// are ordered (item, head, query tile).
+struct WorkTile {
+  int item;
+  int head;
+  int q0;
+};
+
+__device__ __forceinline__ WorkTile map_workgroup(const AttnArgs& a, int block_m) {
+  const int nb = gridDim.x;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, idx = b >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  const int logical = xcd * per + min(xcd, rem) + idx;
+  int it = 0;
+#pragma unroll 1
+  for (int j = 1; j < a.n_items; ++j)
+    if (logical >= a.items[j].tile_begin) it = j;
+  const AttnItemDev& I = a.items[it];
+  const int local = logical - I.tile_begin;
+  WorkTile w;
+  w.item = it;
+  w.head = local / I.q_tiles;
+  w.q0 = (local - w.head * I.q_tiles) * block_m;
+  return w;
+}
+
+// Scalar walk over the key tiles of one (item, head): video frames in list
+// order (ceil(P / 64) tiles each, never straddling a frame), then the text
+// slot. Everything here is wave-uniform. ESZ is the cache element size.
+struct TileCursor {
+  int fi;               // segment: frame-list index, or n_frames (the text slot)
+  int p0;               // first key of the tile within its segment
+  int len;              // keys in the segment (P or n_text)
+  const char* kplane;   // K plane of the segment
+  const char* vplane;   // V^T plane of the segment
+  int vstride;          // tokens per V^T row of the plane (P or text capacity)
+  float kscale;         // fp8 planes: the segment's K and V scales (1 for bf16)
+  float vscale;
+};
+
+template <int ESZ>
+__device__ __forceinline__ void cursor_enter(TileCursor& c, const AttnItemDev& I, int h, int H,
+                                             int P) {
+  c.p0 = 0;
+  c.kscale = 1.0f;
+  c.vscale = 1.0f;
+  if (c.fi < I.n_frames_kv) {
+    const int frame = I.frames[c.fi];
+    const size_t plane = (static_cast<size_t>(frame) * H + h) * static_cast<size_t>(P) * kD * ESZ;
+    c.kplane = static_cast<const char*>(I.k) + plane;
+    c.vplane = static_cast<const char*>(I.v) + plane;
+    c.len = P;
+    c.vstride = P;
+    if (ESZ == 1) {
+      c.kscale = I.k_scale[static_cast<size_t>(frame) * H + h];
+      c.vscale = I.v_scale[static_cast<size_t>(frame) * H + h];
+    }
+  } else {
+    const size_t plane = static_cast<size_t>(h) * I.text_cap * kD * ESZ;
+    c.kplane = static_cast<const char*>(I.k_text) + plane;
+    c.vplane = static_cast<const char*>(I.v_text) + plane;
+    c.len = I.n_text_kv;
+    c.vstride = I.text_cap;
+    if (ESZ == 1 && I.n_text_kv > 0) {
+      c.kscale = I.k_text_scale[h];
+      c.vscale = I.v_text_scale[h];
+    }
+  }
+}
+
+template <int ESZ>
+__device__ __forceinline__ void cursor_next(TileCursor& c, const AttnItemDev& I, int h, int H,
+                                            int P) {
+  c.p0 += kKeyTile;
+  if (c.p0 >= c.len) {
+    ++c.fi;
+    if (c.fi <= I.n_frames_kv) cursor_enter<ESZ>(c, I, h, H, P);
+  }
+}
+
+__device__ __forceinline__ int cursor_nvalid(const TileCursor& c) {
+  return min(kKeyTile, c.len - c.p0);
+}
+
+// Buffer resources of the cursor's tile: the K resource covers the tile's
+// valid rows (rows past them read as zero), the V^T resource runs from the
+// tile's first column to the plane end (so no read leaves the plane).
+template <int ESZ>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_k_rsrc(const TileCursor& c) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(c.kplane + static_cast<size_t>(c.p0) * kD * ESZ), static_cast<short>(0),
+      cursor_nvalid(c) * kD * ESZ, kRsrcFlags);
+}
+
+template <int ESZ>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_v_rsrc(const TileCursor& c) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(c.vplane + c.p0 * ESZ),
+                                           static_cast<short>(0),
+                                           (c.vstride * kD - c.p0) * ESZ, kRsrcFlags);
+}
+
+// max(x, x of the lane 32 away): both halves of a wave end with the same value.
+__device__ __forceinline__ float max_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// RoPE position of query row `row` (video rows in raster order, then text).
+__device__ __forceinline__ void query_position(const AttnItemDev& I, const RopeParams& r, int row,
+                                               bool* video, int* t, int* hh, int* ww) {
+  *video = row < I.n_q_video;
+  *t = *hh = *ww = 0;
+  if (*video) {
+    const int f = row / r.P, p = row - (row / r.P) * r.P;
+    *t = I.frame0_q + f;
+    *hh = p / r.lat_w;
+    *ww = p - *hh * r.lat_w;
+  }
+}
+
+}  // namespace segattn

@@ -334,10 +334,9 @@ sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, i
       if (!aligned16(it.q) || !aligned16(it.out)) return fail(SA_E_ALIGN, "item %d: q/out not aligned", i);
     }
   }
-  if (dtype != SA_KV_BF16)
-    return fail(SA_E_UNSUPPORTED, "segment_attention: fp8 cache path is not built yet");
   AttnArgs a{};
-  const int bm = attention_block_m_bf16();
+  const bool fp8 = dtype == SA_KV_FP8_E4M3;
+  const int bm = fp8 ? attention_block_m_fp8() : attention_block_m_bf16();
   int64_t tiles = 0;
   for (int i = 0; i < n_items; ++i) {
     const sa_attn_item& it = items[i];
@@ -374,7 +373,8 @@ sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, i
   a.rope = rope_params(geom);
   // items with no query rows own no tiles; point them past the end
   for (int i = n_items; i < SA_MAX_ITEMS; ++i) a.items[i].tile_begin = a.total_tiles;
-  return hip_status(launch_attention_bf16(a, static_cast<hipStream_t>(stream)),
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(fp8 ? launch_attention_fp8(a, s) : launch_attention_bf16(a, s),
                     "segment_attention launch");
 }
 

@@ -128,6 +128,62 @@ class Session:
             out[:, h], lse[:, h] = oatt.attention(qr[:, h], kr[:, h], v[:, h], scale)
         return out, lse
 
+    def oracle_fp8_cache(self, rows=None, heads=None, split_q=False):
+        """Oracle for an e4m3 cache: fp64 attention over the values the cache
+        stores -- the oracle's own quantised-then-dequantised K and V (per
+        (frame, head) planes, per head for text) -- and the fp64 rotated Q.
+        split_q=True is the diagnostic variant that also models the kernel's
+        query precision (split_query_fp8).
+
+        Returns (out, lse, bound): `bound` is the per-element error that rounding
+        the probabilities to e4m3 can add (the kernel multiplies V by e4m3
+        probabilities p' = p * 256 * vs / vmax): at most 2^-4 relative for each
+        normal p', at most 2^-10 absolute (in p' units) below the normal range,
+        i.e. sum_j (2^-4 p_j + 2^-10 vmax / (256 vs_j)) |v_jd| / sum_j p_j."""
+        from oracle import cache as ocache
+        wl = self.wl
+        hs = list(range(wl.heads)) if heads is None else list(heads)
+        F, P = wl.lat_t, wl.P
+        ks, vs, vsc_key = [], [], []
+        for f in self.frames:
+            seg, fo = divmod(f, F)
+            kin = self.raw_k[seg][fo * P:(fo + 1) * P].float().cpu().double().numpy()
+            vin = self.raw_v[seg][fo * P:(fo + 1) * P].float().cpu().double().numpy()
+            kc, ksc, vc, vsc = ocache.append_fp8(kin, vin, f, wl.lat_h, wl.lat_w, wl.split,
+                                                 self.geom.rope_theta)
+            ks.append(ocache.dequant(kc[0], ksc[0][:, None, None]).transpose(1, 0, 2)[:, hs])
+            vs.append(ocache.dequant(vc[0], vsc[0][:, None, None]).transpose(2, 0, 1)[:, hs])
+            vsc_key.append(np.repeat(vsc[0][None, hs], P, axis=0))
+        tk = self.text_k.float().cpu().double().numpy()
+        tv = self.text_v.float().cpu().double().numpy()
+        kc, ksc, vc, vsc = ocache.append_text_fp8(tk, tv)
+        ks.append(ocache.dequant(kc, ksc[:, None, None]).transpose(1, 0, 2)[:, hs])
+        vs.append(ocache.dequant(vc, vsc[:, None, None]).transpose(2, 0, 1)[:, hs])
+        vsc_key.append(np.repeat(vsc[None, hs], wl.n_text, axis=0))
+        k = np.concatenate(ks)          # already rotated
+        v = np.concatenate(vs)
+        vsk = np.concatenate(vsc_key).astype(np.float64)     # [Lk, heads]
+        q = self.q[:, hs].float().cpu().double().numpy()
+        if rows is None:
+            rows = np.arange(q.shape[0])
+        qr = orope.rope3d(q[rows], self.q_positions()[rows], wl.split, self.geom.rope_theta)
+        qq = qr.copy()
+        if split_q:
+            for i in range(qr.shape[0]):
+                for j in range(qr.shape[1]):
+                    qq[i, j] = split_query_fp8(qr[i, j])
+        scale = 1.0 / math.sqrt(wl.head_dim)
+        out = np.zeros(qq.shape)
+        lse = np.zeros(qq.shape[:2])
+        bound = np.zeros(qq.shape)
+        for j in range(qq.shape[1]):
+            out[:, j], lse[:, j] = oatt.attention(qq[:, j], k[:, j], v[:, j], scale)
+            s_ = (qq[:, j] @ k[:, j].T) * scale
+            p_ = np.exp(s_ - s_.max(axis=1, keepdims=True))
+            floor = 2.0 ** -10 * vsk[:, j].max() / (256.0 * vsk[:, j])
+            bound[:, j] = ((2.0 ** -4 * p_ + floor[None, :]) @ np.abs(v[:, j])) / p_.sum(1)[:, None]
+        return out, lse, bound
+
     def gpu_out(self, rows=None, heads=None):
         o = self.out.float().cpu().double().numpy()
         l = self.lse.cpu().double().numpy()
@@ -136,6 +192,22 @@ class Session:
         if heads is not None:
             o, l = o[:, list(heads)], l[:, list(heads)]
         return o, l
+
+
+def split_query_fp8(q):
+    """Real value of a rotated query row as the e4m3 kernel takes it: fp32
+    decisions, amax = max |q|, y = fp32(q * fp32(448 / amax)), hi = e4m3(y),
+    lo = e4m3(16 (y - hi)), value (hi + lo / 16) * fp32(amax / 448)."""
+    q32 = np.asarray(q, dtype=np.float64).astype(np.float32)
+    amax = np.float32(np.max(np.abs(q32)))
+    if amax == 0:
+        return np.zeros(q32.shape)
+    inv = np.float32(448.0) / amax
+    scale = np.float64(amax / np.float32(448.0))
+    y = (q32 * inv).astype(np.float32).astype(np.float64)
+    hi = onum.e4m3_decode(onum.e4m3_encode(y))
+    lo = onum.e4m3_decode(onum.e4m3_encode(16.0 * (y - hi)))
+    return (hi + lo / 16.0) * scale
 
 
 def compare(got, want, max_abs, mean_abs, label=""):
