@@ -200,8 +200,9 @@ sa_status sa_history_gather(const sa_geom* geom, const sa_kv_layer* src, const i
  *   out = softmax(scale * rope(q) . K^T) V over the item's key set
  * (frames list in order, then n_text_kv text keys), fp32 accumulation, bf16
  * output. bf16 layers use bf16 MFMA; fp8 layers use fp8 MFMA with queries
- * quantised per (row, head) and the per-(frame, head) scales applied to the
- * logits and folded into the probabilities. All items must share one dtype.
+ * split per (row, head) into an e4m3 high part and an e4m3 low part (scaled
+ * by 2^-4), and the per-(frame, head) scales applied to the logits and folded
+ * into the probabilities. All items must share one dtype.
  * Source: "How one segment is made" and "What 'world memory' stores".
  * Errors: SA_E_ARG (n_items outside [1, SA_MAX_ITEMS], empty key set),
  * SA_E_RANGE (n_frames_kv > SA_MAX_FRAMES_KV, n_text_kv > text_capacity).   */
