@@ -49,31 +49,30 @@ constexpr int KT = BN * KS;      // elements of one K stage
 constexpr int VT = kD * VS;      // elements of one V^T stage
 constexpr int kKChunks = BN * kD / 8 / kThreads;   // 16-byte K chunks per thread (2)
 constexpr int kVChunks = kD * BN / 8 / kThreads;   // 16-byte V chunks per thread (2)
-constexpr float kRescaleSlack = 8.0f;   // log2 headroom before O is rescaled
-
-// Per-thread byte offsets of this thread's 16-byte chunks inside a tile (K) or
-// a V^T plane (V, for the two row strides in use).
-struct ChunkOffsets {
-  uint32_t k[kKChunks];
-  uint32_t v_video[kVChunks];
-  uint32_t v_text[kVChunks];
-};
+constexpr float kRescaleSum = 256.0f;   // a row's block sum above this moves the running max
 
 // Load tile c: K rows past the valid count and V^T bytes past the plane end
 // read as zero through the buffer bounds; V^T columns past the valid count
 // inside the plane are finite cache values that meet zero probabilities.
-__device__ __forceinline__ void load_tile(const TileCursor& c, const ChunkOffsets& off,
-                                          bool video, u32x4* kr, u32x4* vr) {
+// Thread tid loads the 16-byte chunks tid + 512 i (i = 0, 1) of the K tile
+// (byte 16 * chunk) and of the V^T tile (row chunk / 8, column chunk % 8).
+// koff = 16 * tid.
+__device__ __forceinline__ void load_tile(const TileCursor& c, uint32_t koff, u32x4* kr,
+                                          u32x4* vr) {
   const __amdgpu_buffer_rsrc_t rk = tile_k_rsrc<2>(c);
   const __amdgpu_buffer_rsrc_t rv = tile_v_rsrc<2>(c);
+  // recompute from koff at every tile rather than keep (or spill) its parts
+  uint32_t k = koff;
+  asm("" : "+v"(k));
+  const uint32_t voff = (k >> 7) * static_cast<uint32_t>(c.vstride * 2) + (k & 0x70u);
 #pragma unroll
   for (int i = 0; i < kKChunks; ++i)
-    kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off.k[i], 0, 0));
+    kr[i] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, i * kThreads * 16, 0));
 #pragma unroll
   for (int i = 0; i < kVChunks; ++i)
     vr[i] = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, video ? off.v_video[i] : off.v_text[i],
-                                                     0, 0));
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, i * (kThreads / 8) * c.vstride * 2, 0));
 }
 
 __device__ __forceinline__ void store_tile(uint16_t* Ks, uint16_t* Vs, int tid, const u32x4* kr,
@@ -92,23 +91,33 @@ __device__ __forceinline__ void store_tile(uint16_t* Ks, uint16_t* Vs, int tid, 
   }
 }
 
-// exp2(s * c2 - m) for the 16 keys of a block, packed as two bf16 B operands,
-// with their fp32 sum folded into l. (The sum uses plain adds: this compiler
-// emits v_dot2c_f32_bf16 sequences that read the same source word each time.)
-__device__ __forceinline__ void block_probs(const f32x16& s, float c2, float m, float& l,
-                                            bf16x8* p) {
+// l + lo(a) * lo(b) + hi(a) * hi(b) for packed bf16 pairs, fp32 accumulate.
+// (Written out: the compiler's v_dot2c lowering of the builtin reads one
+// source word for every element of an unrolled chain.)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float l) {
+  float d;
+  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(l));
+  return d;
+}
+
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
+
+// exp2 of the 16 logits of a block (already relative to the running max),
+// packed as two bf16 B operands; returns the sum of the packed values.
+__device__ __forceinline__ float block_probs(const f32x16& s, uint32_t ones, bf16x8* p) {
+  float l = 0.f;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     u32x4 pw;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * c + 2 * k], c2, -m));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * c + 2 * k + 1], c2, -m));
-      pw[k] = pack_bf16x2(p0, p1);
-      l += p0 + p1;
+      pw[k] = pack_bf16x2(__builtin_amdgcn_exp2f(s[8 * c + 2 * k]),
+                          __builtin_amdgcn_exp2f(s[8 * c + 2 * k + 1]));
+      l = dot2_bf16(pw[k], ones, l);
     }
     p[c] = __builtin_bit_cast(bf16x8, pw);
   }
+  return l;
 }
 
 // Keys of a 32-key block at or beyond `nvalid` (relative to the block) get -inf.
@@ -120,55 +129,105 @@ __device__ __forceinline__ void mask_block(f32x16& s, int nvalid, int g) {
   }
 }
 
-// Block max of S^T over its 32 keys (both lane halves), in log2 units.
-__device__ __forceinline__ float block_max(const f32x16& s, float c2) {
+// Block max of S^T over its 32 keys (both lane halves).
+__device__ __forceinline__ float block_max(const f32x16& s) {
   float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
   for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
-  return max_other_half(fmaxf(mx, s[15])) * c2;
+  return max_other_half(fmaxf(mx, s[15]));
 }
 
-// One pipeline step, one basic block: PV of the previous block (P^T in p_prev,
-// V^T rows at vp) and QK^T of the next block (K rows at kp) on the matrix
-// pipe, alternating; next to them the max and the exponentials of the current
-// block s_cur against the running max m_run. Returns the block max (log2).
-__device__ __forceinline__ float fused_step(const uint16_t* vp, const bf16x8* p_prev, f32x16* o,
-                                            const uint16_t* kp, const bf16x8* qf, f32x16& s_next,
-                                            const f32x16& s_cur, float c2, float m_run,
-                                            float& l_run, bf16x8* p_cur) {
-  f32x16 s = {};
+__device__ __forceinline__ bf16x8 lds_op(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// LDS operands of the first two slots of a step, read during the step before.
+struct StepOperands {
+  bf16x8 v[2];
+  bf16x8 k[2];
+};
+
+__device__ __forceinline__ const uint16_t* v_operand(const uint16_t* vp, int j) {
+  return vp + 16 * (j >> 2) + 32 * (j & 3) * VS;   // keys 16(j/4).., dims 32(j%4)..
+}
+
+// One pipeline step. Logits are in log2 units relative to the running max m:
+// the queries carry the softmax scale * log2(e), and the QK^T accumulation
+// starts from C = -m (negm), so a probability is one exp2 of an accumulator.
+// The step issues, slot by slot, PV of the previous block (P^T in p_prev, V^T
+// rows at vp) and QK^T of the next block (K rows at kp) on the matrix pipe,
+// the LDS reads of the operands two slots ahead (the last two slots read the
+// first operands of the next step, at vp_next / kp_next, into `pre`), and the
+// exponentials of the current block s_cur with their packing and sum.
+// `work` runs in slot 1, once the first MFMAs are queued. Returns the block's
+// sum.
+template <typename Work>
+__device__ __forceinline__ float fused_step(const uint16_t* vp, const uint16_t* kp,
+                                            const uint16_t* vp_next, const uint16_t* kp_next,
+                                            StepOperands& pre, const bf16x8* p_prev, f32x16* o,
+                                            const bf16x8* qf, const f32x16& negm, f32x16& s_next,
+                                            const f32x16& s_cur, uint32_t ones, bf16x8* p_cur,
+                                            Work&& work) {
+  bf16x8 av[8], ak[8];
+  av[0] = pre.v[0];
+  av[1] = pre.v[1];
+  ak[0] = pre.k[0];
+  ak[1] = pre.k[1];
+  u32x4 pw[2];
+  float l0 = 0.f, l1 = 0.f;
+  f32x16 s;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
+    const int j = i + 2;
+    if (j < 8) {
+      av[j] = lds_op(v_operand(vp, j));
+      ak[j] = lds_op(kp + 16 * j);
+    } else {
+      pre.v[j - 8] = lds_op(v_operand(vp_next, j - 8));
+      pre.k[j - 8] = lds_op(kp_next + 16 * (j - 8));
+    }
     const int c = i >> 2, db = i & 3;
-    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        *reinterpret_cast<const bf16x8*>(vp + 16 * c + 32 * db * VS), p_prev[c], o[db], 0, 0, 0);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(kp + 16 * i),
-                                                qf[i], s, 0, 0, 0);
+    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], p_prev[c], o[db], 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[i], qf[i], i == 0 ? negm : s, 0, 0, 0);
+    pw[c][db] = pack_bf16x2(__builtin_amdgcn_exp2f(s_cur[2 * i]),
+                            __builtin_amdgcn_exp2f(s_cur[2 * i + 1]));
+    if (i & 1)
+      l1 = dot2_bf16(pw[c][db], ones, l1);
+    else
+      l0 = dot2_bf16(pw[c][db], ones, l0);
+    if (i == 1) work();
+    __builtin_amdgcn_sched_barrier(0);
   }
   s_next = s;
-  const float mt = block_max(s_cur, c2);
-  block_probs(s_cur, c2, m_run, l_run, p_cur);
+  p_cur[0] = __builtin_bit_cast(bf16x8, pw[0]);
+  p_cur[1] = __builtin_bit_cast(bf16x8, pw[1]);
+  float l = l0 + l1;
   // materialise the probabilities here, so that they are not sunk past the
   // branch that follows (they must share this block with the MFMAs)
-  asm volatile("" : "+v"(p_cur[0]), "+v"(p_cur[1]), "+v"(l_run));
-  return mt;
+  asm volatile("" : "+v"(p_cur[0]), "+v"(p_cur[1]), "+v"(l));
+  return l;
 }
 
-// Rare path of a step: move the running max to the block max where it ran
-// ahead by more than the slack, rescale O (which holds every block before this
-// one) and the sum accumulated before this block, and recompute the block's
-// probabilities against the new max.
-__device__ __forceinline__ void rescale_step(float mt, float& m_run, float l_before, float& l_run,
-                                             f32x16* o, const f32x16& s_cur, float c2,
-                                             bf16x8* p_cur) {
-  const bool need = mt > m_run + kRescaleSlack;
-  const float mn = need ? mt : m_run;
-  const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+// Rare path of a step, taken by the whole wave when some row's block sum
+// exceeds kRescaleSum (a probability above it, or many close to it): rows
+// whose block max lies above the running max move it there. O (every block
+// before this one), the sum before this block, the -m accumulator seed and the
+// already issued next block are shifted by the same amount, and the block's
+// probabilities are recomputed.
+__device__ __forceinline__ float rescale_step(f32x16& negm, float& l_run, f32x16* o,
+                                              f32x16& s_cur, f32x16& s_next, uint32_t ones,
+                                              bf16x8* p_cur) {
+  const float d = fmaxf(block_max(s_cur), 0.f);
+  const float alpha = __builtin_amdgcn_exp2f(-d);
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] *= alpha;
-  m_run = mn;
-  l_run = l_before * alpha;
-  block_probs(s_cur, c2, m_run, l_run, p_cur);
+  l_run *= alpha;
+  // whole-vector updates, so that each value keeps its registers across the
+  // branch (element-wise updates leave copies on the common path)
+  negm = negm - d;
+  s_cur = s_cur - d;
+  s_next = s_next - d;
+  return block_probs(s_cur, ones, p_cur);
 }
 
 __device__ __forceinline__ f32x16 qk_block(const uint16_t* kp, const bf16x8* qf) {
@@ -196,19 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, r32 = lane & 31;
 
-  ChunkOffsets off;
-#pragma unroll
-  for (int i = 0; i < kKChunks; ++i) {
-    const int c = tid + kThreads * i;
-    off.k[i] = static_cast<uint32_t>((c >> 4) * kD * 2 + (c & 15) * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < kVChunks; ++i) {
-    const int c = tid + kThreads * i;
-    off.v_video[i] = static_cast<uint32_t>((c >> 3) * P * 2 + (c & 7) * 16);
-    off.v_text[i] = static_cast<uint32_t>((c >> 3) * I.text_cap * 2 + (c & 7) * 16);
-  }
-
+  const uint32_t koff_ld = static_cast<uint32_t>(tid) * 16u;
   const int tpf = (P + BN - 1) / BN;
   const int ntiles = I.n_frames_kv * tpf + (I.n_text_kv + BN - 1) / BN;
 
@@ -219,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   cursor_enter<2>(lc, I, h, H, P);
   u32x4 kr[kKChunks], vr[kVChunks];
   int nv0 = cursor_nvalid(lc);
-  load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
+  load_tile(lc, koff_ld, kr, vr);
 
   if (tid < kD / 2) {
     int axis;
@@ -232,10 +279,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     reinterpret_cast<u32x4*>(Vs + (kStages - 1) * VT)[i] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
-  // ---- Q fragments (B operand of S^T = K Q^T), rotated in fp32 -------------
+  // ---- Q fragments (B operand of S^T = K Q^T): rotated in fp32, times the
+  // softmax scale * log2(e), rounded to bf16 ----------------------------------
   const int qrow = q0 + 32 * w + r32;
   bf16x8 qf[8];
   {
+    const float c2 = a.scale_log2;
     bool video;
     int tpos, hpos, wpos;
     query_position(I, a.rope, qrow, &video, &tpos, &hpos, &wpos);
@@ -245,18 +294,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
       if (qrow < I.n_q)
         x = *reinterpret_cast<const u32x4*>(I.q + (static_cast<size_t>(qrow) * H + h) * kD +
                                             16 * cd + 8 * g);
-      if (video) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float xa = __uint_as_float(x[m] << 16);
-          const float xb = __uint_as_float(x[m] & 0xFFFF0000u);
+      for (int m = 0; m < 4; ++m) {
+        float xa = __uint_as_float(x[m] << 16);
+        float xb = __uint_as_float(x[m] & 0xFFFF0000u);
+        if (video) {
           const int pr = 8 * cd + 4 * g + m;
           const int axis = ax[pr];
           const int pos = axis == 0 ? tpos : (axis == 1 ? hpos : wpos);
           float c, s;
           rope_cos_sin(pos, om[pr], &c, &s);
-          x[m] = pack_bf16x2(xa * c - xb * s, xa * s + xb * c);
+          const float ya = xa * c - xb * s;
+          xb = xa * s + xb * c;
+          xa = ya;
         }
+        x[m] = pack_bf16x2(xa * c2, xb * c2);
       }
       qf[cd] = __builtin_bit_cast(bf16x8, x);
     }
@@ -268,13 +320,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   if (ntiles > 1) {
     cursor_next<2>(lc, I, h, H, P);
     nv1 = cursor_nvalid(lc);
-    load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
+    load_tile(lc, koff_ld, kr, vr);
     store_tile(Ks + KT, Vs + VT, tid, kr, vr);
   }
   if (ntiles > 2) {
     cursor_next<2>(lc, I, h, H, P);
     nv2 = cursor_nvalid(lc);
-    load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
+    load_tile(lc, koff_ld, kr, vr);
   }
   __syncthreads();
 
@@ -286,19 +338,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
   float l_run = 0.f;
-  const float c2 = a.scale_log2;
+  const uint32_t ones = kOnesBf16x2;
 
   // Blocks 2t and 2t+1 are the halves of tile t (stage t % 4). Step 2t still
   // reads V of tile t-1, so tile t+2 goes to stage (t+2) % 4, last read before
   // the barrier that precedes the store.
   // Each tile has two steps, so the two S buffers and the two P buffers swap
   // roles between the steps and the loop carries no register copies.
+  // The running max starts at block 0's max (block 0 always has a valid key).
   f32x16 sa = qk_block(Ks + koff0, qf);     // S of block 2t at the top of the loop
   f32x16 sb;                                // S of block 2t+1
   if (nv0 < 32) mask_block(sa, nv0, g);
-  float m_run = block_max(sa, c2);          // block 0 always has a valid key
+  const float m0 = block_max(sa);
+  f32x16 negm;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    negm[r] = -m0;
+    sa[r] -= m0;
+  }
   bf16x8 pa[2], pb[2];                      // P of block 2t-1 at the top; of 2t
   pa[0] = pa[1] = bf16x8{};
+
+  // operands of step 0's first slots: V of "tile -1" (the zeroed last stage,
+  // met by the zero probabilities pa) and block 1's K rows
+  StepOperands pre;
+  pre.v[0] = lds_op(v_operand(Vs + (kStages - 1) * VT + voff + 32, 0));
+  pre.v[1] = lds_op(v_operand(Vs + (kStages - 1) * VT + voff + 32, 1));
+  pre.k[0] = lds_op(Ks + koff1);
+  pre.k[1] = lds_op(Ks + koff1 + 16);
 
 #pragma unroll 1
   for (int t = 0; t < ntiles; ++t) {
@@ -308,32 +375,39 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     const uint16_t* Vprev = Vs + ((t + kStages - 1) & (kStages - 1)) * VT;
     const uint16_t* Knext = Ks + ((t + 1) & (kStages - 1)) * KT;
     const int nvalid = nv0;
-    __syncthreads();
-    // tile t+2: registers -> LDS stage (t+2) % 4; start loading tile t+3
     int nv3 = 0;
-    if (t + 2 < ntiles) {
-      const int s2 = (t + 2) & (kStages - 1);
-      store_tile(Ks + s2 * KT, Vs + s2 * VT, tid, kr, vr);
-      if (t + 3 < ntiles) {
-        cursor_next<2>(lc, I, h, H, P);
-        nv3 = cursor_nvalid(lc);
-        load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
+    // Tile t+2: registers -> LDS stage (t+2) % 4, the stage of tile t-2, whose
+    // last reads (step 2t-2) completed before this barrier; then start loading
+    // tile t+3. Nothing read in this tile's steps lives in that stage, so the
+    // barrier needs no fence and the reads already in flight stay in flight.
+    auto boundary = [&]() {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + 2 < ntiles) {
+        const int s2 = (t + 2) & (kStages - 1);
+        store_tile(Ks + s2 * KT, Vs + s2 * VT, tid, kr, vr);
+        if (t + 3 < ntiles) {
+          cursor_next<2>(lc, I, h, H, P);
+          nv3 = cursor_nvalid(lc);
+          load_tile(lc, koff_ld, kr, vr);
+        }
       }
-    }
+    };
 
     // step 2t: PV(2t-1) [pa] + QK(2t+1) [-> sb] | softmax(2t) [sa -> pb]
     if (nvalid < 32) mask_block(sa, nvalid, g);
-    float l_before = l_run;
-    float mt = fused_step(Vprev + voff + 32, pa, o, Kst + koff1, qf, sb, sa, c2, m_run, l_run, pb);
-    if (__any(mt > m_run + kRescaleSlack))
-      rescale_step(mt, m_run, l_before, l_run, o, sa, c2, pb);
+    float lb = fused_step(Vprev + voff + 32, Kst + koff1, Vst + voff, Knext + koff0, pre, pa, o,
+                          qf, negm, sb, sa, ones, pb, boundary);
+    if (__any(lb > kRescaleSum)) lb = rescale_step(negm, l_run, o, sa, sb, ones, pb);
+    l_run += lb;
 
     // step 2t+1: PV(2t) [pb] + QK(2t+2) [-> sa] | softmax(2t+1) [sb -> pa]
     if (nvalid < BN) mask_block(sb, nvalid - 32, g);
-    l_before = l_run;
-    mt = fused_step(Vst + voff, pb, o, Knext + koff0, qf, sa, sb, c2, m_run, l_run, pa);
-    if (__any(mt > m_run + kRescaleSlack))
-      rescale_step(mt, m_run, l_before, l_run, o, sb, c2, pa);
+    lb = fused_step(Vst + voff, Knext + koff0, Vst + voff + 32, Knext + koff1, pre, pb, o, qf,
+                    negm, sa, sb, ones, pa, [] {});
+    if (__any(lb > kRescaleSum)) lb = rescale_step(negm, l_run, o, sb, sa, ones, pa);
+    l_run += lb;
 
     nv0 = nv1;
     nv1 = nv2;
@@ -349,6 +423,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
           *reinterpret_cast<const bf16x8*>(vp + 16 * c + 32 * db * VS), pa[c], o[db], 0, 0, 0);
     }
   }
+  const float m_run = -negm[0];
 
   // The output MFMAs compute across all lanes of the wave: keep them (and
   // everything feeding them) ahead of the per-row store branch below, where

@@ -104,10 +104,11 @@ class Session:
     def oracle(self, rows=None, heads=None, round_rotated=False):
         """Oracle (out, lse) for the given rows and heads.
 
-        round_rotated=True is the diagnostic variant: rotated queries and keys
-        are rounded to bf16 before the fp64 attention, modelling the documented
-        storage of rotated keys in a bf16 cache and the bf16 MFMA operands, so
-        what remains is the kernel's own arithmetic error.
+        round_rotated=True is the diagnostic variant: it models the bf16
+        operands of the kernel -- rotated keys rounded to bf16 (the cache) and
+        rotated queries times scale * log2(e) rounded to bf16 (the query
+        operand carries the softmax scale in log2 units) -- before the fp64
+        attention, so what remains is the kernel's own arithmetic error.
         """
         wl = self.wl
         k, v, kpos = self.raw_keys(heads)
@@ -119,8 +120,9 @@ class Session:
                                           self.geom.rope_theta, scale, rows=rows)
         if rows is None:
             rows = np.arange(q.shape[0])
+        c2 = float(np.float32(scale * math.log2(math.e)))
         qr = onum.bf16_round(orope.rope3d(q[rows], self.q_positions()[rows], wl.split,
-                                          self.geom.rope_theta))
+                                          self.geom.rope_theta) * c2) / c2
         kr = onum.bf16_round(orope.rope3d(k, kpos, wl.split, self.geom.rope_theta))
         out = np.zeros(qr.shape)
         lse = np.zeros(qr.shape[:2])

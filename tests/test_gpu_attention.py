@@ -24,6 +24,10 @@ from oracle import select as osel
 pytestmark = pytest.mark.gpu
 
 MAX_ABS, MEAN_ABS, REL_L2 = 2e-2, 2e-3, 1e-2
+# lse: the kernel sums the bf16-rounded probabilities (the values that weight
+# V), each within 2^-9 relative of the exact one, so ln(sum) may move by up to
+# 2^-9 ~ 2e-3 beyond what the bf16 rounding of rotated Q and K already costs.
+LSE_ATOL = 4e-3
 
 
 def _wl(name, H, F, lh, lw, n_text, prior, theta=10000.0):
@@ -55,7 +59,7 @@ def test_parity_small(case):
     got, got_lse = s.gpu_out()
     _, _, rel = compare(got, want, MAX_ABS, MEAN_ABS, name)
     assert rel <= REL_L2
-    np.testing.assert_allclose(got_lse, want_lse, atol=2e-3, rtol=0)
+    np.testing.assert_allclose(got_lse, want_lse, atol=LSE_ATOL, rtol=0)
 
 
 @pytest.mark.parametrize("theta", [256.0, 10000.0])

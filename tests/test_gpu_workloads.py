@@ -22,6 +22,9 @@ from helpers import Session, compare
 pytestmark = pytest.mark.gpu
 
 WL = {w.name: w for w in si.workloads(0)}
+# lse: bf16-rounded probabilities in the row sum (2^-9 relative) plus the
+# bf16 rounding of rotated Q and K.
+LSE_ATOL = 4e-3
 
 
 def _rows(wl, n, seed):
@@ -38,7 +41,7 @@ def _check(sessions, n_rows, heads=None, tol=(2e-2, 2e-3, 1e-2), label=""):
         got, got_lse = s.gpu_out(rows=rows, heads=heads)
         _, _, rel = compare(got, want, tol[0], tol[1], f"{label} session {s.session}")
         assert rel <= tol[2]
-        np.testing.assert_allclose(got_lse, want_lse, atol=3e-3, rtol=0)
+        np.testing.assert_allclose(got_lse, want_lse, atol=LSE_ATOL, rtol=0)
 
 
 def test_tiny_full_output():
@@ -49,7 +52,7 @@ def test_tiny_full_output():
     want, want_lse = s.oracle()
     got, got_lse = s.gpu_out()
     compare(got, want, 2e-2, 2e-3, "tiny")
-    np.testing.assert_allclose(got_lse, want_lse, atol=2e-3, rtol=0)
+    np.testing.assert_allclose(got_lse, want_lse, atol=LSE_ATOL, rtol=0)
 
 
 def test_one_prior_segment():
