@@ -92,12 +92,10 @@ __device__ __forceinline__ void store_tile(uint16_t* Ks, uint16_t* Vs, int tid, 
 }
 
 // l + lo(a) * lo(b) + hi(a) * hi(b) for packed bf16 pairs, fp32 accumulate.
-// (Written out: the compiler's v_dot2c lowering of the builtin reads one
-// source word for every element of an unrolled chain.)
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float l) {
-  float d;
-  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(l));
-  return d;
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s16x2, a), __builtin_bit_cast(s16x2, b),
+                                         l, false);
 }
 
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
@@ -262,8 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   // the load cursor runs three tiles ahead of the compute tile; nv0..nv2 keep
   // the valid-key counts of the tiles in between
   TileCursor lc;
-  lc.fi = 0;
-  cursor_enter<2>(lc, I, h, H, P);
+  cursor_start<2>(lc, I, h, H, P);
   u32x4 kr[kKChunks], vr[kVChunks];
   int nv0 = cursor_nvalid(lc);
   load_tile(lc, koff_ld, kr, vr);
@@ -399,14 +396,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     if (nvalid < 32) mask_block(sa, nvalid, g);
     float lb = fused_step(Vprev + voff + 32, Kst + koff1, Vst + voff, Knext + koff0, pre, pa, o,
                           qf, negm, sb, sa, ones, pb, boundary);
-    if (__any(lb > kRescaleSum)) lb = rescale_step(negm, l_run, o, sa, sb, ones, pb);
+    if (__builtin_expect(__any(lb > kRescaleSum), 0)) lb = rescale_step(negm, l_run, o, sa, sb, ones, pb);
     l_run += lb;
 
     // step 2t+1: PV(2t) [pb] + QK(2t+2) [-> sa] | softmax(2t+1) [sb -> pa]
     if (nvalid < BN) mask_block(sb, nvalid - 32, g);
     lb = fused_step(Vst + voff, Knext + koff0, Vst + voff + 32, Knext + koff1, pre, pb, o, qf,
                     negm, sa, sb, ones, pa, [] {});
-    if (__any(lb > kRescaleSum)) lb = rescale_step(negm, l_run, o, sb, sa, ones, pa);
+    if (__builtin_expect(__any(lb > kRescaleSum), 0)) lb = rescale_step(negm, l_run, o, sb, sa, ones, pa);
     l_run += lb;
 
     nv0 = nv1;

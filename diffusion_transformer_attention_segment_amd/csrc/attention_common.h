@@ -41,8 +41,17 @@ __device__ __forceinline__ WorkTile map_workgroup(const AttnArgs& a, int block_m
 // Scalar walk over the key tiles of one (item, head): video frames in list
 // order (ceil(P / 64) tiles each, never straddling a frame), then the text
 // slot. Everything here is wave-uniform. ESZ is the cache element size.
+// Frame-list entries are read with scalar loads through the constant address
+// space (the list is written before the launch and never during it).
+typedef const __attribute__((address_space(4))) int* const_int_ptr;
+
+__device__ __forceinline__ int frame_entry(const AttnItemDev& I, int fi) {
+  return reinterpret_cast<const_int_ptr>(reinterpret_cast<uintptr_t>(I.frames))[fi];
+}
+
 struct TileCursor {
   int fi;               // segment: frame-list index, or n_frames (the text slot)
+  int fnext;            // frame-list entry fi (before entering it), prefetched
   int p0;               // first key of the tile within its segment
   int len;              // keys in the segment (P or n_text)
   const char* kplane;   // K plane of the segment
@@ -59,7 +68,8 @@ __device__ __forceinline__ void cursor_enter(TileCursor& c, const AttnItemDev& I
   c.kscale = 1.0f;
   c.vscale = 1.0f;
   if (c.fi < I.n_frames_kv) {
-    const int frame = I.frames[c.fi];
+    const int frame = c.fnext;
+    if (c.fi + 1 < I.n_frames_kv) c.fnext = frame_entry(I, c.fi + 1);   // one frame ahead
     const size_t plane = (static_cast<size_t>(frame) * H + h) * static_cast<size_t>(P) * kD * ESZ;
     c.kplane = static_cast<const char*>(I.k) + plane;
     c.vplane = static_cast<const char*>(I.v) + plane;
@@ -80,6 +90,15 @@ __device__ __forceinline__ void cursor_enter(TileCursor& c, const AttnItemDev& I
       c.vscale = I.v_text_scale[h];
     }
   }
+}
+
+// Cursor at the first tile of the item.
+template <int ESZ>
+__device__ __forceinline__ void cursor_start(TileCursor& c, const AttnItemDev& I, int h, int H,
+                                             int P) {
+  c.fi = 0;
+  c.fnext = I.n_frames_kv > 0 ? frame_entry(I, 0) : 0;
+  cursor_enter<ESZ>(c, I, h, H, P);
 }
 
 template <int ESZ>

@@ -235,8 +235,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   const int ntiles = I.n_frames_kv * tpf + (I.n_text_kv + BN - 1) / BN;
 
   TileCursor lc;
-  lc.fi = 0;
-  cursor_enter<1>(lc, I, h, H, P);
+  cursor_start<1>(lc, I, h, H, P);
   u32x4 kr, vr;
   TileInfo ti0 = tile_info(lc);
   load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
