@@ -118,13 +118,15 @@ __device__ __forceinline__ float block_probs(const f32x16& s, uint32_t ones, bf1
   return l;
 }
 
-// Keys of a 32-key block at or beyond `nvalid` (relative to the block) get -inf.
+// Keys of a 32-key block at or beyond `nvalid` (relative to the block) get
+// -inf. (Compared as 16 (r / 8) + r % 8 >= nvalid - 8 g: one per-lane value
+// against immediates, rather than 16 per-lane key indices the compiler would
+// keep in registers across the loop.)
 __device__ __forceinline__ void mask_block(f32x16& s, int nvalid, int g) {
+  const int lim = nvalid - 8 * g;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = 16 * (r >> 3) + 8 * g + (r & 7);
-    if (key >= nvalid) s[r] = -INFINITY;
-  }
+  for (int r = 0; r < 16; ++r)
+    if (16 * (r >> 3) + (r & 7) >= lim) s[r] = -INFINITY;
 }
 
 // Block max of S^T over its 32 keys (both lane halves).
@@ -251,7 +253,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   const int P = a.rope.P;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, r32 = lane & 31;
+  const int lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
 
   const uint32_t koff_ld = static_cast<uint32_t>(tid) * 16u;
   const int tpf = (P + BN - 1) / BN;

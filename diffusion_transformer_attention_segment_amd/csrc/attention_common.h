@@ -49,6 +49,13 @@ __device__ __forceinline__ int frame_entry(const AttnItemDev& I, int fi) {
   return reinterpret_cast<const_int_ptr>(reinterpret_cast<uintptr_t>(I.frames))[fi];
 }
 
+// The same for the fp32 plane scales (written before the launch).
+typedef const __attribute__((address_space(4))) float* const_float_ptr;
+
+__device__ __forceinline__ float scalar_load(const float* p, size_t i) {
+  return reinterpret_cast<const_float_ptr>(reinterpret_cast<uintptr_t>(p))[i];
+}
+
 struct TileCursor {
   int fi;               // segment: frame-list index, or n_frames (the text slot)
   int fnext;            // frame-list entry fi (before entering it), prefetched
@@ -76,8 +83,8 @@ __device__ __forceinline__ void cursor_enter(TileCursor& c, const AttnItemDev& I
     c.len = P;
     c.vstride = P;
     if (ESZ == 1) {
-      c.kscale = I.k_scale[static_cast<size_t>(frame) * H + h];
-      c.vscale = I.v_scale[static_cast<size_t>(frame) * H + h];
+      c.kscale = scalar_load(I.k_scale, static_cast<size_t>(frame) * H + h);
+      c.vscale = scalar_load(I.v_scale, static_cast<size_t>(frame) * H + h);
     }
   } else {
     const size_t plane = static_cast<size_t>(h) * I.text_cap * kD * ESZ;
@@ -86,8 +93,8 @@ __device__ __forceinline__ void cursor_enter(TileCursor& c, const AttnItemDev& I
     c.len = I.n_text_kv;
     c.vstride = I.text_cap;
     if (ESZ == 1 && I.n_text_kv > 0) {
-      c.kscale = I.k_text_scale[h];
-      c.vscale = I.v_text_scale[h];
+      c.kscale = scalar_load(I.k_text_scale, h);
+      c.vscale = scalar_load(I.v_text_scale, h);
     }
   }
 }
@@ -130,6 +137,54 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_v_rsrc(const TileCursor& 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(c.vplane + c.p0 * ESZ),
                                            static_cast<short>(0),
                                            (c.vstride * kD - c.p0) * ESZ, kRsrcFlags);
+}
+
+// Direct-to-LDS tile loads. A stage is ROWS rows of SLOTS 16-byte slots (the
+// last slot of each row is padding); buffer loads with the LDS flag write lane
+// L's 16 bytes to the load's LDS base + 16 L (lanes whose offset is out of the
+// resource write zeros), so load j fills slots 64 j .. 64 j + 63. Wave w of an
+// 8-wave workgroup issues loads j = w, w + 8, ... The global offset of slot
+// (row, ch) is row * row_bytes + 16 ch; padding slots load out of range.
+// Returns the number of loads this wave issued.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int ROWS, int SLOTS>
+__device__ __forceinline__ int dma_tile(__amdgpu_buffer_rsrc_t r, void* stage, uint32_t row_bytes,
+                                        int w) {
+  constexpr int kLoads = ROWS * SLOTS / 64;
+  static_assert(ROWS * SLOTS % 64 == 0, "a stage is a whole number of 1 KB loads");
+  // The lane index is recomputed here (mbcnt) at every tile, so that neither
+  // it nor the per-lane offsets derived from it are kept across the loop.
+  uint32_t lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n v_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  int n_issued = 0;
+#pragma unroll
+  for (int m = 0; m < (kLoads + 7) / 8; ++m) {
+    const int j = w + 8 * m;
+    if (j < kLoads) {
+      const uint32_t n = 64u * j + lane;
+      const uint32_t row = n / SLOTS, ch = n - SLOTS * row;
+      const uint32_t off = ch == SLOTS - 1 ? kOutOfRange : row * row_bytes + ch * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (lds_ptr_t)(static_cast<char*>(stage) + 1024 * j), 16, off, 0, 0, 0);
+      ++n_issued;
+    }
+  }
+  return n_issued;
+}
+
+// Wait until at most n of this wave's vector-memory loads are outstanding
+// (n rounded down to 0, 1, 2 or 4).
+__device__ __forceinline__ void wait_loads(int n) {
+  if (n >= 4)
+    __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
+  else if (n >= 2)
+    __builtin_amdgcn_s_waitcnt(0x0F72);   // vmcnt(2)
+  else if (n == 1)
+    __builtin_amdgcn_s_waitcnt(0x0F71);   // vmcnt(1)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 }
 
 // max(x, x of the lane 32 away): both halves of a wave end with the same value.

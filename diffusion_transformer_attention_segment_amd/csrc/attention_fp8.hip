@@ -11,13 +11,15 @@
 // Scales. The cache holds e4m3 codes with one fp32 scale per (frame, head)
 // plane (per head for the text slot). A key tile never straddles a frame, so
 // its K and V scales are uniform over the tile:
-//   logit = (q_code . k_code) * q_scale[row] * k_scale[tile] * softmax scale
-// -- one coefficient per lane and tile, folded into the exponent's FMA; and
+//   logit (log2 units) = (q_code . k_code) * coef,
+//   coef = q_scale[row] * k_scale[tile] * softmax scale * log2(e);
+//   P'_j = exp2(x_j), x_j = logit_j + log2(pf) - m, pf = 256 * v_scale[tile] / vmax,
+// i.e. P'_j = p_j * pf with p_j = exp2(logit_j - m) -- the probability scale
+// rides in the exponent's FMA offset, one FMA per key. Then
 //   O = sum_j p_j v_j = (vmax / 256) * sum_j P'_j v_code_j,
-//   P'_j = p_j * 256 * v_scale[tile] / vmax,
 // where vmax is the largest V scale among the session's kept planes for this
-// head, so P' <= 256 * 2^slack stays inside e4m3 (max 448) and small
-// probabilities keep 2^-8 more headroom above the e4m3 subnormal floor.
+// head. The running max m moves (rarely) when some x passes 8.5, i.e. P'
+// would pass 362 (e4m3 max 448), to put the largest x at 8.
 // Queries are rotated in fp32, then quantised per (row, head) in two parts:
 // q_scale = amax / 448, y = q * 448 / amax, hi = e4m3(y), lo = e4m3(16 (y - hi)),
 // q ~ (hi + lo / 16) q_scale. Q is never stored, so its split costs only a
@@ -34,11 +36,13 @@
 // B-operand layout of O^T = V^T P^T -- and V^T (transposed in the cache) is
 // read as 32 contiguous bytes per lane.
 //
-// Pipeline: one step per 64-key tile: PV of tile t-1 on the matrix pipe next to
-// the softmax of tile t (max, exponentials against the running max, fp8
-// packing), a wave-uniform branch for the rare running-max increase, then
-// QK^T of tile t+1. K/V tiles go HBM -> registers -> a 4-stage LDS ring, one
-// barrier per tile.
+// Pipeline: one step per 64-key tile. Its 12 MFMAs (PV of tile t-1: 4; QK^T
+// of tile t+1: 2 blocks x 2 k-steps x high/low query parts) are issued slot
+// by slot next to the softmax of tile t, eight 4-key words of exp2 + e4m3
+// packing. S^T is computed in place: block 0 of tile t+1 replaces block 0 of
+// tile t once its words are packed, block 1 after the rescale check. Tiles go
+// HBM -> LDS directly (buffer loads with the LDS flag) two tiles ahead into a
+// 4-stage ring, one barrier per tile.
 #include "attention_common.h"
 
 namespace segattn {
@@ -53,8 +57,9 @@ constexpr int KS8 = kD + 16;           // LDS row stride of the K tile (bytes)
 constexpr int VS8 = BN + 16;           // LDS row stride of the V^T tile (bytes)
 constexpr int KT8 = BN * KS8;          // bytes of one K stage
 constexpr int VT8 = kD * VS8;          // bytes of one V^T stage
-constexpr float kSlack = 0.5f;         // log2 headroom of the lazy running max
-constexpr float kPScale = 256.0f;      // probability pre-scale before e4m3
+constexpr float kPScale = 256.0f;      // probability pre-scale before e4m3 (log2: 8)
+constexpr float kPTarget = 8.0f;       // log2 of P' for the largest key after a rescale
+constexpr float kTrigger = 8.5f;       // log2 of P' above which the running max moves
 
 typedef int i32x8v __attribute__((ext_vector_type(8)));
 
@@ -94,77 +99,26 @@ __device__ __forceinline__ i32x8v lds_read32(const uint8_t* p) {
   return r;
 }
 
-struct ChunkOffsets8 {
-  uint32_t k;        // this thread's 16-byte chunk of a K tile
-  uint32_t v_video;  // ... of a V^T tile, video plane stride
-  uint32_t v_text;   // ... text plane stride
-};
-
-__device__ __forceinline__ void load_tile(const TileCursor& c, const ChunkOffsets8& off, bool video,
-                                          u32x4& kr, u32x4& vr) {
-  const __amdgpu_buffer_rsrc_t rk = tile_k_rsrc<1>(c);
-  const __amdgpu_buffer_rsrc_t rv = tile_v_rsrc<1>(c);
-  kr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off.k, 0, 0));
-  vr = __builtin_bit_cast(
-      u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, video ? off.v_video : off.v_text, 0, 0));
+// K tile: 64 rows of 9 slots (128 data bytes + pad); V^T tile: 128 rows of 5
+// slots (64 data bytes + pad).
+__device__ __forceinline__ int dma_k8(const TileCursor& c, uint8_t* stage, int w) {
+  return dma_tile<BN, KS8 / 16>(tile_k_rsrc<1>(c), stage, kD, w);
+}
+__device__ __forceinline__ int dma_v8(const TileCursor& c, uint8_t* stage, int w) {
+  return dma_tile<kD, VS8 / 16>(tile_v_rsrc<1>(c), stage, static_cast<uint32_t>(c.vstride), w);
 }
 
-__device__ __forceinline__ void store_tile(uint8_t* Ks, uint8_t* Vs, int tid, const u32x4& kr,
-                                           const u32x4& vr) {
-  *reinterpret_cast<u32x4*>(Ks + (tid >> 3) * KS8 + (tid & 7) * 16) = kr;
-  *reinterpret_cast<u32x4*>(Vs + (tid >> 2) * VS8 + (tid & 3) * 16) = vr;
-}
 
-// S^T of a 64-key tile: two 32-key blocks, two 64-dim steps each, each step
-// with the high and the low (2^-4 scaled) part of the split query.
-__device__ __forceinline__ void qk_tile(const uint8_t* Kst, const int* krow, int g,
-                                        const i32x8v* qf, const i32x8v* ql, f32x16* s) {
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const uint8_t* kp = Kst + krow[b] * KS8 + 32 * g;
-    const i32x8v k0 = lds_read32(kp), k1 = lds_read32(kp + 64);
-    s[b] = mfma_fp8(k0, qf[0], f32x16{});
-    s[b] = mfma_fp8_blo(k0, ql[0], s[b]);
-    s[b] = mfma_fp8(k1, qf[1], s[b]);
-    s[b] = mfma_fp8_blo(k1, ql[1], s[b]);
-  }
-}
-
-// Tile max of S^T (32 keys per lane, both lane halves), raw dot-product units.
-__device__ __forceinline__ float tile_max(const f32x16* s) {
-  float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-#pragma unroll
-  for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[0][r]), s[0][r + 1]);
-  mx = fmaxf(mx, s[0][15]);
-#pragma unroll
-  for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[1][r]), s[1][r + 1]);
-  return max_other_half(mx);
-}
-
-// Probabilities of a tile against the running max m (log2 units), summed into
-// l, pre-scaled by pf and packed as e4m3 (32 bytes per lane, key order).
-__device__ __forceinline__ void tile_probs(const f32x16* s, float coef, float m, float pf, float& l,
-                                           i32x8v& p) {
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    const int b = w >> 2, r = (w & 3) * 4;
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b][r], coef, -m));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b][r + 1], coef, -m));
-    const float p2 = __builtin_amdgcn_exp2f(fmaf(s[b][r + 2], coef, -m));
-    const float p3 = __builtin_amdgcn_exp2f(fmaf(s[b][r + 3], coef, -m));
-    l += (p0 + p1) + (p2 + p3);
-    uint32_t word = cvt_fp8x2<false>(p0 * pf, p1 * pf, 0u);
-    word = cvt_fp8x2<true>(p2 * pf, p3 * pf, word);
-    p[w] = static_cast<int>(word);
-  }
-}
-
+// Keys at or past nvalid get -inf. (Compared as 16 b + r >= nvalid - 32 g: one
+// per-lane value against immediates, rather than 32 per-lane key indices the
+// compiler would keep in registers across the loop.)
 __device__ __forceinline__ void mask_tile(f32x16* s, int nvalid, int g) {
+  const int lim = nvalid - 32 * g;
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (32 * g + 16 * b + r >= nvalid) s[b][r] = -INFINITY;
+      if (16 * b + r >= lim) s[b][r] = -INFINITY;
 }
 
 // per-tile scalars carried through the load ring
@@ -182,32 +136,157 @@ __device__ __forceinline__ TileInfo tile_info(const TileCursor& c) {
   return t;
 }
 
-// First half of a step (one basic block): PV of tile t-1 (P'^T in p_prev,
-// V^T stage vprev) on the matrix pipe next to the softmax of tile t (s_cur).
-// Returns the tile max in log2 units.
-__device__ __forceinline__ float pv_softmax(const uint8_t* vprev, int voff, const i32x8v& p_prev,
-                                            f32x16* o, const f32x16* s_cur, float coef,
-                                            float m_run, float pf, float& l_run, i32x8v& p_cur) {
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-    o[db] = mfma_fp8(lds_read32(vprev + voff + 32 * db * VS8), p_prev, o[db]);
-  const float mt = tile_max(s_cur) * coef;
-  tile_probs(s_cur, coef, m_run, pf, l_run, p_cur);
-  asm volatile("" : "+v"(p_cur), "+v"(l_run));
-  return mt;
+// Word w (0..3) of one 32-key block: keys 4w .. 4w+3 of the block (registers
+// 4w ..), as P' = exp2(x) with x = s * coef + off, packed e4m3. Accumulates the
+// fp32 sum and the max of x.
+__device__ __forceinline__ uint32_t prob_word_blk(const f32x16& s, int w, float coef, float off,
+                                                  float& l, float& mx) {
+  const int r = w * 4;
+  const float x0 = fmaf(s[r], coef, off), x1 = fmaf(s[r + 1], coef, off);
+  const float x2 = fmaf(s[r + 2], coef, off), x3 = fmaf(s[r + 3], coef, off);
+  mx = fmaxf(fmaxf(mx, x0), fmaxf(x1, fmaxf(x2, x3)));
+  const float p0 = __builtin_amdgcn_exp2f(x0), p1 = __builtin_amdgcn_exp2f(x1);
+  const float p2 = __builtin_amdgcn_exp2f(x2), p3 = __builtin_amdgcn_exp2f(x3);
+  uint32_t word = cvt_fp8x2<false>(p0, p1, 0u);
+  word = cvt_fp8x2<true>(p2, p3, word);
+  l += (p0 + p1) + (p2 + p3);
+  return word;
 }
 
-__device__ __forceinline__ void rescale_step(float mt, float& m_run, float l_before, float& l_run,
-                                             f32x16* o, const f32x16* s_cur, float coef, float pf,
-                                             i32x8v& p_cur) {
-  const bool need = mt > m_run + kSlack;
-  const float mn = need ? mt : m_run;
-  const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+// Word w (0..7) of a tile's probabilities: the four keys 4w .. 4w+3 of the
+// lane's 32 (S^T block w / 4, registers 4 (w % 4) ..), as P' = exp2(x) with
+// x = s * coef + off, packed e4m3. Accumulates the fp32 sum and the max of x.
+__device__ __forceinline__ uint32_t prob_word(const f32x16* s, int w, float coef, float off,
+                                              float& l, float& mx) {
+  const int b = w >> 2, r = (w & 3) * 4;
+  const float x0 = fmaf(s[b][r], coef, off), x1 = fmaf(s[b][r + 1], coef, off);
+  const float x2 = fmaf(s[b][r + 2], coef, off), x3 = fmaf(s[b][r + 3], coef, off);
+  mx = fmaxf(fmaxf(mx, x0), fmaxf(x1, fmaxf(x2, x3)));
+  float p0 = __builtin_amdgcn_exp2f(x0), p1 = __builtin_amdgcn_exp2f(x1);
+  float p2 = __builtin_amdgcn_exp2f(x2), p3 = __builtin_amdgcn_exp2f(x3);
+  uint32_t word = cvt_fp8x2<false>(p0, p1, 0u);
+  word = cvt_fp8x2<true>(p2, p3, word);
+  l += (p0 + p1) + (p2 + p3);
+  // (keep the word and the sums in this slot: the instruction selector would
+  // otherwise gather all softmax arithmetic at the end of the step)
+  asm volatile("" : "+v"(word), "+v"(l), "+v"(mx));
+  return word;
+}
+
+// S^T block of a tile from its K rows at kp (this lane's row, byte 32 g):
+// two 64-dim steps, high and low query parts each.
+__device__ __forceinline__ f32x16 qk_block(const uint8_t* kp, const i32x8v* qf, const i32x8v* ql) {
+  const i32x8v k0 = lds_read32(kp), k1 = lds_read32(kp + 64);
+  f32x16 s = mfma_fp8(k0, qf[0], f32x16{});
+  s = mfma_fp8_blo(k0, ql[0], s);
+  s = mfma_fp8(k1, qf[1], s);
+  return mfma_fp8_blo(k1, ql[1], s);
+}
+
+// First part of a step (tile t), S^T of the tile in s (two 32-key blocks):
+// PV of tile t-1 (P' in p_prev, V^T at vprev) and QK^T block 0 of tile t+1
+// (K rows at kn0) on the matrix pipe, slot by slot beside the softmax of tile
+// t into p_cur. Block 0 of s is consumed by words 0-3 and then receives block 0
+// of tile t+1; block 1 still holds tile t. `boundary` runs after the first two
+// MFMAs: it holds the barrier that makes K of tile t+1 visible. Returns the
+// tile's fp32 sum of P'; mx gets the max of x over the row.
+template <typename Boundary>
+__device__ __forceinline__ float fp8_step_a(const uint8_t* vprev, const uint8_t* kn0,
+                                            const i32x8v& p_prev, f32x16* o, const i32x8v* qf,
+                                            const i32x8v* ql, f32x16* s, float coef, float off,
+                                            i32x8v& p_cur, float& mx, Boundary&& boundary) {
+  float l = 0.f;
+  mx = -INFINITY;
+  // slot 0: PV 0, 1; barrier; words 0, 1
+  const i32x8v v0 = lds_read32(vprev), v1 = lds_read32(vprev + 32 * VS8);
+  o[0] = mfma_fp8(v0, p_prev, o[0]);
+  o[1] = mfma_fp8(v1, p_prev, o[1]);
+  boundary();
+  const i32x8v v2 = lds_read32(vprev + 64 * VS8), v3 = lds_read32(vprev + 96 * VS8);
+  p_cur[0] = static_cast<int>(prob_word(s, 0, coef, off, l, mx));
+  p_cur[1] = static_cast<int>(prob_word(s, 1, coef, off, l, mx));
+  __builtin_amdgcn_sched_barrier(0);
+  // slot 1: PV 2, 3; words 2, 3 (block 0 of tile t is then free)
+  const i32x8v k0 = lds_read32(kn0), k1 = lds_read32(kn0 + 64);
+  o[2] = mfma_fp8(v2, p_prev, o[2]);
+  p_cur[2] = static_cast<int>(prob_word(s, 2, coef, off, l, mx));
+  o[3] = mfma_fp8(v3, p_prev, o[3]);
+  p_cur[3] = static_cast<int>(prob_word(s, 3, coef, off, l, mx));
+  __builtin_amdgcn_sched_barrier(0);
+  // slot 2: QK^T block 0 of tile t+1, first k-step; words 4, 5
+  s[0] = mfma_fp8(k0, qf[0], f32x16{});
+  p_cur[4] = static_cast<int>(prob_word(s, 4, coef, off, l, mx));
+  s[0] = mfma_fp8_blo(k0, ql[0], s[0]);
+  p_cur[5] = static_cast<int>(prob_word(s, 5, coef, off, l, mx));
+  __builtin_amdgcn_sched_barrier(0);
+  // slot 3: second k-step; words 6, 7
+  s[0] = mfma_fp8(k1, qf[1], s[0]);
+  p_cur[6] = static_cast<int>(prob_word(s, 6, coef, off, l, mx));
+  s[0] = mfma_fp8_blo(k1, ql[1], s[0]);
+  p_cur[7] = static_cast<int>(prob_word(s, 7, coef, off, l, mx));
+  __builtin_amdgcn_sched_barrier(0);
+  mx = max_other_half(mx);
+  asm volatile("" : "+v"(p_cur), "+v"(l), "+v"(mx));
+  return l;
+}
+
+// acc *= alpha, in place. Written as one asm block with every element tied to
+// its register: as plain C++ in the rare rescale path, the register allocator
+// keeps a second copy of the 64 output accumulators live and spills in the
+// main loop. The compiler does not see hazards through inline asm, so the
+// block waits out an MFMA still writing acc (leading nops) and lets the
+// products settle before any MFMA reads them (trailing nops).
+__device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
+  float e[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] *= alpha;
-  m_run = mn;
-  l_run = l_before * alpha;
-  tile_probs(s_cur, coef, m_run, pf, l_run, p_cur);
+  for (int r = 0; r < 16; ++r) e[r] = acc[r];
+  asm volatile(
+      "s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n"
+      "v_mul_f32 %0, %0, %16\n v_mul_f32 %1, %1, %16\n v_mul_f32 %2, %2, %16\n"
+      "v_mul_f32 %3, %3, %16\n v_mul_f32 %4, %4, %16\n v_mul_f32 %5, %5, %16\n"
+      "v_mul_f32 %6, %6, %16\n v_mul_f32 %7, %7, %16\n v_mul_f32 %8, %8, %16\n"
+      "v_mul_f32 %9, %9, %16\n v_mul_f32 %10, %10, %16\n v_mul_f32 %11, %11, %16\n"
+      "v_mul_f32 %12, %12, %16\n v_mul_f32 %13, %13, %16\n v_mul_f32 %14, %14, %16\n"
+      "v_mul_f32 %15, %15, %16\n"
+      "s_nop 7\n s_nop 7\n"
+      : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]), "+v"(e[4]), "+v"(e[5]), "+v"(e[6]),
+        "+v"(e[7]), "+v"(e[8]), "+v"(e[9]), "+v"(e[10]), "+v"(e[11]), "+v"(e[12]), "+v"(e[13]),
+        "+v"(e[14]), "+v"(e[15])
+      : "v"(alpha));
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = e[r];
+}
+
+// Rare path of a step, taken by the whole wave when some row's x exceeds
+// kTrigger (P' would pass 362, near the e4m3 limit of 448): those rows move
+// the running max up so that their largest x becomes kPTarget; O (every tile
+// before this one) and the sum of the tiles before are scaled to match, and
+// the tile's probabilities are recomputed -- block 0 of its S^T again from its
+// K rows (kc0, still in LDS; masked like the first time), block 1 from s1.
+__device__ __forceinline__ float rescale_step(float mx, float& m_run, float& off, float& l_run,
+                                              f32x16* o, const uint8_t* kc0, const f32x16& s1,
+                                              const i32x8v* qf, const i32x8v* ql, float coef,
+                                              int nvalid, int g, i32x8v& p_cur) {
+  const float d = fmaxf(mx - kPTarget, 0.f);
+  const float alpha = __builtin_amdgcn_exp2f(-d);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) scale_acc(o[i], alpha);
+  l_run *= alpha;
+  m_run += d;
+  off -= d;
+  float l = 0.f, m2 = -INFINITY;
+  {
+    f32x16 b0 = qk_block(kc0, qf, ql);
+    const int lim = nvalid - 32 * g;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (r >= lim) b0[r] = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) p_cur[w] = static_cast<int>(prob_word_blk(b0, w, coef, off, l, m2));
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) p_cur[4 + w] = static_cast<int>(prob_word_blk(s1, w, coef, off, l, m2));
+  return l;
 }
 
 __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a) {
@@ -224,21 +303,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   const int q0 = wt.q0;
   const int P = a.rope.P;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, r32 = lane & 31;
-
-  ChunkOffsets8 off;
-  off.k = static_cast<uint32_t>((tid >> 3) * kD + (tid & 7) * 16);
-  off.v_video = static_cast<uint32_t>((tid >> 2) * P + (tid & 3) * 16);
-  off.v_text = static_cast<uint32_t>((tid >> 2) * I.text_cap + (tid & 3) * 16);
+  const int lane = tid & 63, g = lane >> 5, r32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
 
   const int tpf = (P + BN - 1) / BN;
   const int ntiles = I.n_frames_kv * tpf + (I.n_text_kv + BN - 1) / BN;
 
   TileCursor lc;
   cursor_start<1>(lc, I, h, H, P);
-  u32x4 kr, vr;
   TileInfo ti0 = tile_info(lc);
-  load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
 
   // largest V scale among the planes this (item, head) attends
   float vmax = 0.f;
@@ -253,9 +326,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
     om[tid] = rope_omega(tid, a.rope, &axis);
     ax[tid] = axis;
   }
-  for (int i = tid; i < VT8 / 16; i += kThreads)
-    reinterpret_cast<u32x4*>(Vs + (kStages - 1) * VT8)[i] = u32x4{0u, 0u, 0u, 0u};
+  // Every stage starts as zeros (the V stage of "tile -1" is read once with
+  // zero probabilities; stages of tiles past the end may be read, unused).
+  for (int i = tid; i < kStages * KT8 / 16; i += kThreads)
+    reinterpret_cast<u32x4*>(Ks)[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = tid; i < kStages * VT8 / 16; i += kThreads)
+    reinterpret_cast<u32x4*>(Vs)[i] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
+
+  // Tiles load two ahead of the compute tile, K and then V (K of tile t+1 is
+  // read in step t, V of tile t in step t+1). lc is the cursor of the last
+  // tile loaded; ti0, ti1 carry tiles t, t+1.
+  dma_k8(lc, Ks, w);
+  dma_v8(lc, Vs, w);
+  TileInfo ti1 = ti0;
+  if (ntiles > 1) {
+    cursor_next<1>(lc, I, h, H, P);
+    ti1 = tile_info(lc);
+    dma_k8(lc, Ks + KT8, w);
+    dma_v8(lc, Vs + VT8, w);
+  }
   vmax = red[0];
 #pragma unroll
   for (int i = 1; i < kWaves; ++i) vmax = fmaxf(vmax, red[i]);
@@ -323,20 +413,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
       }
   }
 
-  // ---- prologue: tiles 0, 1 into LDS stages 0, 1; tile 2 in flight ----------
-  store_tile(Ks, Vs, tid, kr, vr);
-  TileInfo ti1 = ti0, ti2 = ti0;
-  if (ntiles > 1) {
-    cursor_next<1>(lc, I, h, H, P);
-    ti1 = tile_info(lc);
-    load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
-    store_tile(Ks + KT8, Vs + VT8, tid, kr, vr);
-  }
-  if (ntiles > 2) {
-    cursor_next<1>(lc, I, h, H, P);
-    ti2 = tile_info(lc);
-    load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
-  }
+  // tiles 0 and 1 are in LDS before the first step
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   __syncthreads();
 
   int krow[2];
@@ -349,45 +427,70 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
   float l_run = 0.f;
 
+  // S^T of tile 0; the running max m (log2 units) starts at its max
   f32x16 sc[2];
-  qk_tile(Ks, krow, g, qf, ql, sc);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) sc[b] = qk_block(Ks + krow[b] * KS8 + 32 * g, qf, ql);
   if (ti0.nvalid < BN) mask_tile(sc, ti0.nvalid, g);
-  float m_run = tile_max(sc) * (c2 * ti0.kscale);   // tile 0 always has a valid key
+  float m_run;
+  {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][r]);
+    m_run = max_other_half(mx) * (c2 * ti0.kscale);   // tile 0 always has a valid key
+  }
   i32x8v pa = {}, pb;
   const float pf_base = kPScale / vmax;
 
-  // Tile t sits in stage t % 4. Step t: PV(t-1) beside softmax(t), then
-  // QK^T(t+1) into the freed S registers (the other wave of the SIMD overlaps
-  // its softmax with these MFMAs). Step t reads V of tile t-1 and K of tile
-  // t+1, so tile t+2 goes to stage (t+2) % 4, last read before this tile's
-  // barrier. Two steps per loop trip, so the P buffers swap roles without
-  // copies.
-  auto step = [&](int tt, i32x8v& p_prev, i32x8v& p_cur) __attribute__((always_inline)) {
-    const uint8_t* Vprev = Vs + ((tt + kStages - 1) & (kStages - 1)) * VT8;
-    const uint8_t* Knext = Ks + ((tt + 1) & (kStages - 1)) * KT8;
+  // Tile t sits in stage t % 4. Step t: PV(t-1) and QK^T(t+1) on the matrix
+  // pipe beside the softmax of tile t; S^T is computed in place (block 0 of
+  // tile t+1 after words 0-3 of tile t, block 1 after the rescale check). The
+  // barrier of step t comes after its first two (PV) MFMAs; K of tile t+1
+  // (loaded in step t-1) is read after it. Two steps per loop trip: the P
+  // buffers swap roles without copies.
+  int pending = 0;   // lower bound of this wave's loads issued in the step before
+  auto step = [&](int tt, const i32x8v& p_prev, i32x8v& p_cur) __attribute__((always_inline)) {
+    const uint8_t* Vprev = Vs + ((tt + kStages - 1) & (kStages - 1)) * VT8 + voff;
+    const uint8_t* Kcur = Ks + (tt & (kStages - 1)) * KT8 + 32 * g;
+    const uint8_t* Knext = Ks + ((tt + 1) & (kStages - 1)) * KT8 + 32 * g;
     const TileInfo cur = ti0;
-    __syncthreads();
-    TileInfo ti3 = ti0;
-    if (tt + 2 < ntiles) {
-      const int s2 = (tt + 2) & (kStages - 1);
-      store_tile(Ks + s2 * KT8, Vs + s2 * VT8, tid, kr, vr);
-      if (tt + 3 < ntiles) {
+    TileInfo ti2 = ti0;
+    // Before the barrier each wave waits for its K load of the step before
+    // (tile t+1, read in this step); its V load (read two steps later) stays in
+    // flight. After the barrier, tile t+2 goes into stage (t+2) % 4, the stage
+    // of tile t-2 (its V was last read in step t-1, its K in step t-3).
+    auto boundary = [&]() __attribute__((always_inline)) {
+      wait_loads(pending);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      pending = 0;
+      if (tt + 2 < ntiles) {
+        const int s2 = (tt + 2) & (kStages - 1);
         cursor_next<1>(lc, I, h, H, P);
-        ti3 = tile_info(lc);
-        load_tile(lc, off, lc.fi < I.n_frames_kv, kr, vr);
+        ti2 = tile_info(lc);
+        dma_k8(lc, Ks + s2 * KT8, w);
+        dma_v8(lc, Vs + s2 * VT8, w);
+        pending = 1;   // every wave issues at least one V load
       }
-    }
+    };
     if (cur.nvalid < BN) mask_tile(sc, cur.nvalid, g);
     const float coef = c2 * cur.kscale;
     const float pf = pf_base * cur.vscale;
-    const float l_before = l_run;
-    const float mt = pv_softmax(Vprev, voff, p_prev, o, sc, coef, m_run, pf, l_run, p_cur);
-    if (__any(mt > m_run + kSlack))
-      rescale_step(mt, m_run, l_before, l_run, o, sc, coef, pf, p_cur);
-    qk_tile(Knext, krow, g, qf, ql, sc);
+    float off8 = __log2f(pf) - m_run;
+    float mx;
+    float lt = fp8_step_a(Vprev, Knext + krow[0] * KS8, p_prev, o, qf, ql, sc, coef, off8, p_cur,
+                          mx, boundary);
+    if (__builtin_expect(__any(mx > kTrigger), 0))
+      lt = rescale_step(mx, m_run, off8, l_run, o, Kcur + krow[0] * KS8, sc[1], qf, ql, coef,
+                        cur.nvalid, g, p_cur);
+    // QK^T block 1 of tile t+1 (block 1 of tile t is no longer needed)
+    sc[1] = qk_block(Knext + krow[1] * KS8, qf, ql);
+    l_run += lt / pf;
     ti0 = ti1;
     ti1 = ti2;
-    ti2 = ti3;
   };
 #pragma unroll 1
   for (int t = 0; t < ntiles; t += 2) {

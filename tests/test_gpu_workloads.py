@@ -95,11 +95,15 @@ def test_active_history_selection_two_sessions():
 
 def test_fp8_cache_eight_prior_segments():
     """Eight prior segments stored e4m3 with per-(frame, head) scales; values
-    scaled by U[0.5, 2] per (frame, head); 237,856 keys. Gated at 5e-2 / 5e-3
-    against the exact oracle on the unquantised inputs (total error, storage
-    in e4m3 included), and at 2e-2 / 2e-3 against the oracle over the values
-    the cache stores (the cache bytes are bit-exact to the oracle's
-    quantisation), which isolates the kernel's own arithmetic."""
+    scaled by U[0.5, 2] per (frame, head); 237,856 keys.
+
+    The cache bytes are bit-exact to the oracle's quantisation (append tests),
+    so the kernel is gated against the oracle over the values the cache stores,
+    at 2e-2 / 2e-3. Against exact attention on the unquantised inputs the
+    error includes storing K and V in e4m3, which the oracle measures itself
+    on the same rows: max-abs within that storage error + 2e-2, mean-abs
+    within 5e-3, relative L2 within 0.1. (With these inputs the storage error
+    alone reaches about 5e-2 at the worst sampled element.)"""
     wl = WL["fp8seg8"]
     print("workload fp8seg8: 26,656 queries x 237,856 keys x 16 heads", flush=True)
     s = Session(wl, 0, 0, 0)
@@ -108,10 +112,12 @@ def test_fp8_cache_eight_prior_segments():
     rows = _rows(wl, 48, 3)
     heads = [0, 5, 11, 15]
     got, got_lse = s.gpu_out(rows=rows, heads=heads)
-    want, _ = s.oracle(rows=rows, heads=heads)
-    _, _, rel = compare(got, want, 5e-2, 5e-3, "fp8seg8 vs exact")
-    assert rel <= 0.1
     want_c, want_c_lse, _ = s.oracle_fp8_cache(rows=rows, heads=heads)
     _, _, rel = compare(got, want_c, 2e-2, 2e-3, "fp8seg8 vs stored cache")
     assert rel <= 0.05
     np.testing.assert_allclose(got_lse, want_c_lse, atol=2e-2, rtol=0)
+    want, _ = s.oracle(rows=rows, heads=heads)
+    storage = float(np.max(np.abs(want_c - want)))
+    print(f"fp8seg8: e4m3 storage error of the oracle itself {storage:.3e}", flush=True)
+    _, _, rel = compare(got, want, storage + 2e-2, 5e-3, "fp8seg8 vs exact")
+    assert rel <= 0.1
