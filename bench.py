@@ -35,6 +35,41 @@ METRIC = "segment-attention TFLOP/s per GPU + % of MFMA peak; ms per 54-block se
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}     # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0
 
+# HBM traffic of the attention kernel per launch, from the committed rocprofv3
+# counter summaries: FETCH_SIZE reads half the bytes a plain device copy of
+# known size moves and WRITE_SIZE all of them (calibrated with the gather
+# kernel), so bytes = 2.0 * FETCH_SIZE + 1.0 * WRITE_SIZE (KiB per dispatch).
+# The summary records a hash of the kernel source it was taken on; a kernel
+# changed since then reports null.
+COUNTER_SUMMARY = {
+    ("attn_bf16_kernel", "seg1"): ("attn_bf16_seg1_counters.txt", "attention_bf16.hip"),
+    ("attn_fp8_kernel", "fp8seg8"): ("attn_fp8_fp8seg8_counters.txt", "attention_fp8.hip"),
+}
+FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
+
+
+def measured_traffic(kernel, workload):
+    import hashlib
+    entry = COUNTER_SUMMARY.get((kernel, workload))
+    if entry is None:
+        return None
+    summary = os.path.join(ROOT, "profiles", entry[0])
+    src = os.path.join(ROOT, "diffusion_transformer_attention_segment_amd", "csrc", entry[1])
+    if not (os.path.exists(summary) and os.path.exists(src)):
+        return None
+    want = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    got, section, vals = None, None, {}
+    for line in open(summary):
+        if line.startswith("# source hash"):
+            got = line.rsplit(":", 1)[1].strip()
+        elif not line.startswith("#") and not line.startswith(" "):
+            section = line.strip()
+        elif section == kernel and line.split():
+            vals[line.split()[0]] = float(line.split()[1])
+    if got != want or "FETCH_SIZE" not in vals or "WRITE_SIZE" not in vals:
+        return None
+    return int(1024 * (FETCH_FACTOR * vals["FETCH_SIZE"] + WRITE_FACTOR * vals["WRITE_SIZE"]))
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -280,7 +315,8 @@ def main():
         "ms_per_54_block_segment_note": "54 x one layer's step (derived)",
         "attention_kernel_ms": round(attn_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic("attn_" + dtype + "_kernel", wl.name),
                      "kernel": "attn_" + dtype + "_kernel",
                      "flop_per_launch": flops},
         "kv_append": {"ms": round(app_ms, 4), "bytes": app_bytes,
