@@ -41,34 +41,58 @@ PEAK_HBM_GBS = 8000.0
 # kernel), so bytes = 2.0 * FETCH_SIZE + 1.0 * WRITE_SIZE (KiB per dispatch).
 # The summary records a hash of the kernel source it was taken on; a kernel
 # changed since then reports null.
+# Counter summaries under profiles/: (file, kernels of one segment_attention
+# call, sources they were built from). The traffic is read from them only while
+# those sources hash to the value the summary records.
+ATTN_SOURCES = ["attention_common.h", "internal.h", "device_common.h", "attention_combine.hip",
+                "host.cpp"]
 COUNTER_SUMMARY = {
-    ("attn_bf16_kernel", "seg1"): ("attn_bf16_seg1_counters.txt", "attention_bf16.hip"),
-    ("attn_fp8_kernel", "fp8seg8"): ("attn_fp8_fp8seg8_counters.txt", "attention_fp8.hip"),
+    ("bf16", "seg1"): ("attn_bf16_seg1_counters.txt", ["attn_bf16_kernel", "combine_kernel"],
+                       ["attention_bf16.hip"] + ATTN_SOURCES),
+    ("fp8", "fp8seg8"): ("attn_fp8_fp8seg8_counters.txt", ["attn_fp8_kernel", "combine_kernel"],
+                         ["attention_fp8.hip"] + ATTN_SOURCES),
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 
 
-def measured_traffic(kernel, workload):
+def source_hash(files):
     import hashlib
-    entry = COUNTER_SUMMARY.get((kernel, workload))
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "diffusion_transformer_attention_segment_amd", "csrc", f),
+                  "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(dtype, workload):
+    """HBM bytes per segment_attention call (all its kernels) from the counter
+    summary: FETCH_FACTOR * FETCH_SIZE + WRITE_FACTOR * WRITE_SIZE (KiB per
+    dispatch), or None when no summary matches the current sources."""
+    entry = COUNTER_SUMMARY.get((dtype, workload))
     if entry is None:
         return None
     summary = os.path.join(ROOT, "profiles", entry[0])
-    src = os.path.join(ROOT, "diffusion_transformer_attention_segment_amd", "csrc", entry[1])
-    if not (os.path.exists(summary) and os.path.exists(src)):
+    if not os.path.exists(summary):
         return None
-    want = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     got, section, vals = None, None, {}
     for line in open(summary):
         if line.startswith("# source hash"):
             got = line.rsplit(":", 1)[1].strip()
         elif not line.startswith("#") and not line.startswith(" "):
             section = line.strip()
-        elif section == kernel and line.split():
-            vals[line.split()[0]] = float(line.split()[1])
-    if got != want or "FETCH_SIZE" not in vals or "WRITE_SIZE" not in vals:
+        elif section in entry[1] and line.split():
+            vals[(section, line.split()[0])] = float(line.split()[1])
+    if got != source_hash(entry[2]):
         return None
-    return int(1024 * (FETCH_FACTOR * vals["FETCH_SIZE"] + WRITE_FACTOR * vals["WRITE_SIZE"]))
+    total = 0.0
+    for k in entry[1]:
+        if (k, "FETCH_SIZE") not in vals or (k, "WRITE_SIZE") not in vals:
+            if k == entry[1][0]:
+                return None
+            continue     # a merge kernel that did not run in this workload
+        total += FETCH_FACTOR * vals[(k, "FETCH_SIZE")] + WRITE_FACTOR * vals[(k, "WRITE_SIZE")]
+    return int(1024 * total)
 
 
 def parse():
@@ -316,8 +340,8 @@ def main():
         "attention_kernel_ms": round(attn_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic("attn_" + dtype + "_kernel", wl.name),
-                     "kernel": "attn_" + dtype + "_kernel",
+                     "traffic": measured_traffic(dtype, wl.name),
+                     "kernel": "segment_attention: attn_" + dtype + "_kernel + combine_kernel",
                      "flop_per_launch": flops},
         "kv_append": {"ms": round(app_ms, 4), "bytes": app_bytes,
                       "GB_per_s": round(app_bytes / (app_ms * 1e-3) / 1e9, 1),

@@ -15,5 +15,5 @@ from .binding import (  # noqa: F401
     AttnItem, Geom, KVLayer, SegAttnError, KV_BF16, KV_FP8, SEL_ALL, SEL_RECENT, SEL_POWER,
     SEL_ANCHOR_RECENT, MAX_ITEMS, HEAD_DIM, SIGNATURES, LIB_PATH, abi_version, cache_bytes,
     history_gather, history_select, kv_append, kv_dequant, last_error, lib, segment_attention,
-    text_append,
+    segment_attention_workspace, text_append,
 )

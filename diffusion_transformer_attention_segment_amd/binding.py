@@ -72,8 +72,10 @@ SIGNATURES = {
                                          ctypes.POINTER(ctypes.c_int32)]),
     "sa_history_gather": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_kv_layer), _P,
                                          _I, ctypes.POINTER(sa_kv_layer), _P]),
+    "sa_segment_attention_workspace": (ctypes.c_size_t, [ctypes.POINTER(sa_geom),
+                                                         ctypes.POINTER(sa_attn_item), _I]),
     "sa_segment_attention": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_attn_item),
-                                            _I, _P]),
+                                            _I, _P, ctypes.c_size_t, _P]),
     "sa_kv_dequant": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_kv_layer), _P, _I,
                                      _I, ctypes.POINTER(sa_kv_layer), _P]),
 }
@@ -244,12 +246,41 @@ class AttnItem:
         return it
 
 
-def segment_attention(geom, items, stream=None):
+def segment_attention_workspace(geom, items):
+    """Bytes of device workspace the split plan of this call wants (0: none)."""
     g = geom.c()
     arr = (sa_attn_item * max(len(items), 1))()
     for i, it in enumerate(items):
         arr[i] = it.c()
-    _check(lib().sa_segment_attention(ctypes.byref(g), arr, len(items), _stream(stream)))
+    return int(lib().sa_segment_attention_workspace(ctypes.byref(g), arr, len(items)))
+
+
+def segment_attention(geom, items, stream=None, workspace="auto"):
+    """Joint segment attention over the items.
+
+    workspace: "auto" allocates what sa_segment_attention_workspace asks for
+    (the last round's tiles are then split over key ranges and merged); None
+    runs every tile whole; a uint8 CUDA tensor is used as given (too small:
+    whole tiles)."""
+    g = geom.c()
+    arr = (sa_attn_item * max(len(items), 1))()
+    for i, it in enumerate(items):
+        arr[i] = it.c()
+    ws, nbytes = None, 0
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"workspace must be 'auto', None or a tensor, not {workspace!r}")
+        nbytes = int(lib().sa_segment_attention_workspace(ctypes.byref(g), arr, len(items)))
+        if nbytes > 0:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=items[0].q.device)
+            if stream is not None:
+                ext = stream if isinstance(stream, torch.cuda.Stream) else \
+                    torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)))
+                ws.record_stream(ext)
+    elif workspace is not None:
+        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+    _check(lib().sa_segment_attention(ctypes.byref(g), arr, len(items), _ptr(ws), nbytes,
+                                      _stream(stream)))
 
 
 def kv_dequant(geom, src, d_frames, n_frames, n_text, dst, stream=None):

@@ -257,13 +257,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
 
   const uint32_t koff_ld = static_cast<uint32_t>(tid) * 16u;
-  const int tpf = (P + BN - 1) / BN;
-  const int ntiles = I.n_frames_kv * tpf + (I.n_text_kv + BN - 1) / BN;
+  int kt0, kt1;   // this work tile's key tiles
+  key_range(a, I, P, wt.part, &kt0, &kt1);
+  const int ntiles = kt1 - kt0;
 
   // the load cursor runs three tiles ahead of the compute tile; nv0..nv2 keep
   // the valid-key counts of the tiles in between
   TileCursor lc;
-  cursor_start<2>(lc, I, h, H, P);
+  cursor_start<2>(lc, I, h, H, P, kt0);
   u32x4 kr[kKChunks], vr[kVChunks];
   int nv0 = cursor_nvalid(lc);
   load_tile(lc, koff_ld, kr, vr);
@@ -433,6 +434,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   // ---- epilogue ----------------------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
+  if (wt.part >= 0) {   // split tile: partial result for the merge kernel
+    if (qrow < I.n_q)
+      store_partial(a, wt.unit, BM, qrow - q0, g, o, 1.0f, m_run, l_tot);
+    return;
+  }
   if (qrow < I.n_q) {
     uint16_t* orow = I.out + (static_cast<size_t>(qrow) * H + h) * kD;
 #pragma unroll
@@ -455,7 +461,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
 int attention_block_m_bf16() { return BM; }
 
 hipError_t launch_attention_bf16(AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3(a.total_tiles), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(attn_bf16_kernel, dim3(a.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

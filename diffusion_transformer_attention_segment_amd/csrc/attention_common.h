@@ -10,28 +10,43 @@ namespace segattn {
 constexpr int kKeyTile = 64;               // keys per tile (both kernels)
 constexpr int kRsrcFlags = 0x00020000;     // raw buffer resource, 32-bit data format
 
-// Workgroups go round-robin over the 8 XCDs; give each XCD a contiguous run
-// of logical tiles (same head => shared K/V in that XCD's L2). Logical tiles
-// are ordered (item, head, query tile).
+// Workgroups go round-robin over the 8 XCDs. The whole tiles (the first
+// n_full logical tiles) are remapped so that each XCD gets a contiguous run of
+// them (same head => shared K/V in that XCD's L2); logical tiles are ordered
+// (item, head, query tile). The split units that follow (the last tiles, each
+// as split_k key-range parts) keep dispatch order, so they spread over every
+// XCD and fill the CUs that finish their whole tiles first.
 struct WorkTile {
   int item;
   int head;
   int q0;
+  int part;     // key-range part of a split tile, or -1 (whole tile)
+  int unit;     // partial-result slot of a split tile
 };
 
 __device__ __forceinline__ WorkTile map_workgroup(const AttnArgs& a, int block_m) {
-  const int nb = gridDim.x;
   const int b = blockIdx.x;
-  const int xcd = b & 7, idx = b >> 3;
-  const int per = nb >> 3, rem = nb & 7;
-  const int logical = xcd * per + min(xcd, rem) + idx;
+  int logical;
+  WorkTile w;
+  if (b < a.n_full) {
+    const int nb = a.n_full;
+    const int xcd = b & 7, idx = b >> 3;
+    const int per = nb >> 3, rem = nb & 7;
+    logical = xcd * per + min(xcd, rem) + idx;   // XCD x: per + (x < rem) tiles
+    w.part = -1;
+    w.unit = 0;
+  } else {
+    const int u = b - a.n_full;
+    logical = a.n_full + u / a.split_k;
+    w.part = u - (u / a.split_k) * a.split_k;
+    w.unit = u;
+  }
   int it = 0;
 #pragma unroll 1
   for (int j = 1; j < a.n_items; ++j)
     if (logical >= a.items[j].tile_begin) it = j;
   const AttnItemDev& I = a.items[it];
   const int local = logical - I.tile_begin;
-  WorkTile w;
   w.item = it;
   w.head = local / I.q_tiles;
   w.q0 = (local - w.head * I.q_tiles) * block_m;
@@ -99,13 +114,57 @@ __device__ __forceinline__ void cursor_enter(TileCursor& c, const AttnItemDev& I
   }
 }
 
-// Cursor at the first tile of the item.
+// Cursor at key tile `tile` of the item (frames in list order, ceil(P / 64)
+// tiles each, then the text slot).
 template <int ESZ>
 __device__ __forceinline__ void cursor_start(TileCursor& c, const AttnItemDev& I, int h, int H,
-                                             int P) {
-  c.fi = 0;
-  c.fnext = I.n_frames_kv > 0 ? frame_entry(I, 0) : 0;
+                                             int P, int tile = 0) {
+  const int tpf = (P + kKeyTile - 1) / kKeyTile;
+  const int nvid = I.n_frames_kv * tpf;
+  c.fi = tile < nvid ? tile / tpf : I.n_frames_kv;
+  c.fnext = c.fi < I.n_frames_kv ? frame_entry(I, c.fi) : 0;
   cursor_enter<ESZ>(c, I, h, H, P);
+  c.p0 = (tile < nvid ? tile - c.fi * tpf : tile - nvid) * kKeyTile;
+}
+
+// Key tiles [begin, end) of a work tile: all of the item's, or part `part` of
+// split_k.
+__device__ __forceinline__ void key_range(const AttnArgs& a, const AttnItemDev& I, int P, int part,
+                                          int* begin, int* end) {
+  const int tpf = (P + kKeyTile - 1) / kKeyTile;
+  const int n = I.n_frames_kv * tpf + (I.n_text_kv + kKeyTile - 1) / kKeyTile;
+  if (part < 0) {
+    *begin = 0;
+    *end = n;
+  } else {
+    *begin = static_cast<int>(static_cast<int64_t>(part) * n / a.split_k);
+    *end = static_cast<int>(static_cast<int64_t>(part + 1) * n / a.split_k);
+  }
+}
+
+// Partial result of one row of a split tile: unnormalised O (128 floats, the
+// lane's 64 in MFMA output order: dims 32 db + 8 r4 + 4 g .. +3 hold
+// o[db][4 r4 .. 4 r4 + 3]), then (lane half 0) m and l.
+__device__ __forceinline__ void store_partial(const AttnArgs& a, int unit, int block_m, int row,
+                                              int g, const f32x16* o, float scale, float m,
+                                              float l) {
+  float* base = a.ws + static_cast<size_t>(unit) * block_m * kPartialStride;
+  float* orow = base + static_cast<size_t>(row) * kD;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float4 v;
+      v.x = o[db][4 * r4] * scale;
+      v.y = o[db][4 * r4 + 1] * scale;
+      v.z = o[db][4 * r4 + 2] * scale;
+      v.w = o[db][4 * r4 + 3] * scale;
+      *reinterpret_cast<float4*>(orow + 32 * db + 8 * r4 + 4 * g) = v;
+    }
+  if (g == 0) {
+    base[static_cast<size_t>(block_m) * kD + row] = m;
+    base[static_cast<size_t>(block_m) * (kD + 1) + row] = l;
+  }
 }
 
 template <int ESZ>

@@ -306,11 +306,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   const int lane = tid & 63, g = lane >> 5, r32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
 
-  const int tpf = (P + BN - 1) / BN;
-  const int ntiles = I.n_frames_kv * tpf + (I.n_text_kv + BN - 1) / BN;
+  int kt0, kt1;   // this work tile's key tiles
+  key_range(a, I, P, wt.part, &kt0, &kt1);
+  const int ntiles = kt1 - kt0;
 
   TileCursor lc;
-  cursor_start<1>(lc, I, h, H, P);
+  cursor_start<1>(lc, I, h, H, P, kt0);
   TileInfo ti0 = tile_info(lc);
 
   // largest V scale among the planes this (item, head) attends
@@ -513,6 +514,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   // ---- epilogue ----------------------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = vmax / (kPScale * l_tot);
+  if (wt.part >= 0) {   // split tile: partial result for the merge kernel
+    if (qrow < I.n_q)
+      store_partial(a, wt.unit, BM, qrow - q0, g, o, vmax / kPScale, m_run, l_tot);
+    return;
+  }
   if (qrow < I.n_q) {
     uint16_t* orow = I.out + (static_cast<size_t>(qrow) * H + h) * kD;
 #pragma unroll
@@ -535,7 +541,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
 int attention_block_m_fp8() { return BM; }
 
 hipError_t launch_attention_fp8(AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_fp8_kernel, dim3(a.total_tiles), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(attn_fp8_kernel, dim3(a.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

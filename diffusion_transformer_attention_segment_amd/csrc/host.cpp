@@ -3,6 +3,7 @@
 // call and reports failures through a status code plus a thread-local message.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -300,8 +301,19 @@ sa_status sa_history_gather(const sa_geom* geom, const sa_kv_layer* src, const i
   return hip_status(launch_gather(a, static_cast<hipStream_t>(stream)), "history_gather launch");
 }
 
-sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
-                               void* stream) {
+namespace {
+
+// Validated attention call: device arguments plus the per-item key-tile
+// counts the split planner needs.
+struct AttnPlan {
+  AttnArgs a;
+  bool fp8;
+  int bm;
+  int32_t key_tiles[SA_MAX_ITEMS];
+};
+
+sa_status prepare_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
+                            AttnPlan& plan) {
   sa_status st = check_geom(geom);
   if (st != SA_OK) return st;
   if (items == nullptr) return fail(SA_E_ARG, "items is NULL");
@@ -334,9 +346,12 @@ sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, i
       if (!aligned16(it.q) || !aligned16(it.out)) return fail(SA_E_ALIGN, "item %d: q/out not aligned", i);
     }
   }
-  AttnArgs a{};
-  const bool fp8 = dtype == SA_KV_FP8_E4M3;
-  const int bm = fp8 ? attention_block_m_fp8() : attention_block_m_bf16();
+  AttnArgs& a = plan.a;
+  a = AttnArgs{};
+  plan.fp8 = dtype == SA_KV_FP8_E4M3;
+  plan.bm = plan.fp8 ? attention_block_m_fp8() : attention_block_m_bf16();
+  const int bm = plan.bm;
+  const int tpf = (P + 63) / 64;
   int64_t tiles = 0;
   for (int i = 0; i < n_items; ++i) {
     const sa_attn_item& it = items[i];
@@ -362,20 +377,109 @@ sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, i
     d.q_tiles = (d.n_q + bm - 1) / bm;
     d.tile_begin = static_cast<int32_t>(tiles);
     tiles += static_cast<int64_t>(d.q_tiles) * geom->heads;
+    plan.key_tiles[i] = it.n_frames_kv * tpf + (it.n_text_kv + 63) / 64;
   }
-  if (tiles == 0) return ok();
   if (tiles > (int64_t(1) << 31) - 1) return fail(SA_E_SHAPE, "too many tiles");
   a.n_items = n_items;
   a.heads = geom->heads;
   a.total_tiles = static_cast<int32_t>(tiles);
+  a.n_full = a.total_tiles;
+  a.split_k = 1;
+  a.grid = a.total_tiles;
   const double scale = geom->softmax_scale > 0.f ? geom->softmax_scale : 1.0 / std::sqrt(128.0);
   a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
   a.rope = rope_params(geom);
   // items with no query rows own no tiles; point them past the end
   for (int i = n_items; i < SA_MAX_ITEMS; ++i) a.items[i].tile_begin = a.total_tiles;
+  return ok();
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Split plan: the tiles of the last partial round (r = total mod CUs, or all
+// tiles when there are fewer than CUs) are cut into k key-range parts, k in
+// [2, 32] with at least 8 key tiles per part. k minimises the predicted time
+// of that round in whole-tile units: rounds(r k) * (1/k + c0) + r k c1, where
+// c0 ~ 3 key tiles of prologue per part and c1 ~ the merge's read of one
+// part's fp32 partial (133 KB at ~5 TB/s against ~1.9 us per key tile), both
+// relative to the tile's kt key tiles. Returns the workspace bytes (0: no
+// split).
+size_t plan_split(AttnPlan& plan) {
+  AttnArgs& a = plan.a;
+  const int cus = device_cus();
+  const int T = a.total_tiles;
+  if (cus <= 0 || T == 0) return 0;
+  const int r = T >= cus ? T % cus : T;
+  if (r == 0) return 0;
+  const int first = T - r;
+  int min_kt = 1 << 30;
+  for (int i = 0; i < a.n_items; ++i) {
+    const AttnItemDev& d = a.items[i];
+    const int end = d.tile_begin + d.q_tiles * a.heads;
+    if (end > first && d.q_tiles > 0) min_kt = std::min(min_kt, plan.key_tiles[i]);
+  }
+  const int kmax = std::min(32, min_kt / 8);
+  const double c0 = 3.0 / min_kt, c1 = 0.014 / min_kt;
+  double best = std::ceil(static_cast<double>(r) / cus);
+  int best_k = 1;
+  for (int k = 2; k <= kmax; ++k) {
+    const double cost = std::ceil(static_cast<double>(r) * k / cus) * (1.0 / k + c0) +
+                        static_cast<double>(r) * k * c1;
+    if (cost < best - 1e-9) {
+      best = cost;
+      best_k = k;
+    }
+  }
+  if (best_k == 1) return 0;
+  a.n_full = first;
+  a.split_k = best_k;
+  a.grid = first + r * best_k;
+  return static_cast<size_t>(r) * best_k * plan.bm * kPartialStride * sizeof(float);
+}
+
+}  // namespace
+
+size_t sa_segment_attention_workspace(const sa_geom* geom, const sa_attn_item* items,
+                                      int32_t n_items) {
+  static thread_local AttnPlan plan;
+  if (prepare_attention(geom, items, n_items, plan) != SA_OK) return 0;
+  const size_t bytes = plan_split(plan);
+  ok();
+  return bytes;
+}
+
+sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  static thread_local AttnPlan plan;
+  sa_status st = prepare_attention(geom, items, n_items, plan);
+  if (st != SA_OK) return st;
+  AttnArgs& a = plan.a;
+  if (a.total_tiles == 0) return ok();
+  const size_t need = plan_split(plan);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))) {
+    a.n_full = a.total_tiles;   // no room for partials: run unsplit
+    a.split_k = 1;
+    a.grid = a.total_tiles;
+  }
+  a.ws = static_cast<float*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(fp8 ? launch_attention_fp8(a, s) : launch_attention_bf16(a, s),
-                    "segment_attention launch");
+  if ((st = hip_status(plan.fp8 ? launch_attention_fp8(a, s) : launch_attention_bf16(a, s),
+                       "segment_attention launch")) != SA_OK)
+    return st;
+  if (a.split_k > 1)
+    return hip_status(launch_attention_combine(a, plan.bm, s), "segment_attention combine launch");
+  return ok();
 }
 
 sa_status sa_kv_dequant(const sa_geom* geom, const sa_kv_layer* src, const int32_t* d_frames,

@@ -63,17 +63,30 @@ struct AttnItemDev {
   int32_t tile_begin;    // first logical tile of this item (over heads * q_tiles)
 };
 
+// Work: total_tiles logical query tiles ordered (item, head, query tile). The
+// first n_full run whole; each later one runs as split_k parts over its key
+// tiles (part p: [p n / split_k, (p+1) n / split_k)), writing partials to ws:
+// for unit u = (tile - n_full) * split_k + part, O [BM][128] at
+// ws + u * BM * kPartialStride, then m [BM] and l [BM] (log2-unit max and sum
+// of the exponentials against it; O is not normalised).
 struct AttnArgs {
   AttnItemDev items[SA_MAX_ITEMS];
   int32_t n_items;
   int32_t heads;
   int32_t total_tiles;
+  int32_t n_full;
+  int32_t split_k;        // 1: nothing is split
+  int32_t grid;           // n_full + (total_tiles - n_full) * split_k
+  float* ws;
   float scale_log2;       // softmax scale * log2(e)
   RopeParams rope;
 };
 
+constexpr int kPartialStride = kD + 2;   // floats per row of a partial: O, m, l
+
 hipError_t launch_attention_bf16(AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_fp8(AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_combine(const AttnArgs& a, int block_m, hipStream_t s);
 int attention_block_m_bf16();
 int attention_block_m_fp8();
 

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 1
+#define SA_ABI_VERSION 2
 #define SA_HEAD_DIM 128       /* the only head dim the kernels are built for */
 #define SA_MAX_ITEMS 8        /* sessions per sa_segment_attention call     */
 #define SA_MAX_FRAMES_KV 65536
@@ -203,11 +203,25 @@ sa_status sa_history_gather(const sa_geom* geom, const sa_kv_layer* src, const i
  * split per (row, head) into an e4m3 high part and an e4m3 low part (scaled
  * by 2^-4), and the per-(frame, head) scales applied to the logits and folded
  * into the probabilities. All items must share one dtype.
+ * Work is split into 256-row query tiles per (item, head). When the tiles do
+ * not fill the device evenly, the tiles of the last partial round are split
+ * further over their key range, and a second kernel merges the partial
+ * results (max, sum and unnormalised output per row, combined in fixed order:
+ * results are deterministic). The partials live in the caller's workspace of
+ * sa_segment_attention_workspace() bytes (device memory, 16-byte aligned,
+ * owned by the caller, overlapping no input or output; calls that share one
+ * workspace must not overlap in time). With a smaller, unaligned or NULL
+ * workspace nothing is split and the result is the same up to rounding.
+ * sa_segment_attention_workspace returns 0 when no split pays, when the
+ * arguments are invalid (sa_segment_attention then reports the error) or
+ * when no device is current; it launches nothing.
  * Source: "How one segment is made" and "What 'world memory' stores".
  * Errors: SA_E_ARG (n_items outside [1, SA_MAX_ITEMS], empty key set),
  * SA_E_RANGE (n_frames_kv > SA_MAX_FRAMES_KV, n_text_kv > text_capacity).   */
+size_t sa_segment_attention_workspace(const sa_geom* geom, const sa_attn_item* items,
+                                      int32_t n_items);
 sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
-                               void* stream);
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* kv_dequant: fp8 frames[i] of src -> bf16 frame slot i of dst (K and V
  * planes: value = code * scale, rounded to bf16), and, when n_text > 0, the

@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 1
+    assert sa.abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -167,7 +167,8 @@ def _item(L, rows=True, n_frames_kv=2, n_text_kv=3, frames=FAKE):
 def _attn(items, n=None):
     g = _geom()
     arr = (B.sa_attn_item * max(len(items), 1))(*items)
-    return sa.lib().sa_segment_attention(ctypes.byref(g), arr, len(items) if n is None else n, None)
+    return sa.lib().sa_segment_attention(ctypes.byref(g), arr, len(items) if n is None else n,
+                                         None, 0, None)
 
 
 def test_attention_validation(lib):
@@ -183,6 +184,19 @@ def test_attention_validation(lib):
     bad = _item(L)
     bad.q = FAKE + 8
     assert _attn([bad]) == 3
+
+
+def test_attention_workspace_query_without_split(lib):
+    """The workspace query launches nothing; invalid arguments (and, here, no
+    device) give 0, so the call would run every tile whole."""
+    L = _layer()
+    g = _geom()
+    q = lib.sa_segment_attention_workspace
+    arr = (B.sa_attn_item * 1)(_item(L))
+    assert q(ctypes.byref(g), arr, 1) == 0
+    assert q(ctypes.byref(g), arr, 0) == 0
+    bad = (B.sa_attn_item * 1)(_item(L, n_text_kv=17))
+    assert q(ctypes.byref(g), bad, 1) == 0
 
 
 def test_gather_and_dequant_validation(lib):

@@ -7,7 +7,8 @@ sharpened logits. Gate: max-abs <= 2e-2 and mean-abs <= 2e-3 (the bf16 bar);
 relative L2 is also bounded (1e-2) so that a wrong kernel cannot hide under
 the absolute bar. Closed forms: a single key copies its value bitwise; Q = 0
 with one-hot values counts every key exactly once; uniform V gives V within
-one bf16 ulp. Determinism: two runs are bitwise identical.
+one bf16 ulp. Determinism: two runs are bitwise identical. Split tiles (key
+ranges merged from fp32 partials) against whole tiles.
 """
 
 import math
@@ -116,6 +117,72 @@ def test_parity_gathered_power_history_two_sessions():
         got, _ = s.gpu_out()
         _, _, rel = compare(got, want, MAX_ABS, MEAN_ABS, f"session {s.session}")
         assert rel <= REL_L2
+
+
+def _fp8_wl(name, H, F, lh, lw, nt, prior):
+    return si.Workload(name, heads=H, lat_t=F, lat_h=lh, lat_w=lw, n_text=nt,
+                       prior_segments=(prior,), kv_dtype="fp8", scale_factors=True)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_split_tiles_match_whole_tiles(kv):
+    """With a workspace the last round's query tiles are cut into key-range
+    parts whose fp32 partials (O, m, l) a second kernel merges. Both paths
+    meet the bar against the oracle and agree with each other to within a
+    few bf16 ulps; a workspace that is too small runs every tile whole, bit
+    for bit like no workspace."""
+    print(f"split vs whole tiles kv={kv}", flush=True)
+    if kv == "bf16":
+        wl = _wl("split", 4, 6, 8, 16, 256, 2)
+    else:
+        wl = _fp8_wl("split8", 4, 6, 8, 16, 256, 2)
+    s = Session(wl, seed=29, layer=0, session=0)
+    need = sa.segment_attention_workspace(s.geom, [s.item()])
+    assert need > 0
+    sa.segment_attention(s.geom, [s.item()], workspace=None)
+    torch.cuda.synchronize()
+    whole, whole_lse = s.gpu_out()
+    small = torch.empty(need // 2, dtype=torch.uint8, device="cuda")
+    sa.segment_attention(s.geom, [s.item()], workspace=small)
+    torch.cuda.synchronize()
+    again, again_lse = s.gpu_out()
+    assert np.array_equal(again, whole) and np.array_equal(again_lse, whole_lse)
+    sa.segment_attention(s.geom, [s.item()])
+    torch.cuda.synchronize()
+    split, split_lse = s.gpu_out()
+    diff = np.abs(split - whole)
+    print(f"split vs whole: max_abs={diff.max():.3e}", flush=True)
+    assert diff.max() <= 8 * 2.0 ** -8 * max(1.0, np.abs(whole).max())
+    np.testing.assert_allclose(split_lse, whole_lse, atol=2e-3, rtol=0)
+    if kv == "bf16":
+        want, want_lse = s.oracle()
+        for got, got_lse, lab in ((whole, whole_lse, "whole"), (split, split_lse, "split")):
+            _, _, rel = compare(got, want, MAX_ABS, MEAN_ABS, lab)
+            assert rel <= REL_L2
+            np.testing.assert_allclose(got_lse, want_lse, atol=LSE_ATOL, rtol=0)
+    else:
+        wq, wq_lse, bound = s.oracle_fp8_cache()
+        for got, got_lse in ((whole, whole_lse), (split, split_lse)):
+            assert np.all(np.abs(got - wq) <= bound + 5e-3)
+            np.testing.assert_allclose(got_lse, wq_lse, atol=2e-2, rtol=0)
+
+
+def test_split_tiles_across_two_sessions():
+    """Split parts of tiles from two items (different key sets) in one call."""
+    wl = si.Workload("split2", heads=2, lat_t=4, lat_h=8, lat_w=16, n_text=16,
+                     prior_segments=(3, 2), capacity_segments=4)
+    s0 = Session(wl, seed=31, layer=0, session=0)
+    s1 = Session(wl, seed=31, layer=0, session=1, history=[5, 0, 7, 2, 1])
+    items = [s0.item(), s1.item()]
+    assert sa.segment_attention_workspace(s0.geom, items) > 0
+    sa.segment_attention(s0.geom, items)
+    torch.cuda.synchronize()
+    for s in (s0, s1):
+        want, want_lse = s.oracle()
+        got, got_lse = s.gpu_out()
+        _, _, rel = compare(got, want, MAX_ABS, MEAN_ABS, f"split session {s.session}")
+        assert rel <= REL_L2
+        np.testing.assert_allclose(got_lse, want_lse, atol=LSE_ATOL, rtol=0)
 
 
 def test_single_key_copies_value_bitwise():
@@ -238,8 +305,7 @@ def test_fp8_parity_small(case):
     rotation."""
     name, H, F, lh, lw, nt, prior = case
     print(f"fp8 attention parity case={name}", flush=True)
-    wl = si.Workload(name, heads=H, lat_t=F, lat_h=lh, lat_w=lw, n_text=nt,
-                     prior_segments=(prior,), kv_dtype="fp8", scale_factors=True)
+    wl = _fp8_wl(name, H, F, lh, lw, nt, prior)
     s = Session(wl, seed=23, layer=0, session=0)
     sa.segment_attention(s.geom, [s.item()])
     torch.cuda.synchronize()

@@ -64,6 +64,20 @@ def test_one_prior_segment():
     _check([s], 192, label="seg1")
 
 
+def test_one_prior_segment_two_heads():
+    """One GPU's share of the one-prior-segment workload when the 16 heads are
+    spread over 8 GPUs: 2 heads, 210 query tiles, fewer than the compute
+    units, so every tile runs as key-range parts merged afterwards."""
+    wl = si.Workload("seg1h2", heads=2, lat_t=30, lat_h=22, lat_w=40, n_text=256,
+                     prior_segments=(1,))
+    print("workload seg1 at 2 heads: 26,656 queries x 53,056 keys", flush=True)
+    s = Session(wl, 0, 0, 0)
+    assert sa.segment_attention_workspace(s.geom, [s.item()]) > 0
+    sa.segment_attention(s.geom, [s.item()])
+    torch.cuda.synchronize()
+    _check([s], 192, label="seg1 2 heads")
+
+
 def test_long_history_54_layers():
     """Four prior segments, 54 independent seeded layers: every layer checked on
     a row sample over two heads; layers 0 and 53 on all heads."""
