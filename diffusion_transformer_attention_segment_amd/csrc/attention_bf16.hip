@@ -33,6 +33,8 @@
 // block max exceeds the running max by more than the slack -- rare after the
 // first blocks -- a wave-uniform branch rescales O and the sum and recomputes
 // the block's probabilities.
+#include <type_traits>
+
 #include "attention_common.h"
 
 namespace segattn {
@@ -50,6 +52,7 @@ constexpr int VT = kD * VS;      // elements of one V^T stage
 constexpr int kKChunks = BN * kD / 8 / kThreads;   // 16-byte K chunks per thread (2)
 constexpr int kVChunks = kD * BN / 8 / kThreads;   // 16-byte V chunks per thread (2)
 constexpr float kRescaleSum = 256.0f;   // a row's block sum above this moves the running max
+constexpr float kFastLimit = 1.8446744e19f;   // 2^64: a block sum above it sends the workgroup to the rescaling loop
 
 // Load tile c: K rows past the valid count and V^T bytes past the plane end
 // read as zero through the buffer bounds; V^T columns past the valid count
@@ -195,6 +198,9 @@ __device__ __forceinline__ float fused_step(const uint16_t* vp, const uint16_t* 
       l1 = dot2_bf16(pw[c][db], ones, l1);
     else
       l0 = dot2_bf16(pw[c][db], ones, l0);
+    // pin this slot's softmax work here: without it instruction selection
+    // gathers every exponential of the step after the MFMAs
+    asm volatile("" : "+v"(pw[c][db]), "+v"(l0), "+v"(l1));
     if (i == 1) work();
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -261,23 +267,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   key_range(a, I, P, wt.part, &kt0, &kt1);
   const int ntiles = kt1 - kt0;
 
-  // the load cursor runs three tiles ahead of the compute tile; nv0..nv2 keep
-  // the valid-key counts of the tiles in between
-  TileCursor lc;
-  cursor_start<2>(lc, I, h, H, P, kt0);
-  u32x4 kr[kKChunks], vr[kVChunks];
-  int nv0 = cursor_nvalid(lc);
-  load_tile(lc, koff_ld, kr, vr);
-
   if (tid < kD / 2) {
     int axis;
     om[tid] = rope_omega(tid, a.rope, &axis);
     ax[tid] = axis;
   }
-  // the last V stage is read once with zero probabilities before it is first
-  // written: give it finite contents
-  for (int i = tid; i < VT / 8; i += kThreads)
-    reinterpret_cast<u32x4*>(Vs + (kStages - 1) * VT)[i] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
   // ---- Q fragments (B operand of S^T = K Q^T): rotated in fp32, times the
@@ -315,115 +309,150 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     }
   }
 
-  // ---- prologue: tiles 0, 1 into LDS stages 0, 1; tile 2 in flight ----------
-  store_tile(Ks, Vs, tid, kr, vr);
-  int nv1 = 0, nv2 = 0;
-  if (ntiles > 1) {
-    cursor_next<2>(lc, I, h, H, P);
-    nv1 = cursor_nvalid(lc);
-    load_tile(lc, koff_ld, kr, vr);
-    store_tile(Ks + KT, Vs + VT, tid, kr, vr);
-  }
-  if (ntiles > 2) {
-    cursor_next<2>(lc, I, h, H, P);
-    nv2 = cursor_nvalid(lc);
-    load_tile(lc, koff_ld, kr, vr);
-  }
-  __syncthreads();
-
   const int pi_row = (r32 & ~0xC) | ((r32 & 4) << 1) | ((r32 & 8) >> 1);
   const int koff0 = pi_row * KS + 8 * g;          // block 0 K row of this lane
   const int koff1 = (32 + pi_row) * KS + 8 * g;   // block 1
   const int voff = r32 * VS + 8 * g;
-  f32x16 o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float l_run = 0.f;
   const uint32_t ones = kOnesBf16x2;
-
-  // Blocks 2t and 2t+1 are the halves of tile t (stage t % 4). Step 2t still
-  // reads V of tile t-1, so tile t+2 goes to stage (t+2) % 4, last read before
-  // the barrier that precedes the store.
-  // Each tile has two steps, so the two S buffers and the two P buffers swap
-  // roles between the steps and the loop carries no register copies.
-  // The running max starts at block 0's max (block 0 always has a valid key).
-  f32x16 sa = qk_block(Ks + koff0, qf);     // S of block 2t at the top of the loop
-  f32x16 sb;                                // S of block 2t+1
-  if (nv0 < 32) mask_block(sa, nv0, g);
-  const float m0 = block_max(sa);
+  f32x16 o[4];
   f32x16 negm;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    negm[r] = -m0;
-    sa[r] -= m0;
-  }
-  bf16x8 pa[2], pb[2];                      // P of block 2t-1 at the top; of 2t
-  pa[0] = pa[1] = bf16x8{};
+  float l_run;
 
-  // operands of step 0's first slots: V of "tile -1" (the zeroed last stage,
-  // met by the zero probabilities pa) and block 1's K rows
-  StepOperands pre;
-  pre.v[0] = lds_op(v_operand(Vs + (kStages - 1) * VT + voff + 32, 0));
-  pre.v[1] = lds_op(v_operand(Vs + (kStages - 1) * VT + voff + 32, 1));
-  pre.k[0] = lds_op(Ks + koff1);
-  pre.k[1] = lds_op(Ks + koff1 + 16);
+  // The whole key loop, run first without the rescale: the running max stays
+  // at block 0's max, and a block sum above kFastLimit only raises a flag
+  // (probabilities up to 2^64 stay exact in fp32 and bf16, so nothing before
+  // the flag is lost; the flag is raised long before anything could
+  // overflow). Without rescale code in the loop the register allocator keeps
+  // every block in place. If any row of the workgroup raised the flag, the
+  // whole loop runs again, rescaling in place.
+  auto attend = [&](auto safe_tag) __attribute__((always_inline)) {
+    constexpr bool kSafe = decltype(safe_tag)::value;
+    bool over = false;
+    // the load cursor runs three tiles ahead of the compute tile; nv0..nv2
+    // keep the valid-key counts of the tiles in between
+    TileCursor lc;
+    cursor_start<2>(lc, I, h, H, P, kt0);
+    u32x4 kr[kKChunks], vr[kVChunks];
+    int nv0 = cursor_nvalid(lc);
+    load_tile(lc, koff_ld, kr, vr);
+    // the last V stage is read once with zero probabilities before it is
+    // first written: give it finite contents
+    for (int i = tid; i < VT / 8; i += kThreads)
+      reinterpret_cast<u32x4*>(Vs + (kStages - 1) * VT)[i] = u32x4{0u, 0u, 0u, 0u};
 
-#pragma unroll 1
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & (kStages - 1);
-    const uint16_t* Kst = Ks + st * KT;
-    const uint16_t* Vst = Vs + st * VT;
-    const uint16_t* Vprev = Vs + ((t + kStages - 1) & (kStages - 1)) * VT;
-    const uint16_t* Knext = Ks + ((t + 1) & (kStages - 1)) * KT;
-    const int nvalid = nv0;
-    int nv3 = 0;
-    // Tile t+2: registers -> LDS stage (t+2) % 4, the stage of tile t-2, whose
-    // last reads (step 2t-2) completed before this barrier; then start loading
-    // tile t+3. Nothing read in this tile's steps lives in that stage, so the
-    // barrier needs no fence and the reads already in flight stay in flight.
-    auto boundary = [&]() {
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (t + 2 < ntiles) {
-        const int s2 = (t + 2) & (kStages - 1);
-        store_tile(Ks + s2 * KT, Vs + s2 * VT, tid, kr, vr);
-        if (t + 3 < ntiles) {
-          cursor_next<2>(lc, I, h, H, P);
-          nv3 = cursor_nvalid(lc);
-          load_tile(lc, koff_ld, kr, vr);
-        }
-      }
-    };
-
-    // step 2t: PV(2t-1) [pa] + QK(2t+1) [-> sb] | softmax(2t) [sa -> pb]
-    if (nvalid < 32) mask_block(sa, nvalid, g);
-    float lb = fused_step(Vprev + voff + 32, Kst + koff1, Vst + voff, Knext + koff0, pre, pa, o,
-                          qf, negm, sb, sa, ones, pb, boundary);
-    if (__builtin_expect(__any(lb > kRescaleSum), 0)) lb = rescale_step(negm, l_run, o, sa, sb, ones, pb);
-    l_run += lb;
-
-    // step 2t+1: PV(2t) [pb] + QK(2t+2) [-> sa] | softmax(2t+1) [sb -> pa]
-    if (nvalid < BN) mask_block(sb, nvalid - 32, g);
-    lb = fused_step(Vst + voff, Knext + koff0, Vst + voff + 32, Knext + koff1, pre, pb, o, qf,
-                    negm, sa, sb, ones, pa, [] {});
-    if (__builtin_expect(__any(lb > kRescaleSum), 0)) lb = rescale_step(negm, l_run, o, sb, sa, ones, pa);
-    l_run += lb;
-
-    nv0 = nv1;
-    nv1 = nv2;
-    nv2 = nv3;
-  }
-  {
-    const uint16_t* Vlast = Vs + ((ntiles - 1) & (kStages - 1)) * VT;
-    const uint16_t* vp = Vlast + voff + 32;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = i >> 2, db = i & 3;
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *reinterpret_cast<const bf16x8*>(vp + 16 * c + 32 * db * VS), pa[c], o[db], 0, 0, 0);
+    // ---- prologue: tiles 0, 1 into LDS stages 0, 1; tile 2 in flight ----------
+    store_tile(Ks, Vs, tid, kr, vr);
+    int nv1 = 0, nv2 = 0;
+    if (ntiles > 1) {
+      cursor_next<2>(lc, I, h, H, P);
+      nv1 = cursor_nvalid(lc);
+      load_tile(lc, koff_ld, kr, vr);
+      store_tile(Ks + KT, Vs + VT, tid, kr, vr);
     }
-  }
+    if (ntiles > 2) {
+      cursor_next<2>(lc, I, h, H, P);
+      nv2 = cursor_nvalid(lc);
+      load_tile(lc, koff_ld, kr, vr);
+    }
+    __syncthreads();
+
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+      l_run = 0.f;
+
+    // Blocks 2t and 2t+1 are the halves of tile t (stage t % 4). Step 2t still
+    // reads V of tile t-1, so tile t+2 goes to stage (t+2) % 4, last read before
+    // the barrier that precedes the store.
+    // Each tile has two steps, so the two S buffers and the two P buffers swap
+    // roles between the steps and the loop carries no register copies.
+    // The running max starts at block 0's max (block 0 always has a valid key).
+    f32x16 sa = qk_block(Ks + koff0, qf);     // S of block 2t at the top of the loop
+    f32x16 sb;                                // S of block 2t+1
+    if (nv0 < 32) mask_block(sa, nv0, g);
+    const float m0 = block_max(sa);
+  #pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      negm[r] = -m0;
+      sa[r] -= m0;
+    }
+    bf16x8 pa[2], pb[2];                      // P of block 2t-1 at the top; of 2t
+    pa[0] = pa[1] = bf16x8{};
+
+    // operands of step 0's first slots: V of "tile -1" (the zeroed last stage,
+    // met by the zero probabilities pa) and block 1's K rows
+    StepOperands pre;
+    pre.v[0] = lds_op(v_operand(Vs + (kStages - 1) * VT + voff + 32, 0));
+    pre.v[1] = lds_op(v_operand(Vs + (kStages - 1) * VT + voff + 32, 1));
+    pre.k[0] = lds_op(Ks + koff1);
+    pre.k[1] = lds_op(Ks + koff1 + 16);
+
+  #pragma unroll 1
+    for (int t = 0; t < ntiles; ++t) {
+      const int st = t & (kStages - 1);
+      const uint16_t* Kst = Ks + st * KT;
+      const uint16_t* Vst = Vs + st * VT;
+      const uint16_t* Vprev = Vs + ((t + kStages - 1) & (kStages - 1)) * VT;
+      const uint16_t* Knext = Ks + ((t + 1) & (kStages - 1)) * KT;
+      const int nvalid = nv0;
+      int nv3 = 0;
+      // Tile t+2: registers -> LDS stage (t+2) % 4, the stage of tile t-2, whose
+      // last reads (step 2t-2) completed before this barrier; then start loading
+      // tile t+3. Nothing read in this tile's steps lives in that stage, so the
+      // barrier needs no fence and the reads already in flight stay in flight.
+      auto boundary = [&]() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (t + 2 < ntiles) {
+          const int s2 = (t + 2) & (kStages - 1);
+          store_tile(Ks + s2 * KT, Vs + s2 * VT, tid, kr, vr);
+          if (t + 3 < ntiles) {
+            cursor_next<2>(lc, I, h, H, P);
+            nv3 = cursor_nvalid(lc);
+            load_tile(lc, koff_ld, kr, vr);
+          }
+        }
+      };
+
+      // step 2t: PV(2t-1) [pa] + QK(2t+1) [-> sb] | softmax(2t) [sa -> pb]
+      if (nvalid < 32) mask_block(sa, nvalid, g);
+      float lb = fused_step(Vprev + voff + 32, Kst + koff1, Vst + voff, Knext + koff0, pre, pa, o,
+                            qf, negm, sb, sa, ones, pb, boundary);
+      if constexpr (kSafe) {
+        if (__builtin_expect(__any(lb > kRescaleSum), 0)) lb = rescale_step(negm, l_run, o, sa, sb, ones, pb);
+      } else {
+        over |= lb > kFastLimit;
+      }
+      l_run += lb;
+
+      // step 2t+1: PV(2t) [pb] + QK(2t+2) [-> sa] | softmax(2t+1) [sb -> pa]
+      if (nvalid < BN) mask_block(sb, nvalid - 32, g);
+      lb = fused_step(Vst + voff, Knext + koff0, Vst + voff + 32, Knext + koff1, pre, pb, o, qf,
+                      negm, sa, sb, ones, pa, [] {});
+      if constexpr (kSafe) {
+        if (__builtin_expect(__any(lb > kRescaleSum), 0)) lb = rescale_step(negm, l_run, o, sb, sa, ones, pa);
+      } else {
+        over |= lb > kFastLimit;
+      }
+      l_run += lb;
+
+      nv0 = nv1;
+      nv1 = nv2;
+      nv2 = nv3;
+    }
+    {
+      const uint16_t* Vlast = Vs + ((ntiles - 1) & (kStages - 1)) * VT;
+      const uint16_t* vp = Vlast + voff + 32;
+  #pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = i >> 2, db = i & 3;
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *reinterpret_cast<const bf16x8*>(vp + 16 * c + 32 * db * VS), pa[c], o[db], 0, 0, 0);
+      }
+    }
+    return over;
+  };
+  if (__syncthreads_or(attend(std::false_type{}))) attend(std::true_type{});
   const float m_run = -negm[0];
 
   // The output MFMAs compute across all lanes of the wave: keep them (and

@@ -90,6 +90,34 @@ def test_parity_theta_and_sharpened(theta, q_scale):
     assert rel <= REL_L2
 
 
+def test_logits_far_above_the_first_block():
+    """Q x 40: logits spread over hundreds of log2 units, so rows meet keys far
+    above their first block's max. Workgroups whose block sums pass the fast
+    loop's limit redo the key loop with the running max moving in place; the
+    test first checks, with the oracle's own logits, that such rows exist."""
+    wl = _wl("far", 2, 4, 6, 8, 24, 2)
+    s = Session(wl, seed=13, layer=0, session=0, q_scale=40.0)
+    k, _, kpos = s.raw_keys()
+    q = s.q.float().cpu().double().numpy()
+    from oracle import rope as orope
+    qr = orope.rope3d(q, s.q_positions(), wl.split, s.geom.rope_theta)
+    kr = orope.rope3d(k, kpos, wl.split, s.geom.rope_theta)
+    c2 = math.log2(math.e) / math.sqrt(wl.head_dim)
+    jump = 0.0
+    for hh in range(wl.heads):
+        lg = (qr[:, hh] @ kr[:, hh].T) * c2
+        jump = max(jump, float(np.max(lg.max(axis=1) - lg[:, :min(32, wl.P)].max(axis=1))))
+    print(f"largest rise of a row's max past its first block: {jump:.1f} log2 units", flush=True)
+    assert jump > 80.0
+    sa.segment_attention(s.geom, [s.item()])
+    torch.cuda.synchronize()
+    got, got_lse = s.gpu_out()
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(got_lse))
+    wr, wr_lse = s.oracle(round_rotated=True)
+    compare(got, wr, MAX_ABS, MEAN_ABS, "q*40 vs bf16-rounded Q/K")
+    np.testing.assert_allclose(got_lse, wr_lse, rtol=2e-3, atol=0.05)
+
+
 @pytest.mark.parametrize("case", CASES[:3], ids=[c[0] for c in CASES[:3]])
 def test_kernel_error_against_rounded_inputs(case):
     """Against the oracle that rounds rotated Q and K to bf16, the kernel's own
