@@ -36,7 +36,13 @@ __device__ __forceinline__ WorkTile map_workgroup(const AttnArgs& a, int block_m
     w.part = -1;
     w.unit = 0;
   } else {
-    const int u = b - a.n_full;
+    // split parts: the same remap over the parts, so that an XCD runs whole
+    // tiles' parts of few heads (their K/V stay in its L2)
+    const int bp = b - a.n_full;
+    const int nu = a.grid - a.n_full;
+    const int xcd = bp & 7, idx = bp >> 3;
+    const int per = nu >> 3, rem = nu & 7;
+    const int u = xcd * per + min(xcd, rem) + idx;
     logical = a.n_full + u / a.split_k;
     w.part = u - (u / a.split_k) * a.split_k;
     w.unit = u;
