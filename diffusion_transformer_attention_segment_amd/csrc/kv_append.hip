@@ -6,15 +6,23 @@
 // and "Writing the segment into memory" (the finished segment's K/V are
 // stored); "The 4090 preset" (the cache is quantised once per segment).
 //
-// HBM-bound: per token and head the kernel reads 2 x 256 B of bf16 input and
-// writes 2 x 256 B (bf16) or 2 x 128 B (e4m3) of cache.
+// HBM-bound: per token and head the kernels read 2 x 256 B of bf16 input and
+// write 2 x 256 B (bf16) or 2 x 128 B (e4m3) of cache. Blocks run heads
+// fastest, so that concurrent blocks read the same tokens' rows of all heads
+// (4 KB contiguous per token). The bf16 kernel transposes V through LDS and
+// stores 16-byte runs of V^T rows. The e4m3 kernel holds one (frame, head)
+// plane per block (the scale needs the plane's amax); it tabulates the
+// rotation angles in LDS once per block (they depend on the band position and
+// the pair only) and transposes V in registers (a thread holds the same dims
+// of 4 consecutive tokens and stores whole 4-byte words of V^T rows).
 #include "device_common.h"
 
 namespace segattn {
 namespace {
 
-constexpr int kTileTok = 64;          // tokens per block tile
+constexpr int kTileTok = 64;          // tokens per bf16 block tile
 constexpr int kVtStride = kD + 8;     // LDS row stride (elements) of the V tile
+constexpr int kLutMax = 4096;         // rotation table entries (cos, sin) within the LDS budget
 
 // Rotate the 8 bf16 values of one 16-byte chunk (dims ch*8 .. ch*8+7) of a key
 // at (t, h, w), in fp32, and return them rounded to bf16.
@@ -40,9 +48,9 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(const AppendArgs a) {
   __shared__ double om[kD / 2];
   __shared__ int ax[kD / 2];
   const int tid = threadIdx.x;
-  const int p0 = blockIdx.x * kTileTok;
-  const int fr = blockIdx.y;
-  const int h = blockIdx.z;
+  const int p0 = blockIdx.y * kTileTok;
+  const int fr = blockIdx.z;
+  const int h = blockIdx.x;
   const int H = a.heads;
   if (tid < kD / 2) {
     int axis;
@@ -96,38 +104,118 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(const AppendArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- e4m3 path
-// fp32 -> OCP e4m3fn code, round to nearest even, saturating at 448.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = fabsf(y);
-  if (a != a) return 0x7Fu;
-  if (a >= 448.0f) return 0x7Eu | sign;
-  uint32_t code;
-  if (a < 0.015625f) {                       // below 2^-6: subnormal grid 2^-9
-    code = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
-  } else {
-    const uint32_t ua = __float_as_uint(a);
-    int e = static_cast<int>((ua >> 23) & 0xFF) - 127 + 7;
-    uint32_t m3 = (ua >> 20) & 0x7u;
-    const uint32_t rest = ua & 0xFFFFFu;
-    if (rest > 0x80000u || (rest == 0x80000u && (m3 & 1u))) ++m3;
-    if (m3 == 8u) { m3 = 0u; ++e; }
-    code = (static_cast<uint32_t>(e) << 3) | m3;
-    if (code > 0x7Eu) code = 0x7Eu;
+// ---- RoPE table ------------------------------------------------------------------
+struct LutShape {
+  int nt, nh, nw;   // pairs per band (t, h, w)
+  int lat_h;
+  int size;         // entries: nt + lat_h * nh + lat_w * nw
+};
+
+__device__ __forceinline__ LutShape lut_shape(const RopeParams& r) {
+  LutShape s;
+  s.nt = r.split0 / 2;
+  s.nh = r.split1 / 2;
+  s.nw = r.split2 / 2;
+  s.lat_h = r.P / r.lat_w;
+  s.size = s.nt + s.lat_h * s.nh + r.lat_w * s.nw;
+  return s;
+}
+
+// Entry i: t-band pair i at position t, then [hh][j] for the h band, then
+// [ww][j] for the w band; each from the same fp64-reduced angle as the direct
+// evaluation (rope_cos_sin), so a table lookup and the direct path agree
+// bit for bit.
+__device__ void build_lut(float2* lut, const LutShape& s, int t, const RopeParams& r, int tid,
+                          int nthreads) {
+  for (int i = tid; i < s.size; i += nthreads) {
+    int pair, pos;
+    if (i < s.nt) {
+      pair = i;
+      pos = t;
+    } else if (i < s.nt + s.lat_h * s.nh) {
+      const int j = i - s.nt;
+      pos = j / s.nh;
+      pair = s.nt + (j - pos * s.nh);
+    } else {
+      const int j = i - s.nt - s.lat_h * s.nh;
+      pos = j / s.nw;
+      pair = s.nt + s.nh + (j - pos * s.nw);
+    }
+    int axis;
+    const double om = rope_omega(pair, r, &axis);
+    float c, sn;
+    rope_cos_sin(pos, om, &c, &sn);
+    lut[i] = make_float2(c, sn);
   }
+}
+
+__device__ __forceinline__ float2 lut_get(const float2* lut, const LutShape& s, int pair, int hh,
+                                          int ww) {
+  if (pair < s.nt) return lut[pair];
+  if (pair < s.nt + s.nh) return lut[s.nt + hh * s.nh + (pair - s.nt)];
+  return lut[s.nt + s.lat_h * s.nh + ww * s.nw + (pair - s.nt - s.nh)];
+}
+
+// The 8 values of one 16-byte chunk (dims 8 ch .. 8 ch + 7) of a key at
+// (t, hh, ww): rotated in fp32 (cos/sin from the table when given, else
+// evaluated), or, for text keys, unrotated.
+template <bool kLut>
+__device__ __forceinline__ void key_chunk(const u32x4& x, int ch, int t, int hh, int ww,
+                                          bool rotate, const float2* lut, const LutShape& ls,
+                                          const RopeParams& r, float* y) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float a = __uint_as_float(x[m] << 16);
+    const float b = __uint_as_float(x[m] & 0xFFFF0000u);
+    if (!rotate) {
+      y[2 * m] = a;
+      y[2 * m + 1] = b;
+      continue;
+    }
+    const int pr = ch * 4 + m;
+    float c, s;
+    if constexpr (kLut) {
+      const float2 cs = lut_get(lut, ls, pr, hh, ww);
+      c = cs.x;
+      s = cs.y;
+    } else {
+      int axis;
+      const double om = rope_omega(pr, r, &axis);
+      rope_cos_sin(axis == 0 ? t : (axis == 1 ? hh : ww), om, &c, &s);
+    }
+    y[2 * m] = a * c - b * s;
+    y[2 * m + 1] = a * s + b * c;
+  }
+}
+
+__device__ __forceinline__ u32x4 load_chunk(const uint16_t* base, size_t off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+
+// ---- e4m3 ------------------------------------------------------------------------
+// fp32 -> OCP e4m3fn code, round to nearest even, saturating at 448 (NaN ->
+// 0x7F). Normal range: round the fp32 pattern to 3 mantissa bits (ties to
+// even) and rebias the exponent; below 2^-6: nearest multiple of 2^-9.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  const uint32_t ua = __float_as_uint(a);
+  const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);
+  const int normal = static_cast<int>(r >> 20) - (120 << 3);
+  const int sub = static_cast<int>(__builtin_rintf(a * 512.0f));
+  uint32_t code = static_cast<uint32_t>(min(a < 0.015625f ? sub : normal, 0x7E));
+  if (a != a) return 0x7Fu;
   return code | sign;
 }
 
-__device__ __forceinline__ float block_max(float v, float* red) {
+__device__ __forceinline__ float block_max(float v, float* red, int nthreads) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
   float r = red[0];
-  for (int i = 1; i < static_cast<int>(blockDim.x >> 6); ++i) r = fmaxf(r, red[i]);
+  for (int i = 1; i < nthreads / 64; ++i) r = fmaxf(r, red[i]);
   __syncthreads();
   return r;
 }
@@ -135,40 +223,37 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 constexpr int kFp8Threads = 512;
 
 // One block per (frame, head) plane (or per head of the text slot): pass 1
-// finds amax of the rotated K and of V, pass 2 quantises and stores.
+// finds amax of the rotated K and of V, pass 2 quantises and stores (K rows of
+// 8-byte chunks; V^T rows in 4-byte words of 4 consecutive tokens).
+template <bool kLut>
 __global__ __launch_bounds__(kFp8Threads) void append_fp8_kernel(const AppendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kTileTok * kVtStride];
-  __shared__ double om[kD / 2];
-  __shared__ int ax[kD / 2];
+  __shared__ float2 lut_mem[kLutMax];
   __shared__ float red[kFp8Threads / 64];
   const int tid = threadIdx.x;
-  const int fr = blockIdx.x;
-  const int h = blockIdx.y;
+  const int h = blockIdx.x;
+  const int fr = blockIdx.y;
   const int H = a.heads;
-  if (tid < kD / 2) {
-    int axis;
-    om[tid] = rope_omega(tid, a.rope, &axis);
-    ax[tid] = axis;
-  }
-  __syncthreads();
   const int f = a.frame0 + fr;
+  const bool rotate = !a.is_text;
+  const LutShape ls = lut_shape(a.rope);
+  if constexpr (kLut) {
+    build_lut(lut_mem, ls, f, a.rope, tid, kFp8Threads);
+    __syncthreads();
+  }
+  const float2* lut = lut_mem;
+  const int lat_w = a.rope.lat_w;
   const int n_chunks = a.n_tok * 16;
+  auto in_off = [&](int p, int ch) {
+    return (static_cast<size_t>(fr * a.n_tok + p) * H + h) * kD + ch * 8;
+  };
   float amk = 0.f, amv = 0.f;
+#pragma unroll 2
   for (int c = tid; c < n_chunks; c += kFp8Threads) {
     const int p = c >> 4, ch = c & 15;
-    const size_t in_off = (static_cast<size_t>(fr * a.n_tok + p) * H + h) * kD + ch * 8;
-    const u32x4 kx = *reinterpret_cast<const u32x4*>(a.k_in + in_off);
-    const u32x4 vx = *reinterpret_cast<const u32x4*>(a.v_in + in_off);
+    const u32x4 kx = load_chunk(a.k_in, in_off(p, ch));
+    const u32x4 vx = load_chunk(a.v_in, in_off(p, ch));
     float y[8];
-    if (!a.is_text) {
-      rotate_chunk(kx, ch, f, p / a.rope.lat_w, p % a.rope.lat_w, om, ax, y);
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        y[2 * m] = __uint_as_float(kx[m] << 16);
-        y[2 * m + 1] = __uint_as_float(kx[m] & 0xFFFF0000u);
-      }
-    }
+    key_chunk<kLut>(kx, ch, f, p / lat_w, p % lat_w, rotate, lut, ls, a.rope, y);
 #pragma unroll
     for (int m = 0; m < 8; ++m) amk = fmaxf(amk, fabsf(y[m]));
 #pragma unroll
@@ -177,8 +262,8 @@ __global__ __launch_bounds__(kFp8Threads) void append_fp8_kernel(const AppendArg
       amv = fmaxf(amv, fabsf(__uint_as_float(vx[m] & 0xFFFF0000u)));
     }
   }
-  amk = block_max(amk, red);
-  amv = block_max(amv, red);
+  amk = block_max(amk, red, kFp8Threads);
+  amv = block_max(amv, red, kFp8Threads);
   const float ik = amk > 0.f ? 448.0f / amk : 1.0f;
   const float iv = amv > 0.f ? 448.0f / amv : 1.0f;
   if (tid == 0) {
@@ -188,74 +273,66 @@ __global__ __launch_bounds__(kFp8Threads) void append_fp8_kernel(const AppendArg
   const size_t plane = static_cast<size_t>(a.plane_len) * kD;
   uint8_t* kdst = static_cast<uint8_t*>(a.k) + (static_cast<size_t>(f) * H + h) * plane;
   uint8_t* vdst = static_cast<uint8_t*>(a.v) + (static_cast<size_t>(f) * H + h) * plane;
+#pragma unroll 2
   for (int c = tid; c < n_chunks; c += kFp8Threads) {
     const int p = c >> 4, ch = c & 15;
-    const size_t in_off = (static_cast<size_t>(fr * a.n_tok + p) * H + h) * kD + ch * 8;
-    const u32x4 kx = *reinterpret_cast<const u32x4*>(a.k_in + in_off);
     float y[8];
-    if (!a.is_text) {
-      rotate_chunk(kx, ch, f, p / a.rope.lat_w, p % a.rope.lat_w, om, ax, y);
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        y[2 * m] = __uint_as_float(kx[m] << 16);
-        y[2 * m + 1] = __uint_as_float(kx[m] & 0xFFFF0000u);
-      }
-    }
+    key_chunk<kLut>(load_chunk(a.k_in, in_off(p, ch)), ch, f, p / lat_w, p % lat_w, rotate, lut,
+                    ls, a.rope, y);
     u32x2 o;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < 2; ++m)
       o[m] = f32_to_e4m3(y[4 * m] * ik) | (f32_to_e4m3(y[4 * m + 1] * ik) << 8) |
              (f32_to_e4m3(y[4 * m + 2] * ik) << 16) | (f32_to_e4m3(y[4 * m + 3] * ik) << 24);
-    }
     *reinterpret_cast<u32x2*>(kdst + static_cast<size_t>(p) * kD + ch * 8) = o;
   }
-  // V: transpose through LDS, 64 tokens at a time; 16 tokens (16 bytes) per store.
-  for (int p0 = 0; p0 < a.plane_len; p0 += kTileTok) {
-    for (int c = tid; c < kTileTok * 16; c += kFp8Threads) {
-      const int tok = c >> 4, ch = c & 15;
-      const int p = p0 + tok;
-      u32x4 vx = {0u, 0u, 0u, 0u};
-      if (p < a.n_tok) {
-        const size_t in_off = (static_cast<size_t>(fr * a.n_tok + p) * H + h) * kD + ch * 8;
-        vx = *reinterpret_cast<const u32x4*>(a.v_in + in_off);
-      }
-      *reinterpret_cast<u32x4*>(&vt[tok * kVtStride + ch * 8]) = vx;
-    }
-    __syncthreads();
-    {
-      const int d = tid >> 2, tc = tid & 3;      // 128 rows x 4 chunks of 16 tokens
-      const int p = p0 + 16 * tc;
-      if (p < a.plane_len) {
-        u32x4 o;
+  // V^T: item = (token quad j, chunk ch), j fastest; plane_len % 16 == 0
+  const int nq = a.plane_len / 4;
+  for (int it = tid; it < nq * 16; it += kFp8Threads) {
+    const int ch = it / nq, j = it - ch * nq;
+    const int p = 4 * j;
+    uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (p + q < a.n_tok) {
+        const u32x4 vx = load_chunk(a.v_in, in_off(p + q, ch));
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const float x = bf16_to_f32(vt[(16 * tc + 4 * m + b) * kVtStride + d]);
-            word |= f32_to_e4m3(x * iv) << (8 * b);
-          }
-          o[m] = word;
+          w[2 * m] |= f32_to_e4m3(__uint_as_float(vx[m] << 16) * iv) << (8 * q);
+          w[2 * m + 1] |= f32_to_e4m3(__uint_as_float(vx[m] & 0xFFFF0000u) * iv) << (8 * q);
         }
-        *reinterpret_cast<u32x4*>(vdst + static_cast<size_t>(d) * a.plane_len + p) = o;
       }
     }
-    __syncthreads();
+    uint32_t* row = reinterpret_cast<uint32_t*>(vdst + static_cast<size_t>(8 * ch) * a.plane_len + p);
+    const size_t stride = a.plane_len / 4;   // words per V^T row
+#pragma unroll
+    for (int e = 0; e < 8; ++e) row[e * stride] = w[e];
   }
 }
 
 }  // namespace
 
+// the rotation table serves video planes whose table fits the LDS budget
+static bool use_lut(const AppendArgs& a) {
+  const RopeParams& r = a.rope;
+  const int64_t size = r.split0 / 2 + static_cast<int64_t>(r.P / r.lat_w) * (r.split1 / 2) +
+                       static_cast<int64_t>(r.lat_w) * (r.split2 / 2);
+  return !a.is_text && size <= kLutMax;
+}
+
 hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s) {
-  dim3 grid((a.plane_len + kTileTok - 1) / kTileTok, a.n_frames, a.heads);
+  // heads fastest: concurrent blocks read the same tokens' rows of all heads
+  dim3 grid(a.heads, (a.plane_len + kTileTok - 1) / kTileTok, a.n_frames);
   hipLaunchKernelGGL(append_bf16_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_append_fp8(const AppendArgs& a, hipStream_t s) {
-  dim3 grid(a.n_frames, a.heads);
-  hipLaunchKernelGGL(append_fp8_kernel, grid, dim3(kFp8Threads), 0, s, a);
+  dim3 grid(a.heads, a.n_frames);   // heads fastest, as for bf16
+  if (use_lut(a))
+    hipLaunchKernelGGL(append_fp8_kernel<true>, grid, dim3(kFp8Threads), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_fp8_kernel<false>, grid, dim3(kFp8Threads), 0, s, a);
   return hipGetLastError();
 }
 
