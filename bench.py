@@ -207,6 +207,33 @@ def measure_gather(sa, geom, n_frames=99, capacity=128, reps=5):
             "frac_of_hbm_peak": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+def measure_dequant(sa, geom, n_frames=99, capacity=128, reps=5):
+    """kv_dequant of n_frames picked out of a capacity-frame e4m3 layer into
+    bf16 planes: per element 1 byte read and 2 bytes written, K and V."""
+    src = sa.KVLayer.allocate(geom, sa.KV_FP8, capacity, 16)
+    dst = sa.KVLayer.allocate(geom, sa.KV_BF16, n_frames, 16)
+    torch.manual_seed(4321)
+    for t in (src.k, src.v):     # random finite e4m3 codes (no NaN pattern)
+        t.random_(0, 256)
+        t.bitwise_and_(0xF7)
+    g = torch.Generator().manual_seed(4321)
+    frames = torch.randperm(capacity, generator=g)[:n_frames].sort().values.to(torch.int32)
+    d_frames = frames.cuda()
+    sa.kv_dequant(geom, src, d_frames, n_frames, 0, dst)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        sa.kv_dequant(geom, src, d_frames, n_frames, 0, dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    elems = 2 * n_frames * geom.heads * geom.P * 128
+    moved = 3 * elems
+    return {"frames": n_frames, "ms": round(ms, 4), "bytes_read_plus_written": moved,
+            "GB_per_s": round(moved / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(state, rows_wanted, seed):
     """Time the fp64 oracle on a bounded sample of the first session of the workload."""
     import numpy as np
@@ -348,6 +375,7 @@ def main():
                       "frac_of_hbm_peak": round(app_bytes / (app_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
     }
     line["history_gather"] = measure_gather(sa, state.geom)
+    line["kv_dequant"] = measure_dequant(sa, state.geom)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(state, args.cpu_rows, args.seed)
     print(json.dumps(line), flush=True)
