@@ -356,9 +356,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     }
     __syncthreads();
 
-  #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-      l_run = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+    l_run = 0.f;
 
     // Blocks 2t and 2t+1 are the halves of tile t (stage t % 4). Step 2t still
     // reads V of tile t-1, so tile t+2 goes to stage (t+2) % 4, last read before
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     f32x16 sb;                                // S of block 2t+1
     if (nv0 < 32) mask_block(sa, nv0, g);
     const float m0 = block_max(sa);
-  #pragma unroll
+#pragma unroll
     for (int r = 0; r < 16; ++r) {
       negm[r] = -m0;
       sa[r] -= m0;
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     pre.k[0] = lds_op(Ks + koff1);
     pre.k[1] = lds_op(Ks + koff1 + 16);
 
-  #pragma unroll 1
+#pragma unroll 1
     for (int t = 0; t < ntiles; ++t) {
       const int st = t & (kStages - 1);
       const uint16_t* Kst = Ks + st * KT;
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     {
       const uint16_t* Vlast = Vs + ((ntiles - 1) & (kStages - 1)) * VT;
       const uint16_t* vp = Vlast + voff + 32;
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int c = i >> 2, db = i & 3;
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(

@@ -36,16 +36,15 @@ __device__ __forceinline__ WorkTile map_workgroup(const AttnArgs& a, int block_m
     w.part = -1;
     w.unit = 0;
   } else {
-    // split parts: the same remap over the parts, so that an XCD runs whole
-    // tiles' parts of few heads (their K/V stay in its L2)
+    // split parts, dispatched part-major: the workgroups an XCD runs at the
+    // same time hold the same key range of many tiles, which then share one
+    // pass of it through the XCD's L2
     const int bp = b - a.n_full;
-    const int nu = a.grid - a.n_full;
-    const int xcd = bp & 7, idx = bp >> 3;
-    const int per = nu >> 3, rem = nu & 7;
-    const int u = xcd * per + min(xcd, rem) + idx;
-    logical = a.n_full + u / a.split_k;
-    w.part = u - (u / a.split_k) * a.split_k;
-    w.unit = u;
+    const int r = (a.grid - a.n_full) / a.split_k;   // split tiles
+    w.part = bp / r;
+    const int tile = bp - w.part * r;
+    logical = a.n_full + tile;
+    w.unit = tile * a.split_k + w.part;                // partial slot: parts of a tile together
   }
   int it = 0;
 #pragma unroll 1
