@@ -213,6 +213,41 @@ def test_split_tiles_across_two_sessions():
         np.testing.assert_allclose(got_lse, want_lse, atol=LSE_ATOL, rtol=0)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_eight_sessions_in_one_call(kv):
+    """SA_MAX_ITEMS sessions of different history lengths (0 to 7 prior
+    segments, one with a reversed, gappy frame list) in one call, every other
+    one without lse; the work tiles of all items, whole and split, come out
+    against each session's own oracle."""
+    print(f"eight sessions kv={kv}", flush=True)
+    prior = (0, 3, 1, 7, 2, 5, 4, 6)
+    wl = si.Workload("eight", heads=2, lat_t=2, lat_h=8, lat_w=16, n_text=24,
+                     prior_segments=prior, capacity_segments=8,
+                     kv_dtype=kv, scale_factors=(kv == "fp8"))
+    ss = []
+    for i in range(8):
+        hist = None
+        if i == 3:
+            hist = [13, 11, 8, 6, 5, 2, 0]
+        ss.append(Session(wl, seed=41, layer=0, session=i, history=hist))
+    items = [s.item(with_lse=(i % 2 == 0)) for i, s in enumerate(ss)]
+    assert len(items) == sa.MAX_ITEMS
+    sa.segment_attention(ss[0].geom, items)
+    torch.cuda.synchronize()
+    for i, s in enumerate(ss):
+        got, got_lse = s.gpu_out()
+        if kv == "bf16":
+            want, want_lse = s.oracle()
+            _, _, rel = compare(got, want, MAX_ABS, MEAN_ABS, f"session {i}")
+            assert rel <= REL_L2
+        else:
+            want, want_lse, bound = s.oracle_fp8_cache()
+            assert np.all(np.abs(got - want) <= bound + 5e-3), f"session {i}"
+        if i % 2 == 0:
+            np.testing.assert_allclose(got_lse, want_lse, atol=LSE_ATOL if kv == "bf16" else 2e-2,
+                                       rtol=0)
+
+
 def test_single_key_copies_value_bitwise():
     H = 2
     geom = sa.Geom(heads=H, lat_h=4, lat_w=6)
@@ -260,7 +295,7 @@ def test_zero_query_counts_every_key_once():
         want[f % 127] += P / Lk
     want[127] += n_text / Lk
     got = out.float().cpu().numpy()
-    bf = np.array(torch.tensor(want).to(torch.bfloat16).float())
+    bf = torch.tensor(want).to(torch.bfloat16).float().numpy()
     assert np.all(np.abs(got - bf[None, None, :]) <= np.abs(bf)[None, None, :] * 2 ** -7 + 1e-7)
 
 
