@@ -296,7 +296,7 @@ def cpu_baseline(state, rows_wanted, seed):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding "
+        print(json.dumps({"error": "this bench runs on one GPU only; multi-GPU sharding "
                                    "(heads across GPUs) is a design note, not built"}))
         sys.exit(2)
     import diffusion_transformer_attention_segment_amd as sa
