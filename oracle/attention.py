@@ -23,13 +23,14 @@ import numpy as np
 from .rope import rope3d
 
 
-def attention(q, k, v, scale):
+def attention(q, k, v, scale, visible=None):
     """Plain softmax attention for one head: softmax(scale * q k^T) v.
 
     q [M, D], k [N, D], v [N, D], all float64. Returns (out [M, D], lse [M]),
     lse = natural log of sum_j exp(scale * q.k_j). Exact row max first, then
     the sums (two passes). N == 0 is rejected: softmax over nothing is
-    undefined.
+    undefined. `visible` [M, N] (bool, optional) drops the keys a row may not
+    see: their logits become -inf; a row that sees no key is rejected.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -37,6 +38,11 @@ def attention(q, k, v, scale):
     if k.shape[0] == 0:
         raise ValueError("attention over an empty key set is undefined")
     s = (q @ k.T) * scale
+    if visible is not None:
+        visible = np.asarray(visible, dtype=bool)
+        if not np.all(visible.any(axis=1)):
+            raise ValueError("a query row sees no key")
+        s = np.where(visible, s, -np.inf)
     m = s.max(axis=1, keepdims=True)
     p = np.exp(s - m)
     lsum = p.sum(axis=1, keepdims=True)
@@ -45,8 +51,35 @@ def attention(q, k, v, scale):
     return out, lse
 
 
+def timed_text_visibility(q_frame, key_text, window):
+    """Which keys each query row may see under timed text windows.
+
+    The pages (same article, "How one segment is made") give a second mask
+    beside the segment-wise causal one: a timed action is visible only to the
+    video frames inside its window. Reading (the window encoding is not on the
+    pages): text token j carries an inclusive latent-frame range
+    window[j] = (first, last); a video query in frame t sees it iff
+    first <= t <= last; text queries and every non-text key are unaffected.
+
+    q_frame  [M] latent frame of each query row, negative for text rows
+    key_text [N] text-token index of each key, negative for video keys
+    window   [n_text, 2] int
+    Returns bool [M, N].
+    """
+    q_frame = np.asarray(q_frame, dtype=np.int64)
+    key_text = np.asarray(key_text, dtype=np.int64)
+    window = np.asarray(window, dtype=np.int64).reshape(-1, 2)
+    is_text = key_text >= 0
+    lo = np.where(is_text, window[np.maximum(key_text, 0), 0], 0)
+    hi = np.where(is_text, window[np.maximum(key_text, 0), 1], 0)
+    video_row = q_frame[:, None] >= 0
+    inside = (lo[None, :] <= q_frame[:, None]) & (q_frame[:, None] <= hi[None, :])
+    return ~is_text[None, :] | ~video_row | inside
+
+
 def segment_attention(q, q_pos, k, k_pos, v, split=(16, 56, 56), theta=10000.0,
-                      scale=None, rows=None, chunk=1024):
+                      scale=None, rows=None, chunk=1024, q_frame=None, key_text=None,
+                      text_window=None):
     """Joint attention of one session over its key set, every head.
 
     q     [Lq, H, D]  raw (unrotated) queries, float64 (exact bf16 values)
@@ -55,6 +88,8 @@ def segment_attention(q, q_pos, k, k_pos, v, split=(16, 56, 56), theta=10000.0,
                       frames, the own segment, the own text), float64
     k_pos [Lk, 3]     positions of the keys
     rows  optional index array of query rows to evaluate (sampling)
+    q_frame, key_text, text_window: optional timed text windows
+          (timed_text_visibility); all three or none
     Returns (out [len(rows), H, D], lse [len(rows), H]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -74,7 +109,11 @@ def segment_attention(q, q_pos, k, k_pos, v, split=(16, 56, 56), theta=10000.0,
         kh = np.ascontiguousarray(kr[:, h, :])
         vh = np.ascontiguousarray(v[:, h, :])
         for c0 in range(0, len(rows), chunk):
-            o, l = attention(qr[c0:c0 + chunk, h, :], kh, vh, scale)
+            vis = None
+            if text_window is not None:
+                vis = timed_text_visibility(np.asarray(q_frame)[rows[c0:c0 + chunk]], key_text,
+                                            text_window)
+            o, l = attention(qr[c0:c0 + chunk, h, :], kh, vh, scale, vis)
             out[c0:c0 + chunk, h, :] = o
             lse[c0:c0 + chunk, h] = l
     return out, lse

@@ -5,7 +5,9 @@ value, Q = 0 gives the mean of V, one dominant key gives its value), key
 permutation invariance, the split/merge identity of log-sum-exp partials,
 scalar brute-force triple loops written independently here, torch's
 scaled_dot_product_attention in float64 on the CPU (an independent library
-routine for the same definition) and scipy's logsumexp for the LSE.
+routine for the same definition) and scipy's logsumexp for the LSE. Timed
+text windows: masked attention equals deleting the invisible keys, the
+visibility cases of the reading, torch's SDPA with a boolean mask.
 """
 
 import math
@@ -132,6 +134,87 @@ def test_segment_attention_rotates_then_attends():
 def test_empty_key_set_rejected():
     try:
         attention.attention(np.zeros((1, 4)), np.zeros((0, 4)), np.zeros((0, 4)), 1.0)
+    except ValueError:
+        return
+    raise AssertionError("expected ValueError")
+
+
+# ---- timed text windows ------------------------------------------------------------
+def _window_case(seed):
+    """A small session: 3 video frames of 4 query rows, 3 text query rows; keys
+    are 10 video keys and 6 text keys with assorted windows (all frames, one
+    frame, an empty range, a range past the segment)."""
+    rng = np.random.default_rng(seed)
+    q_frame = np.array([5] * 4 + [6] * 4 + [7] * 4 + [-1] * 3)
+    key_text = np.array([-1] * 10 + list(range(6)))
+    window = np.array([[0, 1 << 30], [6, 6], [7, 5], [5, 6], [8, 9], [7, 7]])
+    q = rng.standard_normal((len(q_frame), 32))
+    k = rng.standard_normal((len(key_text), 32))
+    v = rng.standard_normal((len(key_text), 32))
+    return q_frame, key_text, window, q, k, v
+
+
+def test_text_window_is_deletion_of_invisible_keys():
+    """Masked attention of each row equals plain attention over the keys that
+    row keeps, computed by deleting the others from the key set."""
+    q_frame, key_text, window, q, k, v = _window_case(41)
+    vis = attention.timed_text_visibility(q_frame, key_text, window)
+    out, lse = attention.attention(q, k, v, 0.2, vis)
+    for r in range(len(q_frame)):
+        keep = np.flatnonzero(vis[r])
+        o1, l1 = attention.attention(q[r:r + 1], k[keep], v[keep], 0.2)
+        np.testing.assert_allclose(out[r], o1[0], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse[r], l1[0], rtol=1e-13)
+
+
+def test_text_window_visibility_cases():
+    """Text rows and video keys are never masked; an all-frames window masks
+    nothing; the one-frame window [6, 6] reaches frame 6 only; the empty range
+    [7, 5] reaches no video row; a window past the segment reaches none."""
+    q_frame, key_text, window, _, _, _ = _window_case(42)
+    vis = attention.timed_text_visibility(q_frame, key_text, window)
+    assert vis[:, :10].all()                         # video keys
+    assert vis[12:, :].all()                         # text rows
+    assert vis[:12, 10].all()                        # window (0, 2^30)
+    assert np.array_equal(vis[:12, 11], q_frame[:12] == 6)
+    assert not vis[:12, 12].any()                    # (7, 5): empty
+    assert np.array_equal(vis[:12, 13], q_frame[:12] <= 6)
+    assert not vis[:12, 14].any()                    # (8, 9): past the segment
+    assert np.array_equal(vis[:12, 15], q_frame[:12] == 7)
+
+
+def test_text_window_matches_torch_masked_sdpa():
+    """Against torch's scaled_dot_product_attention with a boolean mask, fp64."""
+    q_frame, key_text, window, q, k, v = _window_case(43)
+    vis = attention.timed_text_visibility(q_frame, key_text, window)
+    out, _ = attention.attention(q, k, v, 1.0 / math.sqrt(32), vis)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=torch.from_numpy(vis)[None])[0].numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_segment_attention_with_windows_all_frames_is_unmasked():
+    """Windows that cover every frame leave segment_attention unchanged."""
+    H, D = 2, 128
+    Lq, Lk, nt = 12, 30, 5
+    q, k, v = _rand((Lq, H, D), 44), _rand((Lk, H, D), 45), _rand((Lk, H, D), 46)
+    qp = np.random.default_rng(47).integers(0, 30, (Lq, 3))
+    kp = np.random.default_rng(48).integers(0, 30, (Lk, 3))
+    q_frame = np.array([3] * 8 + [-1] * 4)
+    key_text = np.array([-1] * (Lk - nt) + list(range(nt)))
+    win = np.array([[0, 100]] * nt)
+    o, l = attention.segment_attention(q, qp, k, kp, v, q_frame=q_frame, key_text=key_text,
+                                       text_window=win)
+    o0, l0 = attention.segment_attention(q, qp, k, kp, v)
+    np.testing.assert_allclose(o, o0, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(l, l0, rtol=1e-13)
+
+
+def test_row_that_sees_no_key_rejected():
+    try:
+        attention.attention(np.zeros((1, 4)), np.zeros((2, 4)), np.zeros((2, 4)), 1.0,
+                            np.zeros((1, 2), dtype=bool))
     except ValueError:
         return
     raise AssertionError("expected ValueError")
