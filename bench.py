@@ -104,6 +104,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--text-windows", action="store_true",
+                    help="give every session timed text windows (seeded recipe)")
     return ap.parse_args()
 
 
@@ -117,7 +119,7 @@ def workload(name, seed):
 class LayerState:
     """Device state of one layer for every session of the workload."""
 
-    def __init__(self, sa, wl, seed, layer, sessions=None):
+    def __init__(self, sa, wl, seed, layer, sessions=None, windows=False):
         self.wl = wl
         self.geom = sa.Geom(heads=wl.heads, lat_h=wl.lat_h, lat_w=wl.lat_w, rope_split=wl.split,
                             rope_theta=wl.theta)
@@ -139,9 +141,10 @@ class LayerState:
             d_frames = torch.empty(n_hist + F, dtype=torch.int32, device="cuda")
             pinned = torch.empty(n_hist + F, dtype=torch.int32, pin_memory=True)
             out = torch.empty_like(q)
+            win = si.text_windows(wl, seed, S * F).cuda() if windows else None
             self.sess.append(dict(S=S, kv=kv, k=k, v=v, kt=kt, vt=vt, q=q, out=out,
                                   d_frames=d_frames, pinned=pinned, n_frames=n_hist + F,
-                                  copied=None))
+                                  copied=None, win=win))
 
     def select(self, sa, s):
         wl = self.wl
@@ -176,7 +179,8 @@ class LayerState:
             sa.kv_append(self.geom, d["kv"], d["k"], d["v"], d["S"] * F, F)
             sa.text_append(self.geom, d["kv"], d["kt"], d["vt"], wl.n_text)
             items.append(sa.AttnItem(d["q"], d["kv"], d["d_frames"], d["n_frames"], wl.n_text,
-                                     d["out"], frame0_q=d["S"] * F, n_frames_q=F, n_text_q=wl.n_text))
+                                     d["out"], frame0_q=d["S"] * F, n_frames_q=F, n_text_q=wl.n_text,
+                                     text_window=d["win"]))
         if ev is not None:
             ev[0].record()
         sa.segment_attention(self.geom, items)
@@ -278,8 +282,14 @@ def cpu_baseline(state, rows_wanted, seed):
     t1 = time.perf_counter()
     qr = orope.rope3d(q[rows], qpos[rows], wl.split, wl.theta)
     scale = 1.0 / math.sqrt(wl.head_dim)
+    vis = None
+    if d["win"] is not None:
+        q_frame = np.concatenate([d["S"] * F + np.arange(F * P) // P, -np.ones(wl.n_text, np.int64)])
+        key_text = np.concatenate([-np.ones(len(frames) * P, np.int64), np.arange(wl.n_text)])
+        vis = oatt.timed_text_visibility(q_frame[rows], key_text, d["win"].cpu().numpy())
     for h in range(wl.heads):
-        oatt.attention(qr[:, h], np.ascontiguousarray(kr[:, h]), np.ascontiguousarray(v[:, h]), scale)
+        oatt.attention(qr[:, h], np.ascontiguousarray(kr[:, h]), np.ascontiguousarray(v[:, h]), scale,
+                       vis)
     t2 = time.perf_counter()
     t_full = (t1 - t0) + (t2 - t1) * wl.Lq / len(rows)
     lk = k.shape[0]
@@ -303,7 +313,7 @@ def main():
     sa.lib()
     wl = workload(args.workload, args.seed)
     torch.cuda.init()
-    state = LayerState(sa, wl, args.seed, 0)
+    state = LayerState(sa, wl, args.seed, 0, windows=args.text_windows)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -359,7 +369,7 @@ def main():
                             f"latent + {wl.n_text} text tokens (Lq {wl.Lq}) over "
                             f"{list(wl.prior_segments)} prior segment(s), keys per session {lk}"),
             "sessions": wl.sessions, "Lq": wl.Lq, "Lk": lk, "kv_dtype": wl.kv_dtype,
-            "rope_theta": wl.theta,
+            "rope_theta": wl.theta, "text_windows": bool(args.text_windows),
         },
         "pct_of_peak": round(100.0 * value / peak, 2),
         "ms_per_54_block_segment": round(54 * ms_step, 2),
@@ -367,7 +377,7 @@ def main():
         "attention_kernel_ms": round(attn_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(dtype, wl.name),
+                     "traffic": None if args.text_windows else measured_traffic(dtype, wl.name),
                      "kernel": "segment_attention: attn_" + dtype + "_kernel + combine_kernel",
                      "flop_per_launch": flops},
         "kv_append": {"ms": round(app_ms, 4), "bytes": app_bytes,

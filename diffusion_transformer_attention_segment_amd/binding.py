@@ -52,7 +52,7 @@ class sa_attn_item(ctypes.Structure):
                 ("reserved0", ctypes.c_int32), ("kv", ctypes.POINTER(sa_kv_layer)),
                 ("frames", ctypes.c_void_p), ("n_frames_kv", ctypes.c_int32),
                 ("n_text_kv", ctypes.c_int32), ("out", ctypes.c_void_p),
-                ("lse", ctypes.c_void_p)]
+                ("lse", ctypes.c_void_p), ("text_window", ctypes.c_void_p)]
 
 
 # exported symbol -> (restype, argtypes); also the list of ABI entry points
@@ -112,6 +112,15 @@ def _stream(stream):
 
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _check_i32(t, n, name):
+    """A device index tensor must be contiguous int32 with at least n entries."""
+    if t is None:
+        return
+    if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{name}: need a contiguous int32 tensor of at least {n} entries, "
+                         f"got {t.dtype} {tuple(t.shape)}")
 
 
 class Geom:
@@ -226,15 +235,20 @@ def history_gather(geom, src, d_frames, n, dst, stream=None):
 
 
 class AttnItem:
-    """One session's attention call (sa_attn_item)."""
+    """One session's attention call (sa_attn_item). text_window: optional
+    int32 device tensor [n_text_kv, 2] of (first, last) absolute query frames
+    that see each text key."""
 
     def __init__(self, q, layer, frames, n_frames_kv, n_text_kv, out, frame0_q, n_frames_q,
-                 n_text_q, lse=None):
+                 n_text_q, lse=None, text_window=None):
         self.q, self.layer, self.frames, self.out, self.lse = q, layer, frames, out, lse
+        self.text_window = text_window
         self.n_frames_kv, self.n_text_kv = n_frames_kv, n_text_kv
         self.frame0_q, self.n_frames_q, self.n_text_q = frame0_q, n_frames_q, n_text_q
 
     def c(self):
+        _check_i32(self.frames, self.n_frames_kv, "frames")
+        _check_i32(self.text_window, 2 * self.n_text_kv, "text_window")
         it = sa_attn_item()
         it.q = _ptr(self.q).value
         it.frame0_q, it.n_frames_q, it.n_text_q = self.frame0_q, self.n_frames_q, self.n_text_q
@@ -243,6 +257,7 @@ class AttnItem:
         it.n_frames_kv, it.n_text_kv = self.n_frames_kv, self.n_text_kv
         it.out = _ptr(self.out).value
         it.lse = _ptr(self.lse).value
+        it.text_window = _ptr(self.text_window).value
         return it
 
 

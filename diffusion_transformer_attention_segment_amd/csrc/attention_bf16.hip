@@ -132,6 +132,15 @@ __device__ __forceinline__ void mask_block(f32x16& s, int nvalid, int g) {
     if (16 * (r >> 3) + (r & 7) >= lim) s[r] = -INFINITY;
 }
 
+// Timed text windows on a 32-key block: `word` is the block's visibility
+// word for this lane's query row (bit b: key b of the block), and register r
+// of lane group g holds key 16 (r / 8) + 8 g + r % 8 (as in mask_block).
+__device__ __forceinline__ void window_mask_block(f32x16& s, uint32_t word, int g) {
+  const uint32_t wg = word >> (8 * g);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = keep_if_bit(s[r], wg, 16 * (r >> 3) + (r & 7));
+}
+
 // Block max of S^T over its 32 keys (both lane halves).
 __device__ __forceinline__ float block_max(const f32x16& s) {
   float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
@@ -250,6 +259,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   __shared__ __attribute__((aligned(16))) uint16_t Vs[kStages * VT];
   __shared__ double om[kD / 2];
   __shared__ int ax[kD / 2];
+  // timed-window bits (+ 1 word: block 1 of the last text tile may read one
+  // word past the table; its keys are all masked by the valid count)
+  __shared__ uint32_t wtab[kWindowWords + 1];
 
   const WorkTile wt = map_workgroup(a, BM);
   const AttnItemDev& I = a.items[wt.item];
@@ -266,17 +278,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   int kt0, kt1;   // this work tile's key tiles
   key_range(a, I, P, wt.part, &kt0, &kt1);
   const int ntiles = kt1 - kt0;
+  const int flag_fi = window_flag_segment(I);
 
   if (tid < kD / 2) {
     int axis;
     om[tid] = rope_omega(tid, a.rope, &axis);
     ax[tid] = axis;
   }
+  stage_window_table(I, wtab, q0, BM, P, tid, kThreads);
   __syncthreads();
 
   // ---- Q fragments (B operand of S^T = K Q^T): rotated in fp32, times the
   // softmax scale * log2(e), rounded to bf16 ----------------------------------
   const int qrow = q0 + 32 * w + r32;
+  const uint32_t* wrow = wtab + window_row_offset(I, q0, qrow, P);   // this row's window bits
   bf16x8 qf[8];
   {
     const float c2 = a.scale_log2;
@@ -333,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     TileCursor lc;
     cursor_start<2>(lc, I, h, H, P, kt0);
     u32x4 kr[kKChunks], vr[kVChunks];
-    int nv0 = cursor_nvalid(lc);
+    int nv0 = cursor_mask_code(lc, flag_fi);
     load_tile(lc, koff_ld, kr, vr);
     // the last V stage is read once with zero probabilities before it is
     // first written: give it finite contents
@@ -345,13 +360,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     int nv1 = 0, nv2 = 0;
     if (ntiles > 1) {
       cursor_next<2>(lc, I, h, H, P);
-      nv1 = cursor_nvalid(lc);
+      nv1 = cursor_mask_code(lc, flag_fi);
       load_tile(lc, koff_ld, kr, vr);
       store_tile(Ks + KT, Vs + VT, tid, kr, vr);
     }
     if (ntiles > 2) {
       cursor_next<2>(lc, I, h, H, P);
-      nv2 = cursor_nvalid(lc);
+      nv2 = cursor_mask_code(lc, flag_fi);
       load_tile(lc, koff_ld, kr, vr);
     }
     __syncthreads();
@@ -368,7 +383,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     // The running max starts at block 0's max (block 0 always has a valid key).
     f32x16 sa = qk_block(Ks + koff0, qf);     // S of block 2t at the top of the loop
     f32x16 sb;                                // S of block 2t+1
-    if (nv0 < 32) mask_block(sa, nv0, g);
+    if (nv0 < 32) mask_block(sa, tile_count(nv0), g);
+    // (tile 0 is never a text tile under timed windows: the key ranges of such
+    // items start on a video tile, so every row sees block 0's valid keys)
     const float m0 = block_max(sa);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -393,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
       const uint16_t* Vst = Vs + st * VT;
       const uint16_t* Vprev = Vs + ((t + kStages - 1) & (kStages - 1)) * VT;
       const uint16_t* Knext = Ks + ((t + 1) & (kStages - 1)) * KT;
-      const int nvalid = nv0;
+      const int nvalid = nv0;   // count, sign bit set on a text tile under windows
       int nv3 = 0;
       // Tile t+2: registers -> LDS stage (t+2) % 4, the stage of tile t-2, whose
       // last reads (step 2t-2) completed before this barrier; then start loading
@@ -408,14 +425,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
           store_tile(Ks + s2 * KT, Vs + s2 * VT, tid, kr, vr);
           if (t + 3 < ntiles) {
             cursor_next<2>(lc, I, h, H, P);
-            nv3 = cursor_nvalid(lc);
+            nv3 = cursor_mask_code(lc, flag_fi);
             load_tile(lc, koff_ld, kr, vr);
           }
         }
       };
 
       // step 2t: PV(2t-1) [pa] + QK(2t+1) [-> sb] | softmax(2t) [sa -> pb]
-      if (nvalid < 32) mask_block(sa, nvalid, g);
+      if (nvalid < 32) {   // partial tile, or text tile with windows
+        if (tile_count(nvalid) < 32) mask_block(sa, tile_count(nvalid), g);
+        if (nvalid < 0) window_mask_block(sa, wrow[text_tile_base(I, P, kt0 + t) >> 5], g);
+      }
       float lb = fused_step(Vprev + voff + 32, Kst + koff1, Vst + voff, Knext + koff0, pre, pa, o,
                             qf, negm, sb, sa, ones, pb, boundary);
       if constexpr (kSafe) {
@@ -426,7 +446,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
       l_run += lb;
 
       // step 2t+1: PV(2t) [pb] + QK(2t+2) [-> sa] | softmax(2t+1) [sb -> pa]
-      if (nvalid < BN) mask_block(sb, nvalid - 32, g);
+      if (nvalid < BN) {
+        if (tile_count(nvalid) < BN) mask_block(sb, tile_count(nvalid) - 32, g);
+        if (nvalid < 0) window_mask_block(sb, wrow[(text_tile_base(I, P, kt0 + t) >> 5) + 1], g);
+      }
       lb = fused_step(Vst + voff, Knext + koff0, Vst + voff + 32, Knext + koff1, pre, pb, o, qf,
                       negm, sa, sb, ones, pa, [] {});
       if constexpr (kSafe) {

@@ -142,8 +142,13 @@ __device__ __forceinline__ void key_range(const AttnArgs& a, const AttnItemDev& 
     *begin = 0;
     *end = n;
   } else {
-    *begin = static_cast<int>(static_cast<int64_t>(part) * n / a.split_k);
-    *end = static_cast<int>(static_cast<int64_t>(part + 1) * n / a.split_k);
+    // with timed text windows the parts divide the video tiles (at least one
+    // each) and the last part takes the text tiles as well: every part then
+    // starts with a tile whose valid keys every query row sees
+    const int ns = I.text_window != nullptr ? I.n_frames_kv * tpf : n;
+    *begin = static_cast<int>(static_cast<int64_t>(part) * ns / a.split_k);
+    *end = part + 1 == a.split_k ? n
+                                 : static_cast<int>(static_cast<int64_t>(part + 1) * ns / a.split_k);
   }
 }
 
@@ -186,6 +191,22 @@ __device__ __forceinline__ int cursor_nvalid(const TileCursor& c) {
   return min(kKeyTile, c.len - c.p0);
 }
 
+// Valid-key count of the cursor's tile, with the sign bit set when the tile
+// holds text keys under timed text windows: one signed compare against the
+// tile size then sends partial tiles and windowed text tiles alike to the
+// (rare) masking path. tile_count() takes the count back out. flag_fi is the
+// first segment whose tiles carry the flag (window_flag_segment), kept in a
+// register so that the per-tile code reads nothing from memory.
+constexpr int kWindowFlag = static_cast<int>(0x80000000u);
+__device__ __forceinline__ int window_flag_segment(const AttnItemDev& I) {
+  return __builtin_amdgcn_readfirstlane(I.text_window != nullptr ? I.n_frames_kv : 0x7fffffff);
+}
+__device__ __forceinline__ int cursor_mask_code(const TileCursor& c, int flag_fi) {
+  const int n = cursor_nvalid(c);
+  return c.fi >= flag_fi ? (n | kWindowFlag) : n;
+}
+__device__ __forceinline__ int tile_count(int code) { return code & ~kWindowFlag; }
+
 // Buffer resources of the cursor's tile: the K resource covers the tile's
 // valid rows (rows past them read as zero), the V^T resource runs from the
 // tile's first column to the plane end (so no read leaves the plane).
@@ -213,15 +234,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_v_rsrc(const TileCursor& 
 constexpr uint32_t kOutOfRange = 0x80000000u;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// The lane's index in its wave, recomputed (mbcnt) where it is used: as
+// volatile asm it is not hoisted out of a loop, so neither it nor the
+// per-lane values derived from it occupy a register across the loop.
+__device__ __forceinline__ uint32_t lane_here() {
+  uint32_t lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n v_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  return lane;
+}
+
 template <int ROWS, int SLOTS>
 __device__ __forceinline__ int dma_tile(__amdgpu_buffer_rsrc_t r, void* stage, uint32_t row_bytes,
                                         int w) {
   constexpr int kLoads = ROWS * SLOTS / 64;
   static_assert(ROWS * SLOTS % 64 == 0, "a stage is a whole number of 1 KB loads");
-  // The lane index is recomputed here (mbcnt) at every tile, so that neither
-  // it nor the per-lane offsets derived from it are kept across the loop.
-  uint32_t lane;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n v_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const uint32_t lane = lane_here();   // per tile: no per-lane offsets kept across the loop
   int n_issued = 0;
 #pragma unroll
   for (int m = 0; m < (kLoads + 7) / 8; ++m) {
@@ -256,6 +283,54 @@ __device__ __forceinline__ float max_other_half(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// ---- timed text windows -------------------------------------------------------
+// Optional per item ("How one segment is made": a timed action is visible only
+// to the video frames inside its window): text key j is visible to a video
+// query of absolute frame t only if window[j].x <= t <= window[j].y; text
+// queries see every key. Each workgroup turns the windows into its bit table
+// (layout next to kWindowWords) before its first barrier.
+__device__ __forceinline__ void stage_window_table(const AttnItemDev& I, uint32_t* tab, int q0,
+                                                   int bm, int P, int tid, int nthreads) {
+  if (I.text_window == nullptr) return;
+  const int words = window_row_words(I.n_text_kv);
+  const int last = min(q0 + bm, I.n_q_video) - 1;   // last video row of the workgroup
+  const int fa = q0 / P;
+  const int rows = 1 + (last >= q0 ? last / P - fa + 1 : 0);
+  const int2* win = reinterpret_cast<const int2*>(I.text_window);
+  for (int e = tid; e < rows * words; e += nthreads) {
+    const int row = e / words, w = e - row * words;
+    uint32_t bits = ~0u;
+    if (row > 0) {
+      const int t = I.frame0_q + fa + row - 1;
+      const int nb = min(32, I.n_text_kv - 32 * w);
+      bits = 0u;
+      for (int b = 0; b < nb; ++b) {
+        const int2 wj = win[32 * w + b];
+        bits |= static_cast<uint32_t>(wj.x <= t && t <= wj.y) << b;
+      }
+    }
+    tab[e] = bits;
+  }
+}
+
+// word offset of query row `row`'s table row (0, all visible, for text rows)
+__device__ __forceinline__ int window_row_offset(const AttnItemDev& I, int q0, int row, int P) {
+  if (I.text_window == nullptr || row >= I.n_q_video) return 0;
+  return (row / P - q0 / P + 1) * window_row_words(I.n_text_kv);
+}
+
+// text index of the first key of text tile `tile` (frames first, then text)
+__device__ __forceinline__ int text_tile_base(const AttnItemDev& I, int P, int tile) {
+  return (tile - I.n_frames_kv * ((P + kKeyTile - 1) / kKeyTile)) * kKeyTile;
+}
+
+// s if bit `bit` of `word` is set, else -inf (bit-field insert under a
+// sign-extended one-bit mask)
+__device__ __forceinline__ float keep_if_bit(float s, uint32_t word, int bit) {
+  const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(word << (31 - bit)) >> 31);
+  return __uint_as_float((__float_as_uint(s) & m) | (0xFF800000u & ~m));
 }
 
 // RoPE position of query row `row` (video rows in raster order, then text).

@@ -121,16 +121,25 @@ __device__ __forceinline__ void mask_tile(f32x16* s, int nvalid, int g) {
       if (16 * b + r >= lim) s[b][r] = -INFINITY;
 }
 
+// Timed text windows on a tile: `word` is this lane's visibility word (bit b:
+// key 32 g + b of the tile), register r of block b holds key 32 g + 16 b + r.
+__device__ __forceinline__ void window_mask_tile(f32x16* s, uint32_t word) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[b][r] = keep_if_bit(s[b][r], word, 16 * b + r);
+}
+
 // per-tile scalars carried through the load ring
 struct TileInfo {
-  int nvalid;
+  int nvalid;   // valid-key count, sign bit set on a text tile under windows
   float kscale;
   float vscale;
 };
 
-__device__ __forceinline__ TileInfo tile_info(const TileCursor& c) {
+__device__ __forceinline__ TileInfo tile_info(const TileCursor& c, int flag_fi) {
   TileInfo t;
-  t.nvalid = cursor_nvalid(c);
+  t.nvalid = cursor_mask_code(c, flag_fi);
   t.kscale = c.kscale;
   t.vscale = c.vscale;
   return t;
@@ -174,10 +183,11 @@ __device__ __forceinline__ uint32_t prob_word(const f32x16* s, int w, float coef
 }
 
 // S^T block of a tile from its K rows at kp (this lane's row, byte 32 g):
-// two 64-dim steps, high and low query parts each.
-__device__ __forceinline__ f32x16 qk_block(const uint8_t* kp, const i32x8v* qf, const i32x8v* ql) {
+// two 64-dim steps, high and low query parts each, added to the seed c.
+__device__ __forceinline__ f32x16 qk_block(const uint8_t* kp, const i32x8v* qf, const i32x8v* ql,
+                                           const f32x16& c = f32x16{}) {
   const i32x8v k0 = lds_read32(kp), k1 = lds_read32(kp + 64);
-  f32x16 s = mfma_fp8(k0, qf[0], f32x16{});
+  f32x16 s = mfma_fp8(k0, qf[0], c);
   s = mfma_fp8_blo(k0, ql[0], s);
   s = mfma_fp8(k1, qf[1], s);
   return mfma_fp8_blo(k1, ql[1], s);
@@ -262,11 +272,14 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
 // the running max up so that their largest x becomes kPTarget; O (every tile
 // before this one) and the sum of the tiles before are scaled to match, and
 // the tile's probabilities are recomputed -- block 0 of its S^T again from its
-// K rows (kc0, still in LDS; masked like the first time), block 1 from s1.
+// K rows (kc0, still in LDS), block 1 from s1. Block 0 is masked like the
+// first time, through the accumulator seed: -inf for keys past the count in
+// `code` and for keys whose bit in wword is clear (all ones unless `code`
+// flags a windowed text tile), 0 for the others.
 __device__ __forceinline__ float rescale_step(float mx, float& m_run, float& off, float& l_run,
                                               f32x16* o, const uint8_t* kc0, const f32x16& s1,
                                               const i32x8v* qf, const i32x8v* ql, float coef,
-                                              int nvalid, int g, i32x8v& p_cur) {
+                                              int code, int g, uint32_t wword, i32x8v& p_cur) {
   const float d = fmaxf(mx - kPTarget, 0.f);
   const float alpha = __builtin_amdgcn_exp2f(-d);
 #pragma unroll
@@ -276,11 +289,11 @@ __device__ __forceinline__ float rescale_step(float mx, float& m_run, float& off
   off -= d;
   float l = 0.f, m2 = -INFINITY;
   {
-    f32x16 b0 = qk_block(kc0, qf, ql);
-    const int lim = nvalid - 32 * g;
+    f32x16 b0;
+    const int lim = tile_count(code) - 32 * g;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (r >= lim) b0[r] = -INFINITY;
+    for (int r = 0; r < 16; ++r) b0[r] = r >= lim ? -INFINITY : keep_if_bit(0.f, wword, r);
+    b0 = qk_block(kc0, qf, ql, b0);
 #pragma unroll
     for (int w = 0; w < 4; ++w) p_cur[w] = static_cast<int>(prob_word_blk(b0, w, coef, off, l, m2));
   }
@@ -295,6 +308,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   __shared__ double om[kD / 2];
   __shared__ int ax[kD / 2];
   __shared__ float red[kWaves];
+  // timed-window bits (+ 1 word: lanes of group 1 on the last text tile may
+  // read one word past the table; their keys are all masked by the valid count)
+  __shared__ uint32_t wtab[kWindowWords + 1];
+  __shared__ int woff[kThreads];
 
   const WorkTile wt = map_workgroup(a, BM);
   const AttnItemDev& I = a.items[wt.item];
@@ -309,10 +326,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   int kt0, kt1;   // this work tile's key tiles
   key_range(a, I, P, wt.part, &kt0, &kt1);
   const int ntiles = kt1 - kt0;
+  const int flag_fi = window_flag_segment(I);
 
   TileCursor lc;
   cursor_start<1>(lc, I, h, H, P, kt0);
-  TileInfo ti0 = tile_info(lc);
+  TileInfo ti0 = tile_info(lc, flag_fi);
 
   // largest V scale among the planes this (item, head) attends
   float vmax = 0.f;
@@ -327,6 +345,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
     om[tid] = rope_omega(tid, a.rope, &axis);
     ax[tid] = axis;
   }
+  stage_window_table(I, wtab, q0, BM, P, tid, kThreads);
   // Every stage starts as zeros (the V stage of "tile -1" is read once with
   // zero probabilities; stages of tiles past the end may be read, unused).
   for (int i = tid; i < kStages * KT8 / 16; i += kThreads)
@@ -343,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   TileInfo ti1 = ti0;
   if (ntiles > 1) {
     cursor_next<1>(lc, I, h, H, P);
-    ti1 = tile_info(lc);
+    ti1 = tile_info(lc, flag_fi);
     dma_k8(lc, Ks + KT8, w);
     dma_v8(lc, Vs + VT8, w);
   }
@@ -356,6 +375,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   // The query is split: qf = e4m3(q * 448 / amax), ql = e4m3(16 * residual), so
   // that qf + ql / 16 carries about 7 significant bits instead of 4.
   const int qrow = q0 + 32 * w + r32;
+  // This lane's window word for key tile kt0 + tt (a text tile under
+  // windows): bits of keys 32 g .. 32 g + 31. Each thread's table offset waits
+  // in LDS (woff, read back only by the same thread) and is found from the
+  // lane index on each use, which keeps it out of the loop's registers.
+  woff[tid] = window_row_offset(I, q0, qrow, P) + g;
+  auto window_word = [&](int tt) __attribute__((always_inline)) {
+    const int t = static_cast<int>(lane_here()) + 64 * w;
+    return wtab[woff[t] + (max(text_tile_base(I, P, kt0 + tt), 0) >> 5)];
+  };
   i32x8v qf[2], ql[2];
   float q_scale;
   {
@@ -432,7 +460,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   f32x16 sc[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) sc[b] = qk_block(Ks + krow[b] * KS8 + 32 * g, qf, ql);
-  if (ti0.nvalid < BN) mask_tile(sc, ti0.nvalid, g);
+  if (ti0.nvalid < BN) mask_tile(sc, tile_count(ti0.nvalid), g);
+  // (tile 0 is never a text tile under timed windows: the key ranges of such
+  // items start on a video tile, so every row sees tile 0's valid keys)
   float m_run;
   {
     float mx = -INFINITY;
@@ -471,13 +501,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
       if (tt + 2 < ntiles) {
         const int s2 = (tt + 2) & (kStages - 1);
         cursor_next<1>(lc, I, h, H, P);
-        ti2 = tile_info(lc);
+        ti2 = tile_info(lc, flag_fi);
         dma_k8(lc, Ks + s2 * KT8, w);
         dma_v8(lc, Vs + s2 * VT8, w);
         pending = 1;   // every wave issues at least one V load
       }
     };
-    if (cur.nvalid < BN) mask_tile(sc, cur.nvalid, g);
+    if (cur.nvalid < BN) {   // partial tile, or text tile with windows
+      if (tile_count(cur.nvalid) < BN) mask_tile(sc, tile_count(cur.nvalid), g);
+      if (cur.nvalid < 0) window_mask_tile(sc, window_word(tt));
+    }
     const float coef = c2 * cur.kscale;
     const float pf = pf_base * cur.vscale;
     float off8 = __log2f(pf) - m_run;
@@ -486,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
                           mx, boundary);
     if (__builtin_expect(__any(mx > kTrigger), 0))
       lt = rescale_step(mx, m_run, off8, l_run, o, Kcur + krow[0] * KS8, sc[1], qf, ql, coef,
-                        cur.nvalid, g, p_cur);
+                        cur.nvalid, g, cur.nvalid < 0 ? window_word(tt) : ~0u, p_cur);
     // QK^T block 1 of tile t+1 (block 1 of tile t is no longer needed)
     sc[1] = qk_block(Knext + krow[1] * KS8, qf, ql);
     l_run += lt / pf;

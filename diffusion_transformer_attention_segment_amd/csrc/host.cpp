@@ -312,6 +312,11 @@ struct AttnPlan {
   int32_t key_tiles[SA_MAX_ITEMS];
 };
 
+// Timed text windows take effect only where a video query meets a text key.
+bool windowed(const sa_attn_item& it) {
+  return it.text_window != nullptr && it.n_text_kv > 0 && it.n_frames_q > 0;
+}
+
 sa_status prepare_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
                             AttnPlan& plan) {
   sa_status st = check_geom(geom);
@@ -339,6 +344,17 @@ sa_status prepare_attention(const sa_geom* geom, const sa_attn_item* items, int3
     const int64_t lk = static_cast<int64_t>(it.n_frames_kv) * P + it.n_text_kv;
     if (lk < 1) return fail(SA_E_ARG, "item %d: empty key set", i);
     if (it.n_frames_kv > 0 && it.frames == nullptr) return fail(SA_E_ARG, "item %d: frames is NULL", i);
+    if (windowed(it)) {
+      if ((reinterpret_cast<uintptr_t>(it.text_window) & 7) != 0)
+        return fail(SA_E_ALIGN, "item %d: text_window not 8-byte aligned", i);
+      if (it.n_frames_kv == 0)
+        return fail(SA_E_ARG, "item %d: timed text windows with video queries need video keys", i);
+      const int wbm = dtype == SA_KV_FP8_E4M3 ? attention_block_m_fp8() : attention_block_m_bf16();
+      const int words = window_table_rows(P, wbm) * window_row_words(it.n_text_kv);
+      if (words > kWindowWords)
+        return fail(SA_E_RANGE, "item %d: timed windows of %d text keys over frames of %d tokens "
+                    "need %d table words > %d", i, it.n_text_kv, P, words, kWindowWords);
+    }
     const int64_t rows = static_cast<int64_t>(it.n_frames_q) * P + it.n_text_q;
     if (rows > (int64_t(1) << 30)) return fail(SA_E_SHAPE, "item %d: too many query rows", i);
     if (rows > 0) {
@@ -374,10 +390,12 @@ sa_status prepare_attention(const sa_geom* geom, const sa_attn_item* items, int3
     d.n_frames_kv = it.n_frames_kv;
     d.n_text_kv = it.n_text_kv;
     d.text_cap = it.kv->text_capacity;
+    d.text_window = windowed(it) ? it.text_window : nullptr;
     d.q_tiles = (d.n_q + bm - 1) / bm;
     d.tile_begin = static_cast<int32_t>(tiles);
     tiles += static_cast<int64_t>(d.q_tiles) * geom->heads;
-    plan.key_tiles[i] = it.n_frames_kv * tpf + (it.n_text_kv + 63) / 64;
+    // (split parts of an item with windows divide its video tiles only)
+    plan.key_tiles[i] = it.n_frames_kv * tpf + (windowed(it) ? 0 : (it.n_text_kv + 63) / 64);
   }
   if (tiles > (int64_t(1) << 31) - 1) return fail(SA_E_SHAPE, "too many tiles");
   a.n_items = n_items;

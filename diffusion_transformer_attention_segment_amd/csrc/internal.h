@@ -59,6 +59,7 @@ struct AttnItemDev {
   int32_t n_frames_kv;
   int32_t n_text_kv;
   int32_t text_cap;
+  const int32_t* text_window;   // [n_text_kv][2] (first, last) frames, or NULL: no windows
   int32_t q_tiles;       // ceil(n_q / BLOCK_M)
   int32_t tile_begin;    // first logical tile of this item (over heads * q_tiles)
 };
@@ -83,6 +84,15 @@ struct AttnArgs {
 };
 
 constexpr int kPartialStride = kD + 2;   // floats per row of a partial: O, m, l
+
+// Timed text windows reach the kernels as a per-workgroup visibility table in
+// LDS: one bit per text key (bit b of word w: key 32 w + b), row 0 all ones
+// (text query rows), then one row per latent frame that the workgroup's video
+// query rows span, in frame order. A workgroup of block_m rows spans at most
+// (block_m - 1) / P + 2 frames of P tokens.
+constexpr int kWindowWords = SA_WINDOW_TABLE_WORDS;   // table capacity (words)
+__host__ __device__ inline int window_row_words(int n_text) { return (n_text + 31) / 32; }
+__host__ __device__ inline int window_table_rows(int P, int block_m) { return (block_m - 1) / P + 3; }
 
 hipError_t launch_attention_bf16(AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_fp8(AttnArgs& a, hipStream_t s);

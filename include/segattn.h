@@ -5,8 +5,9 @@
  * attention of each dual-stream block takes as queries the current segment's
  * latent video tokens followed by its text tokens, and as keys/values the
  * per-layer KV cache of earlier segments plus the segment itself, with no mask
- * inside the segment, 3D rotary position embedding over (t, h, w) and 16 heads
- * of 128 dimensions.
+ * inside the segment (optionally, timed text windows hide text keys from
+ * video queries outside their frames: sa_attn_item.text_window), 3D rotary
+ * position embedding over (t, h, w) and 16 heads of 128 dimensions.
  *   Source: "Hy-Nomas: an 8.6B world model whose memory is a KV cache"
  *   (ai.thesatyajit.com), sections "How one segment is made" (token grid,
  *   heads, RoPE split [16, 56, 56] with theta 256, segment-wise causal joint
@@ -45,10 +46,11 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 2
+#define SA_ABI_VERSION 3
 #define SA_HEAD_DIM 128       /* the only head dim the kernels are built for */
 #define SA_MAX_ITEMS 8        /* sessions per sa_segment_attention call     */
 #define SA_MAX_FRAMES_KV 65536
+#define SA_WINDOW_TABLE_WORDS 2048   /* bound on timed text windows, see below  */
 
 typedef enum {
   SA_OK = 0,
@@ -128,6 +130,18 @@ typedef struct sa_kv_layer {
  *   out        bf16, same shape as q
  *   lse        optional fp32 [rows][H] natural-log sum of exp of the scaled
  *              logits per row and head (NULL to skip)
+ *   text_window optional device int32 [n_text_kv][2]: timed text windows.
+ *              Text key j is visible to a video query of absolute frame t
+ *              only if text_window[2j] <= t <= text_window[2j + 1]; text
+ *              queries see every text key. NULL: every query sees every key.
+ *              ("How one segment is made": a timed action is visible only to
+ *              the video frames inside its window.) 8-byte aligned; read
+ *              on the stream by this call's kernels. With video queries and text keys the
+ *              item needs n_frames_kv >= 1 (SA_E_ARG otherwise: a video
+ *              query sees at least its own segment's frames), and
+ *              (255 / P + 3) * ceil(n_text_kv / 32) <= SA_WINDOW_TABLE_WORDS
+ *              (SA_E_RANGE otherwise; frames of 128 tokens allow 16384 text
+ *              keys, frames of 16 tokens 3616).
  * At least one key is required (n_frames_kv * P + n_text_kv >= 1).         */
 typedef struct sa_attn_item {
   const void* q;
@@ -141,6 +155,7 @@ typedef struct sa_attn_item {
   int32_t n_text_kv;
   void* out;
   float* lse;
+  const int32_t* text_window;
 } sa_attn_item;
 
 int sa_abi_version(void);

@@ -148,3 +148,32 @@ def sample_rows(n_rows, n_sample, seed, boundaries=()):
     base = torch.randint(0, n_rows, (n_sample,), generator=g).tolist()
     extra = [0, n_rows - 1] + [b for b in boundaries if 0 <= b < n_rows]
     return sorted(set(base) | set(extra))
+
+
+def text_windows(wl, seed, frame0, n_actions=4):
+    """Timed text windows for the current segment's text tokens: int32
+    [n_text, 2] of inclusive absolute latent frames (first, last).
+
+    Recipe: the text tokens are cut at seeded points into n_actions contiguous
+    spans (one prompt each). Span 0 is always on (frames 0 .. frame0 + F + 8);
+    span 1 is off for the whole segment (a window entirely before frame0); the
+    others get seeded windows [a, b] with frame0 - 2 <= a <= b <= frame0 + F + 1,
+    so that most frames see some actions and not others."""
+    n = wl.n_text
+    F = wl.lat_t
+    g = torch.Generator().manual_seed(int(derive_seed(seed, wl.name, "windows", frame0)))
+    k = max(1, min(n_actions, n))
+    cuts = sorted(torch.randperm(max(n - 1, 1), generator=g)[:k - 1].add(1).tolist()) if n > 1 else []
+    bounds = [0] + cuts + [n]
+    win = torch.zeros((n, 2), dtype=torch.int32)
+    for i in range(len(bounds) - 1):
+        if i == 0:
+            lo, hi = 0, frame0 + F + 8
+        elif i == 1:
+            lo, hi = max(frame0 - 6, 0), max(frame0 - 3, 0) if frame0 >= 3 else -1
+        else:
+            a, b = torch.randint(frame0 - 2, frame0 + F + 2, (2,), generator=g).tolist()
+            lo, hi = min(a, b), max(a, b)
+        win[bounds[i]:bounds[i + 1], 0] = lo
+        win[bounds[i]:bounds[i + 1], 1] = hi
+    return win

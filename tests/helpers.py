@@ -65,13 +65,37 @@ class Session:
         self.d_frames = torch.tensor(self.frames, dtype=torch.int32, device=device)
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((wl.Lq, wl.heads), dtype=torch.float32, device=device)
+        self.text_window = None      # timed text windows (set_windows)
+        self.d_window = None
+
+    def set_windows(self, win):
+        """Timed text windows: int32 [n_text, 2] (first, last) absolute frames."""
+        self.text_window = np.asarray(win, dtype=np.int64).reshape(-1, 2)
+        self.d_window = torch.as_tensor(np.asarray(win, dtype=np.int32)).to(self.q.device).contiguous()
+
+    def q_frames(self):
+        """Absolute latent frame of each query row, -1 for text rows."""
+        wl = self.wl
+        vid = self.S * wl.lat_t + np.arange(wl.lat_t * wl.P) // wl.P
+        return np.concatenate([vid, -np.ones(wl.n_text, dtype=np.int64)])
+
+    def key_text(self):
+        """Text index of each key of the key set, -1 for video keys."""
+        return np.concatenate([-np.ones(len(self.frames) * self.wl.P, dtype=np.int64),
+                               np.arange(self.wl.n_text)])
+
+    def visibility(self, rows):
+        """bool [len(rows), Lk]: keys each row sees (all, without windows)."""
+        if self.text_window is None:
+            return None
+        return oatt.timed_text_visibility(self.q_frames()[rows], self.key_text(), self.text_window)
 
     def item(self, with_lse=True):
         import diffusion_transformer_attention_segment_amd as sa
         wl = self.wl
         return sa.AttnItem(self.q, self.kv, self.d_frames, len(self.frames), wl.n_text, self.out,
                            frame0_q=self.S * wl.lat_t, n_frames_q=wl.lat_t, n_text_q=wl.n_text,
-                           lse=self.lse if with_lse else None)
+                           lse=self.lse if with_lse else None, text_window=self.d_window)
 
     @property
     def Lk(self):
@@ -115,11 +139,16 @@ class Session:
         hs = slice(None) if heads is None else list(heads)
         q = self.q[:, hs].float().cpu().double().numpy()
         scale = 1.0 / math.sqrt(wl.head_dim)
+        win = {}
+        if self.text_window is not None:
+            win = dict(q_frame=self.q_frames(), key_text=self.key_text(),
+                       text_window=self.text_window)
         if not round_rotated:
             return oatt.segment_attention(q, self.q_positions(), k, kpos, v, wl.split,
-                                          self.geom.rope_theta, scale, rows=rows)
+                                          self.geom.rope_theta, scale, rows=rows, **win)
         if rows is None:
             rows = np.arange(q.shape[0])
+        vis = self.visibility(rows)
         c2 = float(np.float32(scale * math.log2(math.e)))
         qr = onum.bf16_round(orope.rope3d(q[rows], self.q_positions()[rows], wl.split,
                                           self.geom.rope_theta) * c2) / c2
@@ -127,7 +156,7 @@ class Session:
         out = np.zeros(qr.shape)
         lse = np.zeros(qr.shape[:2])
         for h in range(qr.shape[1]):
-            out[:, h], lse[:, h] = oatt.attention(qr[:, h], kr[:, h], v[:, h], scale)
+            out[:, h], lse[:, h] = oatt.attention(qr[:, h], kr[:, h], v[:, h], scale, vis)
         return out, lse
 
     def oracle_fp8_cache(self, rows=None, heads=None, split_q=False):
@@ -178,12 +207,16 @@ class Session:
         out = np.zeros(qq.shape)
         lse = np.zeros(qq.shape[:2])
         bound = np.zeros(qq.shape)
+        vis = self.visibility(rows)
         for j in range(qq.shape[1]):
-            out[:, j], lse[:, j] = oatt.attention(qq[:, j], k[:, j], v[:, j], scale)
+            out[:, j], lse[:, j] = oatt.attention(qq[:, j], k[:, j], v[:, j], scale, vis)
             s_ = (qq[:, j] @ k[:, j].T) * scale
+            if vis is not None:
+                s_ = np.where(vis, s_, -np.inf)
             p_ = np.exp(s_ - s_.max(axis=1, keepdims=True))
             floor = 2.0 ** -10 * vsk[:, j].max() / (256.0 * vsk[:, j])
-            bound[:, j] = ((2.0 ** -4 * p_ + floor[None, :]) @ np.abs(v[:, j])) / p_.sum(1)[:, None]
+            fl = floor[None, :] if vis is None else np.where(vis, floor[None, :], 0.0)
+            bound[:, j] = ((2.0 ** -4 * p_ + fl) @ np.abs(v[:, j])) / p_.sum(1)[:, None]
         return out, lse, bound
 
     def gpu_out(self, rows=None, heads=None):

@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 2
+    assert sa.abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -184,6 +184,29 @@ def test_attention_validation(lib):
     bad = _item(L)
     bad.q = FAKE + 8
     assert _attn([bad]) == 3
+
+
+def test_attention_window_validation(lib):
+    """Timed text windows: 8-byte alignment, video keys required when video
+    rows meet text keys, and the per-workgroup table bound (255 / P + 3) *
+    ceil(n_text / 32) <= 2048 words (P = 24 here: 13 rows, 157 words)."""
+    def win(it, ptr):
+        it.text_window = ptr
+        return it
+    L = _layer()
+    assert _attn([win(_item(L), FAKE + 4)]) == 3
+    assert _attn([win(_item(L, n_frames_kv=0), FAKE)]) == 1
+    big = _layer(tc=5040)
+    assert _attn([win(_item(big, n_text_kv=5025), FAKE)]) == 5
+    assert b"table words" in lib.sa_last_error()
+    # within the bound the item passes validation; the second item fails
+    assert _attn([win(_item(big, n_text_kv=5024), FAKE), _item(L, frames=0)]) == 1
+    assert b"item 1" in lib.sa_last_error()
+    # windows are ignored without video rows or without text keys
+    assert _attn([win(_item(L, n_text_kv=0), FAKE + 4), _item(L, frames=0)]) == 1
+    assert b"item 1" in lib.sa_last_error()
+    no_rows = win(_item(L, rows=False, n_frames_kv=0), FAKE + 4)
+    assert _attn([no_rows]) == 0
 
 
 def test_attention_workspace_query_without_split(lib):
