@@ -79,7 +79,7 @@ def timed_text_visibility(q_frame, key_text, window):
 
 def segment_attention(q, q_pos, k, k_pos, v, split=(16, 56, 56), theta=10000.0,
                       scale=None, rows=None, chunk=1024, q_frame=None, key_text=None,
-                      text_window=None):
+                      text_window=None, block_lists=None, n_hist_frames=0, P=None):
     """Joint attention of one session over its key set, every head.
 
     q     [Lq, H, D]  raw (unrotated) queries, float64 (exact bf16 values)
@@ -90,8 +90,13 @@ def segment_attention(q, q_pos, k, k_pos, v, split=(16, 56, 56), theta=10000.0,
     rows  optional index array of query rows to evaluate (sampling)
     q_frame, key_text, text_window: optional timed text windows
           (timed_text_visibility); all three or none
+    block_lists, n_hist_frames, P: optional block-sparse history
+          (sparse.sparse_visibility): block_lists [H, n_qblocks, keep] of kept
+          candidate blocks over the first n_hist_frames frames (P tokens each)
+          of the key set
     Returns (out [len(rows), H, D], lse [len(rows), H]).
     """
+    from .sparse import sparse_visibility
     q = np.asarray(q, dtype=np.float64)
     D = q.shape[-1]
     if scale is None:
@@ -113,6 +118,10 @@ def segment_attention(q, q_pos, k, k_pos, v, split=(16, 56, 56), theta=10000.0,
             if text_window is not None:
                 vis = timed_text_visibility(np.asarray(q_frame)[rows[c0:c0 + chunk]], key_text,
                                             text_window)
+            if block_lists is not None:
+                sv = sparse_visibility(rows[c0:c0 + chunk], block_lists[h], n_hist_frames, P,
+                                       kh.shape[0])
+                vis = sv if vis is None else (vis & sv)
             o, l = attention(qr[c0:c0 + chunk, h, :], kh, vh, scale, vis)
             out[c0:c0 + chunk, h, :] = o
             lse[c0:c0 + chunk, h] = l
