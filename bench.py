@@ -188,6 +188,53 @@ class LayerState:
             ev[1].record()
 
 
+def measure_sparse(sa, state, percent=25, reps=5):
+    """One block-sparse pass (the steps after the first two: the pages' preset
+    keeps 25 % of the candidate video blocks) at the workload: sparse_select
+    then segment_attention with the lists, each timed with events over reps
+    calls. Candidates are the kept history frames; the own segment and the
+    text stay dense. FLOP counted over the keys actually attended."""
+    wl = state.wl
+    F, P = wl.lat_t, wl.P
+    tpf = -(-P // 64)
+    items, sel_items, lists, flops = [], [], [], 0
+    for d in state.sess:
+        n_hist = d["n_frames"] - F
+        if n_hist <= 0:
+            return None
+        keep = sa.sparse_keep(n_hist * tpf, percent)
+        it = sa.AttnItem(d["q"], d["kv"], d["d_frames"], d["n_frames"], wl.n_text, d["out"],
+                         frame0_q=d["S"] * F, n_frames_q=F, n_text_q=wl.n_text,
+                         text_window=d["win"], n_hist_frames=n_hist, keep_blocks=keep)
+        bl = sa.sparse_select(state.geom, it)
+        it.block_list = bl
+        items.append(it)
+        lists.append(bl)
+        kept_keys = min(keep * 64, n_hist * P) + F * P + wl.n_text   # upper bound on kept keys
+        flops += 4 * wl.Lq * kept_keys * wl.head_dim * wl.heads
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(reps):
+        for it, bl in zip(items, lists):
+            sa.sparse_select(state.geom, it, block_list=bl)
+    ev[1].record()
+    for _ in range(reps):
+        sa.segment_attention(state.geom, items)
+    ev[2].record()
+    torch.cuda.synchronize()
+    sel_ms = ev[0].elapsed_time(ev[1]) / reps
+    att_ms = ev[1].elapsed_time(ev[2]) / reps
+    dense_tiles = sum(d["n_frames"] * tpf + -(-wl.n_text // 64) for d in state.sess)
+    sparse_tiles = sum(sa.sparse_keep((d["n_frames"] - F) * tpf, percent) + F * tpf
+                       + -(-wl.n_text // 64) for d in state.sess)
+    return {"keep_percent": percent, "select_ms": round(sel_ms, 4), "attention_ms": round(att_ms, 4),
+            "pass_ms": round(sel_ms + att_ms, 4),
+            "key_tiles_per_work_tile": [sparse_tiles, dense_tiles],
+            "attention_TFLOP_s_on_kept_keys": round(flops / (att_ms * 1e-3) / 1e12, 1),
+            "note": "kept-key FLOP count uses 64 keys per kept block (an upper bound)"}
+
+
 def measure_gather(sa, geom, n_frames=99, capacity=128, reps=5):
     """history_gather of n_frames picked out of a capacity-frame bf16 layer:
     a plain copy of 2 planes x n_frames x H x P x 128 x 2 bytes, read and written."""
@@ -384,6 +431,10 @@ def main():
                       "GB_per_s": round(app_bytes / (app_ms * 1e-3) / 1e9, 1),
                       "frac_of_hbm_peak": round(app_bytes / (app_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
     }
+    sp = measure_sparse(sa, state)
+    if sp is not None:
+        sp["speedup_vs_dense_attention"] = round(attn_ms / sp["pass_ms"], 3)
+        line["sparse_25pct"] = sp
     line["history_gather"] = measure_gather(sa, state.geom)
     line["kv_dequant"] = measure_dequant(sa, state.geom)
     if not args.no_cpu_baseline:

@@ -52,7 +52,9 @@ class sa_attn_item(ctypes.Structure):
                 ("reserved0", ctypes.c_int32), ("kv", ctypes.POINTER(sa_kv_layer)),
                 ("frames", ctypes.c_void_p), ("n_frames_kv", ctypes.c_int32),
                 ("n_text_kv", ctypes.c_int32), ("out", ctypes.c_void_p),
-                ("lse", ctypes.c_void_p), ("text_window", ctypes.c_void_p)]
+                ("lse", ctypes.c_void_p), ("text_window", ctypes.c_void_p),
+                ("block_list", ctypes.c_void_p), ("n_hist_frames", ctypes.c_int32),
+                ("keep_blocks", ctypes.c_int32)]
 
 
 # exported symbol -> (restype, argtypes); also the list of ABI entry points
@@ -76,6 +78,10 @@ SIGNATURES = {
                                                          ctypes.POINTER(sa_attn_item), _I]),
     "sa_segment_attention": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_attn_item),
                                             _I, _P, ctypes.c_size_t, _P]),
+    "sa_sparse_select_workspace": (ctypes.c_size_t, [ctypes.POINTER(sa_geom),
+                                                     ctypes.POINTER(sa_attn_item)]),
+    "sa_sparse_select": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_attn_item), _P,
+                                        ctypes.c_size_t, _P, _P]),
     "sa_kv_dequant": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_kv_layer), _P, _I,
                                      _I, ctypes.POINTER(sa_kv_layer), _P]),
 }
@@ -237,18 +243,23 @@ def history_gather(geom, src, d_frames, n, dst, stream=None):
 class AttnItem:
     """One session's attention call (sa_attn_item). text_window: optional
     int32 device tensor [n_text_kv, 2] of (first, last) absolute query frames
-    that see each text key."""
+    that see each text key. block_list: optional int32 device tensor
+    [H, ceil(rows / 256), keep_blocks] of kept history blocks over the first
+    n_hist_frames frames (block-sparse history; sparse_select writes it)."""
 
     def __init__(self, q, layer, frames, n_frames_kv, n_text_kv, out, frame0_q, n_frames_q,
-                 n_text_q, lse=None, text_window=None):
+                 n_text_q, lse=None, text_window=None, block_list=None, n_hist_frames=0,
+                 keep_blocks=0):
         self.q, self.layer, self.frames, self.out, self.lse = q, layer, frames, out, lse
         self.text_window = text_window
+        self.block_list, self.n_hist_frames, self.keep_blocks = block_list, n_hist_frames, keep_blocks
         self.n_frames_kv, self.n_text_kv = n_frames_kv, n_text_kv
         self.frame0_q, self.n_frames_q, self.n_text_q = frame0_q, n_frames_q, n_text_q
 
     def c(self):
         _check_i32(self.frames, self.n_frames_kv, "frames")
         _check_i32(self.text_window, 2 * self.n_text_kv, "text_window")
+        _check_i32(self.block_list, self.keep_blocks, "block_list")
         it = sa_attn_item()
         it.q = _ptr(self.q).value
         it.frame0_q, it.n_frames_q, it.n_text_q = self.frame0_q, self.n_frames_q, self.n_text_q
@@ -258,6 +269,8 @@ class AttnItem:
         it.out = _ptr(self.out).value
         it.lse = _ptr(self.lse).value
         it.text_window = _ptr(self.text_window).value
+        it.block_list = _ptr(self.block_list).value
+        it.n_hist_frames, it.keep_blocks = self.n_hist_frames, self.keep_blocks
         return it
 
 
@@ -296,6 +309,39 @@ def segment_attention(geom, items, stream=None, workspace="auto"):
         ws, nbytes = workspace, workspace.numel() * workspace.element_size()
     _check(lib().sa_segment_attention(ctypes.byref(g), arr, len(items), _ptr(ws), nbytes,
                                       _stream(stream)))
+
+
+SPARSE_KEY_BLOCK, SPARSE_QUERY_BLOCK = 64, 256
+
+
+def sparse_keep(n_candidates, percent):
+    """Blocks kept out of n_candidates at `percent` (ceil, at least 1, at most all)."""
+    if n_candidates <= 0:
+        return 0
+    return min(n_candidates, max(1, -(-n_candidates * percent // 100)))
+
+
+def sparse_select(geom, item, block_list=None, stream=None):
+    """Block lists of the item (its n_hist_frames and keep_blocks) for
+    block-sparse history attention: int32 [H, ceil(rows / 256), keep_blocks]
+    (allocated when block_list is None). The pooled-key workspace is
+    allocated through torch."""
+    g = geom.c()
+    it = item.c()
+    nbytes = int(lib().sa_sparse_select_workspace(ctypes.byref(g), ctypes.byref(it)))
+    rows = item.n_frames_q * geom.P + item.n_text_q
+    if block_list is None:
+        nq = -(-rows // SPARSE_QUERY_BLOCK)
+        block_list = torch.empty((geom.heads, max(nq, 1), max(item.keep_blocks, 1)),
+                                 dtype=torch.int32, device=item.q.device)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=item.q.device)
+    _check(lib().sa_sparse_select(ctypes.byref(g), ctypes.byref(it), _ptr(ws), nbytes,
+                                  _ptr(block_list), _stream(stream)))
+    if stream is not None:
+        ext = stream if isinstance(stream, torch.cuda.Stream) else \
+            torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)))
+        ws.record_stream(ext)
+    return block_list
 
 
 def kv_dequant(geom, src, d_frames, n_frames, n_text, dst, stream=None):

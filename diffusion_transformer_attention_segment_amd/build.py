@@ -19,7 +19,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsegattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["host.cpp", "kv_append.hip", "attention_bf16.hip", "attention_fp8.hip", "attention_combine.hip", "gather.hip"]
+SOURCES = ["host.cpp", "kv_append.hip", "attention_bf16.hip", "attention_fp8.hip", "attention_combine.hip",
+           "gather.hip", "sparse_select.hip"]
 
 # Packed-fp32 VALU forms are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -41,6 +41,7 @@ namespace segattn {
 namespace {
 
 constexpr int BM = 256;          // query rows per workgroup
+static_assert(BM == SA_SPARSE_QUERY_BLOCK, "a work tile reads one block list");
 constexpr int BN = kKeyTile;     // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -254,6 +255,7 @@ __device__ __forceinline__ f32x16 qk_block(const uint16_t* kp, const bf16x8* qf)
   return s;
 }
 
+template <bool kSparse>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kStages * KT];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[kStages * VT];
@@ -275,7 +277,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
 
   const uint32_t koff_ld = static_cast<uint32_t>(tid) * 16u;
-  int kt0, kt1;   // this work tile's key tiles
+  const TileSeq seq = tile_seq(I, h, q0, BM, P);   // dense, or kept history blocks first
+  int kt0, kt1;   // this work tile's logical key tiles
   key_range(a, I, P, wt.part, &kt0, &kt1);
   const int ntiles = kt1 - kt0;
   const int flag_fi = window_flag_segment(I);
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     // the load cursor runs three tiles ahead of the compute tile; nv0..nv2
     // keep the valid-key counts of the tiles in between
     TileCursor lc;
-    cursor_start<2>(lc, I, h, H, P, kt0);
+    seq_start<kSparse, 2>(lc, I, h, H, P, seq, kt0);
     u32x4 kr[kKChunks], vr[kVChunks];
     int nv0 = cursor_mask_code(lc, flag_fi);
     load_tile(lc, koff_ld, kr, vr);
@@ -359,13 +362,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     store_tile(Ks, Vs, tid, kr, vr);
     int nv1 = 0, nv2 = 0;
     if (ntiles > 1) {
-      cursor_next<2>(lc, I, h, H, P);
+      seq_next<kSparse, 2>(lc, I, h, H, P, seq, kt0 + 1);
       nv1 = cursor_mask_code(lc, flag_fi);
       load_tile(lc, koff_ld, kr, vr);
       store_tile(Ks + KT, Vs + VT, tid, kr, vr);
     }
     if (ntiles > 2) {
-      cursor_next<2>(lc, I, h, H, P);
+      seq_next<kSparse, 2>(lc, I, h, H, P, seq, kt0 + 2);
       nv2 = cursor_mask_code(lc, flag_fi);
       load_tile(lc, koff_ld, kr, vr);
     }
@@ -424,7 +427,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
           const int s2 = (t + 2) & (kStages - 1);
           store_tile(Ks + s2 * KT, Vs + s2 * VT, tid, kr, vr);
           if (t + 3 < ntiles) {
-            cursor_next<2>(lc, I, h, H, P);
+            seq_next<kSparse, 2>(lc, I, h, H, P, seq, kt0 + t + 3);
             nv3 = cursor_mask_code(lc, flag_fi);
             load_tile(lc, koff_ld, kr, vr);
           }
@@ -513,7 +516,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
 int attention_block_m_bf16() { return BM; }
 
 hipError_t launch_attention_bf16(AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3(a.grid), dim3(kThreads), 0, s, a);
+  if (a.any_sparse)
+    hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(a.grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(a.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -132,12 +132,82 @@ __device__ __forceinline__ void cursor_start(TileCursor& c, const AttnItemDev& I
   c.p0 = (tile < nvid ? tile - c.fi * tpf : tile - nvid) * kKeyTile;
 }
 
-// Key tiles [begin, end) of a work tile: all of the item's, or part `part` of
-// split_k.
+// Cursor to the next key tile of the item.
+template <int ESZ>
+__device__ __forceinline__ void cursor_next(TileCursor& c, const AttnItemDev& I, int h, int H,
+                                            int P) {
+  c.p0 += kKeyTile;
+  if (c.p0 >= c.len) {
+    ++c.fi;
+    if (c.fi <= I.n_frames_kv) cursor_enter<ESZ>(c, I, h, H, P);
+  }
+}
+
+// Key-tile sequence of a work tile, over logical index li. Dense: the item's
+// tiles in order. Block-sparse history: first the kept candidate tiles of
+// this (head, query tile), read from its block list, then every tile after the
+// history (the remaining frames, then the text slot).
+struct TileSeq {
+  const int32_t* list;   // this work tile's kept tiles, or nullptr (dense)
+  int keep;              // list length (0: dense)
+  int after;             // first tile after the history
+};
+
+__device__ __forceinline__ TileSeq tile_seq(const AttnItemDev& I, int h, int q0, int block_m,
+                                            int P) {
+  TileSeq s{nullptr, 0, 0};
+  if (I.block_list != nullptr) {
+    const int qt = q0 / block_m;
+    s.list = I.block_list + (static_cast<size_t>(h) * I.q_tiles + qt) * I.keep;
+    s.keep = I.keep;
+    s.after = I.n_hist_frames * ((P + kKeyTile - 1) / kKeyTile);
+  }
+  return s;
+}
+
+// tiles of the text slot, and logical tiles before it
+__device__ __forceinline__ int text_tiles(const AttnItemDev& I) {
+  return (I.n_text_kv + kKeyTile - 1) / kKeyTile;
+}
+__device__ __forceinline__ int seq_video_tiles(const AttnItemDev& I, int P) {
+  const int tpf = (P + kKeyTile - 1) / kKeyTile;
+  return I.block_list != nullptr ? I.keep + (I.n_frames_kv - I.n_hist_frames) * tpf
+                                 : I.n_frames_kv * tpf;
+}
+
+// item tile of logical tile li (block-list entries read by scalar loads; the
+// list is written before the launch)
+__device__ __forceinline__ int seq_tile(const TileSeq& s, int li) {
+  if (s.list == nullptr) return li;
+  return li < s.keep ? reinterpret_cast<const_int_ptr>(reinterpret_cast<uintptr_t>(s.list))[li]
+                     : s.after + li - s.keep;
+}
+
+// The kernels come in a dense and a sparse instantiation (kSparse), launched
+// for calls without and with block lists: the dense walk keeps the plain
+// cursor steps.
+template <bool kSparse, int ESZ>
+__device__ __forceinline__ void seq_start(TileCursor& c, const AttnItemDev& I, int h, int H, int P,
+                                          const TileSeq& s, int li) {
+  cursor_start<ESZ>(c, I, h, H, P, kSparse ? seq_tile(s, li) : li);
+}
+
+// Move the cursor on to logical tile li (the one after its current tile): a
+// jump while in the kept list and onto the first tile after it, a step after.
+template <bool kSparse, int ESZ>
+__device__ __forceinline__ void seq_next(TileCursor& c, const AttnItemDev& I, int h, int H, int P,
+                                         const TileSeq& s, int li) {
+  if (kSparse && li <= s.keep)   // (never for a dense item: keep 0, li >= 1)
+    cursor_start<ESZ>(c, I, h, H, P, seq_tile(s, li));
+  else
+    cursor_next<ESZ>(c, I, h, H, P);
+}
+
+// Logical key tiles [begin, end) of a work tile: all of them, or part `part`
+// of split_k.
 __device__ __forceinline__ void key_range(const AttnArgs& a, const AttnItemDev& I, int P, int part,
                                           int* begin, int* end) {
-  const int tpf = (P + kKeyTile - 1) / kKeyTile;
-  const int n = I.n_frames_kv * tpf + (I.n_text_kv + kKeyTile - 1) / kKeyTile;
+  const int n = seq_video_tiles(I, P) + text_tiles(I);
   if (part < 0) {
     *begin = 0;
     *end = n;
@@ -145,7 +215,7 @@ __device__ __forceinline__ void key_range(const AttnArgs& a, const AttnItemDev& 
     // with timed text windows the parts divide the video tiles (at least one
     // each) and the last part takes the text tiles as well: every part then
     // starts with a tile whose valid keys every query row sees
-    const int ns = I.text_window != nullptr ? I.n_frames_kv * tpf : n;
+    const int ns = I.text_window != nullptr ? seq_video_tiles(I, P) : n;
     *begin = static_cast<int>(static_cast<int64_t>(part) * ns / a.split_k);
     *end = part + 1 == a.split_k ? n
                                  : static_cast<int>(static_cast<int64_t>(part + 1) * ns / a.split_k);
@@ -174,16 +244,6 @@ __device__ __forceinline__ void store_partial(const AttnArgs& a, int unit, int b
   if (g == 0) {
     base[static_cast<size_t>(block_m) * kD + row] = m;
     base[static_cast<size_t>(block_m) * (kD + 1) + row] = l;
-  }
-}
-
-template <int ESZ>
-__device__ __forceinline__ void cursor_next(TileCursor& c, const AttnItemDev& I, int h, int H,
-                                            int P) {
-  c.p0 += kKeyTile;
-  if (c.p0 >= c.len) {
-    ++c.fi;
-    if (c.fi <= I.n_frames_kv) cursor_enter<ESZ>(c, I, h, H, P);
   }
 }
 
@@ -321,9 +381,9 @@ __device__ __forceinline__ int window_row_offset(const AttnItemDev& I, int q0, i
   return (row / P - q0 / P + 1) * window_row_words(I.n_text_kv);
 }
 
-// text index of the first key of text tile `tile` (frames first, then text)
+// text index of the first key of logical text tile `tile` (text comes last)
 __device__ __forceinline__ int text_tile_base(const AttnItemDev& I, int P, int tile) {
-  return (tile - I.n_frames_kv * ((P + kKeyTile - 1) / kKeyTile)) * kKeyTile;
+  return (tile - seq_video_tiles(I, P)) * kKeyTile;
 }
 
 // s if bit `bit` of `word` is set, else -inf (bit-field insert under a

@@ -49,6 +49,7 @@ namespace segattn {
 namespace {
 
 constexpr int BM = 256;
+static_assert(BM == SA_SPARSE_QUERY_BLOCK, "a work tile reads one block list");
 constexpr int BN = kKeyTile;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -302,6 +303,7 @@ __device__ __forceinline__ float rescale_step(float mx, float& m_run, float& off
   return l;
 }
 
+template <bool kSparse>
 __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t Ks[kStages * KT8];
   __shared__ __attribute__((aligned(16))) uint8_t Vs[kStages * VT8];
@@ -323,13 +325,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   const int lane = tid & 63, g = lane >> 5, r32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
 
-  int kt0, kt1;   // this work tile's key tiles
+  const TileSeq seq = tile_seq(I, h, q0, BM, P);   // dense, or kept history blocks first
+  int kt0, kt1;   // this work tile's logical key tiles
   key_range(a, I, P, wt.part, &kt0, &kt1);
   const int ntiles = kt1 - kt0;
   const int flag_fi = window_flag_segment(I);
 
   TileCursor lc;
-  cursor_start<1>(lc, I, h, H, P, kt0);
+  seq_start<kSparse, 1>(lc, I, h, H, P, seq, kt0);
   TileInfo ti0 = tile_info(lc, flag_fi);
 
   // largest V scale among the planes this (item, head) attends
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   dma_v8(lc, Vs, w);
   TileInfo ti1 = ti0;
   if (ntiles > 1) {
-    cursor_next<1>(lc, I, h, H, P);
+    seq_next<kSparse, 1>(lc, I, h, H, P, seq, kt0 + 1);
     ti1 = tile_info(lc, flag_fi);
     dma_k8(lc, Ks + KT8, w);
     dma_v8(lc, Vs + VT8, w);
@@ -500,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
       pending = 0;
       if (tt + 2 < ntiles) {
         const int s2 = (tt + 2) & (kStages - 1);
-        cursor_next<1>(lc, I, h, H, P);
+        seq_next<kSparse, 1>(lc, I, h, H, P, seq, kt0 + tt + 2);
         ti2 = tile_info(lc, flag_fi);
         dma_k8(lc, Ks + s2 * KT8, w);
         dma_v8(lc, Vs + s2 * VT8, w);
@@ -574,7 +577,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
 int attention_block_m_fp8() { return BM; }
 
 hipError_t launch_attention_fp8(AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_fp8_kernel, dim3(a.grid), dim3(kThreads), 0, s, a);
+  if (a.any_sparse)
+    hipLaunchKernelGGL(attn_fp8_kernel<true>, dim3(a.grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_fp8_kernel<false>, dim3(a.grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -317,6 +317,36 @@ bool windowed(const sa_attn_item& it) {
   return it.text_window != nullptr && it.n_text_kv > 0 && it.n_frames_q > 0;
 }
 
+// Block-sparse history takes effect when there are candidate frames.
+bool sparse(const sa_attn_item& it) { return it.block_list != nullptr && it.n_hist_frames > 0; }
+
+// Device view of a validated item (q_tiles and tile_begin are the caller's).
+void fill_item(const sa_attn_item& it, int32_t P, AttnItemDev& d) {
+  d = AttnItemDev{};
+  d.q = static_cast<const uint16_t*>(it.q);
+  d.out = static_cast<uint16_t*>(it.out);
+  d.lse = it.lse;
+  d.k = it.kv->k;
+  d.v = it.kv->v;
+  d.k_text = it.kv->k_text;
+  d.v_text = it.kv->v_text;
+  d.k_scale = it.kv->k_scale;
+  d.v_scale = it.kv->v_scale;
+  d.k_text_scale = it.kv->k_text_scale;
+  d.v_text_scale = it.kv->v_text_scale;
+  d.frames = it.frames;
+  d.frame0_q = it.frame0_q;
+  d.n_q_video = it.n_frames_q * P;
+  d.n_q = d.n_q_video + it.n_text_q;
+  d.n_frames_kv = it.n_frames_kv;
+  d.n_text_kv = it.n_text_kv;
+  d.text_cap = it.kv->text_capacity;
+  d.text_window = windowed(it) ? it.text_window : nullptr;
+  d.block_list = sparse(it) ? it.block_list : nullptr;
+  d.n_hist_frames = sparse(it) ? it.n_hist_frames : 0;
+  d.keep = sparse(it) ? it.keep_blocks : 0;
+}
+
 sa_status prepare_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
                             AttnPlan& plan) {
   sa_status st = check_geom(geom);
@@ -355,6 +385,17 @@ sa_status prepare_attention(const sa_geom* geom, const sa_attn_item* items, int3
         return fail(SA_E_RANGE, "item %d: timed windows of %d text keys over frames of %d tokens "
                     "need %d table words > %d", i, it.n_text_kv, P, words, kWindowWords);
     }
+    if (sparse(it)) {
+      if (it.n_hist_frames > it.n_frames_kv)
+        return fail(SA_E_RANGE, "item %d: n_hist_frames %d > n_frames_kv %d", i, it.n_hist_frames,
+                    it.n_frames_kv);
+      const int64_t cand = static_cast<int64_t>(it.n_hist_frames) * ((P + 63) / 64);
+      if (it.keep_blocks < 1 || it.keep_blocks > cand)
+        return fail(SA_E_ARG, "item %d: keep_blocks %d outside [1, %lld]", i, it.keep_blocks,
+                    static_cast<long long>(cand));
+      if ((reinterpret_cast<uintptr_t>(it.block_list) & 3) != 0)
+        return fail(SA_E_ALIGN, "item %d: block_list not 4-byte aligned", i);
+    }
     const int64_t rows = static_cast<int64_t>(it.n_frames_q) * P + it.n_text_q;
     if (rows > (int64_t(1) << 30)) return fail(SA_E_SHAPE, "item %d: too many query rows", i);
     if (rows > 0) {
@@ -372,30 +413,16 @@ sa_status prepare_attention(const sa_geom* geom, const sa_attn_item* items, int3
   for (int i = 0; i < n_items; ++i) {
     const sa_attn_item& it = items[i];
     AttnItemDev& d = a.items[i];
-    d.q = static_cast<const uint16_t*>(it.q);
-    d.out = static_cast<uint16_t*>(it.out);
-    d.lse = it.lse;
-    d.k = it.kv->k;
-    d.v = it.kv->v;
-    d.k_text = it.kv->k_text;
-    d.v_text = it.kv->v_text;
-    d.k_scale = it.kv->k_scale;
-    d.v_scale = it.kv->v_scale;
-    d.k_text_scale = it.kv->k_text_scale;
-    d.v_text_scale = it.kv->v_text_scale;
-    d.frames = it.frames;
-    d.frame0_q = it.frame0_q;
-    d.n_q_video = it.n_frames_q * P;
-    d.n_q = d.n_q_video + it.n_text_q;
-    d.n_frames_kv = it.n_frames_kv;
-    d.n_text_kv = it.n_text_kv;
-    d.text_cap = it.kv->text_capacity;
-    d.text_window = windowed(it) ? it.text_window : nullptr;
+    fill_item(it, P, d);
+    if (d.block_list != nullptr) a.any_sparse = 1;
     d.q_tiles = (d.n_q + bm - 1) / bm;
     d.tile_begin = static_cast<int32_t>(tiles);
     tiles += static_cast<int64_t>(d.q_tiles) * geom->heads;
-    // (split parts of an item with windows divide its video tiles only)
-    plan.key_tiles[i] = it.n_frames_kv * tpf + (windowed(it) ? 0 : (it.n_text_kv + 63) / 64);
+    // key tiles a work tile visits (kept history blocks, then the rest); split
+    // parts of an item with windows divide its video tiles only
+    const int vid = sparse(it) ? d.keep + (it.n_frames_kv - it.n_hist_frames) * tpf
+                               : it.n_frames_kv * tpf;
+    plan.key_tiles[i] = vid + (windowed(it) ? 0 : (it.n_text_kv + 63) / 64);
   }
   if (tiles > (int64_t(1) << 31) - 1) return fail(SA_E_SHAPE, "too many tiles");
   a.n_items = n_items;
@@ -498,6 +525,80 @@ sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, i
   if (a.split_k > 1)
     return hip_status(launch_attention_combine(a, plan.bm, s), "segment_attention combine launch");
   return ok();
+}
+
+namespace {
+
+// Validated block selection: kernel arguments and the pooled-key workspace size.
+sa_status prepare_select(const sa_geom* geom, const sa_attn_item* item, SelectArgs& a,
+                         size_t* ws_bytes) {
+  sa_status st = check_geom(geom);
+  if (st != SA_OK) return st;
+  if (item == nullptr) return fail(SA_E_ARG, "sparse_select: item is NULL");
+  const sa_attn_item& it = *item;
+  if ((st = check_layer(geom, it.kv, "sparse_select kv")) != SA_OK) return st;
+  const int32_t P = tokens_per_frame(geom);
+  if (it.n_frames_q < 0 || it.n_text_q < 0 || it.frame0_q < 0)
+    return fail(SA_E_ARG, "sparse_select: negative query counts or frame0_q");
+  const int64_t rows = static_cast<int64_t>(it.n_frames_q) * P + it.n_text_q;
+  if (rows < 1) return fail(SA_E_ARG, "sparse_select: no query rows");
+  if (rows > (int64_t(1) << 30)) return fail(SA_E_SHAPE, "sparse_select: too many query rows");
+  if (it.q == nullptr) return fail(SA_E_ARG, "sparse_select: q is NULL");
+  if (!aligned16(it.q)) return fail(SA_E_ALIGN, "sparse_select: q not 16-byte aligned");
+  if (it.n_hist_frames < 1) return fail(SA_E_ARG, "sparse_select: no candidate frames");
+  if (it.n_hist_frames > it.n_frames_kv)
+    return fail(SA_E_RANGE, "sparse_select: n_hist_frames %d > n_frames_kv %d", it.n_hist_frames,
+                it.n_frames_kv);
+  if (it.n_frames_kv > SA_MAX_FRAMES_KV)
+    return fail(SA_E_RANGE, "sparse_select: n_frames_kv %d > %d", it.n_frames_kv, SA_MAX_FRAMES_KV);
+  if (it.kv->frame_capacity == 0) return fail(SA_E_RANGE, "sparse_select: the layer has no frames");
+  if (it.frames == nullptr) return fail(SA_E_ARG, "sparse_select: frames is NULL");
+  const int64_t cand = static_cast<int64_t>(it.n_hist_frames) * ((P + 63) / 64);
+  if (cand > kMaxCandidates)
+    return fail(SA_E_RANGE, "sparse_select: %lld candidate blocks > %d", static_cast<long long>(cand),
+                kMaxCandidates);
+  if (it.keep_blocks < 1 || it.keep_blocks > cand)
+    return fail(SA_E_ARG, "sparse_select: keep_blocks %d outside [1, %lld]", it.keep_blocks,
+                static_cast<long long>(cand));
+  a = SelectArgs{};
+  fill_item(it, P, a.item);
+  a.item.text_window = nullptr;
+  a.item.block_list = nullptr;
+  a.item.q_tiles = static_cast<int32_t>((rows + SA_SPARSE_QUERY_BLOCK - 1) / SA_SPARSE_QUERY_BLOCK);
+  a.heads = geom->heads;
+  a.fp8 = it.kv->dtype == SA_KV_FP8_E4M3;
+  a.n_cand = static_cast<int32_t>(cand);
+  a.keep = it.keep_blocks;
+  a.rope = rope_params(geom);
+  *ws_bytes = static_cast<size_t>(geom->heads) * static_cast<size_t>(cand) * kD * sizeof(float);
+  return ok();
+}
+
+}  // namespace
+
+size_t sa_sparse_select_workspace(const sa_geom* geom, const sa_attn_item* item) {
+  SelectArgs a;
+  size_t ws = 0;
+  if (prepare_select(geom, item, a, &ws) != SA_OK) return 0;
+  return ws;
+}
+
+sa_status sa_sparse_select(const sa_geom* geom, const sa_attn_item* item, void* workspace,
+                           size_t workspace_bytes, int32_t* block_list, void* stream) {
+  SelectArgs a;
+  size_t ws = 0;
+  sa_status st = prepare_select(geom, item, a, &ws);
+  if (st != SA_OK) return st;
+  if (block_list == nullptr) return fail(SA_E_ARG, "sparse_select: block_list is NULL");
+  if ((reinterpret_cast<uintptr_t>(block_list) & 3) != 0)
+    return fail(SA_E_ALIGN, "sparse_select: block_list not 4-byte aligned");
+  if (workspace == nullptr || workspace_bytes < ws)
+    return fail(SA_E_CAPACITY, "sparse_select: workspace of %zu bytes < %zu", workspace_bytes, ws);
+  if (!aligned16(workspace)) return fail(SA_E_ALIGN, "sparse_select: workspace not 16-byte aligned");
+  if (geom->heads > 256) return fail(SA_E_SHAPE, "sparse_select: more than 256 heads");
+  a.pooled = static_cast<float*>(workspace);
+  a.out = block_list;
+  return hip_status(launch_sparse_select(a, static_cast<hipStream_t>(stream)), "sparse_select launch");
 }
 
 sa_status sa_kv_dequant(const sa_geom* geom, const sa_kv_layer* src, const int32_t* d_frames,

@@ -60,6 +60,9 @@ struct AttnItemDev {
   int32_t n_text_kv;
   int32_t text_cap;
   const int32_t* text_window;   // [n_text_kv][2] (first, last) frames, or NULL: no windows
+  const int32_t* block_list;    // [H][q_tiles][keep] kept history tiles, or NULL: dense
+  int32_t n_hist_frames;        // candidate frames (first entries of `frames`) when sparse
+  int32_t keep;                 // list length when sparse
   int32_t q_tiles;       // ceil(n_q / BLOCK_M)
   int32_t tile_begin;    // first logical tile of this item (over heads * q_tiles)
 };
@@ -78,6 +81,7 @@ struct AttnArgs {
   int32_t n_full;
   int32_t split_k;        // 1: nothing is split
   int32_t grid;           // n_full + (total_tiles - n_full) * split_k
+  int32_t any_sparse;     // 1: some item has a block list (the sparse kernel instantiation)
   float* ws;
   float scale_log2;       // softmax scale * log2(e)
   RopeParams rope;
@@ -93,6 +97,22 @@ constexpr int kPartialStride = kD + 2;   // floats per row of a partial: O, m, l
 constexpr int kWindowWords = SA_WINDOW_TABLE_WORDS;   // table capacity (words)
 __host__ __device__ inline int window_row_words(int n_text) { return (n_text + 31) / 32; }
 __host__ __device__ inline int window_table_rows(int P, int block_m) { return (block_m - 1) / P + 3; }
+
+// ---- sparse history: block selection -------------------------------------------
+// pool_k: mean stored key of every candidate block, fp32 [H][n_cand][128].
+// select: per (head, query block) the keep best blocks by pooled q . pooled k.
+struct SelectArgs {
+  AttnItemDev item;        // q, kv planes, frames, counts of the session
+  int32_t heads;
+  int32_t fp8;             // 1: e4m3 planes with per-(frame, head) scales
+  int32_t n_cand;          // n_hist_frames * ceil(P / 64)
+  int32_t keep;
+  float* pooled;           // workspace [H][n_cand][128]
+  int32_t* out;            // [H][q_tiles][keep]
+  RopeParams rope;
+};
+constexpr int kMaxCandidates = SA_MAX_SPARSE_CANDIDATES;
+hipError_t launch_sparse_select(const SelectArgs& a, hipStream_t s);
 
 hipError_t launch_attention_bf16(AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_fp8(AttnArgs& a, hipStream_t s);

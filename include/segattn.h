@@ -46,11 +46,14 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 3
+#define SA_ABI_VERSION 4
 #define SA_HEAD_DIM 128       /* the only head dim the kernels are built for */
 #define SA_MAX_ITEMS 8        /* sessions per sa_segment_attention call     */
 #define SA_MAX_FRAMES_KV 65536
 #define SA_WINDOW_TABLE_WORDS 2048   /* bound on timed text windows, see below  */
+#define SA_SPARSE_KEY_BLOCK 64       /* keys per candidate history block          */
+#define SA_SPARSE_QUERY_BLOCK 256    /* query rows that share one block list      */
+#define SA_MAX_SPARSE_CANDIDATES 8192 /* candidate blocks sa_sparse_select ranks  */
 
 typedef enum {
   SA_OK = 0,
@@ -142,6 +145,23 @@ typedef struct sa_kv_layer {
  *              (255 / P + 3) * ceil(n_text_kv / 32) <= SA_WINDOW_TABLE_WORDS
  *              (SA_E_RANGE otherwise; frames of 128 tokens allow 16384 text
  *              keys, frames of 16 tokens 3616).
+ *   block_list optional device int32 [H][ceil(rows / 256)][keep_blocks]:
+ *              block-sparse history ("Hy-Nomas en una RTX 4090", "El preset
+ *              de una GPU": after the first denoising steps only a quarter of
+ *              the candidate video blocks are attended). The candidates are
+ *              the first n_hist_frames entries of `frames`, each cut into
+ *              blocks of SA_SPARSE_KEY_BLOCK tokens (the last block of a frame
+ *              is shorter when 64 does not divide P); block b of frame-list
+ *              position f, in-frame index j, is f * ceil(P / 64) + j. Query
+ *              rows [256 i, 256 i + 256) of head h attend only the candidate
+ *              blocks listed at [h][i], plus every key after the history
+ *              (the remaining frames and the text). Entries must be distinct
+ *              and lie in [0, n_hist_frames * ceil(P / 64)); ascending order
+ *              reads the cache in order. NULL: dense. sa_sparse_select
+ *              writes such lists. 4-byte aligned.
+ *   n_hist_frames, keep_blocks: the candidate frames and the list length
+ *              (1 <= keep_blocks <= candidates); ignored when block_list is
+ *              NULL or n_hist_frames is 0.
  * At least one key is required (n_frames_kv * P + n_text_kv >= 1).         */
 typedef struct sa_attn_item {
   const void* q;
@@ -156,6 +176,9 @@ typedef struct sa_attn_item {
   void* out;
   float* lse;
   const int32_t* text_window;
+  const int32_t* block_list;
+  int32_t n_hist_frames;
+  int32_t keep_blocks;
 } sa_attn_item;
 
 int sa_abi_version(void);
@@ -237,6 +260,27 @@ size_t sa_segment_attention_workspace(const sa_geom* geom, const sa_attn_item* i
                                       int32_t n_items);
 sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* sparse_select: block lists for block-sparse history attention. For every
+ * head h and query block i (rows [256 i, 256 i + 256) of the item, video then
+ * text), the score of candidate block b (see sa_attn_item.block_list) is
+ *   mean over the block's rows of rope(q)  .  mean over the block's keys of K
+ * (K as stored: rotated, and for e4m3 codes times the plane's scale), in
+ * fp32; the keep_blocks best scores are kept (ties to the lower index) and
+ * written in ascending order to block_list [H][ceil(rows / 256)][keep_blocks].
+ * Uses item->q, kv, frames, frame0_q, n_frames_q, n_text_q, n_hist_frames
+ * and keep_blocks (its block_list field is ignored). The pooled keys live in
+ * the caller's workspace of sa_sparse_select_workspace() bytes (device, 16-byte
+ * aligned). Source: "El preset de una GPU" (sparse attention keeps 25 % of the
+ * candidate video blocks); the block size, the query block and the pooled
+ * score are readings, not stated on the pages.
+ * Errors: SA_E_ARG (no candidates, keep_blocks outside [1, candidates], no
+ * query rows), SA_E_RANGE (candidates > SA_MAX_SPARSE_CANDIDATES,
+ * n_hist_frames > n_frames_kv), SA_E_CAPACITY (workspace too small),
+ * SA_E_ALIGN.                                                               */
+size_t sa_sparse_select_workspace(const sa_geom* geom, const sa_attn_item* item);
+sa_status sa_sparse_select(const sa_geom* geom, const sa_attn_item* item, void* workspace,
+                           size_t workspace_bytes, int32_t* block_list, void* stream);
 
 /* kv_dequant: fp8 frames[i] of src -> bf16 frame slot i of dst (K and V
  * planes: value = code * scale, rounded to bf16), and, when n_text > 0, the

@@ -67,11 +67,59 @@ class Session:
         self.lse = torch.empty((wl.Lq, wl.heads), dtype=torch.float32, device=device)
         self.text_window = None      # timed text windows (set_windows)
         self.d_window = None
+        self.block_lists = None      # block-sparse history (set_sparse)
+        self.d_lists = None
+        self.n_hist = 0
 
     def set_windows(self, win):
         """Timed text windows: int32 [n_text, 2] (first, last) absolute frames."""
         self.text_window = np.asarray(win, dtype=np.int64).reshape(-1, 2)
         self.d_window = torch.as_tensor(np.asarray(win, dtype=np.int32)).to(self.q.device).contiguous()
+
+    def set_sparse(self, lists, n_hist):
+        """Block-sparse history: int32 [H, n_qblocks, keep] kept candidate
+        blocks over the first n_hist frames of the key set."""
+        self.block_lists = np.asarray(lists, dtype=np.int32)
+        self.d_lists = torch.as_tensor(self.block_lists).to(self.q.device).contiguous()
+        self.n_hist = n_hist
+
+    def clear_sparse(self):
+        self.block_lists, self.d_lists, self.n_hist = None, None, 0
+
+    def q_rotated(self):
+        """Rotated queries (fp64) of every row: [Lq, H, D]."""
+        wl = self.wl
+        q = self.q.float().cpu().double().numpy()
+        return orope.rope3d(q, self.q_positions(), wl.split, self.geom.rope_theta)
+
+    def hist_stored_keys(self, n_hist):
+        """Keys of the first n_hist frames of the key set as the cache stores
+        them (the oracle's own append: rotated, bf16-rounded or e4m3 codes
+        times the plane scale), fp64 [n_hist * P, H, D]."""
+        from oracle import cache as ocache
+        wl = self.wl
+        F, P = wl.lat_t, wl.P
+        out = []
+        for f in self.frames[:n_hist]:
+            seg, fo = divmod(f, F)
+            raw = self.raw_k[seg][fo * P:(fo + 1) * P].float().cpu().double().numpy()
+            if wl.kv_dtype == "fp8":
+                kc, ksc, _, _ = ocache.append_fp8(raw, raw, f, wl.lat_h, wl.lat_w, wl.split,
+                                                  self.geom.rope_theta)
+                k = ocache.dequant(kc[0], ksc[0][:, None, None])
+            else:
+                k = ocache.append_bf16(raw, raw, f, wl.lat_h, wl.lat_w, wl.split,
+                                       self.geom.rope_theta)[0][0]
+            out.append(k.transpose(1, 0, 2))
+        return np.concatenate(out)
+
+    def oracle_select(self, n_hist, keep):
+        """(lists [H, n_qblocks, keep], scores [H, n_qblocks, n_cand]) of the oracle."""
+        from oracle import sparse as osp
+        qr = self.q_rotated()
+        kh = self.hist_stored_keys(n_hist)
+        return (osp.select_blocks(qr, kh, n_hist, self.wl.P, keep),
+                osp.block_scores(qr, kh, n_hist, self.wl.P))
 
     def q_frames(self):
         """Absolute latent frame of each query row, -1 for text rows."""
@@ -84,18 +132,25 @@ class Session:
         return np.concatenate([-np.ones(len(self.frames) * self.wl.P, dtype=np.int64),
                                np.arange(self.wl.n_text)])
 
-    def visibility(self, rows):
-        """bool [len(rows), Lk]: keys each row sees (all, without windows)."""
-        if self.text_window is None:
-            return None
-        return oatt.timed_text_visibility(self.q_frames()[rows], self.key_text(), self.text_window)
+    def visibility(self, rows, head=0):
+        """bool [len(rows), Lk]: keys each row of `head` sees (None: all)."""
+        from oracle import sparse as osp
+        vis = None
+        if self.text_window is not None:
+            vis = oatt.timed_text_visibility(self.q_frames()[rows], self.key_text(), self.text_window)
+        if self.block_lists is not None:
+            sv = osp.sparse_visibility(rows, self.block_lists[head], self.n_hist, self.wl.P, self.Lk)
+            vis = sv if vis is None else (vis & sv)
+        return vis
 
     def item(self, with_lse=True):
         import diffusion_transformer_attention_segment_amd as sa
         wl = self.wl
         return sa.AttnItem(self.q, self.kv, self.d_frames, len(self.frames), wl.n_text, self.out,
                            frame0_q=self.S * wl.lat_t, n_frames_q=wl.lat_t, n_text_q=wl.n_text,
-                           lse=self.lse if with_lse else None, text_window=self.d_window)
+                           lse=self.lse if with_lse else None, text_window=self.d_window,
+                           block_list=self.d_lists, n_hist_frames=self.n_hist,
+                           keep_blocks=0 if self.block_lists is None else self.block_lists.shape[2])
 
     @property
     def Lk(self):
@@ -143,12 +198,15 @@ class Session:
         if self.text_window is not None:
             win = dict(q_frame=self.q_frames(), key_text=self.key_text(),
                        text_window=self.text_window)
+        if self.block_lists is not None:
+            hl = self.block_lists if heads is None else self.block_lists[list(heads)]
+            win.update(block_lists=hl, n_hist_frames=self.n_hist, P=wl.P)
         if not round_rotated:
             return oatt.segment_attention(q, self.q_positions(), k, kpos, v, wl.split,
                                           self.geom.rope_theta, scale, rows=rows, **win)
         if rows is None:
             rows = np.arange(q.shape[0])
-        vis = self.visibility(rows)
+        hsel = list(range(wl.heads)) if heads is None else list(heads)
         c2 = float(np.float32(scale * math.log2(math.e)))
         qr = onum.bf16_round(orope.rope3d(q[rows], self.q_positions()[rows], wl.split,
                                           self.geom.rope_theta) * c2) / c2
@@ -156,7 +214,8 @@ class Session:
         out = np.zeros(qr.shape)
         lse = np.zeros(qr.shape[:2])
         for h in range(qr.shape[1]):
-            out[:, h], lse[:, h] = oatt.attention(qr[:, h], kr[:, h], v[:, h], scale, vis)
+            out[:, h], lse[:, h] = oatt.attention(qr[:, h], kr[:, h], v[:, h], scale,
+                                                  self.visibility(rows, hsel[h]))
         return out, lse
 
     def oracle_fp8_cache(self, rows=None, heads=None, split_q=False):
@@ -207,8 +266,8 @@ class Session:
         out = np.zeros(qq.shape)
         lse = np.zeros(qq.shape[:2])
         bound = np.zeros(qq.shape)
-        vis = self.visibility(rows)
         for j in range(qq.shape[1]):
+            vis = self.visibility(rows, hs[j])
             out[:, j], lse[:, j] = oatt.attention(qq[:, j], k[:, j], v[:, j], scale, vis)
             s_ = (qq[:, j] @ k[:, j].T) * scale
             if vis is not None:
@@ -254,3 +313,25 @@ def compare(got, want, max_abs, mean_abs, label=""):
     assert np.all(np.isfinite(got)), msg
     assert mx <= max_abs and mn <= mean_abs, msg
     return mx, mn, rel
+
+
+def check_block_lists(got, want, scores, rel_tol):
+    """GPU lists vs oracle lists: equal up to near-ties at the threshold."""
+    H, nq, keep = want.shape
+    assert got.shape == want.shape
+    n_cand = scores.shape[2]
+    swaps = 0
+    for h in range(H):
+        for i in range(nq):
+            g = got[h, i]
+            assert np.all(np.diff(g) > 0) and g[0] >= 0 and g[-1] < n_cand, (h, i, g)
+            diff = set(g.tolist()) ^ set(want[h, i].tolist())
+            if not diff:
+                continue
+            sc = scores[h, i]
+            thr = np.sort(sc)[::-1][keep - 1]
+            tol = rel_tol * np.abs(sc).max()
+            for b in diff:
+                assert abs(sc[b] - thr) <= tol, (h, i, b, sc[b], thr)
+            swaps += len(diff) // 2
+    return swaps

@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 3
+    assert sa.abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -207,6 +207,41 @@ def test_attention_window_validation(lib):
     assert b"item 1" in lib.sa_last_error()
     no_rows = win(_item(L, rows=False, n_frames_kv=0), FAKE + 4)
     assert _attn([no_rows]) == 0
+
+
+def test_sparse_validation(lib):
+    """Block-sparse history: the attention item's list fields and the
+    selection call are checked on the host (P = 24: one block per frame)."""
+    L = _layer(fc=8)
+
+    def sp(it, lst=FAKE, nh=2, keep=1):
+        it.block_list, it.n_hist_frames, it.keep_blocks = lst, nh, keep
+        return it
+    assert _attn([sp(_item(L), nh=3)]) == 5                       # n_hist_frames > n_frames_kv
+    assert _attn([sp(_item(L), keep=0)]) == 1
+    assert _attn([sp(_item(L), keep=3)]) == 1                     # > 2 candidates
+    assert _attn([sp(_item(L), lst=FAKE + 2)]) == 3
+    # ignored without candidate frames: the second item's error is reported
+    assert _attn([sp(_item(L), nh=0, keep=0), _item(L, frames=0)]) == 1
+    assert b"item 1" in lib.sa_last_error()
+    g = _geom()
+    sel = lib.sa_sparse_select
+    ws = lib.sa_sparse_select_workspace
+    it = sp(_item(L))
+    assert ws(ctypes.byref(g), ctypes.byref(it)) == 2 * 2 * 128 * 4   # H x candidates x 128 fp32
+    assert sel(ctypes.byref(g), ctypes.byref(it), ctypes.c_void_p(FAKE), 16,
+               ctypes.c_void_p(FAKE), None) == 6                          # workspace too small
+    assert sel(ctypes.byref(g), ctypes.byref(it), ctypes.c_void_p(FAKE), 4096, None, None) == 1
+    assert sel(ctypes.byref(g), ctypes.byref(it), ctypes.c_void_p(FAKE + 4), 4096,
+               ctypes.c_void_p(FAKE), None) == 3
+    assert sel(ctypes.byref(g), ctypes.byref(sp(_item(L), nh=0)), ctypes.c_void_p(FAKE), 4096,
+               ctypes.c_void_p(FAKE), None) == 1
+    assert sel(ctypes.byref(g), ctypes.byref(sp(_item(L, rows=False))), ctypes.c_void_p(FAKE),
+               4096, ctypes.c_void_p(FAKE), None) == 1                   # no query rows
+    big = _layer(fc=9000)
+    assert ws(ctypes.byref(g), ctypes.byref(sp(_item(big, n_frames_kv=8200), nh=8193))) == 0
+    assert b"candidate blocks" in lib.sa_last_error()
+    assert sel(ctypes.byref(g), None, ctypes.c_void_p(FAKE), 4096, ctypes.c_void_p(FAKE), None) == 1
 
 
 def test_attention_workspace_query_without_split(lib):

@@ -17,7 +17,7 @@ import torch
 
 import diffusion_transformer_attention_segment_amd as sa
 import seeded_inputs as si
-from helpers import Session, compare
+from helpers import Session, check_block_lists, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -135,3 +135,29 @@ def test_fp8_cache_eight_prior_segments():
     print(f"fp8seg8: e4m3 storage error of the oracle itself {storage:.3e}", flush=True)
     _, _, rel = compare(got, want, storage + 2e-2, 5e-3, "fp8seg8 vs exact")
     assert rel <= 0.1
+
+
+def test_sparse_history_four_prior_segments_two_heads():
+    """Block-sparse history at full size on one GPU's 2-head share of the
+    four-prior-segment workload: 120 history frames (1,680 candidate blocks,
+    420 kept) for 105 query blocks. sparse_select is checked on every list
+    against the oracle's selection (equal up to near-ties at the threshold);
+    the attention runs with the oracle's lists and is checked on sampled rows
+    against the oracle's sparse attention."""
+    wl = si.Workload("seg4h2", heads=2, lat_t=30, lat_h=22, lat_w=40, n_text=256,
+                     prior_segments=(4,))
+    print("workload seg4 at 2 heads, block-sparse history (25 %)", flush=True)
+    s = Session(wl, 0, 0, 0)
+    n_hist = 4 * 30
+    keep = sa.sparse_keep(n_hist * 14, 25)
+    assert keep == 420
+    it = s.item()
+    it.n_hist_frames, it.keep_blocks = n_hist, keep
+    got_lists = sa.sparse_select(s.geom, it).cpu().numpy()
+    want_lists, scores = s.oracle_select(n_hist, keep)
+    swaps = check_block_lists(got_lists, want_lists, scores, 1e-4)
+    print(f"near-tie swaps: {swaps} of {want_lists.size} list entries", flush=True)
+    s.set_sparse(want_lists, n_hist)
+    sa.segment_attention(s.geom, [s.item()])
+    torch.cuda.synchronize()
+    _check([s], 192, label="seg4 2 heads sparse")
