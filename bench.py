@@ -235,6 +235,32 @@ def measure_sparse(sa, state, percent=25, reps=5):
             "note": "kept-key FLOP count uses 64 keys per kept block (an upper bound)"}
 
 
+def measure_camera(sa, state, chunk=1, reps=10):
+    """Camera cross-attention of the segment's video tokens (one shared
+    camera head, chunk 1 as the pages' config): HBM-bound, algorithmic bytes =
+    the video queries read plus the output written (the camera tokens are a
+    few KB)."""
+    wl = state.wl
+    d = state.sess[0]
+    F = wl.lat_t
+    rows = F * wl.P
+    ck = si.normal_bf16((F, 1, 128), si.derive_seed(0, "bench", "cam_k"), "cuda")
+    cv = si.normal_bf16((F, 1, 128), si.derive_seed(0, "bench", "cam_v"), "cuda")
+    out = torch.empty((rows, wl.heads, 128), dtype=torch.bfloat16, device="cuda")
+    sa.camera_attention(state.geom, d["q"], F, ck, cv, chunk, out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        sa.camera_attention(state.geom, d["q"], F, ck, cv, chunk, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 2 * rows * wl.heads * 128 * 2
+    return {"chunk": chunk, "ms": round(ms, 4), "bytes": nbytes,
+            "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def measure_gather(sa, geom, n_frames=99, capacity=128, reps=5):
     """history_gather of n_frames picked out of a capacity-frame bf16 layer:
     a plain copy of 2 planes x n_frames x H x P x 128 x 2 bytes, read and written."""
@@ -435,6 +461,7 @@ def main():
     if sp is not None:
         sp["speedup_vs_dense_attention"] = round(attn_ms / sp["pass_ms"], 3)
         line["sparse_25pct"] = sp
+    line["camera_attention"] = measure_camera(sa, state)
     line["history_gather"] = measure_gather(sa, state.geom)
     line["kv_dequant"] = measure_dequant(sa, state.geom)
     if not args.no_cpu_baseline:

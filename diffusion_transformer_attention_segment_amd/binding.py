@@ -82,6 +82,8 @@ SIGNATURES = {
                                                      ctypes.POINTER(sa_attn_item)]),
     "sa_sparse_select": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_attn_item), _P,
                                         ctypes.c_size_t, _P, _P]),
+    "sa_camera_attention": (ctypes.c_int, [ctypes.POINTER(sa_geom), _P, _I, _P, _P, _I, _I, _I, _P,
+                                           _P, _P]),
     "sa_kv_dequant": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_kv_layer), _P, _I,
                                      _I, ctypes.POINTER(sa_kv_layer), _P]),
 }
@@ -342,6 +344,19 @@ def sparse_select(geom, item, block_list=None, stream=None):
             torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)))
         ws.record_stream(ext)
     return block_list
+
+
+MAX_CAMERA_CHUNK = 16
+
+
+def camera_attention(geom, q, n_frames, cam_k, cam_v, chunk, out, lse=None, stream=None):
+    """Cross-attention of the video queries q [n_frames * P, H, 128] to the
+    camera tokens cam_k, cam_v [n_cam, kv_heads, 128] (kv_heads 1 or H):
+    latent frame t sees the tokens of its chunk of `chunk` frames."""
+    g = geom.c()
+    _check(lib().sa_camera_attention(ctypes.byref(g), _ptr(q), n_frames, _ptr(cam_k), _ptr(cam_v),
+                                     cam_k.shape[0], cam_k.shape[1], chunk, _ptr(out), _ptr(lse),
+                                     _stream(stream)))
 
 
 def kv_dequant(geom, src, d_frames, n_frames, n_text, dst, stream=None):

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libsegattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["host.cpp", "kv_append.hip", "attention_bf16.hip", "attention_fp8.hip", "attention_combine.hip",
-           "gather.hip", "sparse_select.hip"]
+           "gather.hip", "sparse_select.hip", "camera.hip"]
 
 # Packed-fp32 VALU forms are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -601,6 +601,43 @@ sa_status sa_sparse_select(const sa_geom* geom, const sa_attn_item* item, void* 
   return hip_status(launch_sparse_select(a, static_cast<hipStream_t>(stream)), "sparse_select launch");
 }
 
+sa_status sa_camera_attention(const sa_geom* geom, const void* q, int32_t n_frames,
+                              const void* cam_k, const void* cam_v, int32_t n_cam,
+                              int32_t kv_heads, int32_t chunk, void* out, float* lse,
+                              void* stream) {
+  sa_status st = check_geom(geom);
+  if (st != SA_OK) return st;
+  if (n_frames < 1) return fail(SA_E_ARG, "camera_attention: n_frames %d < 1", n_frames);
+  if (chunk < 1 || chunk > SA_MAX_CAMERA_CHUNK)
+    return fail(SA_E_ARG, "camera_attention: chunk %d outside [1, %d]", chunk, SA_MAX_CAMERA_CHUNK);
+  if (n_cam < n_frames)
+    return fail(SA_E_ARG, "camera_attention: %d camera tokens for %d frames", n_cam, n_frames);
+  if (kv_heads != 1 && kv_heads != geom->heads)
+    return fail(SA_E_ARG, "camera_attention: kv_heads %d is neither 1 nor %d", kv_heads, geom->heads);
+  if (q == nullptr || cam_k == nullptr || cam_v == nullptr || out == nullptr)
+    return fail(SA_E_ARG, "camera_attention: NULL pointer");
+  if (!aligned16(q) || !aligned16(cam_k) || !aligned16(cam_v) || !aligned16(out))
+    return fail(SA_E_ALIGN, "camera_attention: pointers not 16-byte aligned");
+  const int64_t rows = static_cast<int64_t>(n_frames) * tokens_per_frame(geom);
+  if (rows * geom->heads > (int64_t(1) << 31) - 16)
+    return fail(SA_E_SHAPE, "camera_attention: too many rows");
+  CameraArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.cam_k = static_cast<const uint16_t*>(cam_k);
+  a.cam_v = static_cast<const uint16_t*>(cam_v);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.rows = static_cast<int32_t>(rows);
+  a.heads = geom->heads;
+  a.kv_heads = kv_heads;
+  a.P = tokens_per_frame(geom);
+  a.n_cam = n_cam;
+  a.chunk = chunk;
+  const double scale = geom->softmax_scale > 0.f ? geom->softmax_scale : 1.0 / std::sqrt(128.0);
+  a.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
+  return hip_status(launch_camera(a, static_cast<hipStream_t>(stream)), "camera_attention launch");
+}
+
 sa_status sa_kv_dequant(const sa_geom* geom, const sa_kv_layer* src, const int32_t* d_frames,
                         int32_t n_frames, int32_t n_text, const sa_kv_layer* dst, void* stream) {
   sa_status st = check_geom(geom);

@@ -120,6 +120,23 @@ hipError_t launch_attention_combine(const AttnArgs& a, int block_m, hipStream_t 
 int attention_block_m_bf16();
 int attention_block_m_fp8();
 
+// ---- camera cross-attention ------------------------------------------------------
+struct CameraArgs {
+  const uint16_t* q;       // bf16 [rows][H][128]
+  const uint16_t* cam_k;   // bf16 [n_cam][kv_heads][128]
+  const uint16_t* cam_v;
+  uint16_t* out;           // bf16 [rows][H][128]
+  float* lse;              // optional fp32 [rows][H]
+  int32_t rows;            // n_frames * P
+  int32_t heads;
+  int32_t kv_heads;        // 1 or heads
+  int32_t P;
+  int32_t n_cam;
+  int32_t chunk;
+  float scale_log2;        // softmax scale * log2(e)
+};
+hipError_t launch_camera(const CameraArgs& a, hipStream_t s);
+
 // ---- gather / dequant -----------------------------------------------------------
 struct GatherArgs {
   const void* src_k;

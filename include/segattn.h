@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 4
+#define SA_ABI_VERSION 5
 #define SA_HEAD_DIM 128       /* the only head dim the kernels are built for */
 #define SA_MAX_ITEMS 8        /* sessions per sa_segment_attention call     */
 #define SA_MAX_FRAMES_KV 65536
@@ -54,6 +54,7 @@ extern "C" {
 #define SA_SPARSE_KEY_BLOCK 64       /* keys per candidate history block          */
 #define SA_SPARSE_QUERY_BLOCK 256    /* query rows that share one block list      */
 #define SA_MAX_SPARSE_CANDIDATES 8192 /* candidate blocks sa_sparse_select ranks  */
+#define SA_MAX_CAMERA_CHUNK 16       /* latent frames per camera chunk            */
 
 typedef enum {
   SA_OK = 0,
@@ -281,6 +282,26 @@ sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, i
 size_t sa_sparse_select_workspace(const sa_geom* geom, const sa_attn_item* item);
 sa_status sa_sparse_select(const sa_geom* geom, const sa_attn_item* item, void* workspace,
                            size_t workspace_bytes, int32_t* block_list, void* stream);
+
+/* camera_attention: cross-attention of the segment's video tokens to the
+ * camera tokens, one per latent frame ("Hy-Nomas: an 8.6B world model ...",
+ * section "The camera": a small cross-attention after each block; with chunk
+ * size 1 the mask is block-diagonal, latent frame t attends only to its own
+ * camera token; the camera key/value projection is 2,048 x 128).
+ *   q        bf16 [n_frames * P][H][128] video queries, (t, h, w) raster order
+ *            (no rotary embedding)
+ *   cam_k, cam_v  bf16 [n_cam][kv_heads][128]; kv_heads = 1 (one head shared
+ *            by every query head) or H; token i belongs to latent frame i
+ *   out      bf16 like q;  lse  optional fp32 [n_frames * P][H] (NULL: skip)
+ * Rows of latent frame t attend to camera tokens c * floor(t / c) ..
+ * min(n_cam, c * floor(t / c) + c) - 1, c = chunk, softmax scale from geom.
+ * Pointers 16-byte aligned. Errors: SA_E_ARG (n_frames < 1, chunk outside
+ * [1, SA_MAX_CAMERA_CHUNK], n_cam < n_frames, kv_heads not 1 or H, NULL
+ * pointers), SA_E_ALIGN.                                                    */
+sa_status sa_camera_attention(const sa_geom* geom, const void* q, int32_t n_frames,
+                              const void* cam_k, const void* cam_v, int32_t n_cam,
+                              int32_t kv_heads, int32_t chunk, void* out, float* lse,
+                              void* stream);
 
 /* kv_dequant: fp8 frames[i] of src -> bf16 frame slot i of dst (K and V
  * planes: value = code * scale, rounded to bf16), and, when n_text > 0, the

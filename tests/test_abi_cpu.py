@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 4
+    assert sa.abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -242,6 +242,24 @@ def test_sparse_validation(lib):
     assert ws(ctypes.byref(g), ctypes.byref(sp(_item(big, n_frames_kv=8200), nh=8193))) == 0
     assert b"candidate blocks" in lib.sa_last_error()
     assert sel(ctypes.byref(g), None, ctypes.c_void_p(FAKE), 4096, ctypes.c_void_p(FAKE), None) == 1
+
+
+def test_camera_validation(lib):
+    g = _geom()
+    f = lib.sa_camera_attention
+    ok = dict(q=FAKE, n=2, k=FAKE, v=FAKE, nc=2, hk=1, c=1, o=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(ctypes.byref(g), ctypes.c_void_p(a["q"]), a["n"], ctypes.c_void_p(a["k"]),
+                 ctypes.c_void_p(a["v"]), a["nc"], a["hk"], a["c"], ctypes.c_void_p(a["o"]), None,
+                 None)
+    assert call(n=0) == 1
+    assert call(c=0) == 1 and call(c=17) == 1
+    assert call(nc=1) == 1                      # fewer camera tokens than frames
+    assert call(hk=3) == 1                      # neither 1 nor H = 2
+    assert call(q=0) == 1
+    assert call(o=FAKE + 8) == 3
 
 
 def test_attention_workspace_query_without_split(lib):
