@@ -20,6 +20,10 @@ with H heads, D = head_dim, P = lat_h * lat_w tokens per latent frame:
 * fp8 (e4m3fn) planes use the same shapes with one byte per element, plus
   fp32 scales k_scale/v_scale [frame_capacity][H] and k_text_scale /
   v_text_scale [H].
+* int8 planes (the pages' single-GPU format) use the same shapes with one
+  signed byte per element, plus fp32 scales per token and head:
+  k_scale/v_scale [frame_capacity][H][P] and k_text_scale / v_text_scale
+  [H][text_capacity].
 
 Stored values. K is rotated by the 3D RoPE at its absolute position (frame f
 for video token p of frame f; (0, 0, 0) for text) and rounded to the cache
@@ -28,6 +32,11 @@ the text slot) = amax / 448 over that plane's values, computed in fp32
 (amax == 0 gives scale 1); codes = e4m3 round-nearest-even of
 x * (448 / amax) evaluated in fp32 and saturated, so that the quantisation
 decision is taken in the same precision as the kernel's.
+int8 scale per (token, head) = amax / 127 over that token's head_dim values
+in fp32 (amax == 0 gives scale 1); code = round-half-even of
+x * (127 / amax) evaluated in fp32, clamped to [-127, 127] (symmetric: -128
+is never used). The pages give the granularity and the byte count, not the
+rounding; this is the plainest symmetric reading.
 """
 
 import numpy as np
@@ -57,14 +66,16 @@ def bytes_per_token_per_layer(fmt, heads=16, head_dim=128):
 def plane_bytes(dtype, heads, head_dim, P, frame_capacity, text_capacity):
     """Bytes of one layer's cache planes in this library's layout.
 
-    dtype 'bf16' or 'fp8' (fp8 adds fp32 scales per (frame, head) and per
-    head for the text slot, for K and V).
+    dtype 'bf16', 'fp8' (fp32 scales per (frame, head) and per head for the
+    text slot, for K and V) or 'int8' (fp32 scales per token and head).
     """
     elems = 2 * heads * head_dim * (frame_capacity * P + text_capacity)
     if dtype == "bf16":
         return 2 * elems
     if dtype == "fp8":
         return elems + 2 * 4 * heads * (frame_capacity + 1)
+    if dtype == "int8":
+        return elems + 2 * 4 * heads * (frame_capacity * P + text_capacity)
     raise ValueError(dtype)
 
 
@@ -179,3 +190,60 @@ def append_text_fp8(k_in, v_in):
 def dequant(codes, scale):
     """Real value of fp8 codes times their plane scale (float64)."""
     return numerics.e4m3_decode(codes) * np.float64(scale)
+
+
+# ------------------------------------------------------ expected append (int8)
+INT8_MAX = 127
+
+
+def quantize_token_int8(x):
+    """Quantise vectors (last axis: one token's head_dim values) to int8.
+
+    Returns (codes int8 same shape, scale float32 [...]). In fp32: amax over
+    the vector, scale = amax / 127, inv = 127 / amax (both 1 when amax is 0),
+    code = rint(x * inv) clamped to [-127, 127]."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x32).max(axis=-1)
+    nz = amax > 0
+    safe = np.where(nz, amax, np.float32(1)).astype(np.float32)
+    scale = np.where(nz, safe / np.float32(INT8_MAX), np.float32(1)).astype(np.float32)
+    inv = np.where(nz, np.float32(INT8_MAX) / safe, np.float32(1)).astype(np.float32)
+    y = (x32 * inv[..., None]).astype(np.float32)
+    codes = np.clip(np.rint(y), -INT8_MAX, INT8_MAX).astype(np.int8)
+    return codes, scale
+
+
+def append_int8(k_in, v_in, frame0, lat_h, lat_w, split, theta):
+    """Expected int8 planes and per-token scales for frames [frame0, frame0+F).
+
+    As for fp8, K is rotated in exact arithmetic and quantised from its
+    float32 rounding (the kernel rotates in float32: a K code may differ by
+    one step near a rounding boundary); V codes and scales are fully
+    determined. Returns (Kc [F,H,P,D] i8, Ks [F,H,P] f32, Vc [F,H,D,P] i8,
+    Vs [F,H,P] f32)."""
+    k_in = np.asarray(k_in, dtype=np.float64)
+    v_in = np.asarray(v_in, dtype=np.float64)
+    P = lat_h * lat_w
+    n, H, D = k_in.shape
+    F = n // P
+    pos = video_positions(frame0, F, lat_h, lat_w)
+    kr = rope3d(k_in, pos, split, theta).reshape(F, P, H, D).transpose(0, 2, 1, 3)
+    kc, ks = quantize_token_int8(kr)
+    vt = v_in.reshape(F, P, H, D).transpose(0, 2, 1, 3)            # [F, H, P, D]
+    vc, vs = quantize_token_int8(vt)
+    return kc, ks, np.ascontiguousarray(vc.transpose(0, 1, 3, 2)), vs
+
+
+def append_text_int8(k_in, v_in):
+    """Expected int8 text slot: (Kc [H,n,D], Ks [H,n], Vc [H,D,n], Vs [H,n])."""
+    k_in = np.asarray(k_in, dtype=np.float64)
+    v_in = np.asarray(v_in, dtype=np.float64)
+    kc, ks = quantize_token_int8(k_in.transpose(1, 0, 2))
+    vc, vs = quantize_token_int8(v_in.transpose(1, 0, 2))
+    return kc, ks, np.ascontiguousarray(vc.transpose(0, 2, 1)), vs
+
+
+def dequant_int8(codes, scale):
+    """Real value of int8 codes times their per-token scale (float64); scale
+    broadcasts over the codes' token axis as the caller arranges."""
+    return np.asarray(codes, dtype=np.float64) * np.asarray(scale, dtype=np.float64)

@@ -143,3 +143,72 @@ def test_append_fp8_v_codes_follow_fp32_decision():
     dk = cache.dequant(Kc[0, 0], Ks[0, 0])
     kr = rope.rope3d(k[:P], rope.video_positions(3, 1, lat_h, lat_w))[:, 0, :]
     assert np.max(np.abs(dk - kr)) <= np.abs(kr).max() * 2.0 ** -4
+
+
+# ------------------------------------------------------------------- int8 cache
+def test_int8_plane_bytes_per_token_match_page():
+    """The library's int8 layout spends exactly the page's 4,224 bytes per
+    token per layer on frames (one byte per value, an fp32 scale per token
+    and head, for K and V)."""
+    g = FIG["token_grid"]
+    H, D, P = g["heads"], g["head_dim"], g["tokens_per_frame"]
+    one = cache.plane_bytes("int8", H, D, P, 1, 0)
+    assert one == P * FIG["int8_cache"]["bytes_per_token_per_layer"]
+    assert cache.plane_bytes("int8", H, D, P, 3, 32) == (3 * P + 32) * 4224
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def test_int8_quantize_closed_forms():
+    x = _rng(1).standard_normal((50, 128)).astype(np.float32) * 3
+    codes, scale = cache.quantize_token_int8(x)
+    assert codes.dtype == np.int8 and scale.dtype == np.float32
+    assert codes.min() >= -127 and codes.max() <= 127
+    # the largest magnitude of every vector maps to +-127
+    i = np.abs(x).argmax(axis=1)
+    assert np.all(np.abs(codes[np.arange(50), i]) == 127)
+    assert np.all(np.sign(codes[np.arange(50), i]) == np.sign(x[np.arange(50), i]))
+    # scale is amax / 127
+    np.testing.assert_allclose(scale, np.abs(x).max(axis=1) / 127.0, rtol=1e-7)
+    # a zero vector: scale 1, codes 0
+    z, zs = cache.quantize_token_int8(np.zeros((2, 128)))
+    assert np.all(z == 0) and np.all(zs == 1)
+
+
+def test_int8_codes_are_nearest():
+    """Each code is the integer nearest x / scale (brute force over the 255
+    codes), except within fp32 rounding of a half-way point."""
+    x = _rng(2).standard_normal((40, 128)) * 0.7
+    codes, scale = cache.quantize_token_int8(x)
+    cand = np.arange(-127, 128, dtype=np.float64)
+    for r in range(40):
+        t = x[r] / float(scale[r])
+        best = cand[np.abs(cand[None, :] - t[:, None]).argmin(axis=1)]
+        off = codes[r] != best
+        assert np.all(np.abs(np.abs(t[off] - np.floor(t[off])) - 0.5) < 1e-4)
+    err = np.abs(cache.dequant_int8(codes, scale[:, None]) - x)
+    assert np.all(err <= 0.5 * scale[:, None] * (1 + 1e-5))
+
+
+def test_int8_append_round_trip():
+    """Expected planes: K rotated (inverse rotation of the dequantised plane
+    returns k within half a step), V transposed per token, scales per token."""
+    from oracle.rope import rope3d, video_positions
+    F, lh, lw, H, D = 2, 2, 3, 2, 128
+    P = lh * lw
+    k = _rng(3).standard_normal((F * P, H, D))
+    v = _rng(4).standard_normal((F * P, H, D))
+    kc, ks, vc, vs = cache.append_int8(k, v, 5, lh, lw, (16, 56, 56), 256.0)
+    assert kc.shape == (F, H, P, D) and ks.shape == (F, H, P)
+    assert vc.shape == (F, H, D, P) and vs.shape == (F, H, P)
+    kr = rope3d(k, video_positions(5, F, lh, lw), (16, 56, 56), 256.0)
+    kd = cache.dequant_int8(kc, ks[..., None]).transpose(0, 2, 1, 3).reshape(F * P, H, D)
+    kstep = ks.transpose(0, 2, 1).reshape(F * P, H)[..., None]
+    assert np.all(np.abs(kd - kr) <= 0.5 * kstep * 1.0001 + 1e-7)
+    vd = cache.dequant_int8(vc, vs[:, :, None, :]).transpose(0, 3, 1, 2).reshape(F * P, H, D)
+    assert np.all(np.abs(vd - v) <= 0.5 * vs.transpose(0, 2, 1).reshape(F * P, H)[..., None] * 1.0001)
+    tk, tks, tv, tvs = cache.append_text_int8(k[:5], v[:5])
+    assert tk.shape == (H, 5, D) and tks.shape == (H, 5) and tv.shape == (H, D, 5)
+    np.testing.assert_array_equal(tk, cache.quantize_token_int8(k[:5].transpose(1, 0, 2))[0])
