@@ -422,7 +422,11 @@ def main():
     torch.cuda.synchronize()
     app_ms = e0.elapsed_time(e1) / reps
     tok = wl.lat_t * wl.P * wl.heads
-    app_bytes = tok * (2 * 256 + (2 * 256 if dtype == "bf16" else 2 * 128))
+    # reads 2 x 256 B of bf16 input per token and head; writes 2 x 256 B (bf16),
+    # 2 x 128 B (e4m3; the per-plane scales are negligible) or 2 x (128 + 4) B
+    # (int8 codes and their per-token scales)
+    wr = {"bf16": 2 * 256, "fp8": 2 * 128, "int8": 2 * (128 + 4)}[wl.kv_dtype]
+    app_bytes = tok * (2 * 256 + wr)
     line = {
         "metric": METRIC,
         "value": round(value, 2),

@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("SEGATTN_LIBRARY", os.path.join(_PKG, "libsegattn.so")
 SA_OK = 0
 STATUS_NAMES = {0: "SA_OK", 1: "SA_E_ARG", 2: "SA_E_SHAPE", 3: "SA_E_ALIGN",
                 4: "SA_E_UNSUPPORTED", 5: "SA_E_RANGE", 6: "SA_E_CAPACITY", 7: "SA_E_HIP"}
-KV_BF16, KV_FP8 = 0, 1
+KV_BF16, KV_FP8, KV_INT8 = 0, 1, 2
 SEL_ALL, SEL_RECENT, SEL_POWER, SEL_ANCHOR_RECENT = 0, 1, 2, 3
 MAX_ITEMS = 8
 HEAD_DIM = 128
@@ -169,18 +169,23 @@ class KVLayer:
     @classmethod
     def allocate(cls, geom, dtype, frame_capacity, text_capacity, device="cuda"):
         H, P, D = geom.heads, geom.P, geom.head_dim
-        et = torch.bfloat16 if dtype == KV_BF16 else torch.uint8
+        et = {KV_BF16: torch.bfloat16, KV_FP8: torch.uint8, KV_INT8: torch.int8}[dtype]
         kw = dict(device=device, dtype=et)
         k = torch.empty((frame_capacity, H, P, D), **kw)
         v = torch.empty((frame_capacity, H, D, P), **kw)
         kt = torch.empty((H, text_capacity, D), **kw)
         vt = torch.zeros((H, D, text_capacity), **kw)
         sc = {}
+        f32 = dict(device=device, dtype=torch.float32)
         if dtype == KV_FP8:
-            f32 = dict(device=device, dtype=torch.float32)
             sc = dict(k_scale=torch.ones((frame_capacity, H), **f32),
                       v_scale=torch.ones((frame_capacity, H), **f32),
                       k_text_scale=torch.ones((H,), **f32), v_text_scale=torch.ones((H,), **f32))
+        elif dtype == KV_INT8:     # a scale per token and head
+            sc = dict(k_scale=torch.ones((frame_capacity, H, P), **f32),
+                      v_scale=torch.ones((frame_capacity, H, P), **f32),
+                      k_text_scale=torch.zeros((H, text_capacity), **f32),
+                      v_text_scale=torch.zeros((H, text_capacity), **f32))
         return cls(dtype, k, v, kt, vt, **sc)
 
     def c(self):

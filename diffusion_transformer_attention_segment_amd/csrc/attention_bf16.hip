@@ -95,6 +95,96 @@ __device__ __forceinline__ void store_tile(uint16_t* Ks, uint16_t* Vs, int tid, 
   }
 }
 
+// ---- int8 cache (a scale per token and head): tiles are dequantised to bf16
+// while staged in registers, so the LDS tiles and everything after them are
+// those of the bf16 cache. Thread tid stages the 16 K codes of key row
+// tid >> 3 (dims 16 (tid & 7) ..) with that key's scale, and a 4 x 4 block of
+// V^T codes (dim rows 4 (tid >> 4) .. +3, keys 4 (tid & 15) .. +3, one
+// 4-byte load per row) with those keys' scales: 13 registers in flight, fewer
+// than a bf16 tile's 16. Scales of keys past the valid count read as zero.
+struct StagedInt8 {
+  u32x4 k;
+  float ks;
+  uint32_t v[4];
+  float vs[4];
+};
+
+struct StagedBf16 {
+  u32x4 k[kKChunks];
+  u32x4 v[kVChunks];
+};
+
+__device__ __forceinline__ void load_tile_int8(const TileCursor& c, int tid, StagedInt8& st) {
+  const __amdgpu_buffer_rsrc_t rk = tile_k_rsrc<kCkInt8>(c);
+  const __amdgpu_buffer_rsrc_t rv = tile_v_rsrc<kCkInt8>(c);
+  const __amdgpu_buffer_rsrc_t rks = tile_scale_rsrc(c.kst, c);
+  const __amdgpu_buffer_rsrc_t rvs = tile_scale_rsrc(c.vst, c);
+  const int krow = tid >> 3, kq = tid & 15, dg = tid >> 4;
+  st.k = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       rk, static_cast<uint32_t>(tid) * 16u, 0, 0));
+  st.ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, krow * 4, 0, 0));
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    st.v[r] = __builtin_amdgcn_raw_buffer_load_b32(rv, (4 * dg + r) * c.vstride + 4 * kq, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    st.vs[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, (4 * kq + i) * 4, 0, 0));
+}
+
+// byte b of w as a signed code, times s
+__device__ __forceinline__ float dq(uint32_t w, int b, float s) {
+  return static_cast<float>(static_cast<int8_t>(w >> (8 * b))) * s;
+}
+
+__device__ __forceinline__ void store_tile_int8(uint16_t* Ks, uint16_t* Vs, int tid,
+                                                const StagedInt8& st) {
+  const int krow = tid >> 3, kc = tid & 7, kq = tid & 15, dg = tid >> 4;
+  u32x4 lo, hi;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t w = st.k[m];
+    const uint32_t a = pack_bf16x2(dq(w, 0, st.ks), dq(w, 1, st.ks));
+    const uint32_t b = pack_bf16x2(dq(w, 2, st.ks), dq(w, 3, st.ks));
+    if (m < 2) {
+      lo[2 * m] = a;
+      lo[2 * m + 1] = b;
+    } else {
+      hi[2 * m - 4] = a;
+      hi[2 * m - 3] = b;
+    }
+  }
+  *reinterpret_cast<u32x4*>(&Ks[krow * KS + kc * 16]) = lo;
+  *reinterpret_cast<u32x4*>(&Ks[krow * KS + kc * 16 + 8]) = hi;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    u32x2 o;
+    o[0] = pack_bf16x2(dq(st.v[r], 0, st.vs[0]), dq(st.v[r], 1, st.vs[1]));
+    o[1] = pack_bf16x2(dq(st.v[r], 2, st.vs[2]), dq(st.v[r], 3, st.vs[3]));
+    *reinterpret_cast<u32x2*>(&Vs[(4 * dg + r) * VS + 4 * kq]) = o;
+  }
+}
+
+template <bool kInt8>
+using Staged = typename std::conditional<kInt8, StagedInt8, StagedBf16>::type;
+
+template <bool kInt8>
+__device__ __forceinline__ void stage_load(const TileCursor& c, uint32_t koff, int tid,
+                                           Staged<kInt8>& st) {
+  if constexpr (kInt8)
+    load_tile_int8(c, tid, st);
+  else
+    load_tile(c, koff, st.k, st.v);
+}
+
+template <bool kInt8>
+__device__ __forceinline__ void stage_store(uint16_t* Ks, uint16_t* Vs, int tid,
+                                            const Staged<kInt8>& st) {
+  if constexpr (kInt8)
+    store_tile_int8(Ks, Vs, tid, st);
+  else
+    store_tile(Ks, Vs, tid, st.k, st.v);
+}
+
 // l + lo(a) * lo(b) + hi(a) * hi(b) for packed bf16 pairs, fp32 accumulate.
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float l) {
   typedef short s16x2 __attribute__((ext_vector_type(2)));
@@ -255,8 +345,9 @@ __device__ __forceinline__ f32x16 qk_block(const uint16_t* kp, const bf16x8* qf)
   return s;
 }
 
-template <bool kSparse>
+template <bool kSparse, bool kInt8>
 __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a) {
+  constexpr int CK = kInt8 ? kCkInt8 : kCkBf16;   // cache kind of the key-tile walk
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kStages * KT];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[kStages * VT];
   __shared__ double om[kD / 2];
@@ -349,28 +440,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     // the load cursor runs three tiles ahead of the compute tile; nv0..nv2
     // keep the valid-key counts of the tiles in between
     TileCursor lc;
-    seq_start<kSparse, 2>(lc, I, h, H, P, seq, kt0);
-    u32x4 kr[kKChunks], vr[kVChunks];
+    seq_start<kSparse, CK>(lc, I, h, H, P, seq, kt0);
+    Staged<kInt8> stg;
     int nv0 = cursor_mask_code(lc, flag_fi);
-    load_tile(lc, koff_ld, kr, vr);
+    stage_load<kInt8>(lc, koff_ld, tid, stg);
     // the last V stage is read once with zero probabilities before it is
     // first written: give it finite contents
     for (int i = tid; i < VT / 8; i += kThreads)
       reinterpret_cast<u32x4*>(Vs + (kStages - 1) * VT)[i] = u32x4{0u, 0u, 0u, 0u};
 
     // ---- prologue: tiles 0, 1 into LDS stages 0, 1; tile 2 in flight ----------
-    store_tile(Ks, Vs, tid, kr, vr);
+    stage_store<kInt8>(Ks, Vs, tid, stg);
     int nv1 = 0, nv2 = 0;
     if (ntiles > 1) {
-      seq_next<kSparse, 2>(lc, I, h, H, P, seq, kt0 + 1);
+      seq_next<kSparse, CK>(lc, I, h, H, P, seq, kt0 + 1);
       nv1 = cursor_mask_code(lc, flag_fi);
-      load_tile(lc, koff_ld, kr, vr);
-      store_tile(Ks + KT, Vs + VT, tid, kr, vr);
+      stage_load<kInt8>(lc, koff_ld, tid, stg);
+      stage_store<kInt8>(Ks + KT, Vs + VT, tid, stg);
     }
     if (ntiles > 2) {
-      seq_next<kSparse, 2>(lc, I, h, H, P, seq, kt0 + 2);
+      seq_next<kSparse, CK>(lc, I, h, H, P, seq, kt0 + 2);
       nv2 = cursor_mask_code(lc, flag_fi);
-      load_tile(lc, koff_ld, kr, vr);
+      stage_load<kInt8>(lc, koff_ld, tid, stg);
     }
     __syncthreads();
 
@@ -425,11 +516,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
         asm volatile("" ::: "memory");
         if (t + 2 < ntiles) {
           const int s2 = (t + 2) & (kStages - 1);
-          store_tile(Ks + s2 * KT, Vs + s2 * VT, tid, kr, vr);
+          stage_store<kInt8>(Ks + s2 * KT, Vs + s2 * VT, tid, stg);
           if (t + 3 < ntiles) {
-            seq_next<kSparse, 2>(lc, I, h, H, P, seq, kt0 + t + 3);
+            seq_next<kSparse, CK>(lc, I, h, H, P, seq, kt0 + t + 3);
             nv3 = cursor_mask_code(lc, flag_fi);
-            load_tile(lc, koff_ld, kr, vr);
+            stage_load<kInt8>(lc, koff_ld, tid, stg);
           }
         }
       };
@@ -516,10 +607,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
 int attention_block_m_bf16() { return BM; }
 
 hipError_t launch_attention_bf16(AttnArgs& a, hipStream_t s) {
-  if (a.any_sparse)
-    hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(a.grid), dim3(kThreads), 0, s, a);
+  const dim3 g(a.grid), b(kThreads);
+  if (a.int8 && a.any_sparse)
+    hipLaunchKernelGGL((attn_bf16_kernel<true, true>), g, b, 0, s, a);
+  else if (a.int8)
+    hipLaunchKernelGGL((attn_bf16_kernel<false, true>), g, b, 0, s, a);
+  else if (a.any_sparse)
+    hipLaunchKernelGGL((attn_bf16_kernel<true, false>), g, b, 0, s, a);
   else
-    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(a.grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<false, false>), g, b, 0, s, a);
   return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@ __device__ __forceinline__ WorkTile map_workgroup(const AttnArgs& a, int block_m
 
 // Scalar walk over the key tiles of one (item, head): video frames in list
 // order (ceil(P / 64) tiles each, never straddling a frame), then the text
-// slot. Everything here is wave-uniform. ESZ is the cache element size.
+// slot. Everything here is wave-uniform. ESZ is the cache kind (below).
 // Frame-list entries are read with scalar loads through the constant address
 // space (the list is written before the launch and never during it).
 typedef const __attribute__((address_space(4))) int* const_int_ptr;
@@ -86,7 +86,18 @@ struct TileCursor {
   int vstride;          // tokens per V^T row of the plane (P or text capacity)
   float kscale;         // fp8 planes: the segment's K and V scales (1 for bf16)
   float vscale;
+  const float* kst;     // int8 planes: the segment's per-token K and V scales
+  const float* vst;
 };
+
+// Cache kinds, the template argument ESZ of the key-tile walk: bf16 (2 bytes
+// an element), e4m3 with a scale per (frame, head) plane (1 byte), int8 with a
+// scale per token and head (1 byte).
+constexpr int kCkBf16 = 2, kCkFp8 = 1, kCkInt8 = 3;
+template <int ESZ>
+__device__ __forceinline__ constexpr int elem_bytes() {
+  return ESZ == kCkBf16 ? 2 : 1;
+}
 
 template <int ESZ>
 __device__ __forceinline__ void cursor_enter(TileCursor& c, const AttnItemDev& I, int h, int H,
@@ -97,24 +108,33 @@ __device__ __forceinline__ void cursor_enter(TileCursor& c, const AttnItemDev& I
   if (c.fi < I.n_frames_kv) {
     const int frame = c.fnext;
     if (c.fi + 1 < I.n_frames_kv) c.fnext = frame_entry(I, c.fi + 1);   // one frame ahead
-    const size_t plane = (static_cast<size_t>(frame) * H + h) * static_cast<size_t>(P) * kD * ESZ;
+    const size_t pl = static_cast<size_t>(frame) * H + h;
+    const size_t plane = pl * static_cast<size_t>(P) * kD * elem_bytes<ESZ>();
     c.kplane = static_cast<const char*>(I.k) + plane;
     c.vplane = static_cast<const char*>(I.v) + plane;
     c.len = P;
     c.vstride = P;
-    if (ESZ == 1) {
-      c.kscale = scalar_load(I.k_scale, static_cast<size_t>(frame) * H + h);
-      c.vscale = scalar_load(I.v_scale, static_cast<size_t>(frame) * H + h);
+    if (ESZ == kCkFp8) {
+      c.kscale = scalar_load(I.k_scale, pl);
+      c.vscale = scalar_load(I.v_scale, pl);
+    }
+    if (ESZ == kCkInt8) {
+      c.kst = I.k_scale + pl * P;
+      c.vst = I.v_scale + pl * P;
     }
   } else {
-    const size_t plane = static_cast<size_t>(h) * I.text_cap * kD * ESZ;
+    const size_t plane = static_cast<size_t>(h) * I.text_cap * kD * elem_bytes<ESZ>();
     c.kplane = static_cast<const char*>(I.k_text) + plane;
     c.vplane = static_cast<const char*>(I.v_text) + plane;
     c.len = I.n_text_kv;
     c.vstride = I.text_cap;
-    if (ESZ == 1 && I.n_text_kv > 0) {
+    if (ESZ == kCkFp8 && I.n_text_kv > 0) {
       c.kscale = scalar_load(I.k_text_scale, h);
       c.vscale = scalar_load(I.v_text_scale, h);
+    }
+    if (ESZ == kCkInt8) {
+      c.kst = I.k_text_scale + static_cast<size_t>(h) * I.text_cap;
+      c.vst = I.v_text_scale + static_cast<size_t>(h) * I.text_cap;
     }
   }
 }
@@ -273,15 +293,23 @@ __device__ __forceinline__ int tile_count(int code) { return code & ~kWindowFlag
 template <int ESZ>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_k_rsrc(const TileCursor& c) {
   return __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(c.kplane + static_cast<size_t>(c.p0) * kD * ESZ), static_cast<short>(0),
-      cursor_nvalid(c) * kD * ESZ, kRsrcFlags);
+      const_cast<char*>(c.kplane + static_cast<size_t>(c.p0) * kD * elem_bytes<ESZ>()),
+      static_cast<short>(0), cursor_nvalid(c) * kD * elem_bytes<ESZ>(), kRsrcFlags);
 }
 
 template <int ESZ>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_v_rsrc(const TileCursor& c) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(c.vplane + c.p0 * ESZ),
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(c.vplane + c.p0 * elem_bytes<ESZ>()),
                                            static_cast<short>(0),
-                                           (c.vstride * kD - c.p0) * ESZ, kRsrcFlags);
+                                           (c.vstride * kD - c.p0) * elem_bytes<ESZ>(), kRsrcFlags);
+}
+
+// int8 planes: the per-token K / V scales of the tile's valid keys (scales of
+// keys past the valid count read as zero)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_scale_rsrc(const float* st,
+                                                                 const TileCursor& c) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(st + c.p0), static_cast<short>(0),
+                                           cursor_nvalid(c) * 4, kRsrcFlags);
 }
 
 // Direct-to-LDS tile loads. A stage is ROWS rows of SLOTS 16-byte slots (the

@@ -1,4 +1,5 @@
-// history_gather (materialising frame gather) and kv_dequant (e4m3 -> bf16).
+// history_gather (materialising frame gather) and kv_dequant (e4m3 or int8
+// -> bf16).
 //
 // Source: "Hy-Nomas: an 8.6B world model whose memory is a KV cache",
 // section "The 4090 preset": before each segment the picked past frames are
@@ -38,11 +39,14 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(const GatherArgs
     const int64_t c = base + threadIdx.x + j * kGatherThreads;
     if (c < n16) __builtin_nontemporal_store(x[j], reinterpret_cast<u32x4*>(dst) + c);
   }
-  if (a.src_ks != nullptr && blockIdx.x == 0 && threadIdx.x < a.heads) {
-    const float* ss = which ? a.src_vs : a.src_ks;
-    float* ds = which ? a.dst_vs : a.dst_ks;
-    ds[static_cast<int64_t>(i) * a.heads + threadIdx.x] =
-        ss[static_cast<int64_t>(frame) * a.heads + threadIdx.x];
+  // the frame's scales (fp8: one per head; int8: one per token and head),
+  // spread over the frame's blocks
+  if (a.src_ks != nullptr) {
+    const float* ss = (which ? a.src_vs : a.src_ks) + static_cast<int64_t>(frame) * a.scale_floats;
+    float* ds = (which ? a.dst_vs : a.dst_ks) + static_cast<int64_t>(i) * a.scale_floats;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * kGatherThreads + threadIdx.x;
+         e < a.scale_floats; e += static_cast<int64_t>(gridDim.x) * kGatherThreads)
+      ds[e] = ss[e];
   }
 }
 
@@ -110,6 +114,44 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
   }
 }
 
+// int8 planes with a scale per token and head -> bf16 (code * scale, rounded).
+// Same grid and chunking as dequant_kernel: a K chunk is 16 dims of one token
+// (one scale), a V^T chunk 16 tokens of one dim row (16 scales).
+__global__ __launch_bounds__(256) void dequant_int8_kernel(const DequantArgs a) {
+  const int i = blockIdx.y;
+  const int h = blockIdx.z >> 1;
+  const int which = blockIdx.z & 1;
+  const int frame = a.frames != nullptr ? a.frames[i] : 0;
+  const int64_t pl = static_cast<int64_t>(frame) * a.heads + h;
+  const int8_t* src = reinterpret_cast<const int8_t*>(which ? a.src_v : a.src_k) + pl * a.src_len * kD;
+  const float* sc = (which ? a.src_vs : a.src_ks) + pl * a.src_len;
+  uint16_t* dst = (which ? a.dst_v : a.dst_k) +
+                  (static_cast<int64_t>(i) * a.heads + h) * a.dst_len * kD;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  int row, col, src_row_len, dst_row_len, row_valid, rows;
+  if (which == 0) {
+    rows = a.n_tok; row = c >> 3; col = (c & 7) * 16;
+    src_row_len = kD; dst_row_len = kD; row_valid = kD;
+  } else {
+    const int cpr = (a.n_tok + 15) / 16;
+    rows = kD; row = c / cpr; col = (c - row * cpr) * 16;
+    src_row_len = a.src_len; dst_row_len = a.dst_len; row_valid = a.n_tok;
+  }
+  if (row >= rows) return;
+  const int8_t* s = src + static_cast<int64_t>(row) * src_row_len + col;
+  uint16_t* d = dst + static_cast<int64_t>(row) * dst_row_len + col;
+  const int n = min(16, row_valid - col);
+  for (int j = 0; j < n; j += 2) {
+    const float s0 = which ? sc[col + j] : sc[row];
+    const float s1 = which ? (j + 1 < n ? sc[col + j + 1] : 0.f) : sc[row];
+    const float v0 = static_cast<float>(s[j]) * s0;
+    const float v1 = j + 1 < n ? static_cast<float>(s[j + 1]) * s1 : 0.f;
+    const uint32_t w = pack_bf16x2(v0, v1);
+    d[j] = static_cast<uint16_t>(w & 0xFFFFu);
+    if (j + 1 < n) d[j + 1] = static_cast<uint16_t>(w >> 16);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
@@ -125,7 +167,10 @@ hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {
   const int chunks_v = kD * ((a.n_tok + 15) / 16);
   const int chunks = chunks_k > chunks_v ? chunks_k : chunks_v;
   dim3 grid((chunks + 255) / 256, a.n, a.heads * 2);
-  hipLaunchKernelGGL(dequant_kernel, grid, dim3(256), 0, s, a);
+  if (a.int8)
+    hipLaunchKernelGGL(dequant_int8_kernel, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(dequant_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

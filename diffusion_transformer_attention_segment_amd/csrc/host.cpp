@@ -66,27 +66,29 @@ int32_t tokens_per_frame(const sa_geom* g) { return g->lat_h * g->lat_w; }
 
 sa_status check_layer(const sa_geom* g, const sa_kv_layer* L, const char* name) {
   if (L == nullptr) return fail(SA_E_ARG, "%s layer is NULL", name);
-  if (L->dtype != SA_KV_BF16 && L->dtype != SA_KV_FP8_E4M3)
+  if (L->dtype != SA_KV_BF16 && L->dtype != SA_KV_FP8_E4M3 && L->dtype != SA_KV_INT8)
     return fail(SA_E_UNSUPPORTED, "%s: unknown dtype %d", name, L->dtype);
+  const bool scaled = L->dtype != SA_KV_BF16;
   if (L->frame_capacity < 0 || L->text_capacity < 0)
     return fail(SA_E_ARG, "%s: negative capacity", name);
   if (L->text_capacity % 16 != 0)
     return fail(SA_E_SHAPE, "%s: text_capacity %d must be a multiple of 16", name, L->text_capacity);
-  if (L->dtype == SA_KV_FP8_E4M3 && tokens_per_frame(g) % 16 != 0)
-    return fail(SA_E_SHAPE, "%s: fp8 planes need P %% 16 == 0 (P=%d)", name, tokens_per_frame(g));
+  if (scaled && tokens_per_frame(g) % 16 != 0)
+    return fail(SA_E_SHAPE, "%s: fp8 and int8 planes need P %% 16 == 0 (P=%d)", name,
+                tokens_per_frame(g));
   if (L->frame_capacity > 0) {
     if (L->k == nullptr || L->v == nullptr) return fail(SA_E_ARG, "%s: k/v plane is NULL", name);
     if (!aligned16(L->k) || !aligned16(L->v)) return fail(SA_E_ALIGN, "%s: k/v not 16-byte aligned", name);
-    if (L->dtype == SA_KV_FP8_E4M3 && (L->k_scale == nullptr || L->v_scale == nullptr))
-      return fail(SA_E_ARG, "%s: fp8 layer needs k_scale and v_scale", name);
+    if (scaled && (L->k_scale == nullptr || L->v_scale == nullptr))
+      return fail(SA_E_ARG, "%s: fp8 and int8 layers need k_scale and v_scale", name);
   }
   if (L->text_capacity > 0) {
     if (L->k_text == nullptr || L->v_text == nullptr)
       return fail(SA_E_ARG, "%s: text slot pointers are NULL", name);
     if (!aligned16(L->k_text) || !aligned16(L->v_text))
       return fail(SA_E_ALIGN, "%s: text slot not 16-byte aligned", name);
-    if (L->dtype == SA_KV_FP8_E4M3 && (L->k_text_scale == nullptr || L->v_text_scale == nullptr))
-      return fail(SA_E_ARG, "%s: fp8 text slot needs scales", name);
+    if (scaled && (L->k_text_scale == nullptr || L->v_text_scale == nullptr))
+      return fail(SA_E_ARG, "%s: fp8 and int8 text slots need scales", name);
   }
   return SA_OK;
 }
@@ -100,6 +102,12 @@ RopeParams rope_params(const sa_geom* g) {
   r.P = tokens_per_frame(g);
   r.log2_theta = std::log2(static_cast<double>(g->rope_theta));
   return r;
+}
+
+hipError_t launch_append(int32_t dtype, const AppendArgs& a, hipStream_t s) {
+  if (dtype == SA_KV_BF16) return launch_append_bf16(a, s);
+  if (dtype == SA_KV_INT8) return launch_append_int8(a, s);
+  return launch_append_fp8(a, s);
 }
 
 sa_status hip_status(hipError_t e, const char* what) {
@@ -132,7 +140,7 @@ const char* sa_status_string(int status) {
 size_t sa_cache_bytes(const sa_geom* geom, int32_t dtype, int32_t frame_capacity,
                       int32_t text_capacity) {
   if (check_geom(geom) != SA_OK) return 0;
-  if (dtype != SA_KV_BF16 && dtype != SA_KV_FP8_E4M3) {
+  if (dtype != SA_KV_BF16 && dtype != SA_KV_FP8_E4M3 && dtype != SA_KV_INT8) {
     fail(SA_E_UNSUPPORTED, "unknown dtype %d", dtype);
     return 0;
   }
@@ -144,6 +152,8 @@ size_t sa_cache_bytes(const sa_geom* geom, int32_t dtype, int32_t frame_capacity
   const size_t elems = 2 * H * D * (static_cast<size_t>(frame_capacity) * P + text_capacity);
   ok();
   if (dtype == SA_KV_BF16) return 2 * elems;
+  if (dtype == SA_KV_INT8)   // a scale per token and head, K and V
+    return elems + 2 * sizeof(float) * H * (static_cast<size_t>(frame_capacity) * P + text_capacity);
   return elems + 2 * sizeof(float) * H * (static_cast<size_t>(frame_capacity) + 1);
 }
 
@@ -174,8 +184,7 @@ sa_status sa_kv_append(const sa_geom* geom, const sa_kv_layer* layer, const void
   a.is_text = 0;
   a.rope = rope_params(geom);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = layer->dtype == SA_KV_BF16 ? launch_append_bf16(a, s) : launch_append_fp8(a, s);
-  return hip_status(e, "kv_append launch");
+  return hip_status(launch_append(layer->dtype, a, s), "kv_append launch");
 }
 
 sa_status sa_text_append(const sa_geom* geom, const sa_kv_layer* layer, const void* k_in,
@@ -205,8 +214,7 @@ sa_status sa_text_append(const sa_geom* geom, const sa_kv_layer* layer, const vo
   a.is_text = 1;
   a.rope = rope_params(geom);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = layer->dtype == SA_KV_BF16 ? launch_append_bf16(a, s) : launch_append_fp8(a, s);
-  return hip_status(e, "text_append launch");
+  return hip_status(launch_append(layer->dtype, a, s), "text_append launch");
 }
 
 sa_status sa_history_select(int32_t policy, int32_t t_past, int32_t budget, double gamma,
@@ -288,11 +296,13 @@ sa_status sa_history_gather(const sa_geom* geom, const sa_kv_layer* src, const i
   a.dst_v = dst->v;
   const int64_t elt = src->dtype == SA_KV_BF16 ? 2 : 1;
   a.plane_bytes = elt * geom->heads * static_cast<int64_t>(tokens_per_frame(geom)) * geom->head_dim;
-  if (src->dtype == SA_KV_FP8_E4M3) {
+  if (src->dtype != SA_KV_BF16) {
     a.src_ks = src->k_scale;
     a.src_vs = src->v_scale;
     a.dst_ks = dst->k_scale;
     a.dst_vs = dst->v_scale;
+    a.scale_floats = src->dtype == SA_KV_INT8 ? static_cast<int64_t>(geom->heads) * tokens_per_frame(geom)
+                                              : geom->heads;
   }
   a.frames = d_frames;
   a.n = n;
@@ -406,6 +416,7 @@ sa_status prepare_attention(const sa_geom* geom, const sa_attn_item* items, int3
   AttnArgs& a = plan.a;
   a = AttnArgs{};
   plan.fp8 = dtype == SA_KV_FP8_E4M3;
+  a.int8 = dtype == SA_KV_INT8;   // bf16 kernel, tiles dequantised while staged
   plan.bm = plan.fp8 ? attention_block_m_fp8() : attention_block_m_bf16();
   const int bm = plan.bm;
   const int tpf = (P + 63) / 64;
@@ -567,6 +578,7 @@ sa_status prepare_select(const sa_geom* geom, const sa_attn_item* item, SelectAr
   a.item.q_tiles = static_cast<int32_t>((rows + SA_SPARSE_QUERY_BLOCK - 1) / SA_SPARSE_QUERY_BLOCK);
   a.heads = geom->heads;
   a.fp8 = it.kv->dtype == SA_KV_FP8_E4M3;
+  a.int8 = it.kv->dtype == SA_KV_INT8;
   a.n_cand = static_cast<int32_t>(cand);
   a.keep = it.keep_blocks;
   a.rope = rope_params(geom);
@@ -644,7 +656,7 @@ sa_status sa_kv_dequant(const sa_geom* geom, const sa_kv_layer* src, const int32
   if (st != SA_OK) return st;
   if ((st = check_layer(geom, src, "dequant src")) != SA_OK) return st;
   if ((st = check_layer(geom, dst, "dequant dst")) != SA_OK) return st;
-  if (src->dtype != SA_KV_FP8_E4M3) return fail(SA_E_UNSUPPORTED, "dequant: src must be fp8");
+  if (src->dtype == SA_KV_BF16) return fail(SA_E_UNSUPPORTED, "dequant: src must be fp8 or int8");
   if (dst->dtype != SA_KV_BF16) return fail(SA_E_UNSUPPORTED, "dequant: dst must be bf16");
   if (n_frames < 0 || n_text < 0) return fail(SA_E_ARG, "negative counts");
   if (n_frames > dst->frame_capacity)
@@ -666,6 +678,7 @@ sa_status sa_kv_dequant(const sa_geom* geom, const sa_kv_layer* src, const int32
     a.n = n_frames;
     a.heads = geom->heads;
     a.src_len = a.dst_len = a.n_tok = tokens_per_frame(geom);
+    a.int8 = src->dtype == SA_KV_INT8;
     if ((st = hip_status(launch_dequant(a, s), "kv_dequant launch")) != SA_OK) return st;
   }
   if (n_text > 0) {
@@ -682,6 +695,7 @@ sa_status sa_kv_dequant(const sa_geom* geom, const sa_kv_layer* src, const int32
     a.src_len = src->text_capacity;
     a.dst_len = dst->text_capacity;
     a.n_tok = n_text;
+    a.int8 = src->dtype == SA_KV_INT8;
     if ((st = hip_status(launch_dequant(a, s), "kv_dequant text launch")) != SA_OK) return st;
   }
   return ok();

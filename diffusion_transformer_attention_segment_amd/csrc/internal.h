@@ -25,7 +25,7 @@ struct AppendArgs {
   const uint16_t* v_in;
   void* k;                  // plane base (frame 0 / text slot base)
   void* v;
-  float* k_scale;           // fp8: [frames][H] or [H] for text
+  float* k_scale;           // fp8: [frames][H] or [H] for text; int8: [frames][H][P] or [H][cap]
   float* v_scale;
   int32_t heads;
   int32_t frame0;           // first frame written (video); unused for text
@@ -38,6 +38,7 @@ struct AppendArgs {
 
 hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s);
 hipError_t launch_append_fp8(const AppendArgs& a, hipStream_t s);
+hipError_t launch_append_int8(const AppendArgs& a, hipStream_t s);
 
 // ---- attention ----------------------------------------------------------------
 struct AttnItemDev {
@@ -82,6 +83,7 @@ struct AttnArgs {
   int32_t split_k;        // 1: nothing is split
   int32_t grid;           // n_full + (total_tiles - n_full) * split_k
   int32_t any_sparse;     // 1: some item has a block list (the sparse kernel instantiation)
+  int32_t int8;           // 1: int8 layers (the bf16 kernel dequantises while staging tiles)
   float* ws;
   float scale_log2;       // softmax scale * log2(e)
   RopeParams rope;
@@ -105,6 +107,7 @@ struct SelectArgs {
   AttnItemDev item;        // q, kv planes, frames, counts of the session
   int32_t heads;
   int32_t fp8;             // 1: e4m3 planes with per-(frame, head) scales
+  int32_t int8;            // 1: int8 planes with per-token scales
   int32_t n_cand;          // n_hist_frames * ceil(P / 64)
   int32_t keep;
   float* pooled;           // workspace [H][n_cand][128]
@@ -150,12 +153,13 @@ struct GatherArgs {
   const int32_t* frames;
   int32_t n;
   int64_t plane_bytes;     // bytes of one frame's K (= V) plane over all heads
+  int64_t scale_floats;    // scales per frame (fp8: H, int8: H * P); 0 for bf16
   int32_t heads;
 };
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 
 struct DequantArgs {
-  const uint8_t* src_k;    // fp8 plane base
+  const uint8_t* src_k;    // fp8 or int8 plane base
   const uint8_t* src_v;
   const float* src_ks;     // [frames][H] or [H]
   const float* src_vs;
@@ -167,6 +171,7 @@ struct DequantArgs {
   int32_t src_len;         // tokens per source plane (P or text_capacity)
   int32_t dst_len;         // tokens per destination plane
   int32_t n_tok;           // tokens to convert per plane
+  int32_t int8;            // 1: int8 codes with per-token scales (src_ks/src_vs [planes][src_len])
 };
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 

@@ -320,6 +320,123 @@ static bool use_lut(const AppendArgs& a) {
   return !a.is_text && size <= kLutMax;
 }
 
+namespace {
+
+// ---- int8 with a scale per token and head ---------------------------------------
+// One block = 64 tokens of one (frame, head) plane, 256 threads: 16 lanes own a
+// (token, head) row, 8 dims each. Per row: rotate K in fp32 (video), amax over
+// the 128 dims by butterfly shuffles inside the 16 lanes, scale = amax / 127,
+// code = rint(x * (127 / amax)) clamped to +-127 (amax 0: scale 1, codes 0),
+// all in fp32. K codes go out as 8-byte runs of the row, V codes through an
+// LDS [dim][token] tile so that V^T rows leave as 16-byte runs. Text tokens
+// past n_tok get zero codes and zero scales.
+constexpr int kI8Tok = 64;
+constexpr int kI8Stride = kI8Tok + 16;   // LDS row stride (bytes) of the V^T tile
+
+__device__ __forceinline__ float group16_max(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// 8 values -> 8 int8 codes (two words), and the row's scale
+__device__ __forceinline__ uint2 quantize_row8(const float* y, float* scale) {
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(y[i]));
+  am = group16_max(am);
+  const float inv = am > 0.f ? 127.0f / am : 1.0f;
+  *scale = am > 0.f ? am / 127.0f : 1.0f;
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float c = fminf(fmaxf(__builtin_rintf(y[i] * inv), -127.0f), 127.0f);
+    w[i >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(c)) & 0xFFu) << (8 * (i & 3));
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+__global__ __launch_bounds__(256) void append_int8_kernel(const AppendArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t vt[kD * kI8Stride];
+  __shared__ double om[kD / 2];
+  __shared__ int ax[kD / 2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 15, grp = tid >> 4;
+  const int p0 = blockIdx.y * kI8Tok;
+  const int fr = blockIdx.z;
+  const int h = blockIdx.x;
+  const int H = a.heads;
+  if (tid < kD / 2) {
+    int axis;
+    om[tid] = rope_omega(tid, a.rope, &axis);
+    ax[tid] = axis;
+  }
+  __syncthreads();
+  const int f = a.frame0 + fr;
+  const size_t pl = static_cast<size_t>(f) * H + h;
+  int8_t* kdst = static_cast<int8_t*>(a.k) + pl * a.plane_len * kD;
+  int8_t* vdst = static_cast<int8_t*>(a.v) + pl * a.plane_len * kD;
+  float* ksc = a.k_scale + pl * a.plane_len;
+  float* vsc = a.v_scale + pl * a.plane_len;
+#pragma unroll
+  for (int i = 0; i < kI8Tok / 16; ++i) {
+    const int tok = grp + 16 * i;
+    const int p = p0 + tok;
+    if (p >= a.plane_len) continue;          // (whole 16-lane groups agree)
+    uint2 kc = make_uint2(0u, 0u), vc = make_uint2(0u, 0u);
+    float ks = 0.f, vs = 0.f;
+    if (p < a.n_tok) {
+      const size_t in_off = (static_cast<size_t>(fr * a.n_tok + p) * H + h) * kD + lane * 8;
+      const u32x4 kx = *reinterpret_cast<const u32x4*>(a.k_in + in_off);
+      const u32x4 vx = *reinterpret_cast<const u32x4*>(a.v_in + in_off);
+      float y[8], z[8];
+      if (!a.is_text) {
+        rotate_chunk(kx, lane, f, p / a.rope.lat_w, p % a.rope.lat_w, om, ax, y);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          y[2 * m] = __uint_as_float(kx[m] << 16);
+          y[2 * m + 1] = __uint_as_float(kx[m] & 0xFFFF0000u);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        z[2 * m] = __uint_as_float(vx[m] << 16);
+        z[2 * m + 1] = __uint_as_float(vx[m] & 0xFFFF0000u);
+      }
+      kc = quantize_row8(y, &ks);
+      vc = quantize_row8(z, &vs);
+      *reinterpret_cast<uint2*>(kdst + static_cast<size_t>(p) * kD + lane * 8) = kc;
+    }
+    if (lane == 0) {
+      ksc[p] = ks;
+      vsc[p] = vs;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      vt[(lane * 8 + m) * kI8Stride + tok] = static_cast<uint8_t>((m < 4 ? vc.x : vc.y) >> (8 * (m & 3)));
+  }
+  __syncthreads();
+  // V^T rows: dim d, tokens p0 + 16 q .. + 15 (16-byte runs)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = tid + 256 * i;
+    const int d = c >> 2, q = c & 3;
+    const int p = p0 + 16 * q;
+    if (p < a.plane_len)
+      *reinterpret_cast<u32x4*>(vdst + static_cast<size_t>(d) * a.plane_len + p) =
+          *reinterpret_cast<const u32x4*>(&vt[d * kI8Stride + 16 * q]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append_int8(const AppendArgs& a, hipStream_t s) {
+  dim3 grid(a.heads, (a.plane_len + kI8Tok - 1) / kI8Tok, a.n_frames);   // heads fastest
+  hipLaunchKernelGGL(append_int8_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s) {
   // heads fastest: concurrent blocks read the same tokens' rows of all heads
   dim3 grid(a.heads, (a.plane_len + kTileTok - 1) / kTileTok, a.n_frames);

@@ -10,7 +10,8 @@
 //
 // Two kernels:
 //   pool_k_kernel  one wave per candidate block: the mean of its <= 64 stored
-//                  keys (e4m3 codes times the plane scale), fp32, into the
+//                  keys (e4m3 codes times the plane scale, int8 codes times
+//                  their token's scale), fp32, into the
 //                  workspace [H][n_cand][128]. Reads the history K once.
 //   select_kernel  one workgroup per (query block, head): the mean rotated
 //                  query (fp32, rows summed in a fixed order), one score per
@@ -42,7 +43,19 @@ __global__ __launch_bounds__(64 * kPoolWaves) void pool_k_kernel(const SelectArg
   const int r0 = j * kKeyTile, n = min(kKeyTile, P - r0);
   const size_t plane = (static_cast<size_t>(frame) * H + h) * static_cast<size_t>(P) * kD;
   float s0 = 0.f, s1 = 0.f;
-  if (!a.fp8) {
+  if (a.int8) {
+    const uint16_t* base = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.item.k) +
+                                                             plane) +
+                           static_cast<size_t>(r0) * (kD / 2) + lane;
+    const float* sc = a.item.k_scale + (static_cast<size_t>(frame) * H + h) * P + r0;
+#pragma unroll 8
+    for (int r = 0; r < n; ++r) {
+      const uint32_t w = base[static_cast<size_t>(r) * (kD / 2)];
+      const float scl = sc[r];
+      s0 += static_cast<float>(static_cast<int8_t>(w)) * scl;
+      s1 += static_cast<float>(static_cast<int8_t>(w >> 8)) * scl;
+    }
+  } else if (!a.fp8) {
     const uint32_t* base =
         reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.item.k) + plane) +
         static_cast<size_t>(r0) * (kD / 2) + lane;

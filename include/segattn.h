@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 5
+#define SA_ABI_VERSION 6
 #define SA_HEAD_DIM 128       /* the only head dim the kernels are built for */
 #define SA_MAX_ITEMS 8        /* sessions per sa_segment_attention call     */
 #define SA_MAX_FRAMES_KV 65536
@@ -67,7 +67,7 @@ typedef enum {
   SA_E_HIP = 7           /* a HIP runtime call or launch failed           */
 } sa_status;
 
-typedef enum { SA_KV_BF16 = 0, SA_KV_FP8_E4M3 = 1 } sa_kv_dtype;
+typedef enum { SA_KV_BF16 = 0, SA_KV_FP8_E4M3 = 1, SA_KV_INT8 = 2 } sa_kv_dtype;
 
 typedef enum {
   SA_SEL_ALL = 0,            /* every past frame                              */
@@ -103,9 +103,15 @@ typedef struct sa_geom {
  *                                                (frame, head)
  *   k_text   [H][text_capacity][128]             text keys (no rotation)
  *   v_text   [H][128][text_capacity]             text values, transposed
- *   k_scale, v_scale            [frame_capacity][H] fp32, fp8 only
- *   k_text_scale, v_text_scale  [H] fp32, fp8 only (NULL for bf16)
- * Element type: bf16 (2 bytes) or e4m3 (1 byte) per `dtype`.
+ *   k_scale, v_scale            fp8: [frame_capacity][H] fp32 (one per
+ *                               plane); int8: [frame_capacity][H][P] fp32
+ *                               (one per token and head)
+ *   k_text_scale, v_text_scale  fp8: [H]; int8: [H][text_capacity]
+ *                               (NULL for bf16)
+ * Element type: bf16 (2 bytes), e4m3 or int8 (1 byte) per `dtype`. int8 is
+ * the pages' single-GPU cache ("The 4090 preset": one byte per value plus an
+ * FP32 scale per token and head, 4,224 bytes per token and layer at 16
+ * heads); fp8 and int8 need P % 16 == 0.
  * text_capacity must be a multiple of 16; it may be 0 (no text slot).      */
 typedef struct sa_kv_layer {
   int32_t dtype;
@@ -197,7 +203,9 @@ size_t sa_cache_bytes(const sa_geom* geom, int32_t dtype, int32_t frame_capacity
  * fp64-reduced angle, then rounded to the cache type; V is stored unrotated
  * and transposed. fp8: per (frame, head) plane, scale = amax / 448 (fp32),
  * code = round-nearest-even(x * (448 / amax)) saturated; amax 0 gives scale
- * 1. Source: "Writing the segment into memory" and "How one segment is made"
+ * 1. int8: per token and head, scale = amax / 127 over its 128 values, code
+ * = round-half-even(x * (127 / amax)) clamped to +-127, in fp32 (K after its
+ * rotation in fp32); amax 0 gives scale 1 and codes 0. Source: "Writing the segment into memory" and "How one segment is made"
  * (RoPE). Errors: SA_E_RANGE if frame0 < 0 or frame0 + n_frames >
  * frame_capacity.                                                           */
 sa_status sa_kv_append(const sa_geom* geom, const sa_kv_layer* layer, const void* k_in,
@@ -205,9 +213,11 @@ sa_status sa_kv_append(const sa_geom* geom, const sa_kv_layer* layer, const void
 
 /* text_append: write n_text text tokens into the layer's text slot (no
  * rotation: text sits at position (0,0,0)). k_in, v_in: bf16 [n_text][H][128].
- * fp8: one scale per head over the n_text tokens. Slots [n_text, capacity)
- * of the value plane are zeroed so that a partial last key chunk reads finite
- * values. Errors: SA_E_CAPACITY if n_text > text_capacity.                  */
+ * fp8: one scale per head over the n_text tokens; int8: one per token and
+ * head, and the tokens [n_text, capacity) get zero codes and zero scales.
+ * Slots [n_text, capacity) of the value plane are zeroed so that a partial
+ * last key chunk reads finite values. Errors: SA_E_CAPACITY if n_text >
+ * text_capacity.                                                            */
 sa_status sa_text_append(const sa_geom* geom, const sa_kv_layer* layer, const void* k_in,
                          const void* v_in, int32_t n_text, void* stream);
 
@@ -241,7 +251,9 @@ sa_status sa_history_gather(const sa_geom* geom, const sa_kv_layer* src, const i
  * output. bf16 layers use bf16 MFMA; fp8 layers use fp8 MFMA with queries
  * split per (row, head) into an e4m3 high part and an e4m3 low part (scaled
  * by 2^-4), and the per-(frame, head) scales applied to the logits and folded
- * into the probabilities. All items must share one dtype.
+ * into the probabilities. int8 layers run the bf16 path: each key tile is
+ * dequantised (code * its token's scale, rounded to bf16) as it is staged
+ * ("stored in INT8 and computed in BF16"). All items must share one dtype.
  * Work is split into 256-row query tiles per (item, head). When the tiles do
  * not fill the device evenly, the tiles of the last partial round are split
  * further over their key range, and a second kernel merges the partial
@@ -306,7 +318,8 @@ sa_status sa_camera_attention(const sa_geom* geom, const void* q, int32_t n_fram
 /* kv_dequant: fp8 frames[i] of src -> bf16 frame slot i of dst (K and V
  * planes: value = code * scale, rounded to bf16), and, when n_text > 0, the
  * first n_text tokens of the text slot. The pages' "stored low precision,
- * computed in BF16" route ("El preset de una GPU", inferencekey.com).
+ * computed in BF16" route ("El preset de una GPU", inferencekey.com). src
+ * may also be int8 (value = code * the token's scale).
  * dst must be a bf16 layer with frame_capacity >= n_frames and
  * text_capacity >= n_text.                                                  */
 sa_status sa_kv_dequant(const sa_geom* geom, const sa_kv_layer* src, const int32_t* d_frames,

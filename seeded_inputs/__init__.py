@@ -29,7 +29,7 @@ class Workload:
     lat_w: int
     n_text: int
     prior_segments: tuple  # prior segments per session
-    kv_dtype: str = "bf16"  # "bf16" or "fp8"
+    kv_dtype: str = "bf16"  # "bf16", "fp8" or "int8"
     layers: int = 1
     policy: str = "all"     # history policy: "all" or "anchor_recent"
     recent_segments: int = 3
@@ -62,8 +62,9 @@ def _config4_second_session(seed=0):
 
 
 def workloads(seed=0):
-    """The five workloads, in order: tiny, one prior segment, long history,
-    active-history selection (2 sessions), fp8 cache."""
+    """The workloads, in order: tiny, one prior segment, long history,
+    active-history selection (2 sessions), fp8 cache, int8 cache (the pages'
+    per-token format) over the same eight prior segments."""
     return [
         Workload("tiny", heads=2, lat_t=2, lat_h=4, lat_w=6, n_text=16,
                  prior_segments=(2,)),
@@ -76,6 +77,8 @@ def workloads(seed=0):
                  policy="anchor_recent", capacity_segments=13),
         Workload("fp8seg8", heads=16, lat_t=30, lat_h=22, lat_w=40, n_text=256,
                  prior_segments=(8,), kv_dtype="fp8", scale_factors=True),
+        Workload("int8seg8", heads=16, lat_t=30, lat_h=22, lat_w=40, n_text=256,
+                 prior_segments=(8,), kv_dtype="int8"),
     ]
 
 

@@ -44,7 +44,7 @@ class Session:
         S = wl.prior_segments[session]
         F = wl.lat_t
         self.S = S
-        dtype = sa.KV_FP8 if wl.kv_dtype == "fp8" else sa.KV_BF16
+        dtype = {"fp8": sa.KV_FP8, "int8": sa.KV_INT8}.get(wl.kv_dtype, sa.KV_BF16)
         text_cap = ((wl.n_text + 15) // 16) * 16
         self.kv = sa.KVLayer.allocate(self.geom, dtype, wl.frame_capacity(session), text_cap, device)
         self.raw_k, self.raw_v = [], []
@@ -277,6 +277,42 @@ class Session:
             fl = floor[None, :] if vis is None else np.where(vis, floor[None, :], 0.0)
             bound[:, j] = ((2.0 ** -4 * p_ + fl) @ np.abs(v[:, j])) / p_.sum(1)[:, None]
         return out, lse, bound
+
+    def oracle_int8_cache(self, rows=None, heads=None):
+        """Oracle for an int8 cache: fp64 attention over the values the cache
+        stores (the oracle's own per-token int8 quantisation of rotated K and
+        of V, times the scales) and the fp64 rotated Q. Returns (out, lse)."""
+        from oracle import cache as ocache
+        wl = self.wl
+        hs = list(range(wl.heads)) if heads is None else list(heads)
+        F, P = wl.lat_t, wl.P
+        ks, vs = [], []
+        for f in self.frames:
+            seg, fo = divmod(f, F)
+            kin = self.raw_k[seg][fo * P:(fo + 1) * P][:, hs].float().cpu().double().numpy()
+            vin = self.raw_v[seg][fo * P:(fo + 1) * P][:, hs].float().cpu().double().numpy()
+            kc, ksc, vc, vsc = ocache.append_int8(kin, vin, f, wl.lat_h, wl.lat_w, wl.split,
+                                                  self.geom.rope_theta)
+            ks.append(ocache.dequant_int8(kc[0], ksc[0][..., None]).transpose(1, 0, 2))
+            vs.append(ocache.dequant_int8(vc[0], vsc[0][:, None, :]).transpose(2, 0, 1))
+        tk = self.text_k[:, hs].float().cpu().double().numpy()
+        tv = self.text_v[:, hs].float().cpu().double().numpy()
+        kc, ksc, vc, vsc = ocache.append_text_int8(tk, tv)
+        ks.append(ocache.dequant_int8(kc, ksc[..., None]).transpose(1, 0, 2))
+        vs.append(ocache.dequant_int8(vc, vsc[:, None, :]).transpose(2, 0, 1))
+        k = np.concatenate(ks)          # already rotated
+        v = np.concatenate(vs)
+        q = self.q[:, hs].float().cpu().double().numpy()
+        if rows is None:
+            rows = np.arange(q.shape[0])
+        qr = orope.rope3d(q[rows], self.q_positions()[rows], wl.split, self.geom.rope_theta)
+        scale = 1.0 / math.sqrt(wl.head_dim)
+        out = np.zeros(qr.shape)
+        lse = np.zeros(qr.shape[:2])
+        for j in range(qr.shape[1]):
+            out[:, j], lse[:, j] = oatt.attention(qr[:, j], k[:, j], v[:, j], scale,
+                                                  self.visibility(rows, hs[j]))
+        return out, lse
 
     def gpu_out(self, rows=None, heads=None):
         o = self.out.float().cpu().double().numpy()

@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 5
+    assert sa.abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -98,11 +98,12 @@ def test_history_select_errors(lib):
 
 def test_cache_bytes_matches_oracle(lib):
     g = sa.Geom()
-    for dt, name in ((sa.KV_BF16, "bf16"), (sa.KV_FP8, "fp8")):
+    for dt, name in ((sa.KV_BF16, "bf16"), (sa.KV_FP8, "fp8"), (sa.KV_INT8, "int8")):
         for fc, tc in ((60, 256), (390, 256), (0, 16), (1, 0)):
             assert sa.cache_bytes(g, dt, fc, tc) == ocache.plane_bytes(name, 16, 128, 880, fc, tc)
-    # the page's figure: 8,192 bytes per token per layer in bf16
+    # the page's figures: 8,192 bytes per token per layer in bf16, 4,224 in int8
     assert sa.cache_bytes(g, sa.KV_BF16, 1, 0) == 880 * 8192
+    assert sa.cache_bytes(g, sa.KV_INT8, 1, 0) == 880 * 4224
 
 
 # --------------------------------------------------------------- validation

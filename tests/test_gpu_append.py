@@ -146,3 +146,52 @@ def test_text_append_fp8():
     assert np.array_equal(layer.k_text[:, :n].cpu().numpy(), Kc)
     assert np.array_equal(layer.v_text[:, :, :n].cpu().numpy(), Vc)
     assert np.all(layer.v_text[:, :, n:].cpu().numpy() == 0)
+
+
+# ------------------------------------------------------------------- int8 cache
+@pytest.mark.parametrize("shape", [(2, 4, 8, 3, 2), (16, 22, 40, 2, 7)])
+def test_kv_append_int8(shape):
+    """int8 with a scale per token and head: V codes and scales bit-exact
+    (fp32 decisions on both sides); K is rotated in fp32 by the kernel and in
+    exact arithmetic by the oracle, so a K code may move one step near a
+    rounding boundary and a K scale by fp32 rounding."""
+    H, lh, lw, F, frame0 = shape
+    print(f"kv_append int8 H={H} grid={lh}x{lw} F={F}", flush=True)
+    geom = sa.Geom(heads=H, lat_h=lh, lat_w=lw)
+    layer = sa.KVLayer.allocate(geom, sa.KV_INT8, frame0 + F, 16)
+    wl = si.Workload("t", heads=H, lat_t=F, lat_h=lh, lat_w=lw, n_text=16, prior_segments=(0,),
+                     kv_dtype="fp8", scale_factors=True)
+    k, v = si.segment_kv(wl, 5, 0, 0, 0, "cuda")
+    sa.kv_append(geom, layer, k, v, frame0, F)
+    torch.cuda.synchronize()
+    Kc, Ks, Vc, Vs = ocache.append_int8(k.float().cpu().double().numpy(),
+                                        v.float().cpu().double().numpy(), frame0, lh, lw, SPLIT, 10000.0)
+    assert np.array_equal(layer.v_scale[frame0:].cpu().numpy(), Vs)
+    assert np.array_equal(layer.v[frame0:].cpu().numpy(), Vc)
+    np.testing.assert_allclose(layer.k_scale[frame0:].cpu().numpy(), Ks, rtol=2e-6)
+    step = np.abs(layer.k[frame0:].cpu().numpy().astype(np.int32) - Kc.astype(np.int32))
+    print(f"  K code agreement {np.mean(step == 0):.6f}", flush=True)
+    assert step.max() <= 1
+    assert np.mean(step == 0) >= 0.99
+
+
+def test_text_append_int8():
+    H, n = 4, 40
+    geom = sa.Geom(heads=H, lat_h=4, lat_w=8)
+    layer = sa.KVLayer.allocate(geom, sa.KV_INT8, 1, 48)
+    layer.k_text_scale.fill_(float("nan"))
+    layer.v_text_scale.fill_(float("nan"))
+    k = si.normal_bf16((n, H, 128), 33, "cuda")
+    v = si.normal_bf16((n, H, 128), 34, "cuda")
+    sa.text_append(geom, layer, k, v, n)
+    torch.cuda.synchronize()
+    Kc, Ks, Vc, Vs = ocache.append_text_int8(k.float().cpu().double().numpy(),
+                                             v.float().cpu().double().numpy())
+    assert np.array_equal(layer.k_text_scale[:, :n].cpu().numpy(), Ks)
+    assert np.array_equal(layer.v_text_scale[:, :n].cpu().numpy(), Vs)
+    assert np.array_equal(layer.k_text[:, :n].cpu().numpy(), Kc)
+    assert np.array_equal(layer.v_text[:, :, :n].cpu().numpy(), Vc)
+    # tokens past n_text: zero codes in V and zero scales (finite for masked keys)
+    assert np.all(layer.v_text[:, :, n:].cpu().numpy() == 0)
+    assert np.all(layer.k_text_scale[:, n:].cpu().numpy() == 0)
+    assert np.all(layer.v_text_scale[:, n:].cpu().numpy() == 0)

@@ -23,15 +23,16 @@ def _fill_random(layer, seed):
         b.copy_(torch.randint(0, 256, b.shape, generator=g, device="cuda", dtype=torch.uint8))
         if layer.dtype == sa.KV_FP8:
             b[(b & 0x7F) == 0x7F] = 0x3C           # keep codes finite
-        else:
+        elif layer.dtype == sa.KV_BF16:
             t.view(torch.int16)[torch.isnan(t.float())] = 0
-    if layer.dtype == sa.KV_FP8:
+    if layer.dtype in (sa.KV_FP8, sa.KV_INT8):
         for t in (layer.k_scale, layer.v_scale, layer.k_text_scale, layer.v_text_scale):
             t.copy_(torch.rand(t.shape, generator=g, device="cuda") * 0.05 + 0.001)
 
 
 @pytest.mark.parametrize("dtype,grid", [(sa.KV_BF16, (4, 6)), (sa.KV_FP8, (4, 8)),
-                                        (sa.KV_BF16, (22, 40))])
+                                        (sa.KV_INT8, (4, 8)), (sa.KV_BF16, (22, 40)),
+                                        (sa.KV_INT8, (22, 40))])
 def test_gather_bit_exact(dtype, grid):
     H = 16 if grid == (22, 40) else 3
     geom = sa.Geom(heads=H, lat_h=grid[0], lat_w=grid[1])
@@ -45,7 +46,7 @@ def test_gather_bit_exact(dtype, grid):
     idx = torch.tensor(frames, device="cuda")
     assert torch.equal(dst.k[:len(frames)].view(torch.uint8), src.k[idx].view(torch.uint8))
     assert torch.equal(dst.v[:len(frames)].view(torch.uint8), src.v[idx].view(torch.uint8))
-    if dtype == sa.KV_FP8:
+    if dtype != sa.KV_BF16:       # per plane (fp8) or per token (int8)
         assert torch.equal(dst.k_scale[:len(frames)], src.k_scale[idx])
         assert torch.equal(dst.v_scale[:len(frames)], src.v_scale[idx])
 
@@ -88,3 +89,42 @@ def test_dequant_matches_oracle(n_text):
             assert np.array_equal(tk[h, :n_text], _dequant_ref(sk[h, :n_text], kts[h]))
             assert np.array_equal(tv[h, :, :n_text], _dequant_ref(sv[h, :, :n_text], vts[h]))
             assert np.all(tk[h, n_text:] == 0) and np.all(tv[h, :, n_text:] == 0)
+
+
+def _dequant_int8_ref(codes, scale):
+    """code * scale in fp32, then bf16 nearest-even (as bits)."""
+    val = codes.astype(np.float32) * scale.astype(np.float32)
+    return numerics.bf16_bits(numerics.bf16_round(val.astype(np.float32).astype(np.float64)))
+
+
+@pytest.mark.parametrize("n_text", [0, 29])
+def test_dequant_int8_matches_oracle(n_text):
+    """int8 planes with a scale per token and head: K rows scale per row, V^T
+    columns per column."""
+    H, lh, lw = 3, 4, 8
+    geom = sa.Geom(heads=H, lat_h=lh, lat_w=lw)
+    src = sa.KVLayer.allocate(geom, sa.KV_INT8, 10, 32)
+    _fill_random(src, 3)
+    frames = [9, 2, 4]
+    dst = sa.KVLayer.allocate(geom, sa.KV_BF16, 3, 32)
+    for t in (dst.k, dst.v, dst.k_text, dst.v_text):
+        t.zero_()
+    d_frames = torch.tensor(frames, dtype=torch.int32, device="cuda")
+    sa.kv_dequant(geom, src, d_frames, len(frames), n_text, dst)
+    torch.cuda.synchronize()
+    sk, sv = src.k.cpu().numpy(), src.v.cpu().numpy()
+    ks, vs = src.k_scale.cpu().numpy(), src.v_scale.cpu().numpy()
+    gk = dst.k.view(torch.int16).cpu().numpy().view(np.uint16)
+    gv = dst.v.view(torch.int16).cpu().numpy().view(np.uint16)
+    for i, f in enumerate(frames):
+        for h in range(H):
+            assert np.array_equal(gk[i, h], _dequant_int8_ref(sk[f, h], ks[f, h][:, None]))
+            assert np.array_equal(gv[i, h], _dequant_int8_ref(sv[f, h], vs[f, h][None, :]))
+    if n_text:
+        tk = dst.k_text.view(torch.int16).cpu().numpy().view(np.uint16)
+        tv = dst.v_text.view(torch.int16).cpu().numpy().view(np.uint16)
+        sk, sv = src.k_text.cpu().numpy(), src.v_text.cpu().numpy()
+        kts, vts = src.k_text_scale.cpu().numpy(), src.v_text_scale.cpu().numpy()
+        for h in range(H):
+            assert np.array_equal(tk[h, :n_text], _dequant_int8_ref(sk[h, :n_text], kts[h, :n_text, None]))
+            assert np.array_equal(tv[h, :, :n_text], _dequant_int8_ref(sv[h, :, :n_text], vts[h, None, :n_text]))
