@@ -46,11 +46,17 @@ PEAK_HBM_GBS = 8000.0
 # those sources hash to the value the summary records.
 ATTN_SOURCES = ["attention_common.h", "internal.h", "device_common.h", "attention_combine.hip",
                 "host.cpp"]
+# The attention kernels are templates: <sparse history, int8 cache> for bf16,
+# <sparse history> for fp8; the bench's timed call is the dense instantiation.
 COUNTER_SUMMARY = {
-    ("bf16", "seg1"): ("attn_bf16_seg1_counters.txt", ["attn_bf16_kernel", "combine_kernel"],
+    ("bf16", "seg1"): ("attn_bf16_seg1_counters.txt",
+                       ["attn_bf16_kernel<false, false>", "combine_kernel"],
                        ["attention_bf16.hip"] + ATTN_SOURCES),
-    ("fp8", "fp8seg8"): ("attn_fp8_fp8seg8_counters.txt", ["attn_fp8_kernel", "combine_kernel"],
+    ("fp8", "fp8seg8"): ("attn_fp8_fp8seg8_counters.txt", ["attn_fp8_kernel<false>", "combine_kernel"],
                          ["attention_fp8.hip"] + ATTN_SOURCES),
+    ("bf16", "int8seg8"): ("attn_int8_int8seg8_counters.txt",
+                           ["attn_bf16_kernel<false, true>", "combine_kernel"],
+                           ["attention_bf16.hip"] + ATTN_SOURCES),
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 
@@ -123,7 +129,7 @@ class LayerState:
         self.wl = wl
         self.geom = sa.Geom(heads=wl.heads, lat_h=wl.lat_h, lat_w=wl.lat_w, rope_split=wl.split,
                             rope_theta=wl.theta)
-        dtype = sa.KV_FP8 if wl.kv_dtype == "fp8" else sa.KV_BF16
+        dtype = {"fp8": sa.KV_FP8, "int8": sa.KV_INT8}.get(wl.kv_dtype, sa.KV_BF16)
         F = wl.lat_t
         text_cap = ((wl.n_text + 15) // 16) * 16
         self.sess = []
@@ -405,7 +411,7 @@ def main():
     attn_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
 
     flops = state.flops()
-    dtype = "fp8" if wl.kv_dtype == "fp8" else "bf16"
+    dtype = "fp8" if wl.kv_dtype == "fp8" else "bf16"   # int8 caches compute in bf16
     peak = PEAK_TFLOPS[dtype]
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (attn_ms * 1e-3) / 1e12

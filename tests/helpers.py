@@ -107,6 +107,10 @@ class Session:
                 kc, ksc, _, _ = ocache.append_fp8(raw, raw, f, wl.lat_h, wl.lat_w, wl.split,
                                                   self.geom.rope_theta)
                 k = ocache.dequant(kc[0], ksc[0][:, None, None])
+            elif wl.kv_dtype == "int8":
+                kc, ksc, _, _ = ocache.append_int8(raw, raw, f, wl.lat_h, wl.lat_w, wl.split,
+                                                   self.geom.rope_theta)
+                k = ocache.dequant_int8(kc[0], ksc[0][..., None])
             else:
                 k = ocache.append_bf16(raw, raw, f, wl.lat_h, wl.lat_w, wl.split,
                                        self.geom.rope_theta)[0][0]
