@@ -1,14 +1,17 @@
 """Throughput of the segment-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload seg1|seg4x54|select2|fp8seg8]
-                    [--no-cpu-baseline] [--profile-steps N]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload seg1|seg4x54|select2|fp8seg8|int8seg8] [--layers N]
+                    [--text-windows] [--no-cpu-baseline]
 
-One step = one layer's pass over the hot path for one synthetic segment:
-history_select (host) + upload of the kept-frame list, kv_append of the
-segment's 30 latent frames (fused 3D RoPE + cache write), text_append of its
-256 text tokens, and segment_attention (Q RoPE, Q.K^T, online softmax, .V)
-over [kept history ; own segment ; own text]. Inputs are resident in HBM
-before the timed region starts.
+One step = one pass of the hot path over the workload's layers for one
+synthetic segment (one layer, or the 54 seeded layers of seg4x54):
+history_select (host) and the upload of the kept-frame lists, once per pass
+and shared by its layers; then per layer kv_append of the segment's 30 latent
+frames (fused 3D RoPE + cache write), text_append of its 256 text tokens, and
+segment_attention (Q RoPE, Q.K^T, online softmax, .V) over [kept history ;
+own segment ; own text]. Inputs are resident in HBM before the timed region
+starts.
 
 Prints ONE JSON line. `value` is segment-attention TFLOP/s over the whole step
 (FLOP = 4 * Lq * Lk * 128 * H, the algorithmic work on the kept key set);
@@ -110,6 +113,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layers per step (default: the workload's, 54 for seg4x54, else 1)")
     ap.add_argument("--text-windows", action="store_true",
                     help="give every session timed text windows (seeded recipe)")
     return ap.parse_args()
@@ -168,10 +173,10 @@ class LayerState:
             tot += 4 * wl.Lq * lk * wl.head_dim * wl.heads
         return tot
 
-    def step(self, sa, ev=None):
-        wl = self.wl
-        F = wl.lat_t
-        items = []
+    def upload(self, sa):
+        """history_select on the host and the kept-frame lists' upload, once
+        per segment pass (every layer of the pass reads the same lists)."""
+        F = self.wl.lat_t
         for s, d in enumerate(self.sess):
             hist = self.select(sa, s)
             if d["copied"] is not None:
@@ -182,9 +187,17 @@ class LayerState:
             d["d_frames"].copy_(d["pinned"], non_blocking=True)
             d["copied"] = torch.cuda.Event()
             d["copied"].record()
+        return [d["d_frames"] for d in self.sess]
+
+    def run(self, sa, frames, ev=None):
+        """kv_append + text_append of the segment, then segment_attention."""
+        wl = self.wl
+        F = wl.lat_t
+        items = []
+        for d, d_frames in zip(self.sess, frames):
             sa.kv_append(self.geom, d["kv"], d["k"], d["v"], d["S"] * F, F)
             sa.text_append(self.geom, d["kv"], d["kt"], d["vt"], wl.n_text)
-            items.append(sa.AttnItem(d["q"], d["kv"], d["d_frames"], d["n_frames"], wl.n_text,
+            items.append(sa.AttnItem(d["q"], d["kv"], d_frames, d["n_frames"], wl.n_text,
                                      d["out"], frame0_q=d["S"] * F, n_frames_q=F, n_text_q=wl.n_text,
                                      text_window=d["win"]))
         if ev is not None:
@@ -192,6 +205,15 @@ class LayerState:
         sa.segment_attention(self.geom, items)
         if ev is not None:
             ev[1].record()
+
+
+def pass_step(sa, layers, evs=None):
+    """One pass of the hot path over every layer of the workload: the kept
+    lists are selected and uploaded once, then each layer appends its segment
+    and runs its attention. evs: one event pair per layer, or None."""
+    frames = layers[0].upload(sa)
+    for i, st in enumerate(layers):
+        st.run(sa, frames, None if evs is None else evs[i])
 
 
 def measure_sparse(sa, state, percent=25, reps=5):
@@ -283,11 +305,27 @@ def measure_gather(sa, geom, n_frames=99, capacity=128, reps=5):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
+    # cold: before each timed call a 512 MB write evicts the last-level cache
+    # (MALL, 256 MB) of the planes the previous call touched
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(reps):
+        flush.fill_(1)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        sa.history_gather(geom, src, d_frames, n_frames, dst)
+        c1.record()
+        torch.cuda.synchronize()
+        cold.append(c0.elapsed_time(c1))
+    cold_ms = sorted(cold)[len(cold) // 2]
+    del flush
     plane = geom.heads * geom.P * 128 * 2
     moved = 2 * 2 * n_frames * plane          # K and V, read + write
     return {"frames": n_frames, "ms": round(ms, 4), "bytes_read_plus_written": moved,
             "GB_per_s": round(moved / (ms * 1e-3) / 1e9, 1),
-            "frac_of_hbm_peak": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            "frac_of_hbm_peak": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "cold_ms_median": round(cold_ms, 4),
+            "cold_GB_per_s": round(moved / (cold_ms * 1e-3) / 1e9, 1)}
 
 
 def measure_dequant(sa, geom, n_frames=99, capacity=128, reps=5):
@@ -374,7 +412,8 @@ def cpu_baseline(state, rows_wanted, seed):
     lk = k.shape[0]
     flops_full = 4.0 * wl.Lq * lk * wl.head_dim * wl.heads
     return {"value": flops_full / t_full / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "blas_threads": int(threads), "cpu_count": os.cpu_count(),
+            "usable_cores": len(os.sched_getaffinity(0)),
             "sample": (f"numpy fp64 oracle, session 0: RoPE of all {lk} keys x {wl.heads} heads "
                        f"({t1 - t0:.2f} s) + attention of {len(rows)} of {wl.Lq} query rows, all "
                        f"heads ({t2 - t1:.2f} s), extrapolated linearly in rows to the full "
@@ -392,28 +431,33 @@ def main():
     sa.lib()
     wl = workload(args.workload, args.seed)
     torch.cuda.init()
-    state = LayerState(sa, wl, args.seed, 0, windows=args.text_windows)
+    n_layers = args.layers or wl.layers
+    layers = [LayerState(sa, wl, args.seed, layer, windows=args.text_windows)
+              for layer in range(n_layers)]
+    state = layers[0]
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
-        state.step(sa)
+        pass_step(sa, layers)
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n_layers)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        state.step(sa, evs[i])
+        pass_step(sa, layers, evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    attn_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    launch_ms = sorted(a.elapsed_time(b) for step in evs for a, b in step)
+    attn_ms = sum(launch_ms) / len(launch_ms)                 # mean attention launch
+    attn_median = launch_ms[len(launch_ms) // 2]
 
-    flops = state.flops()
+    flops = state.flops()                                     # per layer (every layer alike)
     dtype = "fp8" if wl.kv_dtype == "fp8" else "bf16"   # int8 caches compute in bf16
     peak = PEAK_TFLOPS[dtype]
-    value = flops / (ms_step * 1e-3) / 1e12
+    value = n_layers * flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (attn_ms * 1e-3) / 1e12
     lk = [d["n_frames"] * wl.P + wl.n_text for d in state.sess]
 
@@ -455,9 +499,14 @@ def main():
             "rope_theta": wl.theta, "text_windows": bool(args.text_windows),
         },
         "pct_of_peak": round(100.0 * value / peak, 2),
-        "ms_per_54_block_segment": round(54 * ms_step, 2),
-        "ms_per_54_block_segment_note": "54 x one layer's step (derived)",
+        "layers_per_step": n_layers,
+        "ms_per_54_block_segment": round(ms_step * 54 / n_layers, 2),
+        "ms_per_54_block_segment_note": ("measured: one step is a pass over 54 seeded layers"
+                                         if n_layers == 54 else
+                                         f"54 / {n_layers} x the measured step (derived)"),
+        "ms_per_9_pass_segment_derived": round(9 * ms_step * 54 / n_layers, 1),
         "attention_kernel_ms": round(attn_ms, 4),
+        "attention_kernel_ms_median": round(attn_median, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": None if args.text_windows else measured_traffic(dtype, wl.name),
