@@ -216,6 +216,71 @@ def pass_step(sa, layers, evs=None):
         st.run(sa, frames, None if evs is None else evs[i])
 
 
+class ClockSampler:
+    """Graphics clock and socket power of the GPU, read through amdsmi every
+    25 ms on a daemon thread while the timed steps run. A power-limited kernel
+    runs below the maximum clock, and the peak is quoted at the maximum, so
+    the observed clock says how much of the gap to the peak is the clock's.
+    Reports None where amdsmi is missing or refuses (no driver access)."""
+
+    def __init__(self):
+        import threading
+        self.samples, self.info = [], None
+        self.stop = threading.Event()
+        self.thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if len(handles) != 1:     # one GPU on the box; otherwise the match is unclear
+                return
+            self.amdsmi, self.h = amdsmi, handles[0]
+            clk = amdsmi.amdsmi_get_clock_info(self.h, amdsmi.AmdSmiClkType.GFX)
+            pw = amdsmi.amdsmi_get_power_info(self.h)
+            self.info = {"max_clk_mhz": clk.get("max_clk"), "power_limit_w": pw.get("power_limit")}
+            self.thread = threading.Thread(target=self._run, daemon=True)
+        except Exception:     # no amdsmi, no driver access: no clock report
+            self.info = None
+
+    def _run(self):
+        while not self.stop.wait(0.025):
+            try:
+                clk = self.amdsmi.amdsmi_get_clock_info(self.h, self.amdsmi.AmdSmiClkType.GFX)["clk"]
+                pw = self.amdsmi.amdsmi_get_power_info(self.h)["current_socket_power"]
+                self.samples.append((time.perf_counter(), float(clk), float(pw)))
+            except Exception:
+                return
+
+    def __enter__(self):
+        if self.thread is not None:
+            self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.thread is not None:
+            self.stop.set()
+            self.thread.join(timeout=2.0)
+
+    def report(self, settle_s=0.5):
+        """Mean and minimum over the samples after the first settle_s seconds
+        (the driver's readings trail the load by a few hundred ms)."""
+        if self.info is None or not self.samples:
+            return None
+        t0 = self.samples[0][0]
+        kept = [(c, p) for t, c, p in self.samples if t - t0 >= settle_s]
+        if self.samples[-1][0] - t0 < settle_s + 1.0 or not kept:    # under a second of readings
+            return None
+        clk = [c for c, _ in kept]
+        pw = [p for _, p in kept]
+        limit = self.info["power_limit_w"]
+        if isinstance(limit, (int, float)) and limit > 1e5:    # reported in microwatts
+            limit = round(limit / 1e6)
+        return dict(self.info, power_limit_w=limit, samples=len(clk),
+                    seconds=round(self.samples[-1][0] - t0, 2),
+                    gfxclk_mhz_mean=round(sum(clk) / len(clk)), gfxclk_mhz_min=round(min(clk)),
+                    socket_power_w_mean=round(sum(pw) / len(pw)))
+
+
 def measure_sparse(sa, state, percent=25, reps=5):
     """One block-sparse pass (the steps after the first two: the pages' preset
     keeps 25 % of the candidate video blocks) at the workload: sparse_select
@@ -443,16 +508,35 @@ def main():
 
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(n_layers)] for _ in range(args.steps)]
+    sampler = ClockSampler()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        pass_step(sa, layers, evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with sampler:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            pass_step(sa, layers, evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     launch_ms = sorted(a.elapsed_time(b) for step in evs for a, b in step)
     attn_ms = sum(launch_ms) / len(launch_ms)                 # mean attention launch
     attn_median = launch_ms[len(launch_ms) // 2]
+
+    # the graphics clock under this load: over the timed steps when they ran
+    # long enough for the driver's readings, else over extra untimed passes
+    # (about 3 s) run only for it
+    clock = sampler.report()
+    if clock is not None:
+        clock["over"] = "the timed steps"
+    elif sampler.info is not None:
+        extra = max(1, int(math.ceil(3000.0 / ms_step)))
+        sampler = ClockSampler()
+        with sampler:
+            for _ in range(extra):
+                pass_step(sa, layers)
+            torch.cuda.synchronize()
+        clock = sampler.report()
+        if clock is not None:
+            clock["over"] = f"{extra} untimed steps after the timed ones"
 
     flops = state.flops()                                     # per layer (every layer alike)
     dtype = "fp8" if wl.kv_dtype == "fp8" else "bf16"   # int8 caches compute in bf16
@@ -507,11 +591,15 @@ def main():
         "ms_per_9_pass_segment_derived": round(9 * ms_step * 54 / n_layers, 1),
         "attention_kernel_ms": round(attn_ms, 4),
         "attention_kernel_ms_median": round(attn_median, 4),
+        "gpu_clock": clock,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": None if args.text_windows else measured_traffic(dtype, wl.name),
                      "kernel": "segment_attention: attn_" + dtype + "_kernel + combine_kernel",
-                     "flop_per_launch": flops},
+                     "flop_per_launch": flops,
+                     "frac_at_observed_clock": (
+                         round(achieved / (peak * clock["gfxclk_mhz_mean"] / clock["max_clk_mhz"]), 4)
+                         if clock and clock.get("max_clk_mhz") else None)},
         "kv_append": {"ms": round(app_ms, 4), "bytes": app_bytes,
                       "GB_per_s": round(app_bytes / (app_ms * 1e-3) / 1e9, 1),
                       "frac_of_hbm_peak": round(app_bytes / (app_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
