@@ -193,19 +193,13 @@ __device__ __forceinline__ u32x4 load_chunk(const uint16_t* base, size_t off) {
 }
 
 // ---- e4m3 ------------------------------------------------------------------------
-// fp32 -> OCP e4m3fn code, round to nearest even, saturating at 448 (NaN ->
-// 0x7F). Normal range: round the fp32 pattern to 3 mantissa bits (ties to
-// even) and rebias the exponent; below 2^-6: nearest multiple of 2^-9.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fabsf(y);
-  const uint32_t ua = __float_as_uint(a);
-  const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);
-  const int normal = static_cast<int>(r >> 20) - (120 << 3);
-  const int sub = static_cast<int>(__builtin_rintf(a * 512.0f));
-  uint32_t code = static_cast<uint32_t>(min(a < 0.015625f ? sub : normal, 0x7E));
-  if (a != a) return 0x7Fu;
-  return code | sign;
+// Four fp32 values already scaled into +-448 (by 448 / amax) -> four OCP
+// e4m3fn codes, first value in the low byte, by the hardware conversion:
+// round to nearest even, values below 2^-6 to the nearest multiple of 2^-9.
+// In this range nothing overflows.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
 }
 
 __device__ __forceinline__ float block_max(float v, float* red, int nthreads) {
@@ -221,6 +215,8 @@ __device__ __forceinline__ float block_max(float v, float* red, int nthreads) {
 }
 
 constexpr int kFp8Threads = 512;
+constexpr int kVtTok = 128;              // tokens per V^T tile
+constexpr int kVtWords = kVtTok / 4 + 4; // LDS row stride of the V^T tile (words): 144 bytes
 
 // One block per (frame, head) plane (or per head of the text slot): pass 1
 // finds amax of the rotated K and of V, pass 2 quantises and stores (K rows of
@@ -229,6 +225,7 @@ template <bool kLut>
 __global__ __launch_bounds__(kFp8Threads) void append_fp8_kernel(const AppendArgs a) {
   __shared__ float2 lut_mem[kLutMax];
   __shared__ float red[kFp8Threads / 64];
+  __shared__ __align__(16) uint32_t vt_tile[kD * kVtWords];
   const int tid = threadIdx.x;
   const int h = blockIdx.x;
   const int fr = blockIdx.y;
@@ -282,31 +279,41 @@ __global__ __launch_bounds__(kFp8Threads) void append_fp8_kernel(const AppendArg
     u32x2 o;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
-      o[m] = f32_to_e4m3(y[4 * m] * ik) | (f32_to_e4m3(y[4 * m + 1] * ik) << 8) |
-             (f32_to_e4m3(y[4 * m + 2] * ik) << 16) | (f32_to_e4m3(y[4 * m + 3] * ik) << 24);
+      o[m] = e4m3x4(y[4 * m] * ik, y[4 * m + 1] * ik, y[4 * m + 2] * ik, y[4 * m + 3] * ik);
     *reinterpret_cast<u32x2*>(kdst + static_cast<size_t>(p) * kD + ch * 8) = o;
   }
-  // V^T: item = (token quad j, chunk ch), j fastest; plane_len % 16 == 0
-  const int nq = a.plane_len / 4;
-  for (int it = tid; it < nq * 16; it += kFp8Threads) {
-    const int ch = it / nq, j = it - ch * nq;
-    const int p = 4 * j;
-    uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  // V^T through LDS, 128 tokens at a time. Load: thread = (token quad jq,
+  // chunk ch), ch fastest, so that 16 lanes read one token's 256 bytes; its 4
+  // tokens x 8 dims become 8 words (4 tokens of one dim each) in the LDS tile
+  // [dim][token]. Store: each V^T row's 128 bytes leave as 8 runs of 16 bytes.
+  // plane_len % 16 == 0; tokens past n_tok store the code of +0.
+  static_assert(kFp8Threads == 512, "one (quad, chunk) item per thread per 128-token tile");
+  for (int t0 = 0; t0 < a.plane_len; t0 += kVtTok) {
+    {
+      const int ch = tid & 15, jq = tid >> 4;
+      const int p = t0 + 4 * jq;
+      u32x4 vx[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (p + q < a.n_tok) {
-        const u32x4 vx = load_chunk(a.v_in, in_off(p + q, ch));
+      for (int q = 0; q < 4; ++q)
+        vx[q] = p + q < a.n_tok ? load_chunk(a.v_in, in_off(p + q, ch)) : u32x4{0u, 0u, 0u, 0u};
+      __syncthreads();               // the previous tile's rows have been read out
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          w[2 * m] |= f32_to_e4m3(__uint_as_float(vx[m] << 16) * iv) << (8 * q);
-          w[2 * m + 1] |= f32_to_e4m3(__uint_as_float(vx[m] & 0xFFFF0000u) * iv) << (8 * q);
-        }
+      for (int m = 0; m < 4; ++m) {
+        auto lo = [&](int q) { return __uint_as_float(vx[q][m] << 16) * iv; };
+        auto hi = [&](int q) { return __uint_as_float(vx[q][m] & 0xFFFF0000u) * iv; };
+        vt_tile[(8 * ch + 2 * m) * kVtWords + jq] = e4m3x4(lo(0), lo(1), lo(2), lo(3));
+        vt_tile[(8 * ch + 2 * m + 1) * kVtWords + jq] = e4m3x4(hi(0), hi(1), hi(2), hi(3));
       }
     }
-    uint32_t* row = reinterpret_cast<uint32_t*>(vdst + static_cast<size_t>(8 * ch) * a.plane_len + p);
-    const size_t stride = a.plane_len / 4;   // words per V^T row
+    __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 8; ++e) row[e * stride] = w[e];
+    for (int r = 0; r < 2; ++r) {
+      const int idx = tid + r * kFp8Threads;
+      const int d = idx >> 3, pc = idx & 7;
+      if (t0 + 16 * pc < a.plane_len)
+        *reinterpret_cast<u32x4*>(vdst + static_cast<size_t>(d) * a.plane_len + t0 + 16 * pc) =
+            *reinterpret_cast<const u32x4*>(&vt_tile[d * kVtWords + 4 * pc]);
+    }
   }
 }
 

@@ -195,3 +195,45 @@ def test_text_append_int8():
     assert np.all(layer.v_text[:, :, n:].cpu().numpy() == 0)
     assert np.all(layer.k_text_scale[:, n:].cpu().numpy() == 0)
     assert np.all(layer.v_text_scale[:, n:].cpu().numpy() == 0)
+
+
+def test_text_append_fp8_ties_and_subnormals():
+    """A text slot whose largest magnitude is 448, so the scale is exactly 1 and
+    the stored codes are the e4m3 roundings of the inputs themselves: exact
+    ties between neighbouring codes (normal and subnormal, resolved to the even
+    code), the largest code, and values that round up into the normal range."""
+    H, n = 2, 16
+    ties = [448.0, -448.0, 440.0, 248.0, 1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -10,
+            5 * 2.0 ** -10, -3 * 2.0 ** -10, 2.0 ** -11, 15 * 2.0 ** -10, 0.0, 1.0, 0.5]
+    x = np.resize(np.array(ties, dtype=np.float32), (n, H, 128))
+    g = np.random.default_rng(7)
+    mix = g.random(x.shape) < 0.5
+    mix[0] = False                           # token 0 keeps the listed values
+    x = np.where(mix, np.float32(g.standard_normal(x.shape) * 4), x)
+    k = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(k.float().numpy()[0], x[0])     # the listed values are bf16-exact
+    assert np.all(np.abs(k.float().numpy()).max(axis=(0, 2)) == 448.0)
+    kd = k.cuda()
+    geom = sa.Geom(heads=H, lat_h=4, lat_w=8)
+    layer = sa.KVLayer.allocate(geom, sa.KV_FP8, 1, 16)
+    sa.text_append(geom, layer, kd, kd, n)
+    torch.cuda.synchronize()
+    xd = k.float().double().numpy()
+    Kc, Ks, Vc, Vs = ocache.append_text_fp8(xd, xd)
+    assert np.all(Ks == 1.0) and np.all(Vs == 1.0)
+    assert np.array_equal(layer.k_text_scale.cpu().numpy(), Ks)
+    assert np.array_equal(layer.k_text[:, :n].cpu().numpy(), Kc)
+    assert np.array_equal(layer.v_text[:, :, :n].cpu().numpy(), Vc)
+    # the ties themselves went to the even code
+    codes = layer.k_text[0, 0, :len(ties)].cpu().numpy()
+    print("tie codes", [hex(c) for c in codes], flush=True)
+    assert np.array_equal(codes, TIE_CODES)
+
+
+# e4m3 codes of the listed values, worked out by hand: 448 = 0x7E; 440 ties
+# 432 (0x7D) and 448 -> 0x7E; 248 ties 240 (0x77) and 256 -> 0x78; 1.0625 ties
+# 1 (0x38) and 1.125 -> 0x38; 1.1875 ties 1.125 and 1.25 -> 0x3A; 2^-10 ties
+# 0 and 2^-9 -> 0; 3 * 2^-10 -> 2^-8 (0x02); 5 * 2^-10 -> 2^-8 (0x02);
+# 2^-11 -> 0; 15 * 2^-10 ties 7 * 2^-9 and 2^-6 -> 0x08; 0.5 = 0x30
+TIE_CODES = np.array([0x7E, 0xFE, 0x7E, 0x78, 0x38, 0x3A, 0xB8, 0x00, 0x02, 0x02, 0x82, 0x00,
+                      0x08, 0x00, 0x38, 0x30], dtype=np.uint8)
