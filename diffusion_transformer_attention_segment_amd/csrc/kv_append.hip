@@ -10,11 +10,12 @@
 // write 2 x 256 B (bf16) or 2 x 128 B (e4m3) of cache. Blocks run heads
 // fastest, so that concurrent blocks read the same tokens' rows of all heads
 // (4 KB contiguous per token). The bf16 kernel transposes V through LDS and
-// stores 16-byte runs of V^T rows. The e4m3 kernel holds one (frame, head)
-// plane per block (the scale needs the plane's amax); it tabulates the
-// rotation angles in LDS once per block (they depend on the band position and
-// the pair only) and transposes V in registers (a thread holds the same dims
-// of 4 consecutive tokens and stores whole 4-byte words of V^T rows).
+// stores 16-byte runs of V^T rows; it tabulates the cos/sin of its tile (the
+// frame's t band, the rows it spans, every column) in LDS first. The e4m3
+// kernel holds one (frame, head) plane per block (the scale needs the plane's
+// amax); it tabulates the rotation angles in LDS once per block (they depend
+// on the band position and the pair only) and transposes V through an LDS
+// tile as well, 128 tokens at a time.
 #include "device_common.h"
 
 namespace segattn {
@@ -23,6 +24,10 @@ namespace {
 constexpr int kTileTok = 64;          // tokens per bf16 block tile
 constexpr int kVtStride = kD + 8;     // LDS row stride (elements) of the V tile
 constexpr int kLutMax = 4096;         // rotation table entries (cos, sin) within the LDS budget
+constexpr int kTileLutMax = 2048;     // entries of a bf16 tile's table
+
+// latent rows a 64-token tile can span (tiles start at any token of a row)
+__host__ __device__ constexpr int tile_rows(int lat_w) { return (kTileTok - 1) / lat_w + 2; }
 
 // Rotate the 8 bf16 values of one 16-byte chunk (dims ch*8 .. ch*8+7) of a key
 // at (t, h, w), in fp32, and return them rounded to bf16.
@@ -40,67 +45,6 @@ __device__ __forceinline__ void rotate_chunk(const u32x4& x, int ch, int t, int 
     rope_cos_sin(pos, om[pr], &c, &s);
     y[2 * m] = a * c - b * s;
     y[2 * m + 1] = a * s + b * c;
-  }
-}
-
-__global__ __launch_bounds__(256) void append_bf16_kernel(const AppendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kTileTok * kVtStride];
-  __shared__ double om[kD / 2];
-  __shared__ int ax[kD / 2];
-  const int tid = threadIdx.x;
-  const int p0 = blockIdx.y * kTileTok;
-  const int fr = blockIdx.z;
-  const int h = blockIdx.x;
-  const int H = a.heads;
-  if (tid < kD / 2) {
-    int axis;
-    om[tid] = rope_omega(tid, a.rope, &axis);
-    ax[tid] = axis;
-  }
-  __syncthreads();
-  const int f = a.frame0 + fr;
-  const size_t plane = static_cast<size_t>(a.plane_len) * kD;
-  uint16_t* kdst = static_cast<uint16_t*>(a.k) + (static_cast<size_t>(f) * H + h) * plane;
-  uint16_t* vdst = static_cast<uint16_t*>(a.v) + (static_cast<size_t>(f) * H + h) * plane;
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    const int tok = c >> 4, ch = c & 15;
-    const int p = p0 + tok;
-    u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-    if (p < a.n_tok) {
-      const size_t in_off = (static_cast<size_t>(fr * a.n_tok + p) * H + h) * kD + ch * 8;
-      kx = *reinterpret_cast<const u32x4*>(a.k_in + in_off);
-      vx = *reinterpret_cast<const u32x4*>(a.v_in + in_off);
-      u32x4 ky = kx;
-      if (!a.is_text) {
-        float y[8];
-        rotate_chunk(kx, ch, f, p / a.rope.lat_w, p % a.rope.lat_w, om, ax, y);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) ky[m] = pack_bf16x2(y[2 * m], y[2 * m + 1]);
-      }
-      *reinterpret_cast<u32x4*>(kdst + static_cast<size_t>(p) * kD + ch * 8) = ky;
-    }
-    *reinterpret_cast<u32x4*>(&vt[tok * kVtStride + ch * 8]) = vx;
-  }
-  __syncthreads();
-  // transposed V: row d, tokens p0 + 8*tc .. +7
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    const int d = c >> 3, tc = c & 7;
-    const int p = p0 + 8 * tc;
-    if (p < a.plane_len) {
-      u32x4 o;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        uint32_t lo = vt[(8 * tc + 2 * m) * kVtStride + d];
-        uint32_t hi = vt[(8 * tc + 2 * m + 1) * kVtStride + d];
-        o[m] = lo | (hi << 16);
-      }
-      *reinterpret_cast<u32x4*>(vdst + static_cast<size_t>(d) * a.plane_len + p) = o;
-    }
   }
 }
 
@@ -126,7 +70,7 @@ __device__ __forceinline__ LutShape lut_shape(const RopeParams& r) {
 // evaluation (rope_cos_sin), so a table lookup and the direct path agree
 // bit for bit.
 __device__ void build_lut(float2* lut, const LutShape& s, int t, const RopeParams& r, int tid,
-                          int nthreads) {
+                          int nthreads, int row0 = 0) {
   for (int i = tid; i < s.size; i += nthreads) {
     int pair, pos;
     if (i < s.nt) {
@@ -134,8 +78,9 @@ __device__ void build_lut(float2* lut, const LutShape& s, int t, const RopeParam
       pos = t;
     } else if (i < s.nt + s.lat_h * s.nh) {
       const int j = i - s.nt;
-      pos = j / s.nh;
-      pair = s.nt + (j - pos * s.nh);
+      const int rr = j / s.nh;
+      pos = row0 + rr;
+      pair = s.nt + (j - rr * s.nh);
     } else {
       const int j = i - s.nt - s.lat_h * s.nh;
       pos = j / s.nw;
@@ -212,6 +157,83 @@ __device__ __forceinline__ float block_max(float v, float* red, int nthreads) {
   for (int i = 1; i < nthreads / 64; ++i) r = fmaxf(r, red[i]);
   __syncthreads();
   return r;
+}
+
+// kLut: the block tabulates the cos/sin its 64 tokens need (the frame's t
+// band, the h band of the latent rows the tile spans, the w band of every
+// column) in LDS, about 1,200 entries at a 22 x 40 grid against 4,096 direct
+// evaluations; else each pair is evaluated directly.
+template <bool kLut>
+__global__ __launch_bounds__(256) void append_bf16_kernel(const AppendArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kTileTok * kVtStride];
+  __shared__ double om[kLut ? 1 : kD / 2];
+  __shared__ int ax[kLut ? 1 : kD / 2];
+  __shared__ float2 lut[kLut ? kTileLutMax : 1];
+  const int tid = threadIdx.x;
+  const int p0 = blockIdx.y * kTileTok;
+  const int fr = blockIdx.z;
+  const int h = blockIdx.x;
+  const int H = a.heads;
+  const int f = a.frame0 + fr;
+  const int lat_w = a.rope.lat_w;
+  const int row0 = p0 / lat_w;
+  LutShape ls = lut_shape(a.rope);
+  if constexpr (kLut) {
+    ls.lat_h = tile_rows(lat_w);
+    ls.size = ls.nt + ls.lat_h * ls.nh + lat_w * ls.nw;
+    if (!a.is_text) build_lut(lut, ls, f, a.rope, tid, 256, row0);
+  } else if (tid < kD / 2) {
+    int axis;
+    om[tid] = rope_omega(tid, a.rope, &axis);
+    ax[tid] = axis;
+  }
+  __syncthreads();
+  const size_t plane = static_cast<size_t>(a.plane_len) * kD;
+  uint16_t* kdst = static_cast<uint16_t*>(a.k) + (static_cast<size_t>(f) * H + h) * plane;
+  uint16_t* vdst = static_cast<uint16_t*>(a.v) + (static_cast<size_t>(f) * H + h) * plane;
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    const int tok = c >> 4, ch = c & 15;
+    const int p = p0 + tok;
+    u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+    if (p < a.n_tok) {
+      const size_t in_off = (static_cast<size_t>(fr * a.n_tok + p) * H + h) * kD + ch * 8;
+      kx = *reinterpret_cast<const u32x4*>(a.k_in + in_off);
+      vx = *reinterpret_cast<const u32x4*>(a.v_in + in_off);
+      u32x4 ky = kx;
+      if (!a.is_text) {
+        float y[8];
+        if constexpr (kLut)
+          key_chunk<true>(kx, ch, f, p / lat_w - row0, p % lat_w, true, lut, ls, a.rope, y);
+        else
+          rotate_chunk(kx, ch, f, p / lat_w, p % lat_w, om, ax, y);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) ky[m] = pack_bf16x2(y[2 * m], y[2 * m + 1]);
+      }
+      *reinterpret_cast<u32x4*>(kdst + static_cast<size_t>(p) * kD + ch * 8) = ky;
+    }
+    *reinterpret_cast<u32x4*>(&vt[tok * kVtStride + ch * 8]) = vx;
+  }
+  __syncthreads();
+  // transposed V: row d, tokens p0 + 8*tc .. +7
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    const int d = c >> 3, tc = c & 7;
+    const int p = p0 + 8 * tc;
+    if (p < a.plane_len) {
+      u32x4 o;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        uint32_t lo = vt[(8 * tc + 2 * m) * kVtStride + d];
+        uint32_t hi = vt[(8 * tc + 2 * m + 1) * kVtStride + d];
+        o[m] = lo | (hi << 16);
+      }
+      *reinterpret_cast<u32x4*>(vdst + static_cast<size_t>(d) * a.plane_len + p) = o;
+    }
+  }
 }
 
 constexpr int kFp8Threads = 512;
@@ -447,7 +469,13 @@ hipError_t launch_append_int8(const AppendArgs& a, hipStream_t s) {
 hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s) {
   // heads fastest: concurrent blocks read the same tokens' rows of all heads
   dim3 grid(a.heads, (a.plane_len + kTileTok - 1) / kTileTok, a.n_frames);
-  hipLaunchKernelGGL(append_bf16_kernel, grid, dim3(256), 0, s, a);
+  const RopeParams& r = a.rope;
+  const int64_t tile_lut = r.split0 / 2 + static_cast<int64_t>(tile_rows(r.lat_w)) * (r.split1 / 2) +
+                           static_cast<int64_t>(r.lat_w) * (r.split2 / 2);
+  if (!a.is_text && tile_lut <= kTileLutMax)
+    hipLaunchKernelGGL(append_bf16_kernel<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_bf16_kernel<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
