@@ -360,7 +360,9 @@ namespace {
 // LDS [dim][token] tile so that V^T rows leave as 16-byte runs. Text tokens
 // past n_tok get zero codes and zero scales.
 constexpr int kI8Tok = 64;
-constexpr int kI8Stride = kI8Tok + 16;   // LDS row stride (bytes) of the V^T tile
+// LDS row stride (bytes) of the V^T tile: 17 words, so that the byte stores of
+// one token's 128 dims (rows 8 apart per lane) fall in 8 banks, not 2
+constexpr int kI8Stride = kI8Tok + 4;
 
 __device__ __forceinline__ float group16_max(float v) {
 #pragma unroll
@@ -385,23 +387,34 @@ __device__ __forceinline__ uint2 quantize_row8(const float* y, float* scale) {
   return make_uint2(w[0], w[1]);
 }
 
+// kLut: the tile's cos/sin table in LDS, as for the bf16 kernel
+template <bool kLut>
 __global__ __launch_bounds__(256) void append_int8_kernel(const AppendArgs a) {
+  static_assert(kI8Tok == kTileTok, "the tile table covers 64 tokens");
   __shared__ __attribute__((aligned(16))) uint8_t vt[kD * kI8Stride];
-  __shared__ double om[kD / 2];
-  __shared__ int ax[kD / 2];
+  __shared__ double om[kLut ? 1 : kD / 2];
+  __shared__ int ax[kLut ? 1 : kD / 2];
+  __shared__ float2 lut[kLut ? kTileLutMax : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 15, grp = tid >> 4;
   const int p0 = blockIdx.y * kI8Tok;
   const int fr = blockIdx.z;
   const int h = blockIdx.x;
   const int H = a.heads;
-  if (tid < kD / 2) {
+  const int f = a.frame0 + fr;
+  const int lat_w = a.rope.lat_w;
+  const int row0 = p0 / lat_w;
+  LutShape ls = lut_shape(a.rope);
+  if constexpr (kLut) {
+    ls.lat_h = tile_rows(lat_w);
+    ls.size = ls.nt + ls.lat_h * ls.nh + lat_w * ls.nw;
+    build_lut(lut, ls, f, a.rope, tid, 256, row0);
+  } else if (tid < kD / 2) {
     int axis;
     om[tid] = rope_omega(tid, a.rope, &axis);
     ax[tid] = axis;
   }
   __syncthreads();
-  const int f = a.frame0 + fr;
   const size_t pl = static_cast<size_t>(f) * H + h;
   int8_t* kdst = static_cast<int8_t*>(a.k) + pl * a.plane_len * kD;
   int8_t* vdst = static_cast<int8_t*>(a.v) + pl * a.plane_len * kD;
@@ -419,8 +432,10 @@ __global__ __launch_bounds__(256) void append_int8_kernel(const AppendArgs a) {
       const u32x4 kx = *reinterpret_cast<const u32x4*>(a.k_in + in_off);
       const u32x4 vx = *reinterpret_cast<const u32x4*>(a.v_in + in_off);
       float y[8], z[8];
-      if (!a.is_text) {
-        rotate_chunk(kx, lane, f, p / a.rope.lat_w, p % a.rope.lat_w, om, ax, y);
+      if constexpr (kLut) {
+        key_chunk<true>(kx, lane, f, p / lat_w - row0, p % lat_w, true, lut, ls, a.rope, y);
+      } else if (!a.is_text) {
+        rotate_chunk(kx, lane, f, p / lat_w, p % lat_w, om, ax, y);
       } else {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -452,27 +467,37 @@ __global__ __launch_bounds__(256) void append_int8_kernel(const AppendArgs a) {
     const int c = tid + 256 * i;
     const int d = c >> 2, q = c & 3;
     const int p = p0 + 16 * q;
-    if (p < a.plane_len)
+    if (p < a.plane_len) {
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(&vt[d * kI8Stride + 16 * q]);
       *reinterpret_cast<u32x4*>(vdst + static_cast<size_t>(d) * a.plane_len + p) =
-          *reinterpret_cast<const u32x4*>(&vt[d * kI8Stride + 16 * q]);
+          u32x4{row[0], row[1], row[2], row[3]};
+    }
   }
 }
 
 }  // namespace
 
+// video planes whose 64-token tile table fits kTileLutMax entries
+static bool use_tile_lut(const AppendArgs& a) {
+  const RopeParams& r = a.rope;
+  const int64_t size = r.split0 / 2 + static_cast<int64_t>(tile_rows(r.lat_w)) * (r.split1 / 2) +
+                       static_cast<int64_t>(r.lat_w) * (r.split2 / 2);
+  return !a.is_text && size <= kTileLutMax;
+}
+
 hipError_t launch_append_int8(const AppendArgs& a, hipStream_t s) {
   dim3 grid(a.heads, (a.plane_len + kI8Tok - 1) / kI8Tok, a.n_frames);   // heads fastest
-  hipLaunchKernelGGL(append_int8_kernel, grid, dim3(256), 0, s, a);
+  if (use_tile_lut(a))
+    hipLaunchKernelGGL(append_int8_kernel<true>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_int8_kernel<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_append_bf16(const AppendArgs& a, hipStream_t s) {
   // heads fastest: concurrent blocks read the same tokens' rows of all heads
   dim3 grid(a.heads, (a.plane_len + kTileTok - 1) / kTileTok, a.n_frames);
-  const RopeParams& r = a.rope;
-  const int64_t tile_lut = r.split0 / 2 + static_cast<int64_t>(tile_rows(r.lat_w)) * (r.split1 / 2) +
-                           static_cast<int64_t>(r.lat_w) * (r.split2 / 2);
-  if (!a.is_text && tile_lut <= kTileLutMax)
+  if (use_tile_lut(a))
     hipLaunchKernelGGL(append_bf16_kernel<true>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(append_bf16_kernel<false>, grid, dim3(256), 0, s, a);
