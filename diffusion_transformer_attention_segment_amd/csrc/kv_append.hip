@@ -238,7 +238,10 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(const AppendArgs a) {
 
 constexpr int kFp8Threads = 512;
 constexpr int kVtTok = 128;              // tokens per V^T tile
-constexpr int kVtWords = kVtTok / 4 + 4; // LDS row stride of the V^T tile (words): 144 bytes
+// LDS row stride of the V^T tile (words): odd, so that the word stores of the
+// 16 chunks of a token quad (rows 8 apart) fall in 8 banks; rows are read out
+// as 4-byte words
+constexpr int kVtWords = kVtTok / 4 + 1;
 
 // One block per (frame, head) plane (or per head of the text slot): pass 1
 // finds amax of the rotated K and of V, pass 2 quantises and stores (K rows of
@@ -332,9 +335,11 @@ __global__ __launch_bounds__(kFp8Threads) void append_fp8_kernel(const AppendArg
     for (int r = 0; r < 2; ++r) {
       const int idx = tid + r * kFp8Threads;
       const int d = idx >> 3, pc = idx & 7;
-      if (t0 + 16 * pc < a.plane_len)
+      if (t0 + 16 * pc < a.plane_len) {
+        const uint32_t* w = &vt_tile[d * kVtWords + 4 * pc];
         *reinterpret_cast<u32x4*>(vdst + static_cast<size_t>(d) * a.plane_len + t0 + 16 * pc) =
-            *reinterpret_cast<const u32x4*>(&vt_tile[d * kVtWords + 4 * pc]);
+            u32x4{w[0], w[1], w[2], w[3]};
+      }
     }
   }
 }
