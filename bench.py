@@ -115,6 +115,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--layers", type=int, default=0,
                     help="layers per step (default: the workload's, 54 for seg4x54, else 1)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the graphics-clock reading (and its extra untimed steps)")
     ap.add_argument("--text-windows", action="store_true",
                     help="give every session timed text windows (seeded recipe)")
     return ap.parse_args()
@@ -223,11 +225,13 @@ class ClockSampler:
     the observed clock says how much of the gap to the peak is the clock's.
     Reports None where amdsmi is missing or refuses (no driver access)."""
 
-    def __init__(self):
+    def __init__(self, enabled=True):
         import threading
         self.samples, self.info = [], None
         self.stop = threading.Event()
         self.thread = None
+        if not enabled:
+            return
         try:
             import amdsmi
             amdsmi.amdsmi_init()
@@ -508,7 +512,7 @@ def main():
 
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(n_layers)] for _ in range(args.steps)]
-    sampler = ClockSampler()
+    sampler = ClockSampler(enabled=not args.no_clock)
     torch.cuda.synchronize()
     with sampler:
         t0 = time.perf_counter()
