@@ -424,6 +424,26 @@ def measure_dequant(sa, geom, n_frames=99, capacity=128, reps=5):
             "frac_of_hbm_peak": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+def measure_copy_ceiling(nbytes=713_687_040, reps=5):
+    """A plain device-to-device copy of nbytes (torch's copy kernel, the size
+    of the gather's planes): the practical HBM ceiling the HBM-bound rows are
+    also priced against (bytes read + written / time)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    del src, dst
+    return {"bytes_read_plus_written": 2 * nbytes, "ms": round(ms, 4), "GB_per_s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(state, rows_wanted, seed):
     """Time the fp64 oracle on a bounded sample of the first session of the workload."""
     import numpy as np
@@ -615,6 +635,15 @@ def main():
     line["camera_attention"] = measure_camera(sa, state)
     line["history_gather"] = measure_gather(sa, state.geom)
     line["kv_dequant"] = measure_dequant(sa, state.geom)
+    # the practical streaming rate: the faster of two plain copies of the same
+    # size, torch's copy kernel and history_gather (which moves whole planes)
+    ceiling = measure_copy_ceiling()
+    best = max(ceiling["GB_per_s"], line["history_gather"]["GB_per_s"])
+    ceiling["ceiling_GB_per_s"] = best
+    ceiling["ceiling_from"] = ("torch copy" if best == ceiling["GB_per_s"] else "history_gather")
+    line["device_copy_ceiling"] = ceiling
+    for k in ("kv_append", "camera_attention", "history_gather", "kv_dequant"):
+        line[k]["frac_of_copy_ceiling"] = round(line[k]["GB_per_s"] / best, 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(state, args.cpu_rows, args.seed)
     print(json.dumps(line), flush=True)
