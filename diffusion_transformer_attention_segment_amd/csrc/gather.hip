@@ -65,8 +65,10 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   return __uint_as_float(__float_as_uint(v) | sign);
 }
 
-// grid: (ceil(n_tok * 128 / (256 * 16)), n planes (frames or 1), H * 2)
-// Each thread converts 16 consecutive bytes of one (frame, head) plane.
+// grid: (ceil(chunks / 256), n planes (frames or 1), H * 2), 8-byte chunks.
+// Each thread converts 8 consecutive bytes of one (frame, head) plane into
+// 16 bytes of bf16, so that a wave's stores are one contiguous run.
+constexpr int kDqChunk = 8;
 __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
   const int i = blockIdx.y;
   const int h = blockIdx.z >> 1;
@@ -77,35 +79,34 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
                        (static_cast<int64_t>(frame) * a.heads + h) * a.src_len * kD;
   uint16_t* dst = (which ? a.dst_v : a.dst_k) +
                   (static_cast<int64_t>(i) * a.heads + h) * a.dst_len * kD;
-  const int c = blockIdx.x * 256 + threadIdx.x;   // 16-element chunk index
+  const int c = blockIdx.x * 256 + threadIdx.x;   // chunk index
   int row, col, src_row_len, dst_row_len, row_valid, rows;
-  if (which == 0) {          // K: rows = tokens, 128 elements each (8 chunks)
-    rows = a.n_tok; row = c >> 3; col = (c & 7) * 16;
+  if (which == 0) {          // K: rows = tokens, 128 elements each (16 chunks)
+    rows = a.n_tok; row = c >> 4; col = (c & 15) * kDqChunk;
     src_row_len = kD; dst_row_len = kD; row_valid = kD;
   } else {                   // V^T: rows = dims, tokens along the row
-    const int cpr = (a.n_tok + 15) / 16;
-    rows = kD; row = c / cpr; col = (c - row * cpr) * 16;
+    const int cpr = (a.n_tok + kDqChunk - 1) / kDqChunk;
+    rows = kD; row = c / cpr; col = (c - row * cpr) * kDqChunk;
     src_row_len = a.src_len; dst_row_len = a.dst_len; row_valid = a.n_tok;
   }
   if (row >= rows) return;
   const uint8_t* s = src + static_cast<int64_t>(row) * src_row_len + col;
   uint16_t* d = dst + static_cast<int64_t>(row) * dst_row_len + col;
-  const int n = min(16, row_valid - col);
-  if (n == 16 && (reinterpret_cast<uintptr_t>(s) & 15) == 0) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(s);
-    u32x4 lo, hi;
+  const int n = min(kDqChunk, row_valid - col);
+  if (n == kDqChunk && (reinterpret_cast<uintptr_t>(s) & 7) == 0 &&
+      (reinterpret_cast<uintptr_t>(d) & 15) == 0) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(s);
+    u32x4 o;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 2; ++m) {
       // the hardware decode of e4m3 is exact (every code is an fp32 value)
       typedef float f32x2v __attribute__((ext_vector_type(2)));
       const f32x2v f01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(x[m]), false);
       const f32x2v f23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(x[m]), true);
-      const uint32_t p0 = pack_bf16x2(f01[0] * scale, f01[1] * scale);
-      const uint32_t p1 = pack_bf16x2(f23[0] * scale, f23[1] * scale);
-      if (m < 2) { lo[2 * m] = p0; lo[2 * m + 1] = p1; } else { hi[2 * m - 4] = p0; hi[2 * m - 3] = p1; }
+      o[2 * m] = pack_bf16x2(f01[0] * scale, f01[1] * scale);
+      o[2 * m + 1] = pack_bf16x2(f23[0] * scale, f23[1] * scale);
     }
-    reinterpret_cast<u32x4*>(d)[0] = lo;
-    reinterpret_cast<u32x4*>(d)[1] = hi;
+    *reinterpret_cast<u32x4*>(d) = o;
   } else {
     for (int j = 0; j < n; ++j) {
       const float v = e4m3_to_f32(s[j]) * scale;
@@ -115,8 +116,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
 }
 
 // int8 planes with a scale per token and head -> bf16 (code * scale, rounded).
-// Same grid and chunking as dequant_kernel: a K chunk is 16 dims of one token
-// (one scale), a V^T chunk 16 tokens of one dim row (16 scales).
+// Same grid layout as dequant_kernel with 16-byte chunks: a K chunk is 16
+// dims of one token (one scale), a V^T chunk 16 tokens of one dim row (16
+// scales).
 __global__ __launch_bounds__(256) void dequant_int8_kernel(const DequantArgs a) {
   const int i = blockIdx.y;
   const int h = blockIdx.z >> 1;
@@ -163,8 +165,9 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {
-  const int chunks_k = a.n_tok * (kD / 16);
-  const int chunks_v = kD * ((a.n_tok + 15) / 16);
+  const int cb = a.int8 ? 16 : kDqChunk;   // bytes per chunk
+  const int chunks_k = a.n_tok * (kD / cb);
+  const int chunks_v = kD * ((a.n_tok + cb - 1) / cb);
   const int chunks = chunks_k > chunks_v ? chunks_k : chunks_v;
   dim3 grid((chunks + 255) / 256, a.n, a.heads * 2);
   if (a.int8)
