@@ -16,6 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SEGATTN_LIBRARY", os.path.join(_PKG, "libsegattn.so"))
 
 SA_OK = 0
+SA_E_ARG_STATUS = 1
 STATUS_NAMES = {0: "SA_OK", 1: "SA_E_ARG", 2: "SA_E_SHAPE", 3: "SA_E_ALIGN",
                 4: "SA_E_UNSUPPORTED", 5: "SA_E_RANGE", 6: "SA_E_CAPACITY", 7: "SA_E_HIP"}
 KV_BF16, KV_FP8, KV_INT8 = 0, 1, 2
@@ -78,6 +79,7 @@ SIGNATURES = {
                                                          ctypes.POINTER(sa_attn_item), _I]),
     "sa_segment_attention": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_attn_item),
                                             _I, _P, ctypes.c_size_t, _P]),
+    "sa_sparse_keep": (ctypes.c_int32, [_I, _I]),
     "sa_sparse_select_workspace": (ctypes.c_size_t, [ctypes.POINTER(sa_geom),
                                                      ctypes.POINTER(sa_attn_item)]),
     "sa_sparse_select": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_attn_item), _P,
@@ -322,10 +324,12 @@ SPARSE_KEY_BLOCK, SPARSE_QUERY_BLOCK = 64, 256
 
 
 def sparse_keep(n_candidates, percent):
-    """Blocks kept out of n_candidates at `percent` (ceil, at least 1, at most all)."""
-    if n_candidates <= 0:
-        return 0
-    return min(n_candidates, max(1, -(-n_candidates * percent // 100)))
+    """Blocks kept out of n_candidates at `percent` (the library's rule:
+    ceil, at least 1, at most all)."""
+    n = lib().sa_sparse_keep(int(n_candidates), int(percent))
+    if n < 0:
+        _check(SA_E_ARG_STATUS)
+    return int(n)
 
 
 def sparse_select(geom, item, block_list=None, stream=None):

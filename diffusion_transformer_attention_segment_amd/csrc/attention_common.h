@@ -374,8 +374,8 @@ __device__ __forceinline__ float max_other_half(float x) {
 }
 
 // ---- timed text windows -------------------------------------------------------
-// Optional per item ("How one segment is made": a timed action is visible only
-// to the video frames inside its window): text key j is visible to a video
+// Optional per item ("How one segment is made", the second mask: an action's
+// text is hidden from video frames outside its time window): text key j is visible to a video
 // query of absolute frame t only if window[j].x <= t <= window[j].y; text
 // queries see every key. Each workgroup turns the windows into its bit table
 // (layout next to kWindowWords) before its first barrier.

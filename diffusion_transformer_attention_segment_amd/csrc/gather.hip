@@ -80,19 +80,21 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
   uint16_t* dst = (which ? a.dst_v : a.dst_k) +
                   (static_cast<int64_t>(i) * a.heads + h) * a.dst_len * kD;
   const int c = blockIdx.x * 256 + threadIdx.x;   // chunk index
-  int row, col, src_row_len, dst_row_len, row_valid, rows;
+  int row, col, src_row_len, dst_row_len, row_valid, row_out, rows;
   if (which == 0) {          // K: rows = tokens, 128 elements each (16 chunks)
     rows = a.n_tok; row = c >> 4; col = (c & 15) * kDqChunk;
-    src_row_len = kD; dst_row_len = kD; row_valid = kD;
-  } else {                   // V^T: rows = dims, tokens along the row
-    const int cpr = (a.n_tok + kDqChunk - 1) / kDqChunk;
+    src_row_len = kD; dst_row_len = kD; row_valid = kD; row_out = kD;
+  } else {                   // V^T: rows = dims, tokens along the row; the
+                             // destination row's columns past n_tok get zeros
+    const int cpr = (a.dst_len + kDqChunk - 1) / kDqChunk;
     rows = kD; row = c / cpr; col = (c - row * cpr) * kDqChunk;
-    src_row_len = a.src_len; dst_row_len = a.dst_len; row_valid = a.n_tok;
+    src_row_len = a.src_len; dst_row_len = a.dst_len; row_valid = a.n_tok; row_out = a.dst_len;
   }
   if (row >= rows) return;
   const uint8_t* s = src + static_cast<int64_t>(row) * src_row_len + col;
   uint16_t* d = dst + static_cast<int64_t>(row) * dst_row_len + col;
-  const int n = min(kDqChunk, row_valid - col);
+  const int n = min(kDqChunk, row_valid - col);   // codes to convert (<= 0: none)
+  const int n_out = min(kDqChunk, row_out - col);
   if (n == kDqChunk && (reinterpret_cast<uintptr_t>(s) & 7) == 0 &&
       (reinterpret_cast<uintptr_t>(d) & 15) == 0) {
     const u32x2 x = *reinterpret_cast<const u32x2*>(s);
@@ -108,8 +110,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
     }
     *reinterpret_cast<u32x4*>(d) = o;
   } else {
-    for (int j = 0; j < n; ++j) {
-      const float v = e4m3_to_f32(s[j]) * scale;
+    for (int j = 0; j < n_out; ++j) {
+      const float v = j < n ? e4m3_to_f32(s[j]) * scale : 0.f;
       d[j] = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xFFFFu);
     }
   }
@@ -130,27 +132,28 @@ __global__ __launch_bounds__(256) void dequant_int8_kernel(const DequantArgs a) 
   uint16_t* dst = (which ? a.dst_v : a.dst_k) +
                   (static_cast<int64_t>(i) * a.heads + h) * a.dst_len * kD;
   const int c = blockIdx.x * 256 + threadIdx.x;
-  int row, col, src_row_len, dst_row_len, row_valid, rows;
+  int row, col, src_row_len, dst_row_len, row_valid, row_out, rows;
   if (which == 0) {
     rows = a.n_tok; row = c >> 3; col = (c & 7) * 16;
-    src_row_len = kD; dst_row_len = kD; row_valid = kD;
-  } else {
-    const int cpr = (a.n_tok + 15) / 16;
+    src_row_len = kD; dst_row_len = kD; row_valid = kD; row_out = kD;
+  } else {                   // columns past n_tok of a V^T row get zeros
+    const int cpr = (a.dst_len + 15) / 16;
     rows = kD; row = c / cpr; col = (c - row * cpr) * 16;
-    src_row_len = a.src_len; dst_row_len = a.dst_len; row_valid = a.n_tok;
+    src_row_len = a.src_len; dst_row_len = a.dst_len; row_valid = a.n_tok; row_out = a.dst_len;
   }
   if (row >= rows) return;
   const int8_t* s = src + static_cast<int64_t>(row) * src_row_len + col;
   uint16_t* d = dst + static_cast<int64_t>(row) * dst_row_len + col;
-  const int n = min(16, row_valid - col);
-  for (int j = 0; j < n; j += 2) {
-    const float s0 = which ? sc[col + j] : sc[row];
-    const float s1 = which ? (j + 1 < n ? sc[col + j + 1] : 0.f) : sc[row];
-    const float v0 = static_cast<float>(s[j]) * s0;
+  const int n = min(16, row_valid - col);         // codes to convert (<= 0: none)
+  const int n_out = min(16, row_out - col);
+  for (int j = 0; j < n_out; j += 2) {
+    const float s0 = j < n ? (which ? sc[col + j] : sc[row]) : 0.f;
+    const float s1 = j + 1 < n ? (which ? sc[col + j + 1] : sc[row]) : 0.f;
+    const float v0 = j < n ? static_cast<float>(s[j]) * s0 : 0.f;
     const float v1 = j + 1 < n ? static_cast<float>(s[j + 1]) * s1 : 0.f;
     const uint32_t w = pack_bf16x2(v0, v1);
     d[j] = static_cast<uint16_t>(w & 0xFFFFu);
-    if (j + 1 < n) d[j + 1] = static_cast<uint16_t>(w >> 16);
+    if (j + 1 < n_out) d[j + 1] = static_cast<uint16_t>(w >> 16);
   }
 }
 
@@ -167,7 +170,7 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s) {
   const int cb = a.int8 ? 16 : kDqChunk;   // bytes per chunk
   const int chunks_k = a.n_tok * (kD / cb);
-  const int chunks_v = kD * ((a.n_tok + cb - 1) / cb);
+  const int chunks_v = kD * ((a.dst_len + cb - 1) / cb);   // V^T rows up to the destination's length
   const int chunks = chunks_k > chunks_v ? chunks_k : chunks_v;
   dim3 grid((chunks + 255) / 256, a.n, a.heads * 2);
   if (a.int8)

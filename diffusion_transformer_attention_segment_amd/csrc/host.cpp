@@ -588,6 +588,17 @@ sa_status prepare_select(const sa_geom* geom, const sa_attn_item* item, SelectAr
 
 }  // namespace
 
+int32_t sa_sparse_keep(int32_t n_candidates, int32_t percent) {
+  if (percent < 1 || percent > 100) {
+    fail(SA_E_ARG, "sparse_keep: percent %d outside [1, 100]", percent);
+    return -1;
+  }
+  ok();
+  if (n_candidates <= 0) return 0;
+  const int64_t keep = (static_cast<int64_t>(n_candidates) * percent + 99) / 100;
+  return static_cast<int32_t>(std::min<int64_t>(n_candidates, std::max<int64_t>(1, keep)));
+}
+
 size_t sa_sparse_select_workspace(const sa_geom* geom, const sa_attn_item* item) {
   SelectArgs a;
   size_t ws = 0;

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 6
+#define SA_ABI_VERSION 7
 #define SA_HEAD_DIM 128       /* the only head dim the kernels are built for */
 #define SA_MAX_ITEMS 8        /* sessions per sa_segment_attention call     */
 #define SA_MAX_FRAMES_KV 65536
@@ -109,9 +109,9 @@ typedef struct sa_geom {
  *   k_text_scale, v_text_scale  fp8: [H]; int8: [H][text_capacity]
  *                               (NULL for bf16)
  * Element type: bf16 (2 bytes), e4m3 or int8 (1 byte) per `dtype`. int8 is
- * the pages' single-GPU cache ("The 4090 preset": one byte per value plus an
- * FP32 scale per token and head, 4,224 bytes per token and layer at 16
- * heads); fp8 and int8 need P % 16 == 0.
+ * the pages' single-GPU cache format ("The 4090 preset": a byte per value
+ * and an fp32 scale for each token and head, 4,224 bytes per token and layer
+ * at 16 heads); fp8 and int8 need P % 16 == 0 (SA_E_SHAPE otherwise).
  * text_capacity must be a multiple of 16; it may be 0 (no text slot).      */
 typedef struct sa_kv_layer {
   int32_t dtype;
@@ -144,8 +144,9 @@ typedef struct sa_kv_layer {
  *              Text key j is visible to a video query of absolute frame t
  *              only if text_window[2j] <= t <= text_window[2j + 1]; text
  *              queries see every text key. NULL: every query sees every key.
- *              ("How one segment is made": a timed action is visible only to
- *              the video frames inside its window.) 8-byte aligned; read
+ *              ("How one segment is made", its second mask: the text of an
+ *              action that has a time window is hidden from video frames
+ *              outside that window.) 8-byte aligned; read
  *              on the stream by this call's kernels. With video queries and text keys the
  *              item needs n_frames_kv >= 1 (SA_E_ARG otherwise: a video
  *              query sees at least its own segment's frames), and
@@ -193,7 +194,11 @@ const char* sa_last_error(void);
 const char* sa_status_string(int status);
 
 /* Bytes of one layer's cache planes in this layout (K + V planes, text slot,
- * and for fp8 the fp32 scales). Returns 0 and sets the error on bad input.  */
+ * and for fp8 / int8 the fp32 scales). For bf16 a token costs 2 * H * 128 * 2
+ * bytes per layer, the 8,192 bytes of "What 'world memory' stores" at 16
+ * heads; for int8, with a scale per token and head for K and V, the 4,224
+ * bytes of "The 4090 preset". Returns 0 and sets the error on bad input
+ * (SA_E_SHAPE geometry, SA_E_UNSUPPORTED dtype, SA_E_ARG negative capacity). */
 size_t sa_cache_bytes(const sa_geom* geom, int32_t dtype, int32_t frame_capacity,
                       int32_t text_capacity);
 
@@ -213,6 +218,9 @@ sa_status sa_kv_append(const sa_geom* geom, const sa_kv_layer* layer, const void
 
 /* text_append: write n_text text tokens into the layer's text slot (no
  * rotation: text sits at position (0,0,0)). k_in, v_in: bf16 [n_text][H][128].
+ * Source: "How one segment is made" (the segment's text tokens join its
+ * video tokens in the joint attention) and "What 'world memory' stores" (the
+ * cache keeps text tokens' keys and values as well as video tokens').
  * fp8: one scale per head over the n_text tokens; int8: one per token and
  * head, and the tokens [n_text, capacity) get zero codes and zero scales.
  * Slots [n_text, capacity) of the value plane are zeroed so that a partial
@@ -238,10 +246,15 @@ sa_status sa_history_select(int32_t policy, int32_t t_past, int32_t budget, doub
                             int32_t* out_frames, int32_t cap, int32_t* out_n);
 
 /* history_gather: materialise frames[i] of src into frame slot i of dst
- * (i < n), K and V planes and, for fp8, their scales; a byte copy. dst must
- * have the same dtype and frame_capacity >= n. d_frames is a device array.
- * This is the pages' "restore the picked frames" step for callers that want
- * a compact buffer; sa_segment_attention reads through a frame list instead. */
+ * (i < n), K and V planes and, for fp8 / int8, their scales; a byte copy.
+ * dst must have the same dtype and frame_capacity >= n. d_frames is a device
+ * array of n entries in [0, src->frame_capacity) (trusted, as every frame
+ * list). Source: "The 4090 preset" (before each segment only the picked past
+ * frames are brought back from the archive to the GPU); this is that step for
+ * callers that want a compact buffer, while sa_segment_attention reads the
+ * picked frames in place through a frame list.
+ * Errors: SA_E_UNSUPPORTED (dtypes differ), SA_E_CAPACITY (n > dst capacity),
+ * SA_E_RANGE (src has no frames), SA_E_ARG.                                 */
 sa_status sa_history_gather(const sa_geom* geom, const sa_kv_layer* src, const int32_t* d_frames,
                             int32_t n, const sa_kv_layer* dst, void* stream);
 
@@ -252,8 +265,9 @@ sa_status sa_history_gather(const sa_geom* geom, const sa_kv_layer* src, const i
  * split per (row, head) into an e4m3 high part and an e4m3 low part (scaled
  * by 2^-4), and the per-(frame, head) scales applied to the logits and folded
  * into the probabilities. int8 layers run the bf16 path: each key tile is
- * dequantised (code * its token's scale, rounded to bf16) as it is staged
- * ("stored in INT8 and computed in BF16"). All items must share one dtype.
+ * dequantised (code * its token's scale, rounded to bf16) as it is staged,
+ * so the cache stays narrow while the arithmetic is BF16 ("El preset de una
+ * GPU"). All items must share one dtype.
  * Work is split into 256-row query tiles per (item, head). When the tiles do
  * not fill the device evenly, the tiles of the last partial round are split
  * further over their key range, and a second kernel merges the partial
@@ -292,6 +306,13 @@ sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, i
  * n_hist_frames > n_frames_kv), SA_E_CAPACITY (workspace too small),
  * SA_E_ALIGN.                                                               */
 size_t sa_sparse_select_workspace(const sa_geom* geom, const sa_attn_item* item);
+
+/* sparse_keep: how many of n_candidates history blocks a block-sparse pass
+ * keeps at `percent` (the pages keep 25 % of the candidate video blocks):
+ * ceil(n_candidates * percent / 100), at least 1 and at most n_candidates;
+ * 0 for n_candidates <= 0. percent must lie in [1, 100] (else -1 and the
+ * error is set). Host only, pure.                                           */
+int32_t sa_sparse_keep(int32_t n_candidates, int32_t percent);
 sa_status sa_sparse_select(const sa_geom* geom, const sa_attn_item* item, void* workspace,
                            size_t workspace_bytes, int32_t* block_list, void* stream);
 
@@ -317,11 +338,15 @@ sa_status sa_camera_attention(const sa_geom* geom, const void* q, int32_t n_fram
 
 /* kv_dequant: fp8 frames[i] of src -> bf16 frame slot i of dst (K and V
  * planes: value = code * scale, rounded to bf16), and, when n_text > 0, the
- * first n_text tokens of the text slot. The pages' "stored low precision,
- * computed in BF16" route ("El preset de una GPU", inferencekey.com). src
- * may also be int8 (value = code * the token's scale).
+ * first n_text tokens of the text slot; the destination's text value plane
+ * gets zeros in its columns [n_text, dst->text_capacity), so that attention
+ * over the first n_text text keys reads finite values there (the K rows
+ * past n_text are never read). The pages' route of a cache kept in a narrow
+ * format with BF16 arithmetic ("El preset de una GPU", inferencekey.com).
+ * src may also be int8 (value = code * the token's scale).
  * dst must be a bf16 layer with frame_capacity >= n_frames and
- * text_capacity >= n_text.                                                  */
+ * text_capacity >= n_text. Errors: SA_E_UNSUPPORTED (src bf16 or dst not
+ * bf16), SA_E_CAPACITY, SA_E_RANGE (src has no frames), SA_E_ARG.          */
 sa_status sa_kv_dequant(const sa_geom* geom, const sa_kv_layer* src, const int32_t* d_frames,
                         int32_t n_frames, int32_t n_text, const sa_kv_layer* dst, void* stream);
 

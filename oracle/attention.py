@@ -55,8 +55,9 @@ def timed_text_visibility(q_frame, key_text, window):
     """Which keys each query row may see under timed text windows.
 
     The pages (same article, "How one segment is made") give a second mask
-    beside the segment-wise causal one: a timed action is visible only to the
-    video frames inside its window. Reading (the window encoding is not on the
+    beside the segment-wise causal one: the text of an action that carries a
+    time window is hidden from the video frames outside it, so the action is
+    not acted out early. Reading (the window encoding is not on the
     pages): text token j carries an inclusive latent-frame range
     window[j] = (first, last); a video query in frame t sees it iff
     first <= t <= last; text queries and every non-text key are unaffected.

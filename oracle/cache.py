@@ -4,8 +4,8 @@ Sources: "Hy-Nomas: an 8.6B world model whose memory is a KV cache"
 (ai.thesatyajit.com), sections "What 'world memory' stores" (K and V are each
 2,048 wide per token and layer; BF16 costs 8,192 bytes per token per layer,
 389 MB per 880-token latent frame over 54 layers) and "The 4090 preset" (the
-INT8 cache stores one byte per value plus an FP32 scale per token and head,
-4,224 bytes per token per layer; 18 kept frames are about 3.6 GB); section
+INT8 cache spends a byte on each value and an FP32 scale on each token and
+head: 4,224 bytes per token per layer; 18 kept frames are about 3.6 GB); section
 "How one segment is made" (3D RoPE on keys; 880 tokens per latent frame).
 
 Plane layout (the library's own design; the pages fix no layout). Per layer,

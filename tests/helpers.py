@@ -238,16 +238,26 @@ class Session:
         wl = self.wl
         hs = list(range(wl.heads)) if heads is None else list(heads)
         F, P = wl.lat_t, wl.P
-        ks, vs, vsc_key = [], [], []
-        for f in self.frames:
-            seg, fo = divmod(f, F)
-            kin = self.raw_k[seg][fo * P:(fo + 1) * P].float().cpu().double().numpy()
-            vin = self.raw_v[seg][fo * P:(fo + 1) * P].float().cpu().double().numpy()
+        raw = [(f, self.raw_k[f // F][(f % F) * P:(f % F + 1) * P].float().cpu().double().numpy(),
+                self.raw_v[f // F][(f % F) * P:(f % F + 1) * P].float().cpu().double().numpy())
+               for f in self.frames]
+
+        def one_frame(args):     # the oracle's own append and decode of one frame
+            f, kin, vin = args
             kc, ksc, vc, vsc = ocache.append_fp8(kin, vin, f, wl.lat_h, wl.lat_w, wl.split,
                                                  self.geom.rope_theta)
-            ks.append(ocache.dequant(kc[0], ksc[0][:, None, None]).transpose(1, 0, 2)[:, hs])
-            vs.append(ocache.dequant(vc[0], vsc[0][:, None, None]).transpose(2, 0, 1)[:, hs])
-            vsc_key.append(np.repeat(vsc[0][None, hs], P, axis=0))
+            return (ocache.dequant(kc[0], ksc[0][:, None, None]).transpose(1, 0, 2)[:, hs],
+                    ocache.dequant(vc[0], vsc[0][:, None, None]).transpose(2, 0, 1)[:, hs],
+                    np.repeat(vsc[0][None, hs], P, axis=0))
+
+        import concurrent.futures   # frames are independent: one per worker thread
+        with concurrent.futures.ThreadPoolExecutor(max_workers=16) as ex:
+            per_frame = list(ex.map(one_frame, raw))
+        del raw
+        ks = [x[0] for x in per_frame]
+        vs = [x[1] for x in per_frame]
+        vsc_key = [x[2] for x in per_frame]
+        del per_frame
         tk = self.text_k.float().cpu().double().numpy()
         tv = self.text_v.float().cpu().double().numpy()
         kc, ksc, vc, vsc = ocache.append_text_fp8(tk, tv)
@@ -326,6 +336,35 @@ class Session:
         if heads is not None:
             o, l = o[:, list(heads)], l[:, list(heads)]
         return o, l
+
+
+def oracle_all_heads(s, rows=None, workers=16):
+    """Session.oracle over every head, one head per worker thread (the
+    oracle's numpy calls release the interpreter lock; BLAS is held to one
+    thread per worker). Same arithmetic as s.oracle(rows): the heads are
+    independent. Prints a line per finished head."""
+    import concurrent.futures
+    from threadpoolctl import threadpool_limits
+    wl = s.wl
+    k, v, kpos = s.raw_keys()
+    q = s.q.float().cpu().double().numpy()
+    qpos = s.q_positions()
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    n = q.shape[0] if rows is None else len(rows)
+    out = np.zeros((n, wl.heads, wl.head_dim))
+    lse = np.zeros((n, wl.heads))
+
+    def one(h):
+        o, l = oatt.segment_attention(q[:, h:h + 1], qpos, k[:, h:h + 1], kpos, v[:, h:h + 1],
+                                      wl.split, s.geom.rope_theta, scale, rows=rows)
+        out[:, h] = o[:, 0]
+        lse[:, h] = l[:, 0]
+        print(f"  oracle head {h} done", flush=True)
+
+    with threadpool_limits(1):
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one, range(wl.heads)))
+    return out, lse
 
 
 def split_query_fp8(q):

@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 6
+    assert sa.abi_version() == 7
 
 
 def test_status_strings(lib):
@@ -71,6 +71,24 @@ def test_history_select_matches_oracle(lib, policy):
                                         recent_segments=3)
                 want = osel.select_anchor_recent(T, budget, 3)
             assert got == want.tolist(), (policy, T, budget)
+
+
+def test_sparse_keep_matches_oracle(lib):
+    """The library's keep count for block-sparse history equals the oracle's
+    rule (ceil of the percentage, at least one block, at most all of them),
+    bit for bit over a sweep; a percentage outside [1, 100] is refused."""
+    from oracle import sparse as osp
+    for n in list(range(0, 300)) + [1679, 1680, 3360, 8191, 8192]:
+        for pct in (1, 10, 25, 33, 50, 99, 100):
+            want = osp.keep_count(n, pct) if n > 0 else 0
+            assert lib.sa_sparse_keep(n, pct) == want, (n, pct)
+            assert sa.sparse_keep(n, pct) == want
+    assert sa.sparse_keep(120 * 14, 25) == 420
+    for pct in (0, -5, 101):
+        assert lib.sa_sparse_keep(10, pct) == -1
+        assert b"percent" in lib.sa_last_error()
+        with pytest.raises(B.SegAttnError):
+            sa.sparse_keep(10, pct)
 
 
 def test_history_select_power_printed_example(lib):

@@ -128,3 +128,43 @@ def test_dequant_int8_matches_oracle(n_text):
         for h in range(H):
             assert np.array_equal(tk[h, :n_text], _dequant_int8_ref(sk[h, :n_text], kts[h, :n_text, None]))
             assert np.array_equal(tv[h, :, :n_text], _dequant_int8_ref(sv[h, :, :n_text], vts[h, None, :n_text]))
+
+
+@pytest.mark.parametrize("src_kind", ["fp8", "int8"])
+def test_dequant_into_uninitialised_layer_then_attend(src_kind):
+    """kv_dequant into a bf16 layer whose planes hold NaN, then attention over
+    the dequantised frames and n_text = 29 text keys (not a multiple of the
+    64-key tile): the dequant writes zeros into the value plane's text columns
+    [29, 32), so the attention meets finite values there and the output
+    matches the oracle over the values the narrow cache stores (bf16 bar;
+    the dequant's own bf16 rounding is far inside it)."""
+    from helpers import Session
+    import seeded_inputs as si
+    wl = si.Workload(f"dq_{src_kind}", heads=2, lat_t=2, lat_h=4, lat_w=8, n_text=29,
+                     prior_segments=(1,), kv_dtype=src_kind)
+    s = Session(wl, seed=5, layer=0, session=0)
+    n_frames = len(s.frames)
+    assert s.frames == list(range(n_frames))           # slot i of dst holds frame i
+    dst = sa.KVLayer.allocate(s.geom, sa.KV_BF16, n_frames, 32)
+    nan = torch.tensor(0x7FC0, dtype=torch.int16).view(torch.bfloat16).item()
+    for t in (dst.k, dst.v, dst.k_text, dst.v_text):
+        t.fill_(nan)
+    sa.kv_dequant(s.geom, s.kv, s.d_frames, n_frames, wl.n_text, dst)
+    torch.cuda.synchronize()
+    assert torch.all(dst.v_text[:, :, wl.n_text:] == 0)
+    assert not torch.isnan(dst.v_text[:, :, :wl.n_text].float()).any()
+    out = torch.empty_like(s.q)
+    item = sa.AttnItem(s.q, dst, s.d_frames, n_frames, wl.n_text, out, frame0_q=s.S * wl.lat_t,
+                       n_frames_q=wl.lat_t, n_text_q=wl.n_text)
+    sa.segment_attention(s.geom, [item], workspace=None)
+    torch.cuda.synchronize()
+    got = out.float().cpu().double().numpy()
+    assert np.all(np.isfinite(got))
+    if src_kind == "fp8":
+        want, _, _ = s.oracle_fp8_cache()
+    else:
+        want, _ = s.oracle_int8_cache()
+    err = np.abs(got - want)
+    print(f"dequant {src_kind} then attend: max_abs={err.max():.3e} mean_abs={err.mean():.3e}",
+          flush=True)
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3

@@ -1,6 +1,7 @@
-"""GPU parity of segment_attention over an int8 cache (one byte per value and
-an fp32 scale per token and head: the pages' single-GPU format, "The 4090
-preset"; "stored in INT8 and computed in BF16", "El preset de una GPU").
+"""GPU parity of segment_attention over an int8 cache (a byte per value with
+an fp32 scale for each token and head: the pages' single-GPU format, "The
+4090 preset"; the cache is kept in INT8 while the arithmetic runs in BF16,
+"El preset de una GPU").
 
 The kernel dequantises each staged key tile to bf16 (code times its token's
 scale) and runs the bf16 path. Reference: the oracle over the values the cache

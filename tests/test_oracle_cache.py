@@ -14,6 +14,7 @@ import os
 import numpy as np
 
 from oracle import cache, numerics, rope
+from e4m3_cases import TIE_CODES, TIE_VALUES, nearest_code_brute
 
 FIG = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
 
@@ -126,23 +127,73 @@ def test_quantize_plane_fp8_properties():
     assert s0 == 1.0 and not z.any()
 
 
-def test_append_fp8_v_codes_follow_fp32_decision():
-    lat_h, lat_w, H, F = 4, 6, 2, 2
+def _fp32_plane_codes(x):
+    """Expected codes and scale of one plane from the reading of the format
+    (amax, 448 / amax and the scaled values in fp32), with the codes found by
+    exhaustive nearest-code search rather than the oracle's encoder."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.abs(x32).max())
+    y = (x32 * (np.float32(448.0) / amax)).astype(np.float32).astype(np.float64)
+    return nearest_code_brute(y, numerics.e4m3_decode), amax / np.float32(448.0)
+
+
+def test_append_fp8_codes_are_brute_force_nearest_per_plane():
+    """V codes of every (frame, head) plane are the nearest e4m3 codes of
+    v * 448 / amax(plane), found by exhaustive search; every plane gets its
+    own scale (each (frame, head) is scaled by its own factor here, so a
+    scale shared across frames or heads fails); V is transposed per plane
+    (V^T[d][p] holds token p's dim d); K codes are those of the rotated keys
+    under the K plane's own scale."""
+    lat_h, lat_w, H, F = 4, 6, 3, 2
     P = lat_h * lat_w
-    k = _bf16_inputs((F * P, H, 128), 5)
-    v = _bf16_inputs((F * P, H, 128), 6) * 3
+    fac = np.array([[0.5, 3.0, 1.25], [7.0, 0.75, 2.0]])           # [F, H]
+    k = _bf16_inputs((F * P, H, 128), 5) * np.repeat(fac, P, axis=0)[:, :, None]
+    v = numerics.bf16_round(_bf16_inputs((F * P, H, 128), 6) * np.repeat(fac[::-1], P, axis=0)[:, :, None])
     Kc, Ks, Vc, Vs = cache.append_fp8(k, v, 3, lat_h, lat_w, (16, 56, 56), 10000.0)
+    assert Kc.shape == (F, H, P, 128) and Vc.shape == (F, H, 128, P)
+    assert Ks.shape == (F, H) and Vs.shape == (F, H)
+    kr = rope.rope3d(k, rope.video_positions(3, F, lat_h, lat_w))
     for f in range(F):
         for h in range(H):
-            plane = v[f * P:(f + 1) * P, h, :].T.astype(np.float32)    # [D, P]
-            amax = np.float32(np.abs(plane).max())
-            inv = np.float32(448.0) / amax
-            y = (plane * inv).astype(np.float32)
-            assert np.array_equal(Vc[f, h], numerics.e4m3_encode(y.astype(np.float64)))
-            assert Vs[f, h] == amax / np.float32(448.0)
-    dk = cache.dequant(Kc[0, 0], Ks[0, 0])
-    kr = rope.rope3d(k[:P], rope.video_positions(3, 1, lat_h, lat_w))[:, 0, :]
-    assert np.max(np.abs(dk - kr)) <= np.abs(kr).max() * 2.0 ** -4
+            vplane = v[f * P:(f + 1) * P, h, :]                        # [P, D]
+            want, scale = _fp32_plane_codes(vplane)
+            assert Vs[f, h] == scale
+            assert np.array_equal(Vc[f, h], want.T)
+            kplane = kr[f * P:(f + 1) * P, h, :]
+            want_k, kscale = _fp32_plane_codes(kplane.astype(np.float32))
+            assert Ks[f, h] == kscale
+            assert np.array_equal(Kc[f, h], want_k)
+    assert len(set(Vs.reshape(-1).tolist())) == F * H       # one scale per plane
+
+
+def test_append_text_fp8_scale_per_head_and_hand_worked_codes():
+    """The text slot: one scale per head over all of its tokens, no rotation,
+    V transposed to [H][D][n]. Head 0 holds the hand-worked tie values in
+    token 0 and smaller values elsewhere, so its amax is 448 and its scale
+    exactly 1: token 0's codes are the hand-worked ones, and the other
+    tokens' codes are the plain e4m3 roundings of their values (a per-token
+    scale would stretch them). Head 1 is head 0 halved: scale exactly 0.5 and
+    the same codes (a scale shared by the heads would give other codes)."""
+    n, H = 12, 2
+    rng = np.random.default_rng(9)
+    base = numerics.bf16_round(rng.standard_normal((n, 128)) * 40.0)
+    base = np.clip(base, -400.0, 400.0)
+    base[0] = np.resize(np.array(TIE_VALUES), 128)
+    x = np.stack([base, base * 0.5], axis=1)                      # [n, H, D]
+    vx = x[:, :, ::-1].copy()                                     # V differs from K
+    Kc, Ks, Vc, Vs = cache.append_text_fp8(x, vx)
+    assert Kc.shape == (H, n, 128) and Vc.shape == (H, 128, n)
+    assert Ks.tolist() == [1.0, 0.5] and Vs.tolist() == [1.0, 0.5]
+    assert np.array_equal(Kc[0, 0, :16], TIE_CODES)
+    assert np.array_equal(Kc[1], Kc[0])
+    assert np.array_equal(Kc[0], nearest_code_brute(base, numerics.e4m3_decode))
+    # V^T[h][d][i] holds token i's dim d; token 0 of V holds the ties reversed
+    assert np.array_equal(Vc[0, 127 - np.arange(16), 0], TIE_CODES)
+    assert np.array_equal(Vc[0], nearest_code_brute(base[:, ::-1], numerics.e4m3_decode).T)
+    assert np.array_equal(Vc[1], Vc[0])
+    # the hand-worked codes are also those of exhaustive search
+    assert np.array_equal(nearest_code_brute(np.array(TIE_VALUES), numerics.e4m3_decode),
+                          TIE_CODES)
 
 
 # ------------------------------------------------------------------- int8 cache
