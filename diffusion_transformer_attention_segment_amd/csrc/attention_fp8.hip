@@ -9,23 +9,25 @@
 // cache is stored narrow and computed at higher precision).
 //
 // Scales. The cache holds e4m3 codes with one fp32 scale per (frame, head)
-// plane (per head for the text slot). A key tile never straddles a frame, so
-// its K and V scales are uniform over the tile:
-//   logit (log2 units) = (q_code . k_code) * coef,
-//   coef = q_scale[row] * k_scale[tile] * softmax scale * log2(e);
-//   P'_j = exp2(x_j), x_j = logit_j + log2(pf) - m, pf = 256 * v_scale[tile] / vmax,
-// i.e. P'_j = p_j * pf with p_j = exp2(logit_j - m) -- the probability scale
-// rides in the exponent's FMA offset, one FMA per key. Then
-//   O = sum_j p_j v_j = (vmax / 256) * sum_j P'_j v_code_j,
-// where vmax is the largest V scale among the session's kept planes for this
-// head. The running max m moves (rarely) when some x passes 8.5, i.e. P'
-// would pass 362 (e4m3 max 448), to put the largest x at 8.
-// Queries are rotated in fp32, then quantised per (row, head) in two parts:
-// q_scale = amax / 448, y = q * 448 / amax, hi = e4m3(y), lo = e4m3(16 (y - hi)),
-// q ~ (hi + lo / 16) q_scale. Q is never stored, so its split costs only a
-// second MFMA per step (the low part enters through the MFMA's E8M0 block
-// scale 2^-4) and removes most of the query's share of the fp8 error; the
-// cache keeps one e4m3 code per value.
+// plane (per head for the text slot), a power of two 2^e (sa_kv_append writes
+// such scales). A key tile never straddles a frame, so its K and V scales are
+// uniform over the tile, and the fp32 exponent field of a scale is exactly the
+// E8M0 block scale (127 + e) of the fp8 MFMA: the K scale enters Q.K^T and the
+// V scale enters P.V through the A operand's block scale, exactly.
+// Queries are rotated in fp32 and multiplied by softmax scale * log2(e), then
+// quantised per (row, head) with a power-of-two scale 2^qe (amax <= 448 * 2^qe)
+// in two parts: y = q * 2^-qe, hi = e4m3(y), lo = e4m3(16 (y - hi)),
+// q ~ (hi + lo / 16) 2^qe. Both parts enter through the B operand's block
+// scales (127 + qe and 127 + qe - 4, two bytes of one register), so the QK^T
+// accumulator holds the logit in log2 units. It starts from 8 - m (m the
+// running max), so a probability is P'_j = exp2(acc_j) = 2^8 p_j, one exp2
+// per key (the 2^8 keeps small probabilities out of the e4m3 subnormal
+// range); O = sum_j P'_j v_j and l = sum_j P'_j, out = O / l. The running
+// max m moves (rarely) when some acc passes 8.5, i.e. P' would pass 362
+// (e4m3 max 448), to put the largest acc at 8.
+// Q is never stored, so its split costs only a second MFMA per k-step and
+// removes most of the query's share of the fp8 error; the cache keeps one
+// e4m3 code per value.
 //
 // Layout. One workgroup = 8 waves = 256 query rows of one head; each wave owns
 // 32 rows. S^T = K Q^T with A = K rows (32 keys x 64 dims per MFMA), B = Q^T.
@@ -58,21 +60,29 @@ constexpr int KS8 = kD + 16;           // LDS row stride of the K tile (bytes)
 constexpr int VS8 = BN + 16;           // LDS row stride of the V^T tile (bytes)
 constexpr int KT8 = BN * KS8;          // bytes of one K stage
 constexpr int VT8 = kD * VS8;          // bytes of one V^T stage
-constexpr float kPScale = 256.0f;      // probability pre-scale before e4m3 (log2: 8)
-constexpr float kPTarget = 8.0f;       // log2 of P' for the largest key after a rescale
+constexpr float kPTarget = 8.0f;       // log2 of P' for the largest key (probabilities x 2^8)
 constexpr float kTrigger = 8.5f;       // log2 of P' above which the running max moves
+constexpr int kMaxShift = 64;          // largest shift of the running max carried by the
+                                       // P.V block scale before O is renormalised
 
 typedef int i32x8v __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ f32x16 mfma_fp8(const i32x8v& a, const i32x8v& b, const f32x16& c) {
-  // A and B formats 0 = e4m3; E8M0 block scales 127 = 2^0
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+// e4m3 x e4m3 MFMA with E8M0 block scales: A scaled by 2^(sa - 127), B by
+// 2^(byte 0 of sb - 127) (mfma_fp8) or 2^(byte 1 of sb - 127) (mfma_fp8_b1).
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8v& a, const i32x8v& b, const f32x16& c,
+                                           int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+__device__ __forceinline__ f32x16 mfma_fp8_b1(const i32x8v& a, const i32x8v& b, const f32x16& c,
+                                              int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 1, sb);
 }
 
-// Same, with the B operand scaled by 2^-4 through its E8M0 block scale (123):
-// adds the low part of a split operand.
-__device__ __forceinline__ f32x16 mfma_fp8_blo(const i32x8v& a, const i32x8v& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 123);
+constexpr int kUnitScale = 127;   // E8M0 2^0
+
+// E8M0 block scale of a power-of-two fp32 scale: its exponent field
+__device__ __forceinline__ int e8m0_of(float pow2_scale) {
+  return static_cast<int>((__float_as_uint(pow2_scale) >> 23) & 0xFFu);
 }
 
 // two fp32 -> two e4m3 codes (round to nearest even) in the low or high half
@@ -134,29 +144,27 @@ __device__ __forceinline__ void window_mask_tile(f32x16* s, uint32_t word) {
 // per-tile scalars carried through the load ring
 struct TileInfo {
   int nvalid;   // valid-key count, sign bit set on a text tile under windows
-  float kscale;
-  float vscale;
+  int ksc;      // E8M0 block scales of the tile's K and V planes
+  int vsc;
 };
 
 __device__ __forceinline__ TileInfo tile_info(const TileCursor& c, int flag_fi) {
   TileInfo t;
   t.nvalid = cursor_mask_code(c, flag_fi);
-  t.kscale = c.kscale;
-  t.vscale = c.vscale;
+  t.ksc = e8m0_of(c.kscale);
+  t.vsc = e8m0_of(c.vscale);
   return t;
 }
 
 // Word w (0..3) of one 32-key block: keys 4w .. 4w+3 of the block (registers
-// 4w ..), as P' = exp2(x) with x = s * coef + off, packed e4m3. Accumulates the
-// fp32 sum and the max of x.
-__device__ __forceinline__ uint32_t prob_word_blk(const f32x16& s, int w, float coef, float off,
-                                                  float& l, float& mx) {
+// 4w ..), as P' = exp2(acc) packed e4m3. Accumulates the fp32 sum of P' and
+// the max of acc.
+__device__ __forceinline__ uint32_t prob_word_blk(const f32x16& s, int w, float& l, float& mx) {
   const int r = w * 4;
-  const float x0 = fmaf(s[r], coef, off), x1 = fmaf(s[r + 1], coef, off);
-  const float x2 = fmaf(s[r + 2], coef, off), x3 = fmaf(s[r + 3], coef, off);
-  mx = fmaxf(fmaxf(mx, x0), fmaxf(x1, fmaxf(x2, x3)));
-  const float p0 = __builtin_amdgcn_exp2f(x0), p1 = __builtin_amdgcn_exp2f(x1);
-  const float p2 = __builtin_amdgcn_exp2f(x2), p3 = __builtin_amdgcn_exp2f(x3);
+  mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
+  mx = fmaxf(fmaxf(mx, s[r + 2]), s[r + 3]);
+  const float p0 = __builtin_amdgcn_exp2f(s[r]), p1 = __builtin_amdgcn_exp2f(s[r + 1]);
+  const float p2 = __builtin_amdgcn_exp2f(s[r + 2]), p3 = __builtin_amdgcn_exp2f(s[r + 3]);
   uint32_t word = cvt_fp8x2<false>(p0, p1, 0u);
   word = cvt_fp8x2<true>(p2, p3, word);
   l += (p0 + p1) + (p2 + p3);
@@ -164,16 +172,14 @@ __device__ __forceinline__ uint32_t prob_word_blk(const f32x16& s, int w, float 
 }
 
 // Word w (0..7) of a tile's probabilities: the four keys 4w .. 4w+3 of the
-// lane's 32 (S^T block w / 4, registers 4 (w % 4) ..), as P' = exp2(x) with
-// x = s * coef + off, packed e4m3. Accumulates the fp32 sum and the max of x.
-__device__ __forceinline__ uint32_t prob_word(const f32x16* s, int w, float coef, float off,
-                                              float& l, float& mx) {
+// lane's 32 (S^T block w / 4, registers 4 (w % 4) ..), as P' = exp2(acc)
+// packed e4m3. Accumulates the fp32 sum of P' and the max of acc.
+__device__ __forceinline__ uint32_t prob_word(const f32x16* s, int w, float& l, float& mx) {
   const int b = w >> 2, r = (w & 3) * 4;
-  const float x0 = fmaf(s[b][r], coef, off), x1 = fmaf(s[b][r + 1], coef, off);
-  const float x2 = fmaf(s[b][r + 2], coef, off), x3 = fmaf(s[b][r + 3], coef, off);
-  mx = fmaxf(fmaxf(mx, x0), fmaxf(x1, fmaxf(x2, x3)));
-  float p0 = __builtin_amdgcn_exp2f(x0), p1 = __builtin_amdgcn_exp2f(x1);
-  float p2 = __builtin_amdgcn_exp2f(x2), p3 = __builtin_amdgcn_exp2f(x3);
+  mx = fmaxf(fmaxf(mx, s[b][r]), s[b][r + 1]);
+  mx = fmaxf(fmaxf(mx, s[b][r + 2]), s[b][r + 3]);
+  float p0 = __builtin_amdgcn_exp2f(s[b][r]), p1 = __builtin_amdgcn_exp2f(s[b][r + 1]);
+  float p2 = __builtin_amdgcn_exp2f(s[b][r + 2]), p3 = __builtin_amdgcn_exp2f(s[b][r + 3]);
   uint32_t word = cvt_fp8x2<false>(p0, p1, 0u);
   word = cvt_fp8x2<true>(p2, p3, word);
   l += (p0 + p1) + (p2 + p3);
@@ -183,15 +189,29 @@ __device__ __forceinline__ uint32_t prob_word(const f32x16* s, int w, float coef
   return word;
 }
 
+// The accumulator seed: 16 copies of this lane's 8 - m, written into the
+// registers of the S^T block it starts (the value passes through an empty asm,
+// so the copies are made where they are used and no 16-register seed stays
+// live across the loop).
+__device__ __forceinline__ f32x16 splat_seed(float negm8) {
+  asm volatile("" : "+v"(negm8));
+  f32x16 c;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) c[r] = negm8;
+  return c;
+}
+
 // S^T block of a tile from its K rows at kp (this lane's row, byte 32 g):
-// two 64-dim steps, high and low query parts each, added to the seed c.
+// two 64-dim steps, high and low query parts each (block scales: the tile's
+// K scale ksc; qsc holds the query's high and low part scales), added to the
+// seed c.
 __device__ __forceinline__ f32x16 qk_block(const uint8_t* kp, const i32x8v* qf, const i32x8v* ql,
-                                           const f32x16& c = f32x16{}) {
+                                           int ksc, int qsc, const f32x16& c) {
   const i32x8v k0 = lds_read32(kp), k1 = lds_read32(kp + 64);
-  f32x16 s = mfma_fp8(k0, qf[0], c);
-  s = mfma_fp8_blo(k0, ql[0], s);
-  s = mfma_fp8(k1, qf[1], s);
-  return mfma_fp8_blo(k1, ql[1], s);
+  f32x16 s = mfma_fp8(k0, qf[0], c, ksc, qsc);
+  s = mfma_fp8_b1(k0, ql[0], s, ksc, qsc);
+  s = mfma_fp8(k1, qf[1], s, ksc, qsc);
+  return mfma_fp8_b1(k1, ql[1], s, ksc, qsc);
 }
 
 // First part of a step (tile t), S^T of the tile in s (two 32-key blocks):
@@ -203,103 +223,82 @@ __device__ __forceinline__ f32x16 qk_block(const uint8_t* kp, const i32x8v* qf, 
 // tile's fp32 sum of P'; mx gets the max of x over the row.
 template <typename Boundary>
 __device__ __forceinline__ float fp8_step_a(const uint8_t* vprev, const uint8_t* kn0,
-                                            const i32x8v& p_prev, f32x16* o, const i32x8v* qf,
-                                            const i32x8v* ql, f32x16* s, float coef, float off,
+                                            const i32x8v& p_prev, int vsc_prev, int psc, f32x16* o,
+                                            const i32x8v* qf, const i32x8v* ql, int ksc_next,
+                                            int qsc, float negm8, f32x16* s,
                                             i32x8v& p_cur, float& mx, Boundary&& boundary) {
   float l = 0.f;
   mx = -INFINITY;
   // slot 0: PV 0, 1; barrier; words 0, 1
   const i32x8v v0 = lds_read32(vprev), v1 = lds_read32(vprev + 32 * VS8);
-  o[0] = mfma_fp8(v0, p_prev, o[0]);
-  o[1] = mfma_fp8(v1, p_prev, o[1]);
+  o[0] = mfma_fp8(v0, p_prev, o[0], vsc_prev, psc);
+  o[1] = mfma_fp8(v1, p_prev, o[1], vsc_prev, psc);
   boundary();
   const i32x8v v2 = lds_read32(vprev + 64 * VS8), v3 = lds_read32(vprev + 96 * VS8);
-  p_cur[0] = static_cast<int>(prob_word(s, 0, coef, off, l, mx));
-  p_cur[1] = static_cast<int>(prob_word(s, 1, coef, off, l, mx));
+  p_cur[0] = static_cast<int>(prob_word(s, 0, l, mx));
+  p_cur[1] = static_cast<int>(prob_word(s, 1, l, mx));
   __builtin_amdgcn_sched_barrier(0);
   // slot 1: PV 2, 3; words 2, 3 (block 0 of tile t is then free)
   const i32x8v k0 = lds_read32(kn0), k1 = lds_read32(kn0 + 64);
-  o[2] = mfma_fp8(v2, p_prev, o[2]);
-  p_cur[2] = static_cast<int>(prob_word(s, 2, coef, off, l, mx));
-  o[3] = mfma_fp8(v3, p_prev, o[3]);
-  p_cur[3] = static_cast<int>(prob_word(s, 3, coef, off, l, mx));
+  o[2] = mfma_fp8(v2, p_prev, o[2], vsc_prev, psc);
+  p_cur[2] = static_cast<int>(prob_word(s, 2, l, mx));
+  o[3] = mfma_fp8(v3, p_prev, o[3], vsc_prev, psc);
+  p_cur[3] = static_cast<int>(prob_word(s, 3, l, mx));
   __builtin_amdgcn_sched_barrier(0);
-  // slot 2: QK^T block 0 of tile t+1, first k-step; words 4, 5
-  s[0] = mfma_fp8(k0, qf[0], f32x16{});
-  p_cur[4] = static_cast<int>(prob_word(s, 4, coef, off, l, mx));
-  s[0] = mfma_fp8_blo(k0, ql[0], s[0]);
-  p_cur[5] = static_cast<int>(prob_word(s, 5, coef, off, l, mx));
+  // slot 2: QK^T block 0 of tile t+1, first k-step (from the seed 8 - m);
+  // words 4, 5
+  s[0] = mfma_fp8(k0, qf[0], splat_seed(negm8), ksc_next, qsc);
+  p_cur[4] = static_cast<int>(prob_word(s, 4, l, mx));
+  s[0] = mfma_fp8_b1(k0, ql[0], s[0], ksc_next, qsc);
+  p_cur[5] = static_cast<int>(prob_word(s, 5, l, mx));
   __builtin_amdgcn_sched_barrier(0);
   // slot 3: second k-step; words 6, 7
-  s[0] = mfma_fp8(k1, qf[1], s[0]);
-  p_cur[6] = static_cast<int>(prob_word(s, 6, coef, off, l, mx));
-  s[0] = mfma_fp8_blo(k1, ql[1], s[0]);
-  p_cur[7] = static_cast<int>(prob_word(s, 7, coef, off, l, mx));
+  s[0] = mfma_fp8(k1, qf[1], s[0], ksc_next, qsc);
+  p_cur[6] = static_cast<int>(prob_word(s, 6, l, mx));
+  s[0] = mfma_fp8_b1(k1, ql[1], s[0], ksc_next, qsc);
+  p_cur[7] = static_cast<int>(prob_word(s, 7, l, mx));
   __builtin_amdgcn_sched_barrier(0);
   mx = max_other_half(mx);
   asm volatile("" : "+v"(p_cur), "+v"(l), "+v"(mx));
   return l;
 }
 
-// acc *= alpha, in place. Written as one asm block with every element tied to
-// its register: as plain C++ in the rare rescale path, the register allocator
-// keeps a second copy of the 64 output accumulators live and spills in the
-// main loop. The compiler does not see hazards through inline asm, so the
-// block waits out an MFMA still writing acc (leading nops) and lets the
-// products settle before any MFMA reads them (trailing nops).
-__device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
-  float e[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) e[r] = acc[r];
-  asm volatile(
-      "s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n"
-      "v_mul_f32 %0, %0, %16\n v_mul_f32 %1, %1, %16\n v_mul_f32 %2, %2, %16\n"
-      "v_mul_f32 %3, %3, %16\n v_mul_f32 %4, %4, %16\n v_mul_f32 %5, %5, %16\n"
-      "v_mul_f32 %6, %6, %16\n v_mul_f32 %7, %7, %16\n v_mul_f32 %8, %8, %16\n"
-      "v_mul_f32 %9, %9, %16\n v_mul_f32 %10, %10, %16\n v_mul_f32 %11, %11, %16\n"
-      "v_mul_f32 %12, %12, %16\n v_mul_f32 %13, %13, %16\n v_mul_f32 %14, %14, %16\n"
-      "v_mul_f32 %15, %15, %16\n"
-      "s_nop 7\n s_nop 7\n"
-      : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]), "+v"(e[4]), "+v"(e[5]), "+v"(e[6]),
-        "+v"(e[7]), "+v"(e[8]), "+v"(e[9]), "+v"(e[10]), "+v"(e[11]), "+v"(e[12]), "+v"(e[13]),
-        "+v"(e[14]), "+v"(e[15])
-      : "v"(alpha));
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = e[r];
-}
-
-// Rare path of a step, taken by the whole wave when some row's x exceeds
+// Rare path of a step, taken by the whole wave when some row's acc exceeds
 // kTrigger (P' would pass 362, near the e4m3 limit of 448): those rows move
-// the running max up so that their largest x becomes kPTarget; O (every tile
-// before this one) and the sum of the tiles before are scaled to match, and
-// the tile's probabilities are recomputed -- block 0 of its S^T again from its
-// K rows (kc0, still in LDS), block 1 from s1. Block 0 is masked like the
-// first time, through the accumulator seed: -inf for keys past the count in
-// `code` and for keys whose bit in wword is clear (all ones unless `code`
-// flags a windowed text tile), 0 for the others.
-__device__ __forceinline__ float rescale_step(float mx, float& m_run, float& off, float& l_run,
-                                              f32x16* o, const uint8_t* kc0, const f32x16& s1,
-                                              const i32x8v* qf, const i32x8v* ql, float coef,
+// the running max up so that their largest acc becomes kPTarget. O (every
+// tile before this one), the sum of the tiles before, the seed 8 - m and
+// block 0 of the next tile (already issued from the old seed) are shifted to
+// match, and the tile's probabilities are recomputed -- block 0 of its S^T
+// again from its K rows (kc0, still in LDS; block scale ksc), block 1 from
+// s[1]. Block 0 is masked like the first time, through the accumulator seed:
+// -inf for keys past the count in `code` and for keys whose bit in wword is
+// clear (all ones unless `code` flags a windowed text tile).
+__device__ __forceinline__ float rescale_step(float mx, float& l_run, int& shift,
+                                              float& negm8, f32x16* s, const uint8_t* kc0,
+                                              const i32x8v* qf, const i32x8v* ql, int ksc, int qsc,
                                               int code, int g, uint32_t wword, i32x8v& p_cur) {
-  const float d = fmaxf(mx - kPTarget, 0.f);
-  const float alpha = __builtin_amdgcn_exp2f(-d);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) scale_acc(o[i], alpha);
-  l_run *= alpha;
-  m_run += d;
-  off -= d;
+  // an integer shift d: O keeps the units of the max before all shifts, and the
+  // later probabilities enter P.V with the block scale 2^shift
+  const float d = fmaxf(ceilf(mx - kPTarget), 0.f);
+  l_run *= __builtin_amdgcn_exp2f(-d);
+  shift += static_cast<int>(d);
+  // whole-vector updates, so that each value keeps its registers across the
+  // branch (element-wise updates leave copies on the common path)
+  negm8 -= d;
+  s[0] = s[0] - d;
   float l = 0.f, m2 = -INFINITY;
   {
     f32x16 b0;
     const int lim = tile_count(code) - 32 * g;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) b0[r] = r >= lim ? -INFINITY : keep_if_bit(0.f, wword, r);
-    b0 = qk_block(kc0, qf, ql, b0);
+    for (int r = 0; r < 16; ++r) b0[r] = (r >= lim ? -INFINITY : keep_if_bit(0.f, wword, r)) + negm8;
+    b0 = qk_block(kc0, qf, ql, ksc, qsc, b0);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) p_cur[w] = static_cast<int>(prob_word_blk(b0, w, coef, off, l, m2));
+    for (int w = 0; w < 4; ++w) p_cur[w] = static_cast<int>(prob_word_blk(b0, w, l, m2));
   }
+  const f32x16 b1 = s[1] - d;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) p_cur[4 + w] = static_cast<int>(prob_word_blk(s1, w, coef, off, l, m2));
+  for (int w = 0; w < 4; ++w) p_cur[4 + w] = static_cast<int>(prob_word_blk(b1, w, l, m2));
   return l;
 }
 
@@ -309,7 +308,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   __shared__ __attribute__((aligned(16))) uint8_t Vs[kStages * VT8];
   __shared__ double om[kD / 2];
   __shared__ int ax[kD / 2];
-  __shared__ float red[kWaves];
   // timed-window bits (+ 1 word: lanes of group 1 on the last text tile may
   // read one word past the table; their keys are all masked by the valid count)
   __shared__ uint32_t wtab[kWindowWords + 1];
@@ -335,14 +333,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   seq_start<kSparse, 1>(lc, I, h, H, P, seq, kt0);
   TileInfo ti0 = tile_info(lc, flag_fi);
 
-  // largest V scale among the planes this (item, head) attends
-  float vmax = 0.f;
-  for (int i = tid; i < I.n_frames_kv; i += kThreads)
-    vmax = fmaxf(vmax, I.v_scale[static_cast<size_t>(I.frames[i]) * H + h]);
-  if (tid == 0 && I.n_text_kv > 0) vmax = fmaxf(vmax, I.v_text_scale[h]);
-#pragma unroll
-  for (int o2 = 32; o2 > 0; o2 >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, o2));
-  if (lane == 0) red[w] = vmax;
   if (tid < kD / 2) {
     int axis;
     om[tid] = rope_omega(tid, a.rope, &axis);
@@ -369,13 +359,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
     dma_k8(lc, Ks + KT8, w);
     dma_v8(lc, Vs + VT8, w);
   }
-  vmax = red[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) vmax = fmaxf(vmax, red[i]);
-
-  // ---- Q: rotate in fp32, quantise per (row, head) to e4m3 ---------------------
+  // ---- Q: rotate in fp32, times softmax scale * log2(e), quantise per (row,
+  // head) to e4m3 -----------------------------------------------------------------
   // lane holds dims 64*kk + 32*g + e (kk = 0, 1; e = 0..31) of its query row.
-  // The query is split: qf = e4m3(q * 448 / amax), ql = e4m3(16 * residual), so
+  // The query is split: qf = e4m3(q * 2^-qe), ql = e4m3(16 * residual), so
   // that qf + ql / 16 carries about 7 significant bits instead of 4.
   const int qrow = q0 + 32 * w + r32;
   // This lane's window word for key tile kt0 + tt (a text tile under
@@ -388,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
     return wtab[woff[t] + (max(text_tile_base(I, P, kt0 + tt), 0) >> 5)];
   };
   i32x8v qf[2], ql[2];
-  float q_scale;
+  int qsc;   // E8M0 block scales of the high (byte 0) and low (byte 1) parts
   {
     bool video;
     int tpos, hpos, wpos;
@@ -416,16 +403,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
             xb = xa * s + xb * c;
             xa = ya;
           }
-          x[32 * kk + 8 * ch + 2 * m] = xa;
-          x[32 * kk + 8 * ch + 2 * m + 1] = xb;
+          x[32 * kk + 8 * ch + 2 * m] = xa * a.scale_log2;
+          x[32 * kk + 8 * ch + 2 * m + 1] = xb * a.scale_log2;
         }
       }
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(x[i]));
     amax = max_other_half(amax);
-    const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
-    q_scale = amax > 0.f ? amax / 448.0f : 1.0f;
+    // 2^qe: the least power of two with amax <= 448 * 2^qe (448 = 1.75 * 2^8),
+    // at least 2^-122 so that the low part's scale 2^(qe - 4) stays an E8M0
+    // value; 2^0 for a zero row
+    int qe = 0;
+    if (amax > 0.f) {
+      const uint32_t b = __float_as_uint(amax);
+      qe = static_cast<int>(b >> 23) - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+      qe = max(qe, -122);
+    }
+    const float inv = __uint_as_float(static_cast<uint32_t>(127 - qe) << 23);   // 2^-qe
+    qsc = (127 + qe) | ((123 + qe) << 8);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -453,30 +449,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
 #pragma unroll
   for (int b = 0; b < 2; ++b) krow[b] = 32 * ((r32 >> 2) & 1) + 16 * b + 4 * (r32 >> 3) + (r32 & 3);
   const int voff = r32 * VS8 + 32 * g;
-  const float c2 = a.scale_log2 * q_scale;   // per-lane logit factor before the K scale
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
   float l_run = 0.f;
 
-  // S^T of tile 0; the running max m (log2 units) starts at its max
+  // S^T of tile 0 (logits in log2 units); the running max m starts at its max,
+  // and every later QK^T accumulation starts from the seed 8 - m
   f32x16 sc[2];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) sc[b] = qk_block(Ks + krow[b] * KS8 + 32 * g, qf, ql);
+  for (int b = 0; b < 2; ++b) sc[b] = qk_block(Ks + krow[b] * KS8 + 32 * g, qf, ql, ti0.ksc, qsc, f32x16{});
   if (ti0.nvalid < BN) mask_tile(sc, tile_count(ti0.nvalid), g);
   // (tile 0 is never a text tile under timed windows: the key ranges of such
   // items start on a video tile, so every row sees tile 0's valid keys)
-  float m_run;
+  // The running max is m_ref + shift: probabilities P' = 2^(x - m_ref - shift + 8)
+  // enter P.V with the block scale 2^shift, so O stays in units of 2^(x - m_ref
+  // + 8) and a rescale never rewrites it; l_run is in the units of the running
+  // max. O is renormalised (m_ref moves up) only when a shift passes kMaxShift.
+  float m_ref;
   {
     float mx = -INFINITY;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][r]);
-    m_run = max_other_half(mx) * (c2 * ti0.kscale);   // tile 0 always has a valid key
+    m_ref = max_other_half(mx);   // tile 0 always has a valid key
   }
+  int shift = 0;
+  float negm8 = kPTarget - m_ref;   // the seed of every later QK^T accumulation
+#pragma unroll
+  for (int b = 0; b < 2; ++b) sc[b] = sc[b] + negm8;
   i32x8v pa = {}, pb;
-  const float pf_base = kPScale / vmax;
+  int vsc_prev = kUnitScale;   // V block scale of the tile before the compute tile
 
   // Tile t sits in stage t % 4. Step t: PV(t-1) and QK^T(t+1) on the matrix
   // pipe beside the softmax of tile t; S^T is computed in place (block 0 of
@@ -514,32 +518,46 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
       if (tile_count(cur.nvalid) < BN) mask_tile(sc, tile_count(cur.nvalid), g);
       if (cur.nvalid < 0) window_mask_tile(sc, window_word(tt));
     }
-    const float coef = c2 * cur.kscale;
-    const float pf = pf_base * cur.vscale;
-    float off8 = __log2f(pf) - m_run;
+    const int ksc_next = ti1.ksc;
     float mx;
-    float lt = fp8_step_a(Vprev, Knext + krow[0] * KS8, p_prev, o, qf, ql, sc, coef, off8, p_cur,
-                          mx, boundary);
+    float lt = fp8_step_a(Vprev, Knext + krow[0] * KS8, p_prev, vsc_prev, kUnitScale + shift, o, qf,
+                          ql, ksc_next, qsc, negm8, sc, p_cur, mx, boundary);
     if (__builtin_expect(__any(mx > kTrigger), 0))
-      lt = rescale_step(mx, m_run, off8, l_run, o, Kcur + krow[0] * KS8, sc[1], qf, ql, coef,
+      lt = rescale_step(mx, l_run, shift, negm8, sc, Kcur + krow[0] * KS8, qf, ql, cur.ksc, qsc,
                         cur.nvalid, g, cur.nvalid < 0 ? window_word(tt) : ~0u, p_cur);
     // QK^T block 1 of tile t+1 (block 1 of tile t is no longer needed)
-    sc[1] = qk_block(Knext + krow[1] * KS8, qf, ql);
-    l_run += lt / pf;
+    sc[1] = qk_block(Knext + krow[1] * KS8, qf, ql, ksc_next, qsc, splat_seed(negm8));
+    l_run += lt;
+    vsc_prev = cur.vsc;
     ti0 = ti1;
     ti1 = ti2;
   };
+  int t = 0;
+  for (;;) {
 #pragma unroll 1
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, pa, pb);
-    if (t + 1 < ntiles) step(t + 1, pb, pa);
+    for (; t < ntiles; t += 2) {
+      step(t, pa, pb);
+      if (t + 1 < ntiles) step(t + 1, pb, pa);
+      if (__builtin_expect(__any(shift > kMaxShift), 0)) {
+        t += 2;
+        break;
+      }
+    }
+    if (!__any(shift > kMaxShift)) break;
+    // (rare) renormalise O to the running max
+    const float alpha = __builtin_amdgcn_exp2f(-static_cast<float>(shift));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = o[i] * alpha;
+    m_ref += static_cast<float>(shift);
+    shift = 0;
   }
   {
     const uint8_t* Vlast = Vs + ((ntiles - 1) & (kStages - 1)) * VT8;
     const i32x8v& p_last = (ntiles & 1) ? pb : pa;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
-      o[db] = mfma_fp8(lds_read32(Vlast + voff + 32 * db * VS8), p_last, o[db]);
+      o[db] = mfma_fp8(lds_read32(Vlast + voff + 32 * db * VS8), p_last, o[db], vsc_prev,
+                       kUnitScale + shift);
   }
 
   // The output MFMAs compute across all lanes of the wave: keep them (and
@@ -548,11 +566,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
 
   // ---- epilogue ----------------------------------------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = vmax / (kPScale * l_tot);
+  // O and l in units of 2^(x - m_ref + 8): m_ref - 8 is the max the merge sees
+  const float l_tot = (l_run + __shfl_xor(l_run, 32)) *
+                      __uint_as_float(static_cast<uint32_t>(127 + shift) << 23);   // x 2^shift
+  const float inv = 1.0f / l_tot;
   if (wt.part >= 0) {   // split tile: partial result for the merge kernel
     if (qrow < I.n_q)
-      store_partial(a, wt.unit, BM, qrow - q0, g, o, vmax / kPScale, m_run, l_tot);
+      store_partial(a, wt.unit, BM, qrow - q0, g, o, 1.0f, m_ref - kPTarget, l_tot);
     return;
   }
   if (qrow < I.n_q) {
@@ -568,7 +588,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
         *reinterpret_cast<u32x2*>(orow + d0) = v2;
       }
     if (I.lse != nullptr && g == 0)
-      I.lse[static_cast<size_t>(qrow) * H + h] = (m_run + __log2f(l_tot)) * 0.6931471805599453f;
+      I.lse[static_cast<size_t>(qrow) * H + h] =
+          (m_ref - kPTarget + __log2f(l_tot)) * 0.6931471805599453f;
   }
 }
 

@@ -138,7 +138,22 @@ __device__ __forceinline__ u32x4 load_chunk(const uint16_t* base, size_t off) {
 }
 
 // ---- e4m3 ------------------------------------------------------------------------
-// Four fp32 values already scaled into +-448 (by 448 / amax) -> four OCP
+// Exponent e of a plane's scale 2^e: the least integer with amax <= 448 * 2^e,
+// at least -126 (0 when amax is 0). With 448 = 1.75 * 2^8 and amax = m * 2^k,
+// 1 <= m < 2: e = k - 8, or k - 7 when m > 1.75 (mantissa field above 0x600000).
+__device__ __forceinline__ int e4m3_scale_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const uint32_t b = __float_as_uint(amax);
+  const int biased = static_cast<int>(b >> 23);
+  if (biased == 0) return -126;                 // below 2^-126: the floor
+  const int e = biased - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return e < -126 ? -126 : e;
+}
+
+// 2^e as an fp32 value (e in [-126, 127])
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float(static_cast<uint32_t>(e + 127) << 23); }
+
+// Four fp32 values already scaled into +-448 (by 2^-e) -> four OCP
 // e4m3fn codes, first value in the low byte, by the hardware conversion:
 // round to nearest even, values below 2^-6 to the nearest multiple of 2^-9.
 // In this range nothing overflows.
@@ -245,7 +260,8 @@ constexpr int kVtWords = kVtTok / 4 + 1;
 
 // One block per (frame, head) plane (or per head of the text slot): pass 1
 // finds amax of the rotated K and of V, pass 2 quantises and stores (K rows of
-// 8-byte chunks; V^T rows in 4-byte words of 4 consecutive tokens).
+// 8-byte chunks; V^T rows in 4-byte words of 4 consecutive tokens). The
+// scale of a plane is the least power of two 2^e with amax <= 448 * 2^e.
 template <bool kLut>
 __global__ __launch_bounds__(kFp8Threads) void append_fp8_kernel(const AppendArgs a) {
   __shared__ float2 lut_mem[kLutMax];
@@ -286,11 +302,13 @@ __global__ __launch_bounds__(kFp8Threads) void append_fp8_kernel(const AppendArg
   }
   amk = block_max(amk, red, kFp8Threads);
   amv = block_max(amv, red, kFp8Threads);
-  const float ik = amk > 0.f ? 448.0f / amk : 1.0f;
-  const float iv = amv > 0.f ? 448.0f / amv : 1.0f;
+  // power-of-two scales: the codes are the e4m3 roundings of x * 2^-e, an
+  // exact product
+  const int ek = e4m3_scale_exp(amk), ev = e4m3_scale_exp(amv);
+  const float ik = pow2f(-ek), iv = pow2f(-ev);
   if (tid == 0) {
-    a.k_scale[static_cast<size_t>(f) * H + h] = amk > 0.f ? amk / 448.0f : 1.0f;
-    a.v_scale[static_cast<size_t>(f) * H + h] = amv > 0.f ? amv / 448.0f : 1.0f;
+    a.k_scale[static_cast<size_t>(f) * H + h] = pow2f(ek);
+    a.v_scale[static_cast<size_t>(f) * H + h] = pow2f(ev);
   }
   const size_t plane = static_cast<size_t>(a.plane_len) * kD;
   uint8_t* kdst = static_cast<uint8_t*>(a.k) + (static_cast<size_t>(f) * H + h) * plane;

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 7
+#define SA_ABI_VERSION 8
 #define SA_HEAD_DIM 128       /* the only head dim the kernels are built for */
 #define SA_MAX_ITEMS 8        /* sessions per sa_segment_attention call     */
 #define SA_MAX_FRAMES_KV 65536
@@ -206,8 +206,9 @@ size_t sa_cache_bytes(const sa_geom* geom, int32_t dtype, int32_t frame_capacity
  * layer. k_in, v_in: bf16 [n_frames * P][H][128], raw projections in raster
  * order. K is rotated by the 3D RoPE at (frame, row, column) in fp32 with an
  * fp64-reduced angle, then rounded to the cache type; V is stored unrotated
- * and transposed. fp8: per (frame, head) plane, scale = amax / 448 (fp32),
- * code = round-nearest-even(x * (448 / amax)) saturated; amax 0 gives scale
+ * and transposed. fp8: per (frame, head) plane, scale = 2^e (an fp32 power
+ * of two), e the least integer with amax <= 448 * 2^e and at least -126;
+ * code = round-nearest-even(x * 2^-e), an exact product; amax 0 gives scale
  * 1. int8: per token and head, scale = amax / 127 over its 128 values, code
  * = round-half-even(x * (127 / amax)) clamped to +-127, in fp32 (K after its
  * rotation in fp32); amax 0 gives scale 1 and codes 0. Source: "Writing the segment into memory" and "How one segment is made"

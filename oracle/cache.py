@@ -28,10 +28,14 @@ with H heads, D = head_dim, P = lat_h * lat_w tokens per latent frame:
 Stored values. K is rotated by the 3D RoPE at its absolute position (frame f
 for video token p of frame f; (0, 0, 0) for text) and rounded to the cache
 format; V is stored unrotated. fp8 scale per (frame, head) plane (per head for
-the text slot) = amax / 448 over that plane's values, computed in fp32
-(amax == 0 gives scale 1); codes = e4m3 round-nearest-even of
-x * (448 / amax) evaluated in fp32 and saturated, so that the quantisation
-decision is taken in the same precision as the kernel's.
+the text slot) = 2**e, e the smallest integer with amax <= 448 * 2**e over
+that plane's (fp32) values, and at least -126 (amax == 0 gives scale 1);
+codes = e4m3 round-nearest-even of x / 2**e, which no rounding precedes (the
+division by a power of two is exact). A power of two is an fp32 scale like
+any other; the choice lets fp8 matrix instructions apply the scale exactly
+through their power-of-two block scales. The pages fix no fp8 format: the
+e4m3 cache with fp32 scales per (frame, head) is the workload's own, and this
+is the reading of how those scales are chosen.
 int8 scale per (token, head) = amax / 127 over that token's head_dim values
 in fp32 (amax == 0 gives scale 1); code = round-half-even of
 x * (127 / amax) evaluated in fp32, clamped to [-127, 127] (symmetric: -128
@@ -125,21 +129,37 @@ def append_text_bf16(k_in, v_in):
 
 
 # ------------------------------------------------------- expected append (fp8)
+E4M3_MIN_SCALE_EXP = -126
+
+
+def plane_scale_exponent(amax):
+    """The exponent e of a plane's scale 2**e: the smallest integer with
+    amax <= 448 * 2**e, raised to -126 if smaller (0 for amax == 0)."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    e = int(np.ceil(np.log2(amax / E4M3_MAX)))
+    while amax > E4M3_MAX * 2.0 ** e:           # settle the exact boundary
+        e += 1
+    while amax <= E4M3_MAX * 2.0 ** (e - 1):
+        e -= 1
+    return max(e, E4M3_MIN_SCALE_EXP)
+
+
 def quantize_plane_fp8(x):
     """Quantise one plane (any shape) of fp32-valued reals to e4m3 codes.
 
-    Returns (codes uint8 same shape, scale float32). The decision path is
-    float32: amax is the fp32 maximum magnitude, inv = fp32(448 / amax),
-    y = fp32(x * inv), code = e4m3 nearest-even of y, saturated.
+    Returns (codes uint8 same shape, scale float32). amax is the fp32 maximum
+    magnitude, scale = 2**plane_scale_exponent(amax), code = e4m3 nearest-even
+    of x / scale (an exact quotient), saturated.
     """
     x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
     amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
     if amax == 0:
         return np.zeros(x32.shape, np.uint8), np.float32(1.0)
-    inv = np.float32(E4M3_MAX) / amax
-    scale = amax / np.float32(E4M3_MAX)
-    y = (x32 * inv).astype(np.float32)
-    return numerics.e4m3_encode(y.astype(np.float64)), np.float32(scale)
+    e = plane_scale_exponent(amax)
+    y = x32.astype(np.float64) * 2.0 ** -e
+    return numerics.e4m3_encode(y), np.float32(2.0 ** e)
 
 
 def append_fp8(k_in, v_in, frame0, lat_h, lat_w, split, theta):

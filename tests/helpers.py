@@ -230,10 +230,12 @@ class Session:
         query precision (split_query_fp8).
 
         Returns (out, lse, bound): `bound` is the per-element error that rounding
-        the probabilities to e4m3 can add (the kernel multiplies V by e4m3
-        probabilities p' = p * 256 * vs / vmax): at most 2^-4 relative for each
-        normal p', at most 2^-10 absolute (in p' units) below the normal range,
-        i.e. sum_j (2^-4 p_j + 2^-10 vmax / (256 vs_j)) |v_jd| / sum_j p_j."""
+        the probabilities to e4m3 can add. The kernel multiplies V by e4m3
+        probabilities P' = 2^(x - m + 8) against its running max m, which never
+        passes the row's true max by a whole unit, so P' >= 2^7 p with p the
+        probability against the true max: the rounding is at most 2^-4 relative
+        for a normal P' and at most 2^-10 absolute in P' units (2^-17 in p units)
+        below the normal range, i.e. sum_j (2^-4 p_j + 2^-17) |v_jd| / sum_j p_j."""
         from oracle import cache as ocache
         wl = self.wl
         hs = list(range(wl.heads)) if heads is None else list(heads)
@@ -272,11 +274,11 @@ class Session:
             rows = np.arange(q.shape[0])
         qr = orope.rope3d(q[rows], self.q_positions()[rows], wl.split, self.geom.rope_theta)
         qq = qr.copy()
+        scale = 1.0 / math.sqrt(wl.head_dim)
         if split_q:
             for i in range(qr.shape[0]):
                 for j in range(qr.shape[1]):
-                    qq[i, j] = split_query_fp8(qr[i, j])
-        scale = 1.0 / math.sqrt(wl.head_dim)
+                    qq[i, j] = split_query_fp8(qr[i, j], np.float32(scale * math.log2(math.e)))
         out = np.zeros(qq.shape)
         lse = np.zeros(qq.shape[:2])
         bound = np.zeros(qq.shape)
@@ -287,7 +289,7 @@ class Session:
             if vis is not None:
                 s_ = np.where(vis, s_, -np.inf)
             p_ = np.exp(s_ - s_.max(axis=1, keepdims=True))
-            floor = 2.0 ** -10 * vsk[:, j].max() / (256.0 * vsk[:, j])
+            floor = np.full(vsk.shape[0], 2.0 ** -17)
             fl = floor[None, :] if vis is None else np.where(vis, floor[None, :], 0.0)
             bound[:, j] = ((2.0 ** -4 * p_ + fl) @ np.abs(v[:, j])) / p_.sum(1)[:, None]
         return out, lse, bound
@@ -367,20 +369,22 @@ def oracle_all_heads(s, rows=None, workers=16):
     return out, lse
 
 
-def split_query_fp8(q):
-    """Real value of a rotated query row as the e4m3 kernel takes it: fp32
-    decisions, amax = max |q|, y = fp32(q * fp32(448 / amax)), hi = e4m3(y),
-    lo = e4m3(16 (y - hi)), value (hi + lo / 16) * fp32(amax / 448)."""
-    q32 = np.asarray(q, dtype=np.float64).astype(np.float32)
-    amax = np.float32(np.max(np.abs(q32)))
+def split_query_fp8(q, scale_log2):
+    """Real value of a rotated query row as the e4m3 kernel takes it: in fp32,
+    x = q * scale_log2 (softmax scale times log2(e)), amax = max |x|, the
+    power of two 2^qe with amax <= 448 * 2^qe (at least 2^-122), y = x * 2^-qe,
+    hi = e4m3(y), lo = e4m3(16 (y - hi)); value (hi + lo / 16) 2^qe / scale_log2."""
+    x = (np.asarray(q, dtype=np.float64).astype(np.float32) * np.float32(scale_log2)).astype(np.float64)
+    amax = float(np.max(np.abs(x)))
     if amax == 0:
-        return np.zeros(q32.shape)
-    inv = np.float32(448.0) / amax
-    scale = np.float64(amax / np.float32(448.0))
-    y = (q32 * inv).astype(np.float32).astype(np.float64)
+        return np.zeros(x.shape)
+    qe = -122
+    while amax > 448.0 * 2.0 ** qe:
+        qe += 1
+    y = x * 2.0 ** -qe
     hi = onum.e4m3_decode(onum.e4m3_encode(y))
     lo = onum.e4m3_decode(onum.e4m3_encode(16.0 * (y - hi)))
-    return (hi + lo / 16.0) * scale
+    return (hi + lo / 16.0) * 2.0 ** qe / float(np.float32(scale_log2))
 
 
 def compare(got, want, max_abs, mean_abs, label=""):

@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 7
+    assert sa.abi_version() == 8
 
 
 def test_status_strings(lib):

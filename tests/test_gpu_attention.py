@@ -343,6 +343,44 @@ def test_no_query_rows_is_a_noop():
 
 
 # ---------------------------------------------------------------- e4m3 cache
+@pytest.mark.parametrize("split", [False, True])
+def test_fp8_logits_far_above_the_first_tile(split):
+    """e4m3 cache, Q x 40: rows meet keys hundreds of log2 units above their
+    first tile's max, so the running max moves many times, its accumulated
+    shift passes the 64 that the P.V block scale carries, and O is
+    renormalised in place. Checked, whole and split, against the oracle over
+    the stored values with the e4m3 probability-rounding bound, as the other
+    small e4m3 cases; the test first checks that such rises exist."""
+    wl = _fp8_wl("fp8_far", 2, 4, 6, 8, 24, 2)
+    s = Session(wl, seed=13, layer=0, session=0, q_scale=40.0)
+    k, _, kpos = s.raw_keys()
+    from oracle import rope as orope
+    qr = orope.rope3d(s.q.float().cpu().double().numpy(), s.q_positions(), wl.split,
+                      s.geom.rope_theta)
+    kr = orope.rope3d(k, kpos, wl.split, s.geom.rope_theta)
+    c2 = math.log2(math.e) / math.sqrt(wl.head_dim)
+    rise = max(float(np.max((qr[:, hh] @ kr[:, hh].T * c2).max(axis=1) -
+                            (qr[:, hh] @ kr[:, hh, :][:64].T * c2).max(axis=1)))
+               for hh in range(wl.heads))
+    print(f"fp8 far: largest rise of a row's max past its first tile {rise:.1f} log2 units",
+          flush=True)
+    assert rise > 80.0
+    ws = "auto" if split else None
+    if split:
+        assert sa.segment_attention_workspace(s.geom, [s.item()]) > 0
+    sa.segment_attention(s.geom, [s.item()], workspace=ws)
+    torch.cuda.synchronize()
+    got, got_lse = s.gpu_out()
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(got_lse))
+    wq, wq_lse, bound = s.oracle_fp8_cache()
+    err = np.abs(got - wq)
+    worst = float(np.max(err / (bound + 5e-3)))
+    print(f"fp8 far split={split}: max_abs={err.max():.3e} max(err / (bound + 5e-3))={worst:.3f}",
+          flush=True)
+    assert worst <= 1.0
+    np.testing.assert_allclose(got_lse, wq_lse, rtol=2e-3, atol=0.05)
+
+
 FP8_CASES = [
     # name, H, F, lat_h, lat_w, n_text, prior segments
     ("fp8_small", 2, 2, 4, 8, 16, 2),       # P = 32

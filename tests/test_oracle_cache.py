@@ -110,14 +110,26 @@ def test_append_text_is_identity_layout():
     assert np.array_equal(K, k.transpose(1, 0, 2)) and np.array_equal(V, v.transpose(1, 2, 0))
 
 
+def test_plane_scale_exponent_hand_worked():
+    """The plane scale is the least power of two 2**e with amax <= 448 * 2**e:
+    worked by hand at and around the boundaries (448 = 1.75 * 2**8)."""
+    f32 = np.float32
+    cases = [(448.0, 0), (np.nextafter(f32(448.0), f32(1e9)), 1), (224.0, -1),
+             (np.nextafter(f32(224.0), f32(1e9)), 0), (1.0, -8), (1.75, -8),
+             (np.nextafter(f32(1.75), f32(9.0)), -7), (3.0e38, 120), (1e-40, -126), (0.0, 0),
+             (2.0 ** -120, -126), (448.0 * 2.0 ** -126, -126), (448.0 * 2.0 ** -125, -125)]
+    for amax, e in cases:
+        assert cache.plane_scale_exponent(f32(amax)) == e, (amax, e)
+
+
 def test_quantize_plane_fp8_properties():
     rng = np.random.default_rng(4)
     x = (rng.standard_normal((24, 128)) * 1.7).astype(np.float32).astype(np.float64)
     codes, scale = cache.quantize_plane_fp8(x)
     amax = np.float32(np.abs(x).max())
-    assert scale == np.float32(amax / np.float32(448.0))
-    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
-    assert codes[i] & 0x7F == 0x7E                          # amax maps to 448
+    e = int(np.log2(scale))
+    assert scale == 2.0 ** e                                # a power of two
+    assert 224.0 < amax / scale <= 448.0                    # the least one that holds amax
     dq = cache.dequant(codes, scale)
     # relative error of e4m3 (3 mantissa bits) is at most 2**-4 for normals
     normal = np.abs(x) / scale >= 2.0 ** -6
@@ -128,13 +140,16 @@ def test_quantize_plane_fp8_properties():
 
 
 def _fp32_plane_codes(x):
-    """Expected codes and scale of one plane from the reading of the format
-    (amax, 448 / amax and the scaled values in fp32), with the codes found by
-    exhaustive nearest-code search rather than the oracle's encoder."""
-    x32 = np.asarray(x, dtype=np.float32)
-    amax = np.float32(np.abs(x32).max())
-    y = (x32 * (np.float32(448.0) / amax)).astype(np.float32).astype(np.float64)
-    return nearest_code_brute(y, numerics.e4m3_decode), amax / np.float32(448.0)
+    """Expected codes and scale of one plane from the reading of the format,
+    by search rather than the oracle's own steps: the scale is the first power
+    of two 2**e (e counted up from -126) with amax <= 448 * 2**e, and the codes
+    are the nearest e4m3 codes of x / 2**e by exhaustive search."""
+    x32 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    amax = np.abs(x32).max()
+    e = -126
+    while amax > 448.0 * 2.0 ** e:
+        e += 1
+    return nearest_code_brute(x32 * 2.0 ** -e, numerics.e4m3_decode), np.float32(2.0 ** e)
 
 
 def test_append_fp8_codes_are_brute_force_nearest_per_plane():
@@ -146,7 +161,8 @@ def test_append_fp8_codes_are_brute_force_nearest_per_plane():
     under the K plane's own scale."""
     lat_h, lat_w, H, F = 4, 6, 3, 2
     P = lat_h * lat_w
-    fac = np.array([[0.5, 3.0, 1.25], [7.0, 0.75, 2.0]])           # [F, H]
+    # [F, H]; factors 4x apart, so that every plane's power-of-two scale differs
+    fac = np.array([[1 / 16, 1.0, 1 / 4], [16.0, 1 / 64, 4.0]])
     k = _bf16_inputs((F * P, H, 128), 5) * np.repeat(fac, P, axis=0)[:, :, None]
     v = numerics.bf16_round(_bf16_inputs((F * P, H, 128), 6) * np.repeat(fac[::-1], P, axis=0)[:, :, None])
     Kc, Ks, Vc, Vs = cache.append_fp8(k, v, 3, lat_h, lat_w, (16, 56, 56), 10000.0)
