@@ -532,28 +532,48 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
     ti0 = ti1;
     ti1 = ti2;
   };
+  // A step whose rescale leaves a shift above kMaxShift stops the loop before
+  // the next step's P.V, which would take block scale 127 + shift: O is
+  // renormalised here, off the loop's path, and the loop resumes. (Stopping
+  // after the first of a trip's two steps, the probabilities of that step move
+  // into pa so that the resumed trip starts with them.)
   int t = 0;
+  int base = 0;     // the step the last (re)started loop began with
   for (;;) {
+    int stop = 0;   // 1: after a trip's first step, 2: after its second
 #pragma unroll 1
     for (; t < ntiles; t += 2) {
       step(t, pa, pb);
-      if (t + 1 < ntiles) step(t + 1, pb, pa);
       if (__builtin_expect(__any(shift > kMaxShift), 0)) {
-        t += 2;
+        stop = 1;
         break;
       }
+      if (t + 1 < ntiles) {
+        step(t + 1, pb, pa);
+        if (__builtin_expect(__any(shift > kMaxShift), 0)) {
+          stop = 2;
+          break;
+        }
+      }
     }
-    if (!__any(shift > kMaxShift)) break;
-    // (rare) renormalise O to the running max
+    if (stop == 0) break;
     const float alpha = __builtin_amdgcn_exp2f(-static_cast<float>(shift));
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = o[i] * alpha;
     m_ref += static_cast<float>(shift);
     shift = 0;
+    if (stop == 1) {
+      pa = pb;
+      t += 1;
+    } else {
+      t += 2;
+    }
+    base = t;
   }
   {
     const uint8_t* Vlast = Vs + ((ntiles - 1) & (kStages - 1)) * VT8;
-    const i32x8v& p_last = (ntiles & 1) ? pb : pa;
+    // trips from `base` write pb, then pa: an odd count of steps ends in pb
+    const i32x8v& p_last = ((ntiles - base) & 1) ? pb : pa;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
       o[db] = mfma_fp8(lds_read32(Vlast + voff + 32 * db * VS8), p_last, o[db], vsc_prev,
