@@ -111,12 +111,60 @@ __device__ __forceinline__ i32x8v lds_read32(const uint8_t* p) {
 }
 
 // K tile: 64 rows of 9 slots (128 data bytes + pad); V^T tile: 128 rows of 5
-// slots (64 data bytes + pad).
-__device__ __forceinline__ int dma_k8(const TileCursor& c, uint8_t* stage, int w) {
-  return dma_tile<BN, KS8 / 16>(tile_k_rsrc<1>(c), stage, kD, w);
+// slots (64 data bytes + pad). Load j of a stage fills its slots 64 j ..
+// 64 j + 63 (dma_tile); wave w issues loads w and w + 8 (the second only where
+// it exists: K has 9 loads, V^T 10). A lane's global offsets for them depend
+// only on the row length, so they are computed once: for K rows (128 bytes)
+// and for V^T rows of a frame plane (P bytes); the text slot's V^T rows
+// (text capacity bytes) take dma_tile's per-tile computation.
+constexpr int kKLoads = BN * (KS8 / 16) / 64;    // 9
+constexpr int kVLoads = kD * (VS8 / 16) / 64;    // 10
+
+struct DmaOffsets {
+  uint32_t k[2];
+  uint32_t v[2];
+};
+
+__device__ __forceinline__ uint32_t slot_offset(uint32_t n, uint32_t slots, uint32_t row_bytes) {
+  const uint32_t row = n / slots, ch = n - slots * row;
+  return ch == slots - 1 ? kOutOfRange : row * row_bytes + ch * 16u;
 }
-__device__ __forceinline__ int dma_v8(const TileCursor& c, uint8_t* stage, int w) {
-  return dma_tile<kD, VS8 / 16>(tile_v_rsrc<1>(c), stage, static_cast<uint32_t>(c.vstride), w);
+
+__device__ __forceinline__ DmaOffsets dma_offsets(int w, int lane, int P) {
+  DmaOffsets d;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const uint32_t n = 64u * (w + 8 * m) + lane;
+    d.k[m] = slot_offset(n, KS8 / 16, kD);
+    d.v[m] = slot_offset(n, VS8 / 16, static_cast<uint32_t>(P));
+  }
+  return d;
+}
+
+__device__ __forceinline__ void dma_k8(const TileCursor& c, uint8_t* stage, int w,
+                                       const DmaOffsets& d) {
+  const __amdgpu_buffer_rsrc_t r = tile_k_rsrc<1>(c);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int j = w + 8 * m;
+    if (j < kKLoads)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(stage + 1024 * j), 16, d.k[m], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void dma_v8(const TileCursor& c, uint8_t* stage, int w, int P,
+                                       const DmaOffsets& d) {
+  if (c.vstride != P) {   // the text slot
+    dma_tile<kD, VS8 / 16>(tile_v_rsrc<1>(c), stage, static_cast<uint32_t>(c.vstride), w);
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t r = tile_v_rsrc<1>(c);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int j = w + 8 * m;
+    if (j < kVLoads)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(stage + 1024 * j), 16, d.v[m], 0, 0, 0);
+  }
 }
 
 
@@ -194,10 +242,16 @@ __device__ __forceinline__ uint32_t prob_word(const f32x16* s, int w, float& l, 
 // so the copies are made where they are used and no 16-register seed stays
 // live across the loop).
 __device__ __forceinline__ f32x16 splat_seed(float negm8) {
-  asm volatile("" : "+v"(negm8));
+  // a register pair holding the value twice, so that the copies are 64-bit moves
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  f32x2v pair = {negm8, negm8};
+  asm volatile("" : "+v"(pair));
   f32x16 c;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) c[r] = negm8;
+  for (int r = 0; r < 16; r += 2) {
+    c[r] = pair[0];
+    c[r + 1] = pair[1];
+  }
   return c;
 }
 
@@ -350,14 +404,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   // Tiles load two ahead of the compute tile, K and then V (K of tile t+1 is
   // read in step t, V of tile t in step t+1). lc is the cursor of the last
   // tile loaded; ti0, ti1 carry tiles t, t+1.
-  dma_k8(lc, Ks, w);
-  dma_v8(lc, Vs, w);
+  const DmaOffsets dmo = dma_offsets(w, lane, P);
+  dma_k8(lc, Ks, w, dmo);
+  dma_v8(lc, Vs, w, P, dmo);
   TileInfo ti1 = ti0;
   if (ntiles > 1) {
     seq_next<kSparse, 1>(lc, I, h, H, P, seq, kt0 + 1);
     ti1 = tile_info(lc, flag_fi);
-    dma_k8(lc, Ks + KT8, w);
-    dma_v8(lc, Vs + VT8, w);
+    dma_k8(lc, Ks + KT8, w, dmo);
+    dma_v8(lc, Vs + VT8, w, P, dmo);
   }
   // ---- Q: rotate in fp32, times softmax scale * log2(e), quantise per (row,
   // head) to e4m3 -----------------------------------------------------------------
@@ -509,8 +564,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
         const int s2 = (tt + 2) & (kStages - 1);
         seq_next<kSparse, 1>(lc, I, h, H, P, seq, kt0 + tt + 2);
         ti2 = tile_info(lc, flag_fi);
-        dma_k8(lc, Ks + s2 * KT8, w);
-        dma_v8(lc, Vs + s2 * VT8, w);
+        dma_k8(lc, Ks + s2 * KT8, w, dmo);
+        dma_v8(lc, Vs + s2 * VT8, w, P, dmo);
         pending = 1;   // every wave issues at least one V load
       }
     };
