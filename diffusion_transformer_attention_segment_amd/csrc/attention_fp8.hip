@@ -242,15 +242,25 @@ __device__ __forceinline__ uint32_t prob_word(const f32x16* s, int w, float& l, 
 // so the copies are made where they are used and no 16-register seed stays
 // live across the loop).
 __device__ __forceinline__ f32x16 splat_seed(float negm8) {
-  // a register pair holding the value twice, so that the copies are 64-bit moves
+  // a register pair holding the value twice, then seven 64-bit copies of it.
+  // The compiler does not see hazards inside inline asm: the trailing nops
+  // give an MFMA that reads the copies as its accumulator the wait states a
+  // VALU write needs before that read.
   typedef float f32x2v __attribute__((ext_vector_type(2)));
   f32x2v pair = {negm8, negm8};
   asm volatile("" : "+v"(pair));
+  f32x2v c1, c2, c3, c4, c5, c6, c7;
+  asm volatile(
+      "v_mov_b64 %0, %7\n v_mov_b64 %1, %7\n v_mov_b64 %2, %7\n v_mov_b64 %3, %7\n"
+      "v_mov_b64 %4, %7\n v_mov_b64 %5, %7\n v_mov_b64 %6, %7\n s_nop 4"
+      : "=v"(c1), "=v"(c2), "=v"(c3), "=v"(c4), "=v"(c5), "=v"(c6), "=v"(c7)
+      : "v"(pair));
+  const f32x2v parts[8] = {pair, c1, c2, c3, c4, c5, c6, c7};
   f32x16 c;
 #pragma unroll
-  for (int r = 0; r < 16; r += 2) {
-    c[r] = pair[0];
-    c[r + 1] = pair[1];
+  for (int r = 0; r < 8; ++r) {
+    c[2 * r] = parts[r][0];
+    c[2 * r + 1] = parts[r][1];
   }
   return c;
 }
