@@ -84,6 +84,8 @@ SIGNATURES = {
                                                      ctypes.POINTER(sa_attn_item)]),
     "sa_sparse_select": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_attn_item), _P,
                                         ctypes.c_size_t, _P, _P]),
+    "sa_sparse_select_noalloc": (ctypes.c_int, [ctypes.POINTER(sa_geom),
+                                                ctypes.POINTER(sa_attn_item), _P, _P]),
     "sa_camera_attention": (ctypes.c_int, [ctypes.POINTER(sa_geom), _P, _I, _P, _P, _I, _I, _I, _P,
                                            _P, _P]),
     "sa_kv_dequant": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_kv_layer), _P, _I,
@@ -345,6 +347,9 @@ def sparse_select(geom, item, block_list=None, stream=None):
         nq = -(-rows // SPARSE_QUERY_BLOCK)
         block_list = torch.empty((geom.heads, max(nq, 1), max(item.keep_blocks, 1)),
                                  dtype=torch.int32, device=item.q.device)
+    else:
+        _check_i32(block_list, geom.heads * -(-rows // SPARSE_QUERY_BLOCK) * item.keep_blocks,
+                   "block_list")
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=item.q.device)
     _check(lib().sa_sparse_select(ctypes.byref(g), ctypes.byref(it), _ptr(ws), nbytes,
                                   _ptr(block_list), _stream(stream)))
@@ -352,6 +357,25 @@ def sparse_select(geom, item, block_list=None, stream=None):
         ext = stream if isinstance(stream, torch.cuda.Stream) else \
             torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)))
         ws.record_stream(ext)
+    return block_list
+
+
+SPARSE_SCRATCH_BYTES = 32 << 20
+
+
+def sparse_select_noalloc(geom, item, block_list, stream=None):
+    """sparse_select with the pooled keys in the library's static device
+    scratch (SPARSE_SCRATCH_BYTES per GPU): the call allocates nothing, so
+    block_list (int32 [H, ceil(rows / 256), keep_blocks], device) is the
+    caller's. Calls that overlap in time on one GPU share the scratch and
+    race."""
+    rows = item.n_frames_q * geom.P + item.n_text_q
+    _check_i32(block_list, geom.heads * -(-rows // SPARSE_QUERY_BLOCK) * item.keep_blocks,
+               "block_list")
+    g = geom.c()
+    it = item.c()
+    _check(lib().sa_sparse_select_noalloc(ctypes.byref(g), ctypes.byref(it), _ptr(block_list),
+                                          _stream(stream)))
     return block_list
 
 

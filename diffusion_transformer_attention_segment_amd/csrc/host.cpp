@@ -586,6 +586,16 @@ sa_status prepare_select(const sa_geom* geom, const sa_attn_item* item, SelectAr
   return ok();
 }
 
+// The block-list output of a selection call, and the head bound of its
+// selection kernel.
+sa_status check_block_list_out(const sa_geom* geom, const int32_t* block_list) {
+  if (block_list == nullptr) return fail(SA_E_ARG, "sparse_select: block_list is NULL");
+  if ((reinterpret_cast<uintptr_t>(block_list) & 3) != 0)
+    return fail(SA_E_ALIGN, "sparse_select: block_list not 4-byte aligned");
+  if (geom->heads > 256) return fail(SA_E_SHAPE, "sparse_select: more than 256 heads");
+  return SA_OK;
+}
+
 }  // namespace
 
 int32_t sa_sparse_keep(int32_t n_candidates, int32_t percent) {
@@ -612,16 +622,35 @@ sa_status sa_sparse_select(const sa_geom* geom, const sa_attn_item* item, void* 
   size_t ws = 0;
   sa_status st = prepare_select(geom, item, a, &ws);
   if (st != SA_OK) return st;
-  if (block_list == nullptr) return fail(SA_E_ARG, "sparse_select: block_list is NULL");
-  if ((reinterpret_cast<uintptr_t>(block_list) & 3) != 0)
-    return fail(SA_E_ALIGN, "sparse_select: block_list not 4-byte aligned");
+  if ((st = check_block_list_out(geom, block_list)) != SA_OK) return st;
   if (workspace == nullptr || workspace_bytes < ws)
     return fail(SA_E_CAPACITY, "sparse_select: workspace of %zu bytes < %zu", workspace_bytes, ws);
   if (!aligned16(workspace)) return fail(SA_E_ALIGN, "sparse_select: workspace not 16-byte aligned");
-  if (geom->heads > 256) return fail(SA_E_SHAPE, "sparse_select: more than 256 heads");
   a.pooled = static_cast<float*>(workspace);
   a.out = block_list;
   return hip_status(launch_sparse_select(a, static_cast<hipStream_t>(stream)), "sparse_select launch");
+}
+
+sa_status sa_sparse_select_noalloc(const sa_geom* geom, const sa_attn_item* item,
+                                   int32_t* block_list, void* stream) {
+  SelectArgs a;
+  size_t ws = 0;
+  sa_status st = prepare_select(geom, item, a, &ws);
+  if (st != SA_OK) return st;
+  if ((st = check_block_list_out(geom, block_list)) != SA_OK) return st;
+  if (ws > SA_SPARSE_SCRATCH_BYTES)
+    return fail(SA_E_CAPACITY,
+                "sparse_select_noalloc: %d heads x %d candidate blocks need %zu bytes of pooled "
+                "keys > the %u-byte static scratch",
+                geom->heads, a.n_cand, ws, SA_SPARSE_SCRATCH_BYTES);
+  float* scratch = nullptr;
+  if ((st = hip_status(sparse_select_scratch(&scratch), "sparse_select_noalloc scratch address")) !=
+      SA_OK)
+    return st;
+  a.pooled = scratch;
+  a.out = block_list;
+  return hip_status(launch_sparse_select(a, static_cast<hipStream_t>(stream)),
+                    "sparse_select_noalloc launch");
 }
 
 sa_status sa_camera_attention(const sa_geom* geom, const void* q, int32_t n_frames,

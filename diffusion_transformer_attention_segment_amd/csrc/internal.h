@@ -116,6 +116,9 @@ struct SelectArgs {
 };
 constexpr int kMaxCandidates = SA_MAX_SPARSE_CANDIDATES;
 hipError_t launch_sparse_select(const SelectArgs& a, hipStream_t s);
+// Device address of the static pooled-key array (SA_SPARSE_SCRATCH_BYTES) on
+// the current device, looked up on the first call per device.
+hipError_t sparse_select_scratch(float** out);
 
 hipError_t launch_attention_bf16(AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_fp8(AttnArgs& a, hipStream_t s);

@@ -20,7 +20,15 @@
 //                  the lower block index, and the kept indices written in
 //                  ascending order through two block scans. Integer counts
 //                  only after the scores: the lists are deterministic.
+#include <mutex>
+
 #include "attention_common.h"
+
+// Pooled keys of sa_sparse_select_noalloc: [H][n_cand][128] fp32 in the
+// library's own device memory, one copy per GPU. Host code never passes this
+// name to a kernel (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) float scratch[SA_SPARSE_SCRATCH_BYTES / sizeof(float)];
 
 namespace segattn {
 namespace {
@@ -256,6 +264,26 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
 }
 
 }  // namespace
+
+hipError_t sparse_select_scratch(float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_sparse_select(const SelectArgs& a, hipStream_t s) {
   static_assert(kPerThread <= 16, "a thread's candidate run stays short");

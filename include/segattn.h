@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 8
+#define SA_ABI_VERSION 9
 #define SA_HEAD_DIM 128       /* the only head dim the kernels are built for */
 #define SA_MAX_ITEMS 8        /* sessions per sa_segment_attention call     */
 #define SA_MAX_FRAMES_KV 65536
@@ -307,6 +307,27 @@ sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, i
  * n_hist_frames > n_frames_kv), SA_E_CAPACITY (workspace too small),
  * SA_E_ALIGN.                                                               */
 size_t sa_sparse_select_workspace(const sa_geom* geom, const sa_attn_item* item);
+sa_status sa_sparse_select(const sa_geom* geom, const sa_attn_item* item, void* workspace,
+                           size_t workspace_bytes, int32_t* block_list, void* stream);
+
+/* sparse_select_noalloc: sa_sparse_select for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels, the same block lists bit for bit,
+ * but the pooled keys live in the library's own static device array of
+ * SA_SPARSE_SCRATCH_BYTES bytes (one per GPU, held until the process ends)
+ * instead of a caller workspace. The caller still passes the inputs and the
+ * output block_list. No allocation of any kind happens in the call (the
+ * array's device address is looked up once per device, on the first call
+ * with that device current). The array needs no clearing: each call writes
+ * every pooled key it reads. All calls on one GPU share the array, so calls
+ * that overlap in time on one GPU (two streams, two threads) race; calls on
+ * one stream are ordered. Errors: those of sa_sparse_select, except that
+ * SA_E_CAPACITY means heads x candidate blocks x 512 bytes exceeds
+ * SA_SPARSE_SCRATCH_BYTES (at most 65,536 head-candidate pairs: e.g. 16
+ * heads x 4,096 candidates); SA_E_HIP if the array's address lookup fails.  */
+#define SA_SPARSE_SCRATCH_BYTES (32u << 20)
+sa_status sa_sparse_select_noalloc(const sa_geom* geom, const sa_attn_item* item,
+                                   int32_t* block_list, void* stream);
 
 /* sparse_keep: how many of n_candidates history blocks a block-sparse pass
  * keeps at `percent` (the pages keep 25 % of the candidate video blocks):
@@ -314,8 +335,6 @@ size_t sa_sparse_select_workspace(const sa_geom* geom, const sa_attn_item* item)
  * 0 for n_candidates <= 0. percent must lie in [1, 100] (else -1 and the
  * error is set). Host only, pure.                                           */
 int32_t sa_sparse_keep(int32_t n_candidates, int32_t percent);
-sa_status sa_sparse_select(const sa_geom* geom, const sa_attn_item* item, void* workspace,
-                           size_t workspace_bytes, int32_t* block_list, void* stream);
 
 /* camera_attention: cross-attention of the segment's video tokens to the
  * camera tokens, one per latent frame ("Hy-Nomas: an 8.6B world model ...",

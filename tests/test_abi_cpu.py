@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 8
+    assert sa.abi_version() == 9
 
 
 def test_status_strings(lib):
@@ -261,6 +261,30 @@ def test_sparse_validation(lib):
     assert ws(ctypes.byref(g), ctypes.byref(sp(_item(big, n_frames_kv=8200), nh=8193))) == 0
     assert b"candidate blocks" in lib.sa_last_error()
     assert sel(ctypes.byref(g), None, ctypes.c_void_p(FAKE), 4096, ctypes.c_void_p(FAKE), None) == 1
+
+
+def test_sparse_noalloc_validation(lib):
+    """The allocation-free selection refuses, on the host, what its static
+    scratch cannot hold (heads x candidates x 512 bytes > 32 MiB) and the
+    block-list errors of sparse_select."""
+    assert sa.SPARSE_SCRATCH_BYTES == 32 << 20
+    nal = lib.sa_sparse_select_noalloc
+    big = _layer(fc=5000)
+    g16 = _geom(heads=16)
+    it = _item(big, n_frames_kv=4097)
+    it.block_list, it.n_hist_frames, it.keep_blocks = FAKE, 4097, 1     # P = 24: one block a frame
+    assert nal(ctypes.byref(g16), ctypes.byref(it), ctypes.c_void_p(FAKE), None) == 6
+    assert b"static scratch" in lib.sa_last_error()
+    assert lib.sa_sparse_select_workspace(ctypes.byref(g16), ctypes.byref(it)) == 16 * 4097 * 512
+    g = _geom()
+    L = _layer(fc=8)
+    it = _item(L)
+    it.block_list, it.n_hist_frames, it.keep_blocks = FAKE, 2, 1
+    assert nal(ctypes.byref(g), ctypes.byref(it), None, None) == 1
+    assert nal(ctypes.byref(g), ctypes.byref(it), ctypes.c_void_p(FAKE + 2), None) == 3
+    it.keep_blocks = 3
+    assert nal(ctypes.byref(g), ctypes.byref(it), ctypes.c_void_p(FAKE), None) == 1
+    assert nal(ctypes.byref(g), None, ctypes.c_void_p(FAKE), None) == 1
 
 
 def test_camera_validation(lib):
