@@ -95,19 +95,25 @@ SIGNATURES = {
 _lib = None
 
 
+def load(path):
+    """A build of the library at `path` with the C signatures set (raises if
+    it is missing)."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run "
+                           "`python -m diffusion_transformer_attention_segment_amd.build`")
+    L = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
 def lib():
     """The loaded library (raises if libsegattn.so is missing)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run "
-                               "`python -m diffusion_transformer_attention_segment_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(L, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
 
 

@@ -4,6 +4,9 @@
 
 Compiles every source under csrc/ to an object in _build/ (at the repository
 root) and links them into diffusion_transformer_attention_segment_amd/libsegattn.so.
+A debug build of the same library, libsegattn_debug.so, differs only in its host
+code (host.cpp with SA_DEBUG_CHECKS): device index lists are checked before
+every launch that reads them, and attention outputs start as NaN canaries.
 """
 
 import concurrent.futures
@@ -17,6 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsegattn.so")
+DEBUG_LIB = os.path.join(PKG, "libsegattn_debug.so")
 ARCH = "gfx950"
 
 SOURCES = ["host.cpp", "kv_append.hip", "attention_bf16.hip", "attention_fp8.hip", "attention_combine.hip",
@@ -38,10 +42,13 @@ def hipcc():
     return exe
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(job):
+    src, defines = job
+    tag = "_debug" if defines else ""
+    obj = os.path.join(BUILD, os.path.basename(src) + tag + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc()] + COMMON + DEVICE_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([hipcc()] + COMMON + DEVICE_FLAGS + defines + lang +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in line)
@@ -50,23 +57,29 @@ def _compile(src):
     return obj, out
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    objs = []
-    for obj, out in results:
-        objs.append(obj)
-        if verbose and out.strip():
-            print(out)
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    assert SOURCES[0] == "host.cpp"   # the debug library swaps the first object
+    jobs = [(src, []) for src in SOURCES] + [("host.cpp", ["-DSA_DEBUG_CHECKS"])]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        results = list(ex.map(_compile, jobs))
+    for _, out in results:
+        if verbose and out.strip():
+            print(out)
+    objs = [obj for obj, _ in results]
+    _link(objs[:len(SOURCES)], LIB)
+    _link([objs[-1]] + objs[1:len(SOURCES)], DEBUG_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", DEBUG_LIB)
     return LIB
 
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -114,6 +115,68 @@ sa_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(SA_E_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
 }
+
+#ifdef SA_DEBUG_CHECKS
+// Debug builds check what release builds trust: the device index lists are
+// copied to the host on the call's stream (the call then waits for that
+// stream) and every entry must lie in [0, hi); with distinct_rows, each run
+// of `row` entries must hold distinct values.
+sa_status debug_check_list(const int32_t* d, int64_t n, int64_t row, int32_t hi, bool distinct_rows,
+                           hipStream_t s, const char* what) {
+  if (n <= 0) return SA_OK;
+  std::vector<int32_t> h(static_cast<size_t>(n));
+  hipError_t e = hipMemcpyAsync(h.data(), d, static_cast<size_t>(n) * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, what);
+  for (int64_t i = 0; i < n; ++i)
+    if (h[i] < 0 || h[i] >= hi)
+      return fail(SA_E_RANGE, "%s: entry %lld is %d, outside [0, %d) (debug check)", what,
+                  static_cast<long long>(i), h[i], hi);
+  if (distinct_rows) {
+    for (int64_t r0 = 0; r0 < n; r0 += row) {
+      std::vector<int32_t> v(h.begin() + r0, h.begin() + std::min(n, r0 + row));
+      std::sort(v.begin(), v.end());
+      if (std::adjacent_find(v.begin(), v.end()) != v.end())
+        return fail(SA_E_ARG, "%s: row %lld repeats an entry (debug check)", what,
+                    static_cast<long long>(r0 / row));
+    }
+  }
+  return SA_OK;
+}
+
+// Frame lists and block lists of an attention call, then NaN canaries in
+// every output row (bf16 and fp32 all-ones bytes are NaN), so that a row the
+// kernels leave unwritten shows in the result.
+sa_status debug_check_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
+                                hipStream_t s) {
+  const int32_t P = tokens_per_frame(geom);
+  char what[64];
+  for (int i = 0; i < n_items; ++i) {
+    const sa_attn_item& it = items[i];
+    std::snprintf(what, sizeof what, "item %d frames", i);
+    sa_status st = debug_check_list(it.frames, it.n_frames_kv, 1, it.kv->frame_capacity, false, s,
+                                    what);
+    if (st != SA_OK) return st;
+    const int64_t rows = static_cast<int64_t>(it.n_frames_q) * P + it.n_text_q;
+    if (it.block_list != nullptr && it.n_hist_frames > 0) {
+      const int64_t qb = (rows + SA_SPARSE_QUERY_BLOCK - 1) / SA_SPARSE_QUERY_BLOCK;
+      const int32_t cand = it.n_hist_frames * ((P + 63) / 64);
+      std::snprintf(what, sizeof what, "item %d block_list", i);
+      st = debug_check_list(it.block_list, geom->heads * qb * it.keep_blocks, it.keep_blocks, cand,
+                            true, s, what);
+      if (st != SA_OK) return st;
+    }
+    if (rows > 0) {
+      const size_t vals = static_cast<size_t>(rows) * geom->heads;
+      hipError_t e = hipMemsetAsync(it.out, 0xFF, vals * geom->head_dim * sizeof(uint16_t), s);
+      if (e == hipSuccess && it.lse != nullptr) e = hipMemsetAsync(it.lse, 0xFF, vals * sizeof(float), s);
+      if (e != hipSuccess) return hip_status(e, "attention output canary");
+    }
+  }
+  return SA_OK;
+}
+#endif
 
 }  // namespace
 
@@ -308,6 +371,11 @@ sa_status sa_history_gather(const sa_geom* geom, const sa_kv_layer* src, const i
   a.n = n;
   a.heads = geom->heads;
   if (geom->heads > 256) return fail(SA_E_SHAPE, "gather: more than 256 heads");
+#ifdef SA_DEBUG_CHECKS
+  if ((st = debug_check_list(d_frames, n, 1, src->frame_capacity, false,
+                             static_cast<hipStream_t>(stream), "gather frames")) != SA_OK)
+    return st;
+#endif
   return hip_status(launch_gather(a, static_cast<hipStream_t>(stream)), "history_gather launch");
 }
 
@@ -450,17 +518,18 @@ sa_status prepare_attention(const sa_geom* geom, const sa_attn_item* items, int3
   return ok();
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; threads that race
+// on the first query store the same value).
 int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Split plan: the tiles of the last partial round (r = total mod CUs, or all
@@ -521,6 +590,10 @@ sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, i
   sa_status st = prepare_attention(geom, items, n_items, plan);
   if (st != SA_OK) return st;
   AttnArgs& a = plan.a;
+#ifdef SA_DEBUG_CHECKS
+  if ((st = debug_check_attention(geom, items, n_items, static_cast<hipStream_t>(stream))) != SA_OK)
+    return st;
+#endif
   if (a.total_tiles == 0) return ok();
   const size_t need = plan_split(plan);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))) {
@@ -626,6 +699,11 @@ sa_status sa_sparse_select(const sa_geom* geom, const sa_attn_item* item, void* 
   if (workspace == nullptr || workspace_bytes < ws)
     return fail(SA_E_CAPACITY, "sparse_select: workspace of %zu bytes < %zu", workspace_bytes, ws);
   if (!aligned16(workspace)) return fail(SA_E_ALIGN, "sparse_select: workspace not 16-byte aligned");
+#ifdef SA_DEBUG_CHECKS
+  if ((st = debug_check_list(item->frames, item->n_hist_frames, 1, item->kv->frame_capacity, false,
+                             static_cast<hipStream_t>(stream), "sparse_select frames")) != SA_OK)
+    return st;
+#endif
   a.pooled = static_cast<float*>(workspace);
   a.out = block_list;
   return hip_status(launch_sparse_select(a, static_cast<hipStream_t>(stream)), "sparse_select launch");
@@ -706,6 +784,11 @@ sa_status sa_kv_dequant(const sa_geom* geom, const sa_kv_layer* src, const int32
   if (n_frames > 0 && d_frames == nullptr) return fail(SA_E_ARG, "frames is NULL");
   if (n_frames > 0 && src->frame_capacity == 0) return fail(SA_E_RANGE, "dequant: src has no frames");
   hipStream_t s = static_cast<hipStream_t>(stream);
+#ifdef SA_DEBUG_CHECKS
+  if ((st = debug_check_list(d_frames, n_frames, 1, src->frame_capacity, false, s,
+                             "dequant frames")) != SA_OK)
+    return st;
+#endif
   if (n_frames > 0) {
     DequantArgs a{};
     a.src_k = static_cast<const uint8_t*>(src->k);

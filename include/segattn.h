@@ -28,9 +28,16 @@
  *    returns an sa_status; on failure nothing is launched and
  *    sa_last_error() describes the problem (thread-local, valid until the
  *    next sa_* call on the same thread). Launch failures return SA_E_HIP.
- *  - Device-side index lists (frame lists) are trusted: entries must lie in
- *    [0, frame_capacity) of the layer they index; sa_history_select only
- *    produces such lists.
+ *  - Device-side index lists (frame lists, block lists) are trusted by this
+ *    library: frame entries must lie in [0, frame_capacity) of the layer they
+ *    index, block entries as sa_attn_item.block_list states;
+ *    sa_history_select and sa_sparse_select only produce such lists. The
+ *    debug build of the same ABI (libsegattn_debug.so, host code compiled
+ *    with SA_DEBUG_CHECKS) copies each list to the host on the call's stream
+ *    and waits for it before the launch that reads it, refuses a bad entry
+ *    (SA_E_RANGE; SA_E_ARG for a block repeated in one list), and fills the
+ *    attention outputs with NaN before the kernels write them. It is for
+ *    finding bad lists, not for graph capture or speed.
  *  - bf16 = bfloat16 (raw 16-bit patterns); e4m3 = OCP 8-bit float e4m3fn
  *    (bias 7, max 448, no infinities).
  *  - Results are bitwise reproducible run to run (no atomics, fixed

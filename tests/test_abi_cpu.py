@@ -44,6 +44,15 @@ def test_exports_every_declared_symbol(lib):
     assert sorted(B.SIGNATURES) == declared
 
 
+def test_debug_library_exports_every_declared_symbol(lib):
+    """The debug build (device index lists checked on the host) has the same ABI."""
+    from diffusion_transformer_attention_segment_amd import build
+    dbg = B.load(build.DEBUG_LIB)
+    for name in _declared_functions():
+        assert hasattr(dbg, name), name
+    assert dbg.sa_abi_version() == sa.abi_version()
+
+
 def test_abi_version(lib):
     assert sa.abi_version() == 9
 
