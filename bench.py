@@ -16,8 +16,20 @@ starts.
 Prints ONE JSON line. `value` is segment-attention TFLOP/s over the whole step
 (FLOP = 4 * Lq * Lk * 128 * H, the algorithmic work on the kept key set);
 `roofline` prices the attention kernel alone against the bf16 (or fp8) dense
-MFMA peak using its HIP-event duration; `cpu_baseline` times the fp64 oracle
-on a bounded sample of the same workload on the host cores.
+MFMA peak using its HIP-event duration, beside the same figure from the
+committed kernel-trace summary; `cpu_baseline` times the fp64 oracle on 25 %
+of the query rows of the same workload on the host cores. Unless
+--headline-only, the line also carries: the slow-path counts of the timed
+call, the attention on sharpened logits (queries x 4 and x 40) and with timed
+text windows, one block-sparse pass, the e4m3 (fp8seg8) and int8 (int8seg8)
+workloads' attention, the HBM-bound calls against a plain device copy, and
+the MFMA throughput probes.
+
+Profile summaries under profiles/ are written by the same script:
+    python bench.py --summarize-trace DIR --workload W [--title T --command C]
+    python bench.py --summarize-pmc DIR [DIR ...] --workload W [--title T --command C]
+read the rocprofv3 output under DIR (kernel_trace.csv / counter_collection.csv)
+and print the per-kernel summary with the hash of the attention sources.
 """
 
 import argparse
@@ -38,28 +50,24 @@ METRIC = "segment-attention TFLOP/s per GPU + % of MFMA peak; ms per 54-block se
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}     # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0
 
-# HBM traffic of the attention kernel per launch, from the committed rocprofv3
+# HBM traffic of the attention call per launch, from the committed rocprofv3
 # counter summaries: FETCH_SIZE reads half the bytes a plain device copy of
-# known size moves and WRITE_SIZE all of them (calibrated with the gather
-# kernel), so bytes = 2.0 * FETCH_SIZE + 1.0 * WRITE_SIZE (KiB per dispatch).
-# The summary records a hash of the kernel source it was taken on; a kernel
+# known size moves and WRITE_SIZE all of them (calibrated with a copy of known
+# size), so bytes = 2.0 * FETCH_SIZE + 1.0 * WRITE_SIZE (KiB per dispatch).
+# Each summary records a hash of the kernel sources it was taken on; a kernel
 # changed since then reports null.
-# Counter summaries under profiles/: (file, kernels of one segment_attention
-# call, sources they were built from). The traffic is read from them only while
-# those sources hash to the value the summary records.
 ATTN_SOURCES = ["attention_common.h", "internal.h", "device_common.h", "attention_combine.hip",
                 "host.cpp"]
+KERNEL_SOURCES = {"bf16": ["attention_bf16.hip"] + ATTN_SOURCES,
+                  "fp8": ["attention_fp8.hip"] + ATTN_SOURCES,
+                  "int8": ["attention_bf16.hip"] + ATTN_SOURCES}
 # The attention kernels are templates: <sparse history, int8 cache> for bf16,
 # <sparse history> for fp8; the bench's timed call is the dense instantiation.
-COUNTER_SUMMARY = {
-    ("bf16", "seg1"): ("attn_bf16_seg1_counters.txt",
-                       ["attn_bf16_kernel<false, false>", "combine_kernel"],
-                       ["attention_bf16.hip"] + ATTN_SOURCES),
-    ("fp8", "fp8seg8"): ("attn_fp8_fp8seg8_counters.txt", ["attn_fp8_kernel<false>", "combine_kernel"],
-                         ["attention_fp8.hip"] + ATTN_SOURCES),
-    ("bf16", "int8seg8"): ("attn_int8_int8seg8_counters.txt",
-                           ["attn_bf16_kernel<false, true>", "combine_kernel"],
-                           ["attention_bf16.hip"] + ATTN_SOURCES),
+# (workload) -> (cache kind, summary name stem, kernels of one segment_attention call)
+PROFILED = {
+    "seg1": ("bf16", "attn_bf16_seg1", ["attn_bf16_kernel<false, false>", "combine_kernel"]),
+    "fp8seg8": ("fp8", "attn_fp8_fp8seg8", ["attn_fp8_kernel<false>", "combine_kernel"]),
+    "int8seg8": ("int8", "attn_int8_int8seg8", ["attn_bf16_kernel<false, true>", "combine_kernel"]),
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 
@@ -74,34 +82,152 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(dtype, workload):
+def short_kernel_name(name):
+    """segattn::(anonymous namespace)::attn_bf16_kernel<false, false>(segattn::AttnArgs)
+    -> attn_bf16_kernel<false, false>; other kernels keep at most 70 characters."""
+    n = name.strip().replace("(anonymous namespace)::", "")
+    if n.startswith("void "):
+        n = n[5:]
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):        # the argument list starts at the first '(' outside <>
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    n = n[:cut]
+    lt = n.find("<")
+    head, tmpl = (n, "") if lt < 0 else (n[:lt], n[lt:])
+    return (head.rsplit("::", 1)[-1] + tmpl)[:70]
+
+
+def _csv_rows(dirs, suffix):
+    import csv
+    import glob
+    rows = []
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+            with open(f, newline="") as fh:
+                rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {dirs}")
+    return rows
+
+
+def summarize_trace(dirs, kind, title, command, skip=2):
+    """Per-kernel durations from rocprofv3 kernel_trace.csv: calls, total,
+    mean, median and the mean after each kernel's first `skip` calls (the
+    bench's warm-up steps), in microseconds."""
+    per = {}
+    for r in sorted(_csv_rows(dirs, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"])):
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per.setdefault(short_kernel_name(r["Kernel_Name"]), []).append(us)
+    total = sum(sum(v) for v in per.values())
+    print(f"# rocprofv3 kernel trace summary: {title}")
+    print(f"# command: {command}")
+    print(f"# source hash of csrc/{{{', '.join(KERNEL_SOURCES[kind])}}}: "
+          f"{source_hash(KERNEL_SOURCES[kind])}")
+    print(f"# durations in microseconds from the kernel dispatch records; 'steady avg' skips "
+          f"each kernel's first {skip} calls")
+    print(f"{'kernel':44s}{'calls':>7s}{'total_us':>13s}{'avg_us':>11s}{'median_us':>11s}"
+          f"{'steady_avg':>11s}{'pct':>7s}")
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        s = sorted(v)
+        steady = v[skip:] if len(v) > skip else v
+        print(f"{k[:44]:44s}{len(v):7d}{sum(v):13.1f}{sum(v) / len(v):11.1f}"
+              f"{s[len(s) // 2]:11.1f}{sum(steady) / len(steady):11.1f}"
+              f"{100 * sum(v) / total:7.2f}")
+
+
+def summarize_pmc(dirs, kind, title, command):
+    """Per kernel and counter, the per-dispatch value (summed over the
+    dispatch's rows) averaged over dispatches, from rocprofv3
+    counter_collection.csv files (one directory per counter pass)."""
+    acc, disp = {}, {}
+    for r in _csv_rows(dirs, "counter_collection.csv"):
+        k = short_kernel_name(r["Kernel_Name"])
+        key = (k, r["Counter_Name"])
+        acc.setdefault(key, {})
+        d = r["Dispatch_Id"]
+        acc[key][d] = acc[key].get(d, 0.0) + float(r["Counter_Value"])
+        disp.setdefault(key, set()).add(d)
+    print(f"# rocprofv3 counter summary: {title}")
+    print(f"# command: {command}")
+    print(f"# source hash of csrc/{{{', '.join(KERNEL_SOURCES[kind])}}}: "
+          f"{source_hash(KERNEL_SOURCES[kind])}")
+    print("# values: per-dispatch average (counter summed over the dispatch's rows), "
+          "dispatches in brackets")
+    for k in sorted({k for k, _ in acc}):
+        print(k)
+        for (kk, c) in sorted(key for key in acc if key[0] == k):
+            vals = acc[(kk, c)]
+            print(f"  {c:32s}{sum(vals.values()) / len(vals):17.6g}  [{len(vals)}]")
+
+
+def _summary(workload, suffix):
+    """Lines of the committed summary profiles/<stem>_<suffix>.txt when its
+    source hash matches the current kernel sources, else None."""
+    entry = PROFILED.get(workload)
+    if entry is None:
+        return None
+    path = os.path.join(ROOT, "profiles", f"{entry[1]}_{suffix}.txt")
+    if not os.path.exists(path):
+        return None
+    lines = open(path).read().splitlines()
+    got = next((ln.rsplit(":", 1)[1].strip() for ln in lines if ln.startswith("# source hash")),
+               None)
+    return lines if got == source_hash(KERNEL_SOURCES[entry[0]]) else None
+
+
+def measured_traffic(workload):
     """HBM bytes per segment_attention call (all its kernels) from the counter
     summary: FETCH_FACTOR * FETCH_SIZE + WRITE_FACTOR * WRITE_SIZE (KiB per
     dispatch), or None when no summary matches the current sources."""
-    entry = COUNTER_SUMMARY.get((dtype, workload))
-    if entry is None:
+    lines = _summary(workload, "counters")
+    if lines is None:
         return None
-    summary = os.path.join(ROOT, "profiles", entry[0])
-    if not os.path.exists(summary):
-        return None
-    got, section, vals = None, None, {}
-    for line in open(summary):
-        if line.startswith("# source hash"):
-            got = line.rsplit(":", 1)[1].strip()
-        elif not line.startswith("#") and not line.startswith(" "):
+    kernels = PROFILED[workload][2]
+    section, vals = None, {}
+    for line in lines:
+        if line.startswith("#"):
+            continue
+        if not line.startswith(" "):
             section = line.strip()
-        elif section in entry[1] and line.split():
+        elif section in kernels and line.split():
             vals[(section, line.split()[0])] = float(line.split()[1])
-    if got != source_hash(entry[2]):
-        return None
     total = 0.0
-    for k in entry[1]:
+    for k in kernels:
         if (k, "FETCH_SIZE") not in vals or (k, "WRITE_SIZE") not in vals:
-            if k == entry[1][0]:
+            if k == kernels[0]:
                 return None
             continue     # a merge kernel that did not run in this workload
         total += FETCH_FACTOR * vals[(k, "FETCH_SIZE")] + WRITE_FACTOR * vals[(k, "WRITE_SIZE")]
     return int(1024 * total)
+
+
+def profiled_call_ms(workload):
+    """Mean duration of one segment_attention call (its kernels' steady means,
+    the merge counted per attention launch) from the committed kernel-trace
+    summary, or None when none matches the current sources."""
+    lines = _summary(workload, "kernel_trace")
+    if lines is None:
+        return None
+    kernels = PROFILED[workload][2]
+    got = {}
+    for line in lines:
+        parts = line.rsplit(None, 6)
+        if line.startswith("#") or len(parts) != 7 or parts[0] not in kernels:
+            continue
+        got[parts[0]] = (int(parts[1]), float(parts[5]))
+    if kernels[0] not in got:
+        return None
+    calls, ms = got[kernels[0]][0], got[kernels[0]][1] / 1e3
+    for k in kernels[1:]:
+        if k in got:
+            ms += got[k][1] / 1e3 * got[k][0] / calls
+    return ms
 
 
 def parse():
@@ -112,7 +238,20 @@ def parse():
     ap.add_argument("--workload", default="seg1")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="query rows the oracle times (default: 25 %% of the segment's rows)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the headline steps only (the command the kernel traces profile)")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="run only the plain device copy (the counters' byte calibration)")
+    ap.add_argument("--summarize-trace", nargs="+", metavar="DIR",
+                    help="print the kernel-trace summary of rocprofv3 output under DIR")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="print the counter summary of rocprofv3 --pmc output under DIR(s)")
+    ap.add_argument("--title", default="", help="summary title")
+    ap.add_argument("--command", default="", help="the profiling command, for the summary")
+    ap.add_argument("--source-hash", choices=sorted(KERNEL_SOURCES),
+                    help="print the hash of the attention sources of a cache kind")
     ap.add_argument("--layers", type=int, default=0,
                     help="layers per step (default: the workload's, 54 for seg4x54, else 1)")
     ap.add_argument("--no-clock", action="store_true",
@@ -426,8 +565,9 @@ def measure_dequant(sa, geom, n_frames=99, capacity=128, reps=5):
 
 def measure_copy_ceiling(nbytes=713_687_040, reps=5):
     """A plain device-to-device copy of nbytes (torch's copy kernel, the size
-    of the gather's planes): the practical HBM ceiling the HBM-bound rows are
-    also priced against (bytes read + written / time)."""
+    of the gather's planes, none of this library's kernels): the practical HBM
+    ceiling the HBM-bound rows are also priced against (bytes read + written /
+    time)."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -442,6 +582,144 @@ def measure_copy_ceiling(nbytes=713_687_040, reps=5):
     del src, dst
     return {"bytes_read_plus_written": 2 * nbytes, "ms": round(ms, 4), "GB_per_s": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def attention_items(sa, state, q_scale=1.0, windows=None, seed=0):
+    """The timed call's items, with the queries scaled by q_scale (rounded to
+    bf16 again) and, when windows is True, seeded timed text windows."""
+    wl = state.wl
+    F = wl.lat_t
+    items = []
+    for d in state.sess:
+        q = d["q"] if q_scale == 1.0 else (d["q"].float() * q_scale).to(torch.bfloat16)
+        win = d["win"] if windows is None else (
+            si.text_windows(wl, seed, d["S"] * F).cuda() if windows else None)
+        items.append(sa.AttnItem(q, d["kv"], d["d_frames"], d["n_frames"], wl.n_text, d["out"],
+                                 frame0_q=d["S"] * F, n_frames_q=F, n_text_q=wl.n_text,
+                                 text_window=win))
+    return items
+
+
+def time_attention(sa, geom, items, reps=5):
+    """Mean ms of segment_attention over reps calls (HIP events on the
+    current stream, after one untimed call)."""
+    sa.segment_attention(geom, items)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        sa.segment_attention(geom, items)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def count_call(sa, geom, items):
+    """Slow-path counts of one call (sa_segment_attention_counted)."""
+    c = torch.zeros(3, dtype=torch.int32, device="cuda")
+    sa.segment_attention(geom, items, counters=c)
+    torch.cuda.synchronize()
+    tiles, slow, resc = (int(x) for x in c.cpu())
+    return {"work_tiles": tiles, "slow_path_events": slow, "rescale_steps": resc}
+
+
+def measure_logit_variants(sa, state, attn_ms, seed):
+    """The timed call again on sharpened logits (queries x 4 and x 40) and
+    with timed text windows: time per call and how often the rescaling paths
+    ran (bf16: work tiles re-run with rescaling; e4m3: renormalisations; and
+    rescale steps of waves)."""
+    out = {"q_x1": dict(attention_ms=round(attn_ms, 4), **count_call(sa, state.geom,
+                                                                      attention_items(sa, state)))}
+    for qs in (4.0, 40.0):
+        items = attention_items(sa, state, q_scale=qs)
+        ms = time_attention(sa, state.geom, items)
+        out[f"q_x{int(qs)}"] = dict(attention_ms=round(ms, 4), ratio_to_q_x1=round(ms / attn_ms, 4),
+                                    **count_call(sa, state.geom, items))
+        del items
+    if state.sess[0]["win"] is None:
+        items = attention_items(sa, state, windows=True, seed=seed)
+        ms = time_attention(sa, state.geom, items)
+        out["text_windows"] = dict(attention_ms=round(ms, 4), ratio_to_q_x1=round(ms / attn_ms, 4),
+                                   **count_call(sa, state.geom, items))
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_workload_attention(sa, name, seed, reps=5):
+    """segment_attention of another workload (one layer; its history written
+    by kv_append before timing): time, TFLOP/s against its dtype's dense
+    peak, slow-path counts, and the same on queries x 4."""
+    wl = workload(name, seed)
+    st = LayerState(sa, wl, seed, 0)
+    st.run(sa, st.upload(sa))
+    torch.cuda.synchronize()
+    dtype = "fp8" if wl.kv_dtype == "fp8" else "bf16"
+    peak = PEAK_TFLOPS[dtype]
+    flops = st.flops()
+    items = attention_items(sa, st)
+    ms = time_attention(sa, st.geom, items, reps)
+    tf = flops / (ms * 1e-3) / 1e12
+    rec = {"kv_dtype": wl.kv_dtype, "mfma_dtype": dtype, "Lq": wl.Lq,
+           "Lk": [d["n_frames"] * wl.P + wl.n_text for d in st.sess], "flop_per_call": flops,
+           "attention_ms": round(ms, 4), "TFLOP_s": round(tf, 1), "peak_TFLOP_s": peak,
+           "frac_of_peak": round(tf / peak, 4)}
+    prof = profiled_call_ms(name)
+    if prof is not None:
+        rec["profile_call_ms"] = round(prof, 4)
+        rec["frac_of_peak_profile"] = round(flops / (prof * 1e-3) / 1e12 / peak, 4)
+    rec["traffic"] = measured_traffic(name)
+    rec.update(count_call(sa, st.geom, items))
+    q4 = attention_items(sa, st, q_scale=4.0)
+    ms4 = time_attention(sa, st.geom, q4, reps)
+    rec["q_x4"] = dict(attention_ms=round(ms4, 4), ratio_to_q_x1=round(ms4 / ms, 4),
+                       **count_call(sa, st.geom, q4))
+    del st, items, q4
+    torch.cuda.empty_cache()
+    return rec
+
+
+def measure_mfma_probe(grid=1024, reps=3):
+    """MFMA throughput on this device at its running clock (libsegattn_probe.so):
+    bf16 with constant register operands, with random register operands, with
+    the A operand read from LDS for every MFMA (as the attention step), and
+    fp8 with random register operands; workgroups of 8 waves, 8 independent
+    accumulators per wave. TFLOP/s and the fraction of the published peak."""
+    import ctypes
+    from diffusion_transformer_attention_segment_amd import build
+    L = ctypes.CDLL(build.PROBE_LIB)
+    L.sa_probe_mfma.restype = ctypes.c_int
+    L.sa_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    n_ops = 65536                                   # 16-byte words of operand bits
+    bf = si.normal_bf16((n_ops * 8,), si.derive_seed(0, "bench", "probe_bf16"), "cuda")
+    g = torch.Generator(device="cuda").manual_seed(si.derive_seed(0, "bench", "probe_fp8"))
+    f8 = torch.randint(0, 256, (n_ops * 16,), dtype=torch.uint8, device="cuda", generator=g)
+    f8.bitwise_and_(0xF7)                           # no e4m3 NaN code
+    out = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {"grid": grid, "waves_per_workgroup": 8}
+    for mode, name, ops, iters, flop, dtype in (
+            (0, "bf16_constant_registers", bf, 8192, 2 * 32 * 32 * 16, "bf16"),
+            (1, "bf16_random_registers", bf, 8192, 2 * 32 * 32 * 16, "bf16"),
+            (2, "bf16_random_lds_operand", bf, 8192, 2 * 32 * 32 * 16, "bf16"),
+            (3, "fp8_random_registers", f8, 4096, 2 * 32 * 32 * 64, "fp8")):
+        def launch():
+            rc = L.sa_probe_mfma(mode, ctypes.c_void_p(ops.data_ptr()), n_ops,
+                                 ctypes.c_void_p(out.data_ptr()), grid, iters, stream)
+            if rc != 0:
+                raise RuntimeError(f"sa_probe_mfma mode {mode}: status {rc}")
+        launch()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            launch()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = grid * 8 * iters * 8 * flop / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "TFLOP_s": round(tf, 1),
+                     "frac_of_peak": round(tf / PEAK_TFLOPS[dtype], 4)}
+    del bf, f8, out
+    return res
 
 
 def cpu_baseline(state, rows_wanted, seed):
@@ -482,6 +760,7 @@ def cpu_baseline(state, rows_wanted, seed):
     q = d["q"].cpu().double().numpy()
     qpos = np.concatenate([orope.video_positions(d["S"] * F, F, wl.lat_h, wl.lat_w),
                            orope.text_positions(wl.n_text)])
+    rows_wanted = rows_wanted or -(-wl.Lq // 4)
     rows = np.linspace(0, wl.Lq - 1, rows_wanted).astype(np.int64)
     t0 = time.perf_counter()
     kr = orope.rope3d(k, kpos, wl.split, wl.theta)
@@ -504,18 +783,35 @@ def cpu_baseline(state, rows_wanted, seed):
             "kind": "oracle", "blas_threads": int(threads), "cpu_count": os.cpu_count(),
             "usable_cores": len(os.sched_getaffinity(0)),
             "sample": (f"numpy fp64 oracle, session 0: RoPE of all {lk} keys x {wl.heads} heads "
-                       f"({t1 - t0:.2f} s) + attention of {len(rows)} of {wl.Lq} query rows, all "
-                       f"heads ({t2 - t1:.2f} s), extrapolated linearly in rows to the full "
+                       f"({t1 - t0:.2f} s) + attention of {len(rows)} of {wl.Lq} query rows "
+                       f"({100.0 * len(rows) / wl.Lq:.1f} %, evenly spaced), all heads "
+                       f"({t2 - t1:.2f} s); the rows' share extrapolated linearly to the full "
                        f"segment: {t_full:.1f} s per layer"),
+            "rows_timed": int(len(rows)), "rows_total": int(wl.Lq),
             "seconds_per_layer_extrapolated": t_full}
 
 
 def main():
     args = parse()
+    if args.source_hash:
+        print(source_hash(KERNEL_SOURCES[args.source_hash]))
+        return
+    if args.summarize_trace or args.summarize_pmc:
+        if args.workload not in PROFILED:
+            raise SystemExit(f"no profiled attention kernel for workload {args.workload}")
+        kind = PROFILED[args.workload][0]
+        if args.summarize_trace:
+            summarize_trace(args.summarize_trace, kind, args.title, args.command)
+        else:
+            summarize_pmc(args.summarize_pmc, kind, args.title, args.command)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this bench runs on one GPU only; multi-GPU sharding "
                                    "(heads across GPUs) is a design note, not built"}))
         sys.exit(2)
+    if args.copy_only:
+        print(json.dumps({"device_copy": measure_copy_ceiling()}), flush=True)
+        return
     import diffusion_transformer_attention_segment_amd as sa
     sa.lib()
     wl = workload(args.workload, args.seed)
@@ -618,32 +914,38 @@ def main():
         "gpu_clock": clock,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None if args.text_windows else measured_traffic(dtype, wl.name),
+                     "traffic": None if args.text_windows else measured_traffic(wl.name),
                      "kernel": "segment_attention: attn_" + dtype + "_kernel + combine_kernel",
-                     "flop_per_launch": flops,
-                     "frac_at_observed_clock": (
-                         round(achieved / (peak * clock["gfxclk_mhz_mean"] / clock["max_clk_mhz"]), 4)
-                         if clock and clock.get("max_clk_mhz") else None)},
+                     "flop_per_launch": flops},
         "kv_append": {"ms": round(app_ms, 4), "bytes": app_bytes,
                       "GB_per_s": round(app_bytes / (app_ms * 1e-3) / 1e9, 1),
                       "frac_of_hbm_peak": round(app_bytes / (app_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
     }
-    sp = measure_sparse(sa, state)
-    if sp is not None:
-        sp["speedup_vs_dense_attention"] = round(attn_ms / sp["pass_ms"], 3)
-        line["sparse_25pct"] = sp
-    line["camera_attention"] = measure_camera(sa, state)
-    line["history_gather"] = measure_gather(sa, state.geom)
-    line["kv_dequant"] = measure_dequant(sa, state.geom)
-    # the practical streaming rate: the faster of two plain copies of the same
-    # size, torch's copy kernel and history_gather (which moves whole planes)
-    ceiling = measure_copy_ceiling()
-    best = max(ceiling["GB_per_s"], line["history_gather"]["GB_per_s"])
-    ceiling["ceiling_GB_per_s"] = best
-    ceiling["ceiling_from"] = ("torch copy" if best == ceiling["GB_per_s"] else "history_gather")
-    line["device_copy_ceiling"] = ceiling
-    for k in ("kv_append", "camera_attention", "history_gather", "kv_dequant"):
-        line[k]["frac_of_copy_ceiling"] = round(line[k]["GB_per_s"] / best, 4)
+    prof = None if args.text_windows or n_layers != 1 else profiled_call_ms(wl.name)
+    if prof is not None:     # the committed kernel trace of the same call
+        line["roofline"]["profile_call_ms"] = round(prof, 4)
+        line["roofline"]["frac_profile"] = round(flops / (prof * 1e-3) / 1e12 / peak, 4)
+    if not args.headline_only:
+        line["logit_variants"] = measure_logit_variants(sa, state, attn_ms, args.seed)
+        sp = measure_sparse(sa, state)
+        if sp is not None:
+            sp["speedup_vs_dense_attention"] = round(attn_ms / sp["pass_ms"], 3)
+            line["sparse_25pct"] = sp
+        line["camera_attention"] = measure_camera(sa, state)
+        line["history_gather"] = measure_gather(sa, state.geom)
+        line["kv_dequant"] = measure_dequant(sa, state.geom)
+        # the practical streaming rate: a plain copy of the same size by torch's
+        # copy kernel (none of the kernels measured here)
+        ceiling = measure_copy_ceiling()
+        line["device_copy_ceiling"] = ceiling
+        for k in ("kv_append", "camera_attention", "history_gather", "kv_dequant"):
+            line[k]["frac_of_copy_ceiling"] = round(line[k]["GB_per_s"] / ceiling["GB_per_s"], 4)
+        others = {}
+        for name in ("fp8seg8", "int8seg8"):
+            if name != wl.name:
+                others[name] = measure_workload_attention(sa, name, args.seed)
+        line["other_workloads"] = others
+        line["mfma_probe"] = measure_mfma_probe()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(state, args.cpu_rows, args.seed)
     print(json.dumps(line), flush=True)

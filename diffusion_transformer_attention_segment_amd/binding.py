@@ -79,6 +79,9 @@ SIGNATURES = {
                                                          ctypes.POINTER(sa_attn_item), _I]),
     "sa_segment_attention": (ctypes.c_int, [ctypes.POINTER(sa_geom), ctypes.POINTER(sa_attn_item),
                                             _I, _P, ctypes.c_size_t, _P]),
+    "sa_segment_attention_counted": (ctypes.c_int, [ctypes.POINTER(sa_geom),
+                                                    ctypes.POINTER(sa_attn_item), _I, _P,
+                                                    ctypes.c_size_t, _P, _P]),
     "sa_sparse_keep": (ctypes.c_int32, [_I, _I]),
     "sa_sparse_select_workspace": (ctypes.c_size_t, [ctypes.POINTER(sa_geom),
                                                      ctypes.POINTER(sa_attn_item)]),
@@ -300,13 +303,15 @@ def segment_attention_workspace(geom, items):
     return int(lib().sa_segment_attention_workspace(ctypes.byref(g), arr, len(items)))
 
 
-def segment_attention(geom, items, stream=None, workspace="auto"):
+def segment_attention(geom, items, stream=None, workspace="auto", counters=None):
     """Joint segment attention over the items.
 
     workspace: "auto" allocates what sa_segment_attention_workspace asks for
     (the last round's tiles are then split over key ranges and merged); None
     runs every tile whole; a uint8 CUDA tensor is used as given (too small:
-    whole tiles)."""
+    whole tiles). counters: an int32 CUDA tensor of >= 3 entries runs
+    sa_segment_attention_counted, which adds [work tiles, slow-path events,
+    rescale steps] into it (same outputs)."""
     g = geom.c()
     arr = (sa_attn_item * max(len(items), 1))()
     for i, it in enumerate(items):
@@ -324,6 +329,11 @@ def segment_attention(geom, items, stream=None, workspace="auto"):
                 ws.record_stream(ext)
     elif workspace is not None:
         ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+    if counters is not None:
+        _check_i32(counters, 3, "counters")
+        _check(lib().sa_segment_attention_counted(ctypes.byref(g), arr, len(items), _ptr(ws),
+                                                  nbytes, _ptr(counters), _stream(stream)))
+        return
     _check(lib().sa_segment_attention(ctypes.byref(g), arr, len(items), _ptr(ws), nbytes,
                                       _stream(stream)))
 

@@ -7,6 +7,8 @@ root) and links them into diffusion_transformer_attention_segment_amd/libsegattn
 A debug build of the same library, libsegattn_debug.so, differs only in its host
 code (host.cpp with SA_DEBUG_CHECKS): device index lists are checked before
 every launch that reads them, and attention outputs start as NaN canaries.
+libsegattn_probe.so holds the MFMA throughput probes the bench reports
+(csrc/mfma_probe.hip); it is not part of the segment-attention ABI.
 """
 
 import concurrent.futures
@@ -21,6 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsegattn.so")
 DEBUG_LIB = os.path.join(PKG, "libsegattn_debug.so")
+PROBE_LIB = os.path.join(PKG, "libsegattn_probe.so")
 ARCH = "gfx950"
 
 SOURCES = ["host.cpp", "kv_append.hip", "attention_bf16.hip", "attention_fp8.hip", "attention_combine.hip",
@@ -69,17 +72,20 @@ def _link(objs, lib):
 def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
     assert SOURCES[0] == "host.cpp"   # the debug library swaps the first object
-    jobs = [(src, []) for src in SOURCES] + [("host.cpp", ["-DSA_DEBUG_CHECKS"])]
+    jobs = ([(src, []) for src in SOURCES] + [("host.cpp", ["-DSA_DEBUG_CHECKS"])] +
+            [("mfma_probe.hip", [])])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         results = list(ex.map(_compile, jobs))
     for _, out in results:
         if verbose and out.strip():
             print(out)
     objs = [obj for obj, _ in results]
-    _link(objs[:len(SOURCES)], LIB)
-    _link([objs[-1]] + objs[1:len(SOURCES)], DEBUG_LIB)
+    n = len(SOURCES)
+    _link(objs[:n], LIB)
+    _link([objs[n]] + objs[1:n], DEBUG_LIB)
+    _link([objs[n + 1]], PROBE_LIB)
     if verbose:
-        print("built", LIB, "and", DEBUG_LIB)
+        print("built", LIB, DEBUG_LIB, "and", PROBE_LIB)
     return LIB
 
 

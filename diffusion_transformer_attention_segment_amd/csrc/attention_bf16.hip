@@ -426,6 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   f32x16 o[4];
   f32x16 negm;
   float l_run;
+  uint32_t n_resc = 0;   // this wave's rescale steps (diagnostic counters only)
 
   // The whole key loop, run first without the rescale: the running max stays
   // at block 0's max, and a block sum above kFastLimit only raises a flag
@@ -533,7 +534,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
       float lb = fused_step(Vprev + voff + 32, Kst + koff1, Vst + voff, Knext + koff0, pre, pa, o,
                             qf, negm, sb, sa, ones, pb, boundary);
       if constexpr (kSafe) {
-        if (__builtin_expect(__any(lb > kRescaleSum), 0)) lb = rescale_step(negm, l_run, o, sa, sb, ones, pb);
+        if (__builtin_expect(__any(lb > kRescaleSum), 0)) {
+          lb = rescale_step(negm, l_run, o, sa, sb, ones, pb);
+          ++n_resc;
+        }
       } else {
         over |= lb > kFastLimit;
       }
@@ -547,7 +551,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
       lb = fused_step(Vst + voff, Knext + koff0, Vst + voff + 32, Knext + koff1, pre, pb, o, qf,
                       negm, sa, sb, ones, pa, [] {});
       if constexpr (kSafe) {
-        if (__builtin_expect(__any(lb > kRescaleSum), 0)) lb = rescale_step(negm, l_run, o, sb, sa, ones, pa);
+        if (__builtin_expect(__any(lb > kRescaleSum), 0)) {
+          lb = rescale_step(negm, l_run, o, sb, sa, ones, pa);
+          ++n_resc;
+        }
       } else {
         over |= lb > kFastLimit;
       }
@@ -569,8 +576,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     }
     return over;
   };
-  if (__syncthreads_or(attend(std::false_type{}))) attend(std::true_type{});
+  const bool rerun = __syncthreads_or(attend(std::false_type{}));
+  if (rerun) attend(std::true_type{});
   const float m_run = -negm[0];
+  if (a.counters != nullptr) add_counts(a.counters, tid, (w == 0 && rerun) ? 1u : 0u, n_resc);
 
   // The output MFMAs compute across all lanes of the wave: keep them (and
   // everything feeding them) ahead of the per-row store branch below, where

@@ -245,6 +245,19 @@ __device__ __forceinline__ void key_range(const AttnArgs& a, const AttnItemDev& 
 // Partial result of one row of a split tile: unnormalised O (128 floats, the
 // lane's 64 in MFMA output order: dims 32 db + 8 r4 + 4 g .. +3 hold
 // o[db][4 r4 .. 4 r4 + 3]), then (lane half 0) m and l.
+// Diagnostic counters of sa_segment_attention_counted, added once per wave
+// after its key loop: [0] work tiles run, [1] slow-path events (bf16: a work
+// tile whose key loop ran again with rescaling; fp8: a wave's renormalisation
+// of O), [2] rescale steps of waves. Device-scope integer adds: the totals do
+// not depend on their order.
+__device__ __forceinline__ void add_counts(uint32_t* c, int tid, uint32_t wave_slow,
+                                           uint32_t wave_rescales) {
+  if ((tid & 63) != 0) return;
+  if (tid == 0) atomicAdd(c, 1u);
+  if (wave_slow != 0) atomicAdd(c + 1, wave_slow);
+  if (wave_rescales != 0) atomicAdd(c + 2, wave_rescales);
+}
+
 __device__ __forceinline__ void store_partial(const AttnArgs& a, int unit, int block_m, int row,
                                               int g, const f32x16* o, float scale, float m,
                                               float l) {

@@ -541,6 +541,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
     m_ref = max_other_half(mx);   // tile 0 always has a valid key
   }
   int shift = 0;
+  uint32_t n_resc = 0, n_renorm = 0;   // this wave's rescales (diagnostic counters only)
   float negm8 = kPTarget - m_ref;   // the seed of every later QK^T accumulation
 #pragma unroll
   for (int b = 0; b < 2; ++b) sc[b] = sc[b] + negm8;
@@ -587,9 +588,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
     float mx;
     float lt = fp8_step_a(Vprev, Knext + krow[0] * KS8, p_prev, vsc_prev, kUnitScale + shift, o, qf,
                           ql, ksc_next, qsc, negm8, sc, p_cur, mx, boundary);
-    if (__builtin_expect(__any(mx > kTrigger), 0))
+    if (__builtin_expect(__any(mx > kTrigger), 0)) {
       lt = rescale_step(mx, l_run, shift, negm8, sc, Kcur + krow[0] * KS8, qf, ql, cur.ksc, qsc,
                         cur.nvalid, g, cur.nvalid < 0 ? window_word(tt) : ~0u, p_cur);
+      ++n_resc;
+    }
     // QK^T block 1 of tile t+1 (block 1 of tile t is no longer needed)
     sc[1] = qk_block(Knext + krow[1] * KS8, qf, ql, ksc_next, qsc, splat_seed(negm8));
     l_run += lt;
@@ -622,6 +625,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
       }
     }
     if (stop == 0) break;
+    ++n_renorm;
     const float alpha = __builtin_amdgcn_exp2f(-static_cast<float>(shift));
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = o[i] * alpha;
@@ -649,6 +653,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   // everything feeding them) ahead of the per-row store branch below, where
   // lanes past the last query row are switched off.
   asm volatile("" : "+v"(o[0]), "+v"(o[1]), "+v"(o[2]), "+v"(o[3]));
+
+  if (a.counters != nullptr) add_counts(a.counters, tid, n_renorm, n_resc);
 
   // ---- epilogue ----------------------------------------------------------------
   // O and l in units of 2^(x - m_ref + 8): m_ref - 8 is the max the merge sees

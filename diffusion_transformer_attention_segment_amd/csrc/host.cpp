@@ -584,12 +584,15 @@ size_t sa_segment_attention_workspace(const sa_geom* geom, const sa_attn_item* i
   return bytes;
 }
 
-sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+sa_status run_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
+                        void* workspace, size_t workspace_bytes, uint32_t* counters, void* stream) {
   static thread_local AttnPlan plan;
   sa_status st = prepare_attention(geom, items, n_items, plan);
   if (st != SA_OK) return st;
   AttnArgs& a = plan.a;
+  a.counters = counters;
 #ifdef SA_DEBUG_CHECKS
   if ((st = debug_check_attention(geom, items, n_items, static_cast<hipStream_t>(stream))) != SA_OK)
     return st;
@@ -609,6 +612,22 @@ sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, i
   if (a.split_k > 1)
     return hip_status(launch_attention_combine(a, plan.bm, s), "segment_attention combine launch");
   return ok();
+}
+
+}  // namespace
+
+sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attention(geom, items, n_items, workspace, workspace_bytes, nullptr, stream);
+}
+
+sa_status sa_segment_attention_counted(const sa_geom* geom, const sa_attn_item* items,
+                                       int32_t n_items, void* workspace, size_t workspace_bytes,
+                                       uint32_t* counters, void* stream) {
+  if (counters == nullptr) return fail(SA_E_ARG, "segment_attention_counted: counters is NULL");
+  if ((reinterpret_cast<uintptr_t>(counters) & 3) != 0)
+    return fail(SA_E_ALIGN, "segment_attention_counted: counters not 4-byte aligned");
+  return run_attention(geom, items, n_items, workspace, workspace_bytes, counters, stream);
 }
 
 namespace {

@@ -87,6 +87,7 @@ struct AttnArgs {
   float* ws;
   float scale_log2;       // softmax scale * log2(e)
   RopeParams rope;
+  uint32_t* counters;     // optional diagnostics (NULL: none), see add_counts
 };
 
 constexpr int kPartialStride = kD + 2;   // floats per row of a partial: O, m, l

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 9
+#define SA_ABI_VERSION 10
 #define SA_HEAD_DIM 128       /* the only head dim the kernels are built for */
 #define SA_MAX_ITEMS 8        /* sessions per sa_segment_attention call     */
 #define SA_MAX_FRAMES_KV 65536
@@ -295,6 +295,27 @@ size_t sa_segment_attention_workspace(const sa_geom* geom, const sa_attn_item* i
                                       int32_t n_items);
 sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* segment_attention_counted: sa_segment_attention, plus diagnostic counts
+ * added (not stored: the caller clears them) into counters, device uint32
+ * [3], 4-byte aligned:
+ *   [0] work tiles run (a query tile of one head, or one key-range part);
+ *   [1] slow-path events: bf16 and int8 caches, work tiles whose key loop
+ *       ran a second time with per-block rescaling (some row's block sum of
+ *       probabilities, taken against the first block's max, passed 2^64);
+ *       e4m3 cache, renormalisations of a wave's output (its running max
+ *       rose more than 64 log2 units above the first tile's max);
+ *   [2] rescale steps of waves: bf16 and int8, in that second run, blocks
+ *       whose probability sum passed 256 and moved the running max; e4m3,
+ *       blocks whose largest scaled probability passed 2^8.5 and moved it.
+ * The outputs are those of sa_segment_attention bit for bit; the counts
+ * tell how often softmax's rescaling paths ran (they are rare for
+ * near-uniform attention and frequent for sharp logits). The extra cost is
+ * one integer add per wave. Errors: those of sa_segment_attention; SA_E_ARG
+ * (counters NULL), SA_E_ALIGN.                                              */
+sa_status sa_segment_attention_counted(const sa_geom* geom, const sa_attn_item* items,
+                                       int32_t n_items, void* workspace, size_t workspace_bytes,
+                                       uint32_t* counters, void* stream);
 
 /* sparse_select: block lists for block-sparse history attention. For every
  * head h and query block i (rows [256 i, 256 i + 256) of the item, video then

@@ -54,7 +54,7 @@ def test_debug_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 9
+    assert sa.abi_version() == 10
 
 
 def test_status_strings(lib):
@@ -201,6 +201,12 @@ def _attn(items, n=None):
 
 def test_attention_validation(lib):
     L = _layer()
+    g = _geom()
+    arr = (B.sa_attn_item * 1)(_item(L))
+    cnt = lib.sa_segment_attention_counted
+    assert cnt(ctypes.byref(g), arr, 1, None, 0, None, None) == 1              # no counters
+    assert cnt(ctypes.byref(g), arr, 1, None, 0, ctypes.c_void_p(FAKE + 2), None) == 3
+    assert cnt(ctypes.byref(g), arr, 0, None, 0, ctypes.c_void_p(FAKE), None) == 1
     assert _attn([_item(L)], n=0) == 1
     assert _attn([_item(L)] * 9) == 1
     assert _attn([_item(L, n_frames_kv=0, n_text_kv=0)]) == 1     # empty key set
