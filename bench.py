@@ -116,6 +116,14 @@ def _csv_rows(dirs, suffix):
     return rows
 
 
+def _print_source_hash(kind):
+    if kind is None:
+        print("# source hash: none (no attention kernel profiled)")
+    else:
+        print(f"# source hash of csrc/{{{', '.join(KERNEL_SOURCES[kind])}}}: "
+              f"{source_hash(KERNEL_SOURCES[kind])}")
+
+
 def summarize_trace(dirs, kind, title, command, skip=2):
     """Per-kernel durations from rocprofv3 kernel_trace.csv: calls, total,
     mean, median and the mean after each kernel's first `skip` calls (the
@@ -127,8 +135,7 @@ def summarize_trace(dirs, kind, title, command, skip=2):
     total = sum(sum(v) for v in per.values())
     print(f"# rocprofv3 kernel trace summary: {title}")
     print(f"# command: {command}")
-    print(f"# source hash of csrc/{{{', '.join(KERNEL_SOURCES[kind])}}}: "
-          f"{source_hash(KERNEL_SOURCES[kind])}")
+    _print_source_hash(kind)
     print(f"# durations in microseconds from the kernel dispatch records; 'steady avg' skips "
           f"each kernel's first {skip} calls")
     print(f"{'kernel':44s}{'calls':>7s}{'total_us':>13s}{'avg_us':>11s}{'median_us':>11s}"
@@ -155,8 +162,7 @@ def summarize_pmc(dirs, kind, title, command):
         disp.setdefault(key, set()).add(d)
     print(f"# rocprofv3 counter summary: {title}")
     print(f"# command: {command}")
-    print(f"# source hash of csrc/{{{', '.join(KERNEL_SOURCES[kind])}}}: "
-          f"{source_hash(KERNEL_SOURCES[kind])}")
+    _print_source_hash(kind)
     print("# values: per-dispatch average (counter summed over the dispatch's rows), "
           "dispatches in brackets")
     for k in sorted({k for k, _ in acc}):
@@ -797,9 +803,7 @@ def main():
         print(source_hash(KERNEL_SOURCES[args.source_hash]))
         return
     if args.summarize_trace or args.summarize_pmc:
-        if args.workload not in PROFILED:
-            raise SystemExit(f"no profiled attention kernel for workload {args.workload}")
-        kind = PROFILED[args.workload][0]
+        kind = PROFILED[args.workload][0] if args.workload in PROFILED else None
         if args.summarize_trace:
             summarize_trace(args.summarize_trace, kind, args.title, args.command)
         else:
