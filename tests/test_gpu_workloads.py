@@ -162,14 +162,13 @@ def test_fp8_cache_eight_prior_segments(fp8seg8):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.xfail(strict=False, raises=AssertionError, reason=(
-    "against exact attention on the unquantised inputs the error includes storing K and V "
-    "in e4m3 with one scale per (frame, head), which the workload prescribes: the oracle's "
-    "own quantised cache alone moves the worst sampled element by about 5e-2"))
 def test_fp8_cache_against_exact_inputs(fp8seg8):
     """The fp8 bar (max-abs 5e-2, mean-abs 5e-3) against exact fp64 attention
-    on the unquantised bf16 inputs. Prints the oracle's own storage error on
-    the same rows next to the kernel's error."""
+    on the unquantised bf16 inputs, on the sampled rows of all 16 heads. The
+    error includes storing K and V in e4m3 with one power-of-two scale per
+    (frame, head), which the workload prescribes; the test prints the
+    oracle's own storage error on the same rows next to the kernel's (3.0e-2
+    and 4.5e-2 max-abs when written)."""
     s, rows, got, got_lse, want_c, want_c_lse = fp8seg8
     want, _ = s.oracle(rows=rows)
     storage = np.abs(want_c - want)
