@@ -569,6 +569,52 @@ def measure_dequant(sa, geom, n_frames=99, capacity=128, reps=5):
             "frac_of_hbm_peak": round(moved / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+def measure_appends(sa, state, reps=5):
+    """kv_append of the segment's 30 latent frames into a fresh layer of each
+    cache kind (bf16, e4m3, int8) at the workload's geometry: warm (mean of
+    reps calls) and cold (median of reps calls, each preceded by a 512 MB
+    write that evicts the 256 MB last-level cache). Algorithmic bytes per
+    (token, head): 2 x 256 B read; written 2 x 256 B (bf16), 2 x 128 B (e4m3),
+    2 x 132 B (int8 codes and the per-token scales)."""
+    wl = state.wl
+    d = state.sess[0]
+    F = wl.lat_t
+    tok = F * wl.P * wl.heads
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    out = {}
+    for name, kind, wr in (("bf16", sa.KV_BF16, 2 * 256), ("e4m3", sa.KV_FP8, 2 * 128),
+                           ("int8", sa.KV_INT8, 2 * 132)):
+        layer = sa.KVLayer.allocate(state.geom, kind, F, 16)
+        sa.kv_append(state.geom, layer, d["k"], d["v"], 0, F)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            sa.kv_append(state.geom, layer, d["k"], d["v"], 0, F)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        cold = []
+        for _ in range(reps):
+            flush.fill_(1)
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            sa.kv_append(state.geom, layer, d["k"], d["v"], 0, F)
+            c1.record()
+            torch.cuda.synchronize()
+            cold.append(c0.elapsed_time(c1))
+        cold_ms = sorted(cold)[len(cold) // 2]
+        nbytes = tok * (2 * 256 + wr)
+        out[name] = {"ms": round(ms, 4), "bytes": nbytes,
+                     "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "cold_ms_median": round(cold_ms, 4),
+                     "cold_GB_per_s": round(nbytes / (cold_ms * 1e-3) / 1e9, 1)}
+        del layer
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_copy_ceiling(nbytes=713_687_040, reps=5):
     """A plain device-to-device copy of nbytes (torch's copy kernel, the size
     of the gather's planes, none of this library's kernels): the practical HBM
@@ -938,12 +984,15 @@ def main():
         line["camera_attention"] = measure_camera(sa, state)
         line["history_gather"] = measure_gather(sa, state.geom)
         line["kv_dequant"] = measure_dequant(sa, state.geom)
+        line["append_rows"] = measure_appends(sa, state)
         # the practical streaming rate: a plain copy of the same size by torch's
         # copy kernel (none of the kernels measured here)
         ceiling = measure_copy_ceiling()
         line["device_copy_ceiling"] = ceiling
         for k in ("kv_append", "camera_attention", "history_gather", "kv_dequant"):
             line[k]["frac_of_copy_ceiling"] = round(line[k]["GB_per_s"] / ceiling["GB_per_s"], 4)
+        for rec in line["append_rows"].values():
+            rec["frac_of_copy_ceiling"] = round(rec["GB_per_s"] / ceiling["GB_per_s"], 4)
         others = {}
         for name in ("fp8seg8", "int8seg8"):
             if name != wl.name:
