@@ -166,6 +166,12 @@ class Geom:
         return g
 
 
+def plane_slots(dtype, P):
+    """Token slots of one (frame, head) plane: P for bf16, P rounded up to a
+    multiple of 16 for the one-byte caches (the library's layout)."""
+    return P if dtype == KV_BF16 else -(-P // 16) * 16
+
+
 class KVLayer:
     """One layer's cache planes as torch tensors (caller-owned device memory)."""
 
@@ -182,6 +188,7 @@ class KVLayer:
     @classmethod
     def allocate(cls, geom, dtype, frame_capacity, text_capacity, device="cuda"):
         H, P, D = geom.heads, geom.P, geom.head_dim
+        P = plane_slots(dtype, P)     # token slots of a frame plane
         et = {KV_BF16: torch.bfloat16, KV_FP8: torch.uint8, KV_INT8: torch.int8}[dtype]
         kw = dict(device=device, dtype=et)
         k = torch.empty((frame_capacity, H, P, D), **kw)

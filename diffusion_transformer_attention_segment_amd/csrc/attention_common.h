@@ -109,18 +109,19 @@ __device__ __forceinline__ void cursor_enter(TileCursor& c, const AttnItemDev& I
     const int frame = c.fnext;
     if (c.fi + 1 < I.n_frames_kv) c.fnext = frame_entry(I, c.fi + 1);   // one frame ahead
     const size_t pl = static_cast<size_t>(frame) * H + h;
-    const size_t plane = pl * static_cast<size_t>(P) * kD * elem_bytes<ESZ>();
+    const int PL = plane_tokens(P, ESZ != kCkBf16);   // token slots of the plane
+    const size_t plane = pl * static_cast<size_t>(PL) * kD * elem_bytes<ESZ>();
     c.kplane = static_cast<const char*>(I.k) + plane;
     c.vplane = static_cast<const char*>(I.v) + plane;
     c.len = P;
-    c.vstride = P;
+    c.vstride = PL;
     if (ESZ == kCkFp8) {
       c.kscale = scalar_load(I.k_scale, pl);
       c.vscale = scalar_load(I.v_scale, pl);
     }
     if (ESZ == kCkInt8) {
-      c.kst = I.k_scale + pl * P;
-      c.vst = I.v_scale + pl * P;
+      c.kst = I.k_scale + pl * PL;
+      c.vst = I.v_scale + pl * PL;
     }
   } else {
     const size_t plane = static_cast<size_t>(h) * I.text_cap * kD * elem_bytes<ESZ>();

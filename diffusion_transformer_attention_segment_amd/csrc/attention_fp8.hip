@@ -115,8 +115,8 @@ __device__ __forceinline__ i32x8v lds_read32(const uint8_t* p) {
 // 64 j + 63 (dma_tile); wave w issues loads w and w + 8 (the second only where
 // it exists: K has 9 loads, V^T 10). A lane's global offsets for them depend
 // only on the row length, so they are computed once: for K rows (128 bytes)
-// and for V^T rows of a frame plane (P bytes); the text slot's V^T rows
-// (text capacity bytes) take dma_tile's per-tile computation.
+// and for V^T rows of a frame plane (PL bytes, its token slots); the text
+// slot's V^T rows (text capacity bytes) take dma_tile's per-tile computation.
 constexpr int kKLoads = BN * (KS8 / 16) / 64;    // 9
 constexpr int kVLoads = kD * (VS8 / 16) / 64;    // 10
 
@@ -130,13 +130,13 @@ __device__ __forceinline__ uint32_t slot_offset(uint32_t n, uint32_t slots, uint
   return ch == slots - 1 ? kOutOfRange : row * row_bytes + ch * 16u;
 }
 
-__device__ __forceinline__ DmaOffsets dma_offsets(int w, int lane, int P) {
+__device__ __forceinline__ DmaOffsets dma_offsets(int w, int lane, int v_row_bytes) {
   DmaOffsets d;
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const uint32_t n = 64u * (w + 8 * m) + lane;
     d.k[m] = slot_offset(n, KS8 / 16, kD);
-    d.v[m] = slot_offset(n, VS8 / 16, static_cast<uint32_t>(P));
+    d.v[m] = slot_offset(n, VS8 / 16, static_cast<uint32_t>(v_row_bytes));
   }
   return d;
 }
@@ -152,9 +152,9 @@ __device__ __forceinline__ void dma_k8(const TileCursor& c, uint8_t* stage, int 
   }
 }
 
-__device__ __forceinline__ void dma_v8(const TileCursor& c, uint8_t* stage, int w, int P,
+__device__ __forceinline__ void dma_v8(const TileCursor& c, uint8_t* stage, int w, int PL,
                                        const DmaOffsets& d) {
-  if (c.vstride != P) {   // the text slot
+  if (c.vstride != PL) {   // the text slot
     dma_tile<kD, VS8 / 16>(tile_v_rsrc<1>(c), stage, static_cast<uint32_t>(c.vstride), w);
     return;
   }
@@ -383,6 +383,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   const int h = wt.head;
   const int q0 = wt.q0;
   const int P = a.rope.P;
+  const int PL = plane_tokens(P, true);   // token slots (V^T row bytes) of a frame plane
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, r32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
@@ -414,15 +415,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   // Tiles load two ahead of the compute tile, K and then V (K of tile t+1 is
   // read in step t, V of tile t in step t+1). lc is the cursor of the last
   // tile loaded; ti0, ti1 carry tiles t, t+1.
-  const DmaOffsets dmo = dma_offsets(w, lane, P);
+  const DmaOffsets dmo = dma_offsets(w, lane, PL);
   dma_k8(lc, Ks, w, dmo);
-  dma_v8(lc, Vs, w, P, dmo);
+  dma_v8(lc, Vs, w, PL, dmo);
   TileInfo ti1 = ti0;
   if (ntiles > 1) {
     seq_next<kSparse, 1>(lc, I, h, H, P, seq, kt0 + 1);
     ti1 = tile_info(lc, flag_fi);
     dma_k8(lc, Ks + KT8, w, dmo);
-    dma_v8(lc, Vs + VT8, w, P, dmo);
+    dma_v8(lc, Vs + VT8, w, PL, dmo);
   }
   // ---- Q: rotate in fp32, times softmax scale * log2(e), quantise per (row,
   // head) to e4m3 -----------------------------------------------------------------
@@ -576,7 +577,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
         seq_next<kSparse, 1>(lc, I, h, H, P, seq, kt0 + tt + 2);
         ti2 = tile_info(lc, flag_fi);
         dma_k8(lc, Ks + s2 * KT8, w, dmo);
-        dma_v8(lc, Vs + s2 * VT8, w, P, dmo);
+        dma_v8(lc, Vs + s2 * VT8, w, PL, dmo);
         pending = 1;   // every wave issues at least one V load
       }
     };

@@ -65,6 +65,11 @@ sa_status check_geom(const sa_geom* g) {
 
 int32_t tokens_per_frame(const sa_geom* g) { return g->lat_h * g->lat_w; }
 
+// Token slots of one (frame, head) plane of a layer of this dtype.
+int32_t frame_slots(const sa_geom* g, int32_t dtype) {
+  return plane_tokens(tokens_per_frame(g), dtype != SA_KV_BF16);
+}
+
 sa_status check_layer(const sa_geom* g, const sa_kv_layer* L, const char* name) {
   if (L == nullptr) return fail(SA_E_ARG, "%s layer is NULL", name);
   if (L->dtype != SA_KV_BF16 && L->dtype != SA_KV_FP8_E4M3 && L->dtype != SA_KV_INT8)
@@ -74,9 +79,6 @@ sa_status check_layer(const sa_geom* g, const sa_kv_layer* L, const char* name) 
     return fail(SA_E_ARG, "%s: negative capacity", name);
   if (L->text_capacity % 16 != 0)
     return fail(SA_E_SHAPE, "%s: text_capacity %d must be a multiple of 16", name, L->text_capacity);
-  if (scaled && tokens_per_frame(g) % 16 != 0)
-    return fail(SA_E_SHAPE, "%s: fp8 and int8 planes need P %% 16 == 0 (P=%d)", name,
-                tokens_per_frame(g));
   if (L->frame_capacity > 0) {
     if (L->k == nullptr || L->v == nullptr) return fail(SA_E_ARG, "%s: k/v plane is NULL", name);
     if (!aligned16(L->k) || !aligned16(L->v)) return fail(SA_E_ALIGN, "%s: k/v not 16-byte aligned", name);
@@ -211,7 +213,7 @@ size_t sa_cache_bytes(const sa_geom* geom, int32_t dtype, int32_t frame_capacity
     fail(SA_E_ARG, "negative capacity");
     return 0;
   }
-  const size_t H = geom->heads, D = geom->head_dim, P = tokens_per_frame(geom);
+  const size_t H = geom->heads, D = geom->head_dim, P = frame_slots(geom, dtype);
   const size_t elems = 2 * H * D * (static_cast<size_t>(frame_capacity) * P + text_capacity);
   ok();
   if (dtype == SA_KV_BF16) return 2 * elems;
@@ -242,8 +244,8 @@ sa_status sa_kv_append(const sa_geom* geom, const sa_kv_layer* layer, const void
   a.heads = geom->heads;
   a.frame0 = frame0;
   a.n_frames = n_frames;
-  a.plane_len = tokens_per_frame(geom);
-  a.n_tok = a.plane_len;
+  a.plane_len = frame_slots(geom, layer->dtype);
+  a.n_tok = tokens_per_frame(geom);
   a.is_text = 0;
   a.rope = rope_params(geom);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -358,14 +360,15 @@ sa_status sa_history_gather(const sa_geom* geom, const sa_kv_layer* src, const i
   a.dst_k = dst->k;
   a.dst_v = dst->v;
   const int64_t elt = src->dtype == SA_KV_BF16 ? 2 : 1;
-  a.plane_bytes = elt * geom->heads * static_cast<int64_t>(tokens_per_frame(geom)) * geom->head_dim;
+  a.plane_bytes = elt * geom->heads * static_cast<int64_t>(frame_slots(geom, src->dtype)) * geom->head_dim;
   if (src->dtype != SA_KV_BF16) {
     a.src_ks = src->k_scale;
     a.src_vs = src->v_scale;
     a.dst_ks = dst->k_scale;
     a.dst_vs = dst->v_scale;
-    a.scale_floats = src->dtype == SA_KV_INT8 ? static_cast<int64_t>(geom->heads) * tokens_per_frame(geom)
-                                              : geom->heads;
+    a.scale_floats = src->dtype == SA_KV_INT8
+                         ? static_cast<int64_t>(geom->heads) * frame_slots(geom, src->dtype)
+                         : geom->heads;
   }
   a.frames = d_frames;
   a.n = n;
@@ -819,7 +822,8 @@ sa_status sa_kv_dequant(const sa_geom* geom, const sa_kv_layer* src, const int32
     a.frames = d_frames;
     a.n = n_frames;
     a.heads = geom->heads;
-    a.src_len = a.dst_len = a.n_tok = tokens_per_frame(geom);
+    a.src_len = frame_slots(geom, src->dtype);
+    a.dst_len = a.n_tok = tokens_per_frame(geom);
     a.int8 = src->dtype == SA_KV_INT8;
     if ((st = hip_status(launch_dequant(a, s), "kv_dequant launch")) != SA_OK) return st;
   }

@@ -20,6 +20,14 @@ struct RopeParams {
 };
 
 // ---- kv_append / text_append ------------------------------------------------
+// Token slots of one (frame, head) plane: P, rounded up to a multiple of 16
+// for the one-byte caches (e4m3, int8) so that every V^T row starts 16-byte
+// aligned. Slots past P hold zero V^T codes (and zero int8 scales); K rows
+// past P are never read.
+__host__ __device__ inline int plane_tokens(int P, bool one_byte) {
+  return one_byte ? (P + 15) & ~15 : P;
+}
+
 struct AppendArgs {
   const uint16_t* k_in;     // bf16 [n_tokens][H][128]
   const uint16_t* v_in;

@@ -49,13 +49,14 @@ __global__ __launch_bounds__(64 * kPoolWaves) void pool_k_kernel(const SelectArg
   const int fi = c / tpf, j = c - fi * tpf;
   const int frame = a.item.frames[fi];
   const int r0 = j * kKeyTile, n = min(kKeyTile, P - r0);
-  const size_t plane = (static_cast<size_t>(frame) * H + h) * static_cast<size_t>(P) * kD;
+  const int PL = plane_tokens(P, a.int8 || a.fp8);   // token slots of a plane
+  const size_t plane = (static_cast<size_t>(frame) * H + h) * static_cast<size_t>(PL) * kD;
   float s0 = 0.f, s1 = 0.f;
   if (a.int8) {
     const uint16_t* base = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(a.item.k) +
                                                              plane) +
                            static_cast<size_t>(r0) * (kD / 2) + lane;
-    const float* sc = a.item.k_scale + (static_cast<size_t>(frame) * H + h) * P + r0;
+    const float* sc = a.item.k_scale + (static_cast<size_t>(frame) * H + h) * PL + r0;
 #pragma unroll 8
     for (int r = 0; r < n; ++r) {
       const uint32_t w = base[static_cast<size_t>(r) * (kD / 2)];

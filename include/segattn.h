@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 10
+#define SA_ABI_VERSION 11
 #define SA_HEAD_DIM 128       /* the only head dim the kernels are built for */
 #define SA_MAX_ITEMS 8        /* sessions per sa_segment_attention call     */
 #define SA_MAX_FRAMES_KV 65536
@@ -105,21 +105,25 @@ typedef struct sa_geom {
 /* One layer's cache planes (device memory, caller-allocated; sizes from
  * sa_cache_bytes / the shapes below). Frames are addressed by their absolute
  * latent-frame index since the world started, which is also their RoPE t.
- *   k        [frame_capacity][H][P][128]         rotated keys
- *   v        [frame_capacity][H][128][P]         values, transposed per
+ *   k        [frame_capacity][H][PL][128]        rotated keys
+ *   v        [frame_capacity][H][128][PL]        values, transposed per
  *                                                (frame, head)
  *   k_text   [H][text_capacity][128]             text keys (no rotation)
  *   v_text   [H][128][text_capacity]             text values, transposed
  *   k_scale, v_scale            fp8: [frame_capacity][H] fp32 (one per
- *                               plane); int8: [frame_capacity][H][P] fp32
+ *                               plane); int8: [frame_capacity][H][PL] fp32
  *                               (one per token and head)
  *   k_text_scale, v_text_scale  fp8: [H]; int8: [H][text_capacity]
  *                               (NULL for bf16)
+ * PL, the token slots of a frame plane, is P for bf16 and P rounded up to a
+ * multiple of 16 for e4m3 and int8 (so every V^T row starts 16-byte
+ * aligned): slots p >= P hold zero V^T codes and zero int8 scales, written by
+ * sa_kv_append; their K rows are never read. For P % 16 == 0, PL = P.
  * Element type: bf16 (2 bytes), e4m3 or int8 (1 byte) per `dtype`. int8 is
  * the pages' single-GPU cache format ("The 4090 preset": a byte per value
  * and an fp32 scale for each token and head, 4,224 bytes per token and layer
- * at 16 heads); fp8 and int8 need P % 16 == 0 (SA_E_SHAPE otherwise).
- * text_capacity must be a multiple of 16; it may be 0 (no text slot).      */
+ * at 16 heads). text_capacity must be a multiple of 16; it may be 0 (no text
+ * slot).                                                                    */
 typedef struct sa_kv_layer {
   int32_t dtype;
   int32_t frame_capacity;
@@ -204,7 +208,8 @@ const char* sa_status_string(int status);
  * and for fp8 / int8 the fp32 scales). For bf16 a token costs 2 * H * 128 * 2
  * bytes per layer, the 8,192 bytes of "What 'world memory' stores" at 16
  * heads; for int8, with a scale per token and head for K and V, the 4,224
- * bytes of "The 4090 preset". Returns 0 and sets the error on bad input
+ * bytes of "The 4090 preset". A frame counts PL token slots (see
+ * sa_kv_layer). Returns 0 and sets the error on bad input
  * (SA_E_SHAPE geometry, SA_E_UNSUPPORTED dtype, SA_E_ARG negative capacity). */
 size_t sa_cache_bytes(const sa_geom* geom, int32_t dtype, int32_t frame_capacity,
                       int32_t text_capacity);

@@ -9,10 +9,14 @@ head: 4,224 bytes per token per layer; 18 kept frames are about 3.6 GB); section
 "How one segment is made" (3D RoPE on keys; 880 tokens per latent frame).
 
 Plane layout (the library's own design; the pages fix no layout). Per layer,
-with H heads, D = head_dim, P = lat_h * lat_w tokens per latent frame:
+with H heads, D = head_dim, P = lat_h * lat_w tokens per latent frame and
+PL = plane_slots(dtype, P) token slots per frame plane (P for bf16; P rounded
+up to a multiple of 16 for the one-byte caches, so that every V^T row starts
+16-byte aligned; slots p >= P hold zero V^T codes and zero int8 scales, and
+their K rows are never read):
 
-* K plane  [frame_capacity][H][P][D]  element ((f*H + h)*P + p)*D + c
-* V plane  [frame_capacity][H][D][P]  element ((f*H + h)*D + c)*P + p
+* K plane  [frame_capacity][H][PL][D]  element ((f*H + h)*PL + p)*D + c
+* V plane  [frame_capacity][H][D][PL]  element ((f*H + h)*D + c)*PL + p
   (V is stored transposed per (frame, head): the P.V contraction runs over
   tokens, so tokens are the contiguous axis)
 * text K   [H][text_capacity][D]      element (h*TC + i)*D + c
@@ -22,7 +26,7 @@ with H heads, D = head_dim, P = lat_h * lat_w tokens per latent frame:
   v_text_scale [H].
 * int8 planes (the pages' single-GPU format) use the same shapes with one
   signed byte per element, plus fp32 scales per token and head:
-  k_scale/v_scale [frame_capacity][H][P] and k_text_scale / v_text_scale
+  k_scale/v_scale [frame_capacity][H][PL] and k_text_scale / v_text_scale
   [H][text_capacity].
 
 Stored values. K is rotated by the 3D RoPE at its absolute position (frame f
@@ -67,29 +71,42 @@ def bytes_per_token_per_layer(fmt, heads=16, head_dim=128):
     raise ValueError(fmt)
 
 
+def plane_slots(dtype, P):
+    """Token slots of one (frame, head) plane: P for bf16, else P rounded up
+    to a multiple of 16."""
+    if dtype == "bf16":
+        return P
+    if dtype in ("fp8", "int8"):
+        return -(-P // 16) * 16
+    raise ValueError(dtype)
+
+
 def plane_bytes(dtype, heads, head_dim, P, frame_capacity, text_capacity):
     """Bytes of one layer's cache planes in this library's layout.
 
     dtype 'bf16', 'fp8' (fp32 scales per (frame, head) and per head for the
     text slot, for K and V) or 'int8' (fp32 scales per token and head).
     """
-    elems = 2 * heads * head_dim * (frame_capacity * P + text_capacity)
+    PL = plane_slots(dtype, P)
+    elems = 2 * heads * head_dim * (frame_capacity * PL + text_capacity)
     if dtype == "bf16":
         return 2 * elems
     if dtype == "fp8":
         return elems + 2 * 4 * heads * (frame_capacity + 1)
-    if dtype == "int8":
-        return elems + 2 * 4 * heads * (frame_capacity * P + text_capacity)
-    raise ValueError(dtype)
+    return elems + 2 * 4 * heads * (frame_capacity * PL + text_capacity)
 
 
 # --------------------------------------------------------------- layout maps
-def k_offset(f, h, p, c, H, P, D):
-    return ((f * H + h) * P + p) * D + c
+def k_offset(f, h, p, c, H, PL, D):
+    """Element offset of K (frame f, head h, token p, dim c) in planes of PL
+    token slots."""
+    return ((f * H + h) * PL + p) * D + c
 
 
-def v_offset(f, h, p, c, H, P, D):
-    return ((f * H + h) * D + c) * P + p
+def v_offset(f, h, p, c, H, PL, D):
+    """Element offset of V (frame f, head h, token p, dim c) in the
+    transposed planes of PL token slots."""
+    return ((f * H + h) * D + c) * PL + p
 
 
 def text_k_offset(h, i, c, TC, D):

@@ -54,7 +54,7 @@ def test_debug_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 10
+    assert sa.abi_version() == 11
 
 
 def test_status_strings(lib):
@@ -128,6 +128,10 @@ def test_cache_bytes_matches_oracle(lib):
     for dt, name in ((sa.KV_BF16, "bf16"), (sa.KV_FP8, "fp8"), (sa.KV_INT8, "int8")):
         for fc, tc in ((60, 256), (390, 256), (0, 16), (1, 0)):
             assert sa.cache_bytes(g, dt, fc, tc) == ocache.plane_bytes(name, 16, 128, 880, fc, tc)
+    # frames of 24 tokens: the one-byte caches count 32 slots per plane
+    g24 = sa.Geom(heads=2, lat_h=4, lat_w=6)
+    for dt, name in ((sa.KV_BF16, "bf16"), (sa.KV_FP8, "fp8"), (sa.KV_INT8, "int8")):
+        assert sa.cache_bytes(g24, dt, 3, 16) == ocache.plane_bytes(name, 2, 128, 24, 3, 16)
     # the page's figures: 8,192 bytes per token per layer in bf16, 4,224 in int8
     assert sa.cache_bytes(g, sa.KV_BF16, 1, 0) == 880 * 8192
     assert sa.cache_bytes(g, sa.KV_INT8, 1, 0) == 880 * 4224
@@ -167,7 +171,10 @@ def test_validation_errors(lib):
     assert _append(_geom(), _layer(k=0)) == 1
     assert _append(_geom(), _layer(k=FAKE + 4)) == 3
     assert _append(_geom(), _layer(tc=8)) == 2                    # text capacity % 16
-    assert _append(_geom(), _layer(dtype=1)) == 2                 # fp8 needs P % 16 (P=24)
+    # fp8 and int8 layers of 24-token frames pass the layer checks (planes of 32 slots)
+    assert _append(_geom(), _layer(dtype=1), n=-1) == 1
+    assert b"n_frames" in lib.sa_last_error()
+    assert _append(_geom(), _layer(dtype=2), n=-1) == 1
     assert _append(_geom(), _layer(), f0=3, n=2) == 5             # frames 3..4 > capacity 4
     assert _append(_geom(), _layer(), f0=-1) == 5
     assert _append(_geom(), _layer(), k=FAKE + 2) == 3

@@ -100,13 +100,17 @@ def test_text_append_bf16(n_text, cap):
     assert torch.all(layer.v_text[:, :, n_text:] == 0)
 
 
-@pytest.mark.parametrize("shape", [(2, 4, 8, 3, 2), (16, 22, 40, 2, 7)])
+@pytest.mark.parametrize("shape", [(2, 4, 8, 3, 2), (2, 4, 6, 3, 1), (16, 22, 40, 2, 7)])
 def test_kv_append_fp8(shape):
+    """Frames of 24 tokens fill planes of 32 slots: the V^T tail holds zero
+    codes."""
     H, lh, lw, F, frame0 = shape
     print(f"kv_append fp8 H={H} grid={lh}x{lw} F={F}", flush=True)
     P = lh * lw
     geom = sa.Geom(heads=H, lat_h=lh, lat_w=lw)
     layer = sa.KVLayer.allocate(geom, sa.KV_FP8, frame0 + F, 16)
+    assert layer.v.shape[-1] == ocache.plane_slots("fp8", P)
+    layer.v.fill_(0x5A)
     wl = si.Workload("t", heads=H, lat_t=F, lat_h=lh, lat_w=lw, n_text=16, prior_segments=(0,),
                      kv_dtype="fp8", scale_factors=True)
     k, v = si.segment_kv(wl, 3, 0, 0, 0, "cuda")
@@ -117,10 +121,11 @@ def test_kv_append_fp8(shape):
     gotVc = layer.v[frame0:].cpu().numpy()
     gotVs = layer.v_scale[frame0:].cpu().numpy()
     assert np.array_equal(gotVs, Vs)
-    assert np.array_equal(gotVc, Vc)
+    assert np.array_equal(gotVc[..., :P], Vc)
+    assert np.all(gotVc[..., P:] == 0)
     gotKs = layer.k_scale[frame0:].cpu().numpy()
     np.testing.assert_allclose(gotKs, Ks, rtol=2e-6)
-    gotKc = layer.k[frame0:].cpu().numpy()
+    gotKc = layer.k[frame0:, :, :P].cpu().numpy()
     step = np.abs(_e4m3_ordered(gotKc) - _e4m3_ordered(Kc))
     print(f"  K code agreement {np.mean(step == 0):.6f}", flush=True)
     assert step.max() <= 1
@@ -150,16 +155,21 @@ def test_text_append_fp8():
 
 
 # ------------------------------------------------------------------- int8 cache
-@pytest.mark.parametrize("shape", [(2, 4, 8, 3, 2), (16, 22, 40, 2, 7)])
+@pytest.mark.parametrize("shape", [(2, 4, 8, 3, 2), (2, 4, 6, 3, 1), (16, 22, 40, 2, 7)])
 def test_kv_append_int8(shape):
     """int8 with a scale per token and head: V codes and scales bit-exact
     (fp32 decisions on both sides); K is rotated in fp32 by the kernel and in
     exact arithmetic by the oracle, so a K code may move one step near a
-    rounding boundary and a K scale by fp32 rounding."""
+    rounding boundary and a K scale by fp32 rounding. Frames of 24 tokens
+    fill planes of 32 slots: zero V^T codes and zero scales in the tail."""
     H, lh, lw, F, frame0 = shape
     print(f"kv_append int8 H={H} grid={lh}x{lw} F={F}", flush=True)
+    P = lh * lw
     geom = sa.Geom(heads=H, lat_h=lh, lat_w=lw)
     layer = sa.KVLayer.allocate(geom, sa.KV_INT8, frame0 + F, 16)
+    layer.v.fill_(0x5A)
+    layer.k_scale.fill_(float("nan"))
+    layer.v_scale.fill_(float("nan"))
     wl = si.Workload("t", heads=H, lat_t=F, lat_h=lh, lat_w=lw, n_text=16, prior_segments=(0,),
                      kv_dtype="fp8", scale_factors=True)
     k, v = si.segment_kv(wl, 5, 0, 0, 0, "cuda")
@@ -167,10 +177,13 @@ def test_kv_append_int8(shape):
     torch.cuda.synchronize()
     Kc, Ks, Vc, Vs = ocache.append_int8(k.float().cpu().double().numpy(),
                                         v.float().cpu().double().numpy(), frame0, lh, lw, SPLIT, 10000.0)
-    assert np.array_equal(layer.v_scale[frame0:].cpu().numpy(), Vs)
-    assert np.array_equal(layer.v[frame0:].cpu().numpy(), Vc)
-    np.testing.assert_allclose(layer.k_scale[frame0:].cpu().numpy(), Ks, rtol=2e-6)
-    step = np.abs(layer.k[frame0:].cpu().numpy().astype(np.int32) - Kc.astype(np.int32))
+    assert np.array_equal(layer.v_scale[frame0:, :, :P].cpu().numpy(), Vs)
+    assert np.array_equal(layer.v[frame0:, :, :, :P].cpu().numpy(), Vc)
+    assert np.all(layer.v[frame0:, :, :, P:].cpu().numpy() == 0)
+    assert np.all(layer.k_scale[frame0:, :, P:].cpu().numpy() == 0)
+    assert np.all(layer.v_scale[frame0:, :, P:].cpu().numpy() == 0)
+    np.testing.assert_allclose(layer.k_scale[frame0:, :, :P].cpu().numpy(), Ks, rtol=2e-6)
+    step = np.abs(layer.k[frame0:, :, :P].cpu().numpy().astype(np.int32) - Kc.astype(np.int32))
     print(f"  K code agreement {np.mean(step == 0):.6f}", flush=True)
     assert step.max() <= 1
     assert np.mean(step == 0) >= 0.99

@@ -391,6 +391,8 @@ FP8_CASES = [
     ("fp8_ragged", 3, 5, 4, 8, 37, 3),      # ragged query and text tails
     ("fp8_p80", 2, 4, 8, 10, 64, 2),        # frame = 64 + 16 keys
     ("fp8_big", 4, 6, 8, 16, 256, 2),
+    ("fp8_p24", 2, 3, 4, 6, 16, 2),         # Tiny's frames: 24 tokens in planes of 32 slots
+    ("fp8_p136", 2, 3, 8, 17, 40, 1),       # 136 tokens in planes of 144 slots
 ]
 
 

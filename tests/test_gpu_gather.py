@@ -31,7 +31,8 @@ def _fill_random(layer, seed):
 
 
 @pytest.mark.parametrize("dtype,grid", [(sa.KV_BF16, (4, 6)), (sa.KV_FP8, (4, 8)),
-                                        (sa.KV_INT8, (4, 8)), (sa.KV_BF16, (22, 40)),
+                                        (sa.KV_INT8, (4, 8)), (sa.KV_FP8, (4, 6)),
+                                        (sa.KV_INT8, (4, 6)), (sa.KV_BF16, (22, 40)),
                                         (sa.KV_INT8, (22, 40))])
 def test_gather_bit_exact(dtype, grid):
     H = 16 if grid == (22, 40) else 3
@@ -57,10 +58,13 @@ def _dequant_ref(codes, scale):
     return numerics.bf16_bits(numerics.bf16_round(val.astype(np.float32).astype(np.float64)))
 
 
-@pytest.mark.parametrize("n_text", [0, 16, 29])
-def test_dequant_matches_oracle(n_text):
+@pytest.mark.parametrize("n_text,lw", [(0, 8), (16, 8), (29, 8), (16, 6)])
+def test_dequant_matches_oracle(n_text, lw):
+    """e4m3 planes to bf16 planes; frames of 24 tokens come from planes of
+    32 slots and go to planes of 24."""
     H = 3
-    geom = sa.Geom(heads=H, lat_h=4, lat_w=8)
+    P = 4 * lw
+    geom = sa.Geom(heads=H, lat_h=4, lat_w=lw)
     src = sa.KVLayer.allocate(geom, sa.KV_FP8, 10, 32)
     _fill_random(src, 2)
     frames = [9, 2, 4]
@@ -78,8 +82,8 @@ def test_dequant_matches_oracle(n_text):
     gv = dst.v.view(torch.int16).cpu().numpy().view(np.uint16)
     for i, f in enumerate(frames):
         for h in range(H):
-            assert np.array_equal(gk[i, h], _dequant_ref(sk[f, h], ks[f, h]))
-            assert np.array_equal(gv[i, h], _dequant_ref(sv[f, h], vs[f, h]))
+            assert np.array_equal(gk[i, h], _dequant_ref(sk[f, h, :P], ks[f, h]))
+            assert np.array_equal(gv[i, h], _dequant_ref(sv[f, h, :, :P], vs[f, h]))
     if n_text:
         tk = dst.k_text.view(torch.int16).cpu().numpy().view(np.uint16)
         tv = dst.v_text.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -97,11 +101,12 @@ def _dequant_int8_ref(codes, scale):
     return numerics.bf16_bits(numerics.bf16_round(val.astype(np.float32).astype(np.float64)))
 
 
-@pytest.mark.parametrize("n_text", [0, 29])
-def test_dequant_int8_matches_oracle(n_text):
+@pytest.mark.parametrize("n_text,lw", [(0, 8), (29, 8), (29, 6)])
+def test_dequant_int8_matches_oracle(n_text, lw):
     """int8 planes with a scale per token and head: K rows scale per row, V^T
-    columns per column."""
-    H, lh, lw = 3, 4, 8
+    columns per column; frames of 24 tokens come from planes of 32 slots."""
+    H, lh = 3, 4
+    P = lh * lw
     geom = sa.Geom(heads=H, lat_h=lh, lat_w=lw)
     src = sa.KVLayer.allocate(geom, sa.KV_INT8, 10, 32)
     _fill_random(src, 3)
@@ -118,8 +123,8 @@ def test_dequant_int8_matches_oracle(n_text):
     gv = dst.v.view(torch.int16).cpu().numpy().view(np.uint16)
     for i, f in enumerate(frames):
         for h in range(H):
-            assert np.array_equal(gk[i, h], _dequant_int8_ref(sk[f, h], ks[f, h][:, None]))
-            assert np.array_equal(gv[i, h], _dequant_int8_ref(sv[f, h], vs[f, h][None, :]))
+            assert np.array_equal(gk[i, h], _dequant_int8_ref(sk[f, h, :P], ks[f, h, :P][:, None]))
+            assert np.array_equal(gv[i, h], _dequant_int8_ref(sv[f, h, :, :P], vs[f, h, :P][None, :]))
     if n_text:
         tk = dst.k_text.view(torch.int16).cpu().numpy().view(np.uint16)
         tv = dst.v_text.view(torch.int16).cpu().numpy().view(np.uint16)

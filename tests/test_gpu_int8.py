@@ -49,6 +49,7 @@ def _check(s, label, rows=None, heads=None):
 CASES = [
     # name, H, F, lat_h, lat_w, n_text, prior segments
     ("i8_small", 2, 2, 4, 8, 16, 2),       # P = 32
+    ("i8_p24", 2, 3, 4, 6, 16, 2),         # P = 24: planes of 32 token slots
     ("i8_ragged", 3, 5, 4, 8, 37, 3),      # ragged query and text tails
     ("i8_p80", 2, 4, 8, 10, 64, 2),        # frame = 64 + 16 keys
     ("i8_big", 4, 6, 8, 16, 256, 2),       # Lq = 1024, Lk = 2560

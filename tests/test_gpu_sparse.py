@@ -60,6 +60,7 @@ CASES = [
     ("s_p128", 2, 4, 8, 16, 40, 3, 25),     # 12 history frames x 2 blocks = 24 candidates
     ("s_p80", 3, 3, 8, 10, 37, 4, 25),      # blocks of 64 and 16 keys; ragged text
     ("s_keep1", 2, 2, 8, 8, 16, 3, 1),      # a single kept block
+    ("s_p24", 2, 4, 4, 6, 16, 3, 25),       # frames of 24 tokens (e4m3 planes of 32 slots)
 ]
 
 

@@ -60,6 +60,32 @@ def test_plane_bytes():
     assert cache.plane_bytes("fp8", 16, 128, 880, 60, 256) == 2 * 2048 * (60 * 880 + 256) + 8 * 16 * 61
 
 
+def test_padded_plane_slots_hand_worked():
+    """One-byte caches pad a frame plane to a multiple of 16 token slots (so
+    V^T rows start 16-byte aligned); bf16 planes keep P."""
+    assert [cache.plane_slots("fp8", P) for P in (24, 136, 880, 16, 8)] == [32, 144, 880, 16, 16]
+    assert cache.plane_slots("int8", 24) == 32 and cache.plane_slots("bf16", 24) == 24
+    # H = 2, D = 128, P = 24 (32 slots), 3 frames, 16 text slots, worked by hand:
+    # values 2 * 2 * 128 * (3 * 32 + 16) = 57,344 bytes
+    assert cache.plane_bytes("fp8", 2, 128, 24, 3, 16) == 57_344 + 2 * 4 * 2 * 4
+    assert cache.plane_bytes("int8", 2, 128, 24, 3, 16) == 57_344 + 2 * 4 * 2 * (96 + 16)
+    assert cache.plane_bytes("bf16", 2, 128, 24, 3, 16) == 2 * 2 * 2 * 128 * (72 + 16)
+
+
+def test_padded_layout_leaves_exactly_the_tail_slots_unused():
+    F, H, P, PL, D = 2, 3, 6, 16, 4
+    ko = {cache.k_offset(f, h, p, c, H, PL, D) for f in range(F) for h in range(H)
+          for p in range(P) for c in range(D)}
+    vo = {cache.v_offset(f, h, p, c, H, PL, D) for f in range(F) for h in range(H)
+          for p in range(P) for c in range(D)}
+    assert len(ko) == len(vo) == F * H * P * D
+    assert ko == {((f * H + h) * PL + p) * D + c for f in range(F) for h in range(H)
+                  for p in range(P) for c in range(D)}
+    unused_v = set(range(F * H * PL * D)) - vo
+    assert unused_v == {((f * H + h) * D + c) * PL + p for f in range(F) for h in range(H)
+                        for c in range(D) for p in range(P, PL)}
+
+
 def test_layout_is_bijection_and_matches_numpy_transposes():
     F, H, P, D, TC = 3, 2, 6, 4, 5
     n = F * H * P * D
