@@ -774,6 +774,44 @@ def measure_mfma_probe(grid=1024, reps=3):
     return res
 
 
+def cpu_baseline_tiny(seed, reps=20):
+    """The oracle over the whole Tiny workload (2 heads, 4 x 6 grid, 2 frames
+    + 16 text tokens over 2 prior segments: 64 queries x 160 keys), all rows
+    and heads, timed in full: RoPE of keys and queries, then attention; the
+    mean of reps runs (one run takes milliseconds)."""
+    import numpy as np
+    from oracle import attention as oatt
+    from oracle import rope as orope
+    wl = workload("tiny", seed)
+    F, P, S = wl.lat_t, wl.P, wl.prior_segments[0]
+    ks, vs = [], []
+    for seg in range(S + 1):
+        k, v = si.segment_kv(wl, seed, 0, 0, seg, "cpu")
+        ks.append(k)
+        vs.append(v)
+    kt, vt = si.text_kv(wl, seed, 0, 0, "cpu")
+    k = torch.cat(ks + [kt]).double().numpy()
+    v = torch.cat(vs + [vt]).double().numpy()
+    q = si.queries(wl, seed, 0, 0, "cpu").double().numpy()
+    frames = list(range((S + 1) * F))
+    kpos = np.concatenate([orope.frame_positions(frames, wl.lat_h, wl.lat_w),
+                           orope.text_positions(wl.n_text)])
+    qpos = np.concatenate([orope.video_positions(S * F, F, wl.lat_h, wl.lat_w),
+                           orope.text_positions(wl.n_text)])
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        kr = orope.rope3d(k, kpos, wl.split, wl.theta)
+        qr = orope.rope3d(q, qpos, wl.split, wl.theta)
+        for h in range(wl.heads):
+            oatt.attention(qr[:, h], np.ascontiguousarray(kr[:, h]), np.ascontiguousarray(v[:, h]),
+                           scale, None)
+    sec = (time.perf_counter() - t0) / reps
+    flops = 4.0 * wl.Lq * k.shape[0] * wl.head_dim * wl.heads
+    return {"workload": "tiny", "Lq": wl.Lq, "Lk": int(k.shape[0]), "seconds": round(sec, 6),
+            "TFLOP_s": flops / sec / 1e12, "timed": f"in full, mean of {reps} runs"}
+
+
 def cpu_baseline(state, rows_wanted, seed):
     """Time the fp64 oracle on a bounded sample of the first session of the workload."""
     import numpy as np
@@ -840,6 +878,7 @@ def cpu_baseline(state, rows_wanted, seed):
                        f"({t2 - t1:.2f} s); the rows' share extrapolated linearly to the full "
                        f"segment: {t_full:.1f} s per layer"),
             "rows_timed": int(len(rows)), "rows_total": int(wl.Lq),
+            "tiny_in_full": cpu_baseline_tiny(seed),
             "seconds_per_layer_extrapolated": t_full}
 
 
