@@ -301,9 +301,10 @@ size_t sa_segment_attention_workspace(const sa_geom* geom, const sa_attn_item* i
 sa_status sa_segment_attention(const sa_geom* geom, const sa_attn_item* items, int32_t n_items,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* segment_attention_counted: sa_segment_attention, plus diagnostic counts
- * added (not stored: the caller clears them) into counters, device uint32
- * [3], 4-byte aligned:
+/* segment_attention_counted: sa_segment_attention (the same joint attention
+ * of "How one segment is made" over the cache of "What 'world memory'
+ * stores"), plus diagnostic counts added (not stored: the caller clears
+ * them) into counters, device uint32 [3], 4-byte aligned:
  *   [0] work tiles run (a query tile of one head, or one key-range part);
  *   [1] slow-path events: bf16 and int8 caches, work tiles whose key loop
  *       ran a second time with per-block rescaling (some row's block sum of
