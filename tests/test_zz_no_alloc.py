@@ -78,3 +78,25 @@ def test_noalloc_select_on_a_side_stream():
         sa.sparse_select_noalloc(s.geom, it, got, stream=side)
     side.synchronize()
     np.testing.assert_array_equal(got.cpu().numpy(), want.cpu().numpy())
+
+
+def test_noalloc_select_fills_the_whole_scratch():
+    """16 heads x 4,096 candidates (4,096 history frames of 64 tokens, one
+    block each) x 512 bytes: exactly the 32 MiB scratch. The lists equal the
+    workspace call's bit for bit; one candidate more is refused."""
+    wl = si.Workload("noalloc_max", heads=16, lat_t=64, lat_h=8, lat_w=8, n_text=16,
+                     prior_segments=(64,))
+    print("noalloc: 16 heads x 4,096 candidates, the whole scratch", flush=True)
+    s = Session(wl, seed=134, layer=0, session=0)
+    n_hist = 64 * 64
+    assert 16 * n_hist * 512 == sa.SPARSE_SCRATCH_BYTES
+    got, want, keep = _lists(s, n_hist, 25)
+    assert keep == 1024
+    np.testing.assert_array_equal(got, want)
+    it = s.item()
+    it.n_hist_frames, it.keep_blocks = n_hist + 1, keep
+    lists = torch.empty((16, -(-wl.Lq // sa.SPARSE_QUERY_BLOCK), keep), dtype=torch.int32,
+                        device="cuda")
+    with pytest.raises(sa.SegAttnError) as e:
+        sa.sparse_select_noalloc(s.geom, it, lists)
+    assert e.value.status == 6 and "static scratch" in str(e.value)
