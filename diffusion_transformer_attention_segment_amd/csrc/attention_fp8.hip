@@ -19,12 +19,15 @@
 // in two parts: y = q * 2^-qe, hi = e4m3(y), lo = e4m3(16 (y - hi)),
 // q ~ (hi + lo / 16) 2^qe. Both parts enter through the B operand's block
 // scales (127 + qe and 127 + qe - 4, two bytes of one register), so the QK^T
-// accumulator holds the logit in log2 units. It starts from 8 - m (m the
-// running max), so a probability is P'_j = exp2(acc_j) = 2^8 p_j, one exp2
-// per key (the 2^8 keeps small probabilities out of the e4m3 subnormal
+// accumulator holds the logit in log2 units. It starts from 6 - m (m the
+// running max), so a probability is P'_j = exp2(acc_j) = 2^6 p_j, one exp2
+// per key (the 2^6 keeps small probabilities out of the e4m3 subnormal
 // range); O = sum_j P'_j v_j and l = sum_j P'_j, out = O / l. The running
-// max m moves (rarely) when some acc passes 8.5, i.e. P' would pass 362
-// (e4m3 max 448), to put the largest acc at 8.
+// max m moves (rarely) when the sum of some lane's four consecutive P'
+// passes 2^8.5 = 362, to put the largest acc at 6. Such a sum is computed
+// for l anyway, so the overflow guard costs one max per eight keys: while no
+// sum passes 362 no P' does (e4m3 max 448), and a sum passes it only if some
+// P' passes 2^6.5, i.e. some acc passes 6.5.
 // Q is never stored, so its split costs only a second MFMA per k-step and
 // removes most of the query's share of the fp8 error; the cache keeps one
 // e4m3 code per value.
@@ -60,8 +63,9 @@ constexpr int KS8 = kD + 16;           // LDS row stride of the K tile (bytes)
 constexpr int VS8 = BN + 16;           // LDS row stride of the V^T tile (bytes)
 constexpr int KT8 = BN * KS8;          // bytes of one K stage
 constexpr int VT8 = kD * VS8;          // bytes of one V^T stage
-constexpr float kPTarget = 8.0f;       // log2 of P' for the largest key (probabilities x 2^8)
-constexpr float kTrigger = 8.5f;       // log2 of P' above which the running max moves
+constexpr float kPTarget = 6.0f;       // log2 of P' for the largest key (probabilities x 2^6)
+constexpr float kTriggerSum = 362.03867f;   // 2^8.5: a lane's sum of four P' above it moves
+                                            // the running max
 constexpr int kMaxShift = 64;          // largest shift of the running max carried by the
                                        // P.V block scale before O is renormalised
 
@@ -205,12 +209,9 @@ __device__ __forceinline__ TileInfo tile_info(const TileCursor& c, int flag_fi) 
 }
 
 // Word w (0..3) of one 32-key block: keys 4w .. 4w+3 of the block (registers
-// 4w ..), as P' = exp2(acc) packed e4m3. Accumulates the fp32 sum of P' and
-// the max of acc.
-__device__ __forceinline__ uint32_t prob_word_blk(const f32x16& s, int w, float& l, float& mx) {
+// 4w ..), as P' = exp2(acc) packed e4m3. Accumulates the fp32 sum of P'.
+__device__ __forceinline__ uint32_t prob_word_blk(const f32x16& s, int w, float& l) {
   const int r = w * 4;
-  mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);
-  mx = fmaxf(fmaxf(mx, s[r + 2]), s[r + 3]);
   const float p0 = __builtin_amdgcn_exp2f(s[r]), p1 = __builtin_amdgcn_exp2f(s[r + 1]);
   const float p2 = __builtin_amdgcn_exp2f(s[r + 2]), p3 = __builtin_amdgcn_exp2f(s[r + 3]);
   uint32_t word = cvt_fp8x2<false>(p0, p1, 0u);
@@ -221,33 +222,34 @@ __device__ __forceinline__ uint32_t prob_word_blk(const f32x16& s, int w, float&
 
 // Word w (0..7) of a tile's probabilities: the four keys 4w .. 4w+3 of the
 // lane's 32 (S^T block w / 4, registers 4 (w % 4) ..), as P' = exp2(acc)
-// packed e4m3. Accumulates the fp32 sum of P' and the max of acc.
-__device__ __forceinline__ uint32_t prob_word(const f32x16* s, int w, float& l, float& mx) {
+// packed e4m3, built in place of `old` (the register's previous word, so that
+// no zero is written first). q gets the four keys' sum of P', which is added
+// to l.
+__device__ __forceinline__ uint32_t prob_word(const f32x16* s, int w, float& l, float& q,
+                                              uint32_t old) {
   const int b = w >> 2, r = (w & 3) * 4;
-  mx = fmaxf(fmaxf(mx, s[b][r]), s[b][r + 1]);
-  mx = fmaxf(fmaxf(mx, s[b][r + 2]), s[b][r + 3]);
   float p0 = __builtin_amdgcn_exp2f(s[b][r]), p1 = __builtin_amdgcn_exp2f(s[b][r + 1]);
   float p2 = __builtin_amdgcn_exp2f(s[b][r + 2]), p3 = __builtin_amdgcn_exp2f(s[b][r + 3]);
-  uint32_t word = cvt_fp8x2<false>(p0, p1, 0u);
+  uint32_t word = cvt_fp8x2<false>(p0, p1, old);
   word = cvt_fp8x2<true>(p2, p3, word);
-  l += (p0 + p1) + (p2 + p3);
+  q = (p0 + p1) + (p2 + p3);
+  l += q;
   // (keep the word and the sums in this slot: the instruction selector would
   // otherwise gather all softmax arithmetic at the end of the step)
-  asm volatile("" : "+v"(word), "+v"(l), "+v"(mx));
+  asm volatile("" : "+v"(word), "+v"(l), "+v"(q));
   return word;
 }
 
-// The accumulator seed: 16 copies of this lane's 8 - m, written into the
-// registers of the S^T block it starts (the value passes through an empty asm,
-// so the copies are made where they are used and no 16-register seed stays
-// live across the loop).
-__device__ __forceinline__ f32x16 splat_seed(float negm8) {
+// The accumulator seed: 16 copies of this lane's 6 - m. It is built once and
+// stays live across the key loop (moved only by a rescale), so every QK^T
+// block reads it as its accumulator input with no copies on the common path.
+__device__ __forceinline__ f32x16 splat_seed(float pseed) {
   // a register pair holding the value twice, then seven 64-bit copies of it.
   // The compiler does not see hazards inside inline asm: the trailing nops
   // give an MFMA that reads the copies as its accumulator the wait states a
   // VALU write needs before that read.
   typedef float f32x2v __attribute__((ext_vector_type(2)));
-  f32x2v pair = {negm8, negm8};
+  f32x2v pair = {pseed, pseed};
   asm volatile("" : "+v"(pair));
   f32x2v c1, c2, c3, c4, c5, c6, c7;
   asm volatile(
@@ -284,85 +286,97 @@ __device__ __forceinline__ f32x16 qk_block(const uint8_t* kp, const i32x8v* qf, 
 // t into p_cur. Block 0 of s is consumed by words 0-3 and then receives block 0
 // of tile t+1; block 1 still holds tile t. `boundary` runs after the first two
 // MFMAs: it holds the barrier that makes K of tile t+1 visible. Returns the
-// tile's fp32 sum of P'; mx gets the max of x over the row.
+// tile's fp32 sum of P' (this lane's 32 keys); mx gets the largest of the
+// lane's eight 4-key sums of P'.
 template <typename Boundary>
 __device__ __forceinline__ float fp8_step_a(const uint8_t* vprev, const uint8_t* kn0,
                                             const i32x8v& p_prev, int vsc_prev, int psc, f32x16* o,
                                             const i32x8v* qf, const i32x8v* ql, int ksc_next,
-                                            int qsc, float negm8, f32x16* s,
+                                            int qsc, const f32x16& seed, f32x16* s,
                                             i32x8v& p_cur, float& mx, Boundary&& boundary) {
-  float l = 0.f;
-  mx = -INFINITY;
+  float l = 0.f, qa, qb;
+  mx = 0.f;
   // slot 0: PV 0, 1; barrier; words 0, 1
   const i32x8v v0 = lds_read32(vprev), v1 = lds_read32(vprev + 32 * VS8);
   o[0] = mfma_fp8(v0, p_prev, o[0], vsc_prev, psc);
   o[1] = mfma_fp8(v1, p_prev, o[1], vsc_prev, psc);
   boundary();
   const i32x8v v2 = lds_read32(vprev + 64 * VS8), v3 = lds_read32(vprev + 96 * VS8);
-  p_cur[0] = static_cast<int>(prob_word(s, 0, l, mx));
-  p_cur[1] = static_cast<int>(prob_word(s, 1, l, mx));
+  p_cur[0] = static_cast<int>(prob_word(s, 0, l, qa, static_cast<uint32_t>(p_cur[0])));
+  p_cur[1] = static_cast<int>(prob_word(s, 1, l, qb, static_cast<uint32_t>(p_cur[1])));
+  mx = fmaxf(fmaxf(mx, qa), qb);
   __builtin_amdgcn_sched_barrier(0);
   // slot 1: PV 2, 3; words 2, 3 (block 0 of tile t is then free)
   const i32x8v k0 = lds_read32(kn0), k1 = lds_read32(kn0 + 64);
   o[2] = mfma_fp8(v2, p_prev, o[2], vsc_prev, psc);
-  p_cur[2] = static_cast<int>(prob_word(s, 2, l, mx));
+  p_cur[2] = static_cast<int>(prob_word(s, 2, l, qa, static_cast<uint32_t>(p_cur[2])));
   o[3] = mfma_fp8(v3, p_prev, o[3], vsc_prev, psc);
-  p_cur[3] = static_cast<int>(prob_word(s, 3, l, mx));
+  p_cur[3] = static_cast<int>(prob_word(s, 3, l, qb, static_cast<uint32_t>(p_cur[3])));
+  mx = fmaxf(fmaxf(mx, qa), qb);
   __builtin_amdgcn_sched_barrier(0);
-  // slot 2: QK^T block 0 of tile t+1, first k-step (from the seed 8 - m);
+  // slot 2: QK^T block 0 of tile t+1, first k-step (from the seed 6 - m);
   // words 4, 5
-  s[0] = mfma_fp8(k0, qf[0], splat_seed(negm8), ksc_next, qsc);
-  p_cur[4] = static_cast<int>(prob_word(s, 4, l, mx));
+  s[0] = mfma_fp8(k0, qf[0], seed, ksc_next, qsc);
+  p_cur[4] = static_cast<int>(prob_word(s, 4, l, qa, static_cast<uint32_t>(p_cur[4])));
   s[0] = mfma_fp8_b1(k0, ql[0], s[0], ksc_next, qsc);
-  p_cur[5] = static_cast<int>(prob_word(s, 5, l, mx));
+  p_cur[5] = static_cast<int>(prob_word(s, 5, l, qb, static_cast<uint32_t>(p_cur[5])));
+  mx = fmaxf(fmaxf(mx, qa), qb);
   __builtin_amdgcn_sched_barrier(0);
   // slot 3: second k-step; words 6, 7
   s[0] = mfma_fp8(k1, qf[1], s[0], ksc_next, qsc);
-  p_cur[6] = static_cast<int>(prob_word(s, 6, l, mx));
+  p_cur[6] = static_cast<int>(prob_word(s, 6, l, qa, static_cast<uint32_t>(p_cur[6])));
   s[0] = mfma_fp8_b1(k1, ql[1], s[0], ksc_next, qsc);
-  p_cur[7] = static_cast<int>(prob_word(s, 7, l, mx));
+  p_cur[7] = static_cast<int>(prob_word(s, 7, l, qb, static_cast<uint32_t>(p_cur[7])));
+  mx = fmaxf(fmaxf(mx, qa), qb);
   __builtin_amdgcn_sched_barrier(0);
-  mx = max_other_half(mx);
   asm volatile("" : "+v"(p_cur), "+v"(l), "+v"(mx));
   return l;
 }
 
-// Rare path of a step, taken by the whole wave when some row's acc exceeds
-// kTrigger (P' would pass 362, near the e4m3 limit of 448): those rows move
-// the running max up so that their largest acc becomes kPTarget. O (every
-// tile before this one), the sum of the tiles before, the seed 8 - m and
-// block 0 of the next tile (already issued from the old seed) are shifted to
-// match, and the tile's probabilities are recomputed -- block 0 of its S^T
-// again from its K rows (kc0, still in LDS; block scale ksc), block 1 from
-// s[1]. Block 0 is masked like the first time, through the accumulator seed:
-// -inf for keys past the count in `code` and for keys whose bit in wword is
-// clear (all ones unless `code` flags a windowed text tile).
-__device__ __forceinline__ float rescale_step(float mx, float& l_run, int& shift,
-                                              float& negm8, f32x16* s, const uint8_t* kc0,
+// Rare path of a step, taken by the whole wave when some lane's 4-key sum of
+// P' passes kTriggerSum (a P' near the e4m3 limit of 448 is possible): rows
+// whose largest acc in the tile passes kPTarget move the running max up so
+// that it becomes kPTarget. The tile's acc is found again for that -- block 0
+// of its S^T from its K rows (kc0, still in LDS; block scale ksc) with the old
+// seed, block 1 in s[1]. O (every tile before this one), the sum of the tiles
+// before, the seed and block 0 of the next tile (already issued from the old
+// seed) are shifted to match, and the tile's probabilities are recomputed.
+// Block 0 is masked like the first time, through the accumulator seed: -inf
+// for keys past the count in `code` and for keys whose bit in wword is clear
+// (all ones unless `code` flags a windowed text tile).
+__device__ __forceinline__ float rescale_step(float& l_run, int& shift,
+                                              float& pseed, f32x16& seed, f32x16* s,
+                                              const uint8_t* kc0,
                                               const i32x8v* qf, const i32x8v* ql, int ksc, int qsc,
                                               int code, int g, uint32_t wword, i32x8v& p_cur) {
   // an integer shift d: O keeps the units of the max before all shifts, and the
   // later probabilities enter P.V with the block scale 2^shift
+  f32x16 b0;
+  {
+    const int lim = tile_count(code) - 32 * g;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) b0[r] = (r >= lim ? -INFINITY : keep_if_bit(0.f, wword, r)) + pseed;
+    b0 = qk_block(kc0, qf, ql, ksc, qsc, b0);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(fmaxf(mx, b0[r]), s[1][r]);
+  mx = max_other_half(mx);
   const float d = fmaxf(ceilf(mx - kPTarget), 0.f);
   l_run *= __builtin_amdgcn_exp2f(-d);
   shift += static_cast<int>(d);
   // whole-vector updates, so that each value keeps its registers across the
   // branch (element-wise updates leave copies on the common path)
-  negm8 -= d;
+  pseed -= d;
+  seed = seed - d;
   s[0] = s[0] - d;
-  float l = 0.f, m2 = -INFINITY;
-  {
-    f32x16 b0;
-    const int lim = tile_count(code) - 32 * g;
+  b0 = b0 - d;
+  float l = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) b0[r] = (r >= lim ? -INFINITY : keep_if_bit(0.f, wword, r)) + negm8;
-    b0 = qk_block(kc0, qf, ql, ksc, qsc, b0);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) p_cur[w] = static_cast<int>(prob_word_blk(b0, w, l, m2));
-  }
+  for (int w = 0; w < 4; ++w) p_cur[w] = static_cast<int>(prob_word_blk(b0, w, l));
   const f32x16 b1 = s[1] - d;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) p_cur[4 + w] = static_cast<int>(prob_word_blk(b1, w, l, m2));
+  for (int w = 0; w < 4; ++w) p_cur[4 + w] = static_cast<int>(prob_word_blk(b1, w, l));
   return l;
 }
 
@@ -521,16 +535,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   float l_run = 0.f;
 
   // S^T of tile 0 (logits in log2 units); the running max m starts at its max,
-  // and every later QK^T accumulation starts from the seed 8 - m
+  // and every later QK^T accumulation starts from the seed 6 - m
   f32x16 sc[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) sc[b] = qk_block(Ks + krow[b] * KS8 + 32 * g, qf, ql, ti0.ksc, qsc, f32x16{});
   if (ti0.nvalid < BN) mask_tile(sc, tile_count(ti0.nvalid), g);
   // (tile 0 is never a text tile under timed windows: the key ranges of such
   // items start on a video tile, so every row sees tile 0's valid keys)
-  // The running max is m_ref + shift: probabilities P' = 2^(x - m_ref - shift + 8)
+  // The running max is m_ref + shift: probabilities P' = 2^(x - m_ref - shift + 6)
   // enter P.V with the block scale 2^shift, so O stays in units of 2^(x - m_ref
-  // + 8) and a rescale never rewrites it; l_run is in the units of the running
+  // + 6) and a rescale never rewrites it; l_run is in the units of the running
   // max. O is renormalised (m_ref moves up) only when a shift passes kMaxShift.
   float m_ref;
   {
@@ -543,10 +557,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   }
   int shift = 0;
   uint32_t n_resc = 0, n_renorm = 0;   // this wave's rescales (diagnostic counters only)
-  float negm8 = kPTarget - m_ref;   // the seed of every later QK^T accumulation
+  float pseed = kPTarget - m_ref;   // the seed of every later QK^T accumulation
 #pragma unroll
-  for (int b = 0; b < 2; ++b) sc[b] = sc[b] + negm8;
-  i32x8v pa = {}, pb;
+  for (int b = 0; b < 2; ++b) sc[b] = sc[b] + pseed;
+  i32x8v pa = {}, pb = {};
+  f32x16 seed = splat_seed(pseed);   // the accumulator seed of every QK^T block
   int vsc_prev = kUnitScale;   // V block scale of the tile before the compute tile
 
   // Tile t sits in stage t % 4. Step t: PV(t-1) and QK^T(t+1) on the matrix
@@ -588,14 +603,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
     const int ksc_next = ti1.ksc;
     float mx;
     float lt = fp8_step_a(Vprev, Knext + krow[0] * KS8, p_prev, vsc_prev, kUnitScale + shift, o, qf,
-                          ql, ksc_next, qsc, negm8, sc, p_cur, mx, boundary);
-    if (__builtin_expect(__any(mx > kTrigger), 0)) {
-      lt = rescale_step(mx, l_run, shift, negm8, sc, Kcur + krow[0] * KS8, qf, ql, cur.ksc, qsc,
+                          ql, ksc_next, qsc, seed, sc, p_cur, mx, boundary);
+    if (__builtin_expect(__any(mx > kTriggerSum), 0)) {
+      lt = rescale_step(l_run, shift, pseed, seed, sc, Kcur + krow[0] * KS8, qf, ql, cur.ksc, qsc,
                         cur.nvalid, g, cur.nvalid < 0 ? window_word(tt) : ~0u, p_cur);
       ++n_resc;
     }
     // QK^T block 1 of tile t+1 (block 1 of tile t is no longer needed)
-    sc[1] = qk_block(Knext + krow[1] * KS8, qf, ql, ksc_next, qsc, splat_seed(negm8));
+    sc[1] = qk_block(Knext + krow[1] * KS8, qf, ql, ksc_next, qsc, seed);
     l_run += lt;
     vsc_prev = cur.vsc;
     ti0 = ti1;
@@ -658,7 +673,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   if (a.counters != nullptr) add_counts(a.counters, tid, n_renorm, n_resc);
 
   // ---- epilogue ----------------------------------------------------------------
-  // O and l in units of 2^(x - m_ref + 8): m_ref - 8 is the max the merge sees
+  // O and l in units of 2^(x - m_ref + 6): m_ref - 6 is the max the merge sees
   const float l_tot = (l_run + __shfl_xor(l_run, 32)) *
                       __uint_as_float(static_cast<uint32_t>(127 + shift) << 23);   // x 2^shift
   const float inv = 1.0f / l_tot;

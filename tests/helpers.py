@@ -231,11 +231,11 @@ class Session:
 
         Returns (out, lse, bound): `bound` is the per-element error that rounding
         the probabilities to e4m3 can add. The kernel multiplies V by e4m3
-        probabilities P' = 2^(x - m + 8) against its running max m, which never
-        passes the row's true max by a whole unit, so P' >= 2^7 p with p the
+        probabilities P' = 2^(x - m + 6) against its running max m, which never
+        passes the row's true max by a whole unit, so P' >= 2^5 p with p the
         probability against the true max: the rounding is at most 2^-4 relative
-        for a normal P' and at most 2^-10 absolute in P' units (2^-17 in p units)
-        below the normal range, i.e. sum_j (2^-4 p_j + 2^-17) |v_jd| / sum_j p_j."""
+        for a normal P' and at most 2^-10 absolute in P' units (2^-15 in p units)
+        below the normal range, i.e. sum_j (2^-4 p_j + 2^-15) |v_jd| / sum_j p_j."""
         from oracle import cache as ocache
         wl = self.wl
         hs = list(range(wl.heads)) if heads is None else list(heads)
@@ -289,7 +289,7 @@ class Session:
             if vis is not None:
                 s_ = np.where(vis, s_, -np.inf)
             p_ = np.exp(s_ - s_.max(axis=1, keepdims=True))
-            floor = np.full(vsk.shape[0], 2.0 ** -17)
+            floor = np.full(vsk.shape[0], 2.0 ** -15)
             fl = floor[None, :] if vis is None else np.where(vis, floor[None, :], 0.0)
             bound[:, j] = ((2.0 ** -4 * p_ + fl) @ np.abs(v[:, j])) / p_.sum(1)[:, None]
         return out, lse, bound
