@@ -1,5 +1,6 @@
 // kv_append / text_append kernels: 3D RoPE on K, cache-plane stores of K and
-// (transposed) V, bf16 or e4m3 + per-(frame, head) scales.
+// (transposed) V, bf16, e4m3 + per-(frame, head) scales, or int8 + per-(token,
+// head) scales.
 //
 // Source: "Hy-Nomas: an 8.6B world model whose memory is a KV cache",
 // sections "How one segment is made" (RoPE split [16, 56, 56] over t, h, w)
@@ -7,7 +8,8 @@
 // stored); "The 4090 preset" (the cache is quantised once per segment).
 //
 // HBM-bound: per token and head the kernels read 2 x 256 B of bf16 input and
-// write 2 x 256 B (bf16) or 2 x 128 B (e4m3) of cache. Blocks run heads
+// write 2 x 256 B (bf16) or 2 x 128 B (e4m3, int8; int8 adds 2 x 4 B of
+// scales) of cache. Blocks run heads
 // fastest, so that concurrent blocks read the same tokens' rows of all heads
 // (4 KB contiguous per token). The bf16 kernel transposes V through LDS and
 // stores 16-byte runs of V^T rows; it tabulates the cos/sin of its tile (the
@@ -375,39 +377,86 @@ static bool use_lut(const AppendArgs& a) {
 namespace {
 
 // ---- int8 with a scale per token and head ---------------------------------------
-// One block = 64 tokens of one (frame, head) plane, 256 threads: 16 lanes own a
-// (token, head) row, 8 dims each. Per row: rotate K in fp32 (video), amax over
-// the 128 dims by butterfly shuffles inside the 16 lanes, scale = amax / 127,
-// code = rint(x * (127 / amax)) clamped to +-127 (amax 0: scale 1, codes 0),
-// all in fp32. K codes go out as 8-byte runs of the row, V codes through an
-// LDS [dim][token] tile so that V^T rows leave as 16-byte runs. Text tokens
-// past n_tok get zero codes and zero scales.
+// One block = 64 tokens of one (frame, head) plane, 256 threads. A row of 16
+// lanes owns four consecutive tokens, each lane 8 dims of each. Per (token,
+// head) row, in fp32: rotate K (video), amax over the 128 dims, scale =
+// amax / 127, inv = 127 / amax (both 1 when amax is 0), code = rint(x * inv)
+// (|x * inv| <= 127 (1 + 2^-24), so no code passes +-127 and no clamp is
+// needed). The amax of a row is a max across its 16 lanes by DPP; the two
+// divisions of the four rows a lane row quantises at a time are spread over
+// its lanes (lanes 0-3: inv of rows 0-3, lanes 4-7: their scales) and the
+// inverses broadcast back. K codes go out as 8-byte runs of the row, V codes
+// through an LDS [dim][token] tile, four tokens to a word, so that V^T rows
+// leave as 16-byte runs. Tokens from n_tok to the plane's end (the padded
+// slots) get zero codes and zero scales.
 constexpr int kI8Tok = 64;
-// LDS row stride (bytes) of the V^T tile: 17 words, so that the byte stores of
-// one token's 128 dims (rows 8 apart per lane) fall in 8 banks, not 2
+// LDS row stride (bytes) of the V^T tile (a word of four tokens per store)
 constexpr int kI8Stride = kI8Tok + 4;
+// 1.5 * 2^23: fl(t + kRoundMagic) for |t| < 2^22 is kRoundMagic + rint(t)
+// (rounding to nearest even), and its low byte is rint(t) as a two's
+// complement byte
+constexpr float kRoundMagic = 12582912.0f;
 
-__device__ __forceinline__ float group16_max(float v) {
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xF, 0xF, false));
+}
+
+// max over the 16 lanes of a row of non-negative fp32 values, as bit patterns
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));    // quad_perm [1, 0, 3, 2]
+  v = max(v, dpp_u32<0x4E>(v));    // quad_perm [2, 3, 0, 1]
+  v = max(v, dpp_u32<0x141>(v));   // row_half_mirror
+  v = max(v, dpp_u32<0x140>(v));   // row_mirror
   return v;
 }
 
-// 8 values -> 8 int8 codes (two words), and the row's scale
-__device__ __forceinline__ uint2 quantize_row8(const float* y, float* scale) {
+// lane n of each row of 16 to the whole row
+template <int kN>
+__device__ __forceinline__ float row16_bcast(float v) {
+  return __uint_as_float(dpp_u32<0x150 + kN>(__float_as_uint(v)));
+}
+
+__device__ __forceinline__ uint32_t amax8(const float* x) {
   float am = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(y[i]));
-  am = group16_max(am);
-  const float inv = am > 0.f ? 127.0f / am : 1.0f;
-  *scale = am > 0.f ? am / 127.0f : 1.0f;
-  uint32_t w[2] = {0u, 0u};
+  for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(x[i]));
+  return __float_as_uint(am);
+}
+
+// kRoundMagic + rint(x * inv): the product rounded to fp32 first, then to an
+// integer (two roundings, as the definition; no fused multiply-add)
+__device__ __forceinline__ uint32_t code_bits(float x, float inv) {
+#pragma clang fp contract(off)
+  const float t = x * inv;
+  return __float_as_uint(t + kRoundMagic);
+}
+
+// the low bytes of four words, first in the low byte
+__device__ __forceinline__ uint32_t low_bytes4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// Four rows (one per token of a lane row, values x[i][0..7] in this lane):
+// inv[i] for each row, in every lane; scale of row (lane & 3) in lanes 4-7 of
+// the lane row (returned, meaningful there).
+__device__ __forceinline__ float row_scales4(const float (*x)[8], int lane, float* inv) {
+  uint32_t am[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float c = fminf(fmaxf(__builtin_rintf(y[i] * inv), -127.0f), 127.0f);
-    w[i >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(c)) & 0xFFu) << (8 * (i & 3));
-  }
-  return make_uint2(w[0], w[1]);
+  for (int i = 0; i < 4; ++i) am[i] = row16_max(amax8(x[i]));
+  const int r = lane & 3;
+  const float a = __uint_as_float(r == 0 ? am[0] : r == 1 ? am[1] : r == 2 ? am[2] : am[3]);
+  const bool scale_lane = (lane & 4) != 0;   // else an inverse lane
+  const float num = scale_lane ? a : 127.0f, den = scale_lane ? 127.0f : a;
+  const float q = a > 0.f ? num / den : 1.0f;   // one correctly rounded division
+  inv[0] = row16_bcast<0>(q);
+  inv[1] = row16_bcast<1>(q);
+  inv[2] = row16_bcast<2>(q);
+  inv[3] = row16_bcast<3>(q);
+  return q;
 }
 
 // kLut: the tile's cos/sin table in LDS, as for the bf16 kernel
@@ -437,51 +486,80 @@ __global__ __launch_bounds__(256) void append_int8_kernel(const AppendArgs a) {
     om[tid] = rope_omega(tid, a.rope, &axis);
     ax[tid] = axis;
   }
-  __syncthreads();
   const size_t pl = static_cast<size_t>(f) * H + h;
   int8_t* kdst = static_cast<int8_t*>(a.k) + pl * a.plane_len * kD;
   int8_t* vdst = static_cast<int8_t*>(a.v) + pl * a.plane_len * kD;
-  float* ksc = a.k_scale + pl * a.plane_len;
-  float* vsc = a.v_scale + pl * a.plane_len;
+  // the lane row's tokens t0 .. t0 + 3: all inside the plane or all past it
+  // (plane lengths of one-byte caches are multiples of 16)
+  const int t0 = p0 + 4 * grp;
+  const bool in_plane = t0 < a.plane_len;
+  u32x4 kx[4], vx[4];
 #pragma unroll
-  for (int i = 0; i < kI8Tok / 16; ++i) {
-    const int tok = grp + 16 * i;
-    const int p = p0 + tok;
-    if (p >= a.plane_len) continue;          // (whole 16-lane groups agree)
-    uint2 kc = make_uint2(0u, 0u), vc = make_uint2(0u, 0u);
-    float ks = 0.f, vs = 0.f;
-    if (p < a.n_tok) {
-      const size_t in_off = (static_cast<size_t>(fr * a.n_tok + p) * H + h) * kD + lane * 8;
-      const u32x4 kx = *reinterpret_cast<const u32x4*>(a.k_in + in_off);
-      const u32x4 vx = *reinterpret_cast<const u32x4*>(a.v_in + in_off);
-      float y[8], z[8];
+  for (int i = 0; i < 4; ++i) {
+    kx[i] = vx[i] = u32x4{0u, 0u, 0u, 0u};
+    if (t0 + i < a.n_tok) {
+      const size_t in_off = (static_cast<size_t>(fr * a.n_tok + t0 + i) * H + h) * kD + lane * 8;
+      kx[i] = *reinterpret_cast<const u32x4*>(a.k_in + in_off);
+      vx[i] = *reinterpret_cast<const u32x4*>(a.v_in + in_off);
+    }
+  }
+  __syncthreads();   // the rotation table
+  // ---- K: rotate, scales, codes (8-byte runs of each token's row)
+  {
+    float y[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = t0 + i;
       if constexpr (kLut) {
-        key_chunk<true>(kx, lane, f, p / lat_w - row0, p % lat_w, true, lut, ls, a.rope, y);
+        key_chunk<true>(kx[i], lane, f, p / lat_w - row0, p % lat_w, true, lut, ls, a.rope, y[i]);
       } else if (!a.is_text) {
-        rotate_chunk(kx, lane, f, p / lat_w, p % lat_w, om, ax, y);
+        rotate_chunk(kx[i], lane, f, p / lat_w, p % lat_w, om, ax, y[i]);
       } else {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          y[2 * m] = __uint_as_float(kx[m] << 16);
-          y[2 * m + 1] = __uint_as_float(kx[m] & 0xFFFF0000u);
+          y[i][2 * m] = __uint_as_float(kx[i][m] << 16);
+          y[i][2 * m + 1] = __uint_as_float(kx[i][m] & 0xFFFF0000u);
         }
       }
+    }
+    float inv[4];
+    const float q = row_scales4(y, lane, inv);
+    if (in_plane) {
+      if ((lane & 12) == 4) {   // lanes 4-7: the scales of tokens t0 .. t0 + 3
+        const int p = t0 + (lane & 3);
+        a.k_scale[pl * a.plane_len + p] = p < a.n_tok ? q : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t c[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) c[m] = code_bits(y[i][m], inv[i]);
+        *reinterpret_cast<uint2*>(kdst + static_cast<size_t>(t0 + i) * kD + lane * 8) =
+            make_uint2(low_bytes4(c[0], c[1], c[2], c[3]), low_bytes4(c[4], c[5], c[6], c[7]));
+      }
+    }
+  }
+  // ---- V: scales, codes as words of four tokens of one dim in the V^T tile
+  {
+    float z[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        z[2 * m] = __uint_as_float(vx[m] << 16);
-        z[2 * m + 1] = __uint_as_float(vx[m] & 0xFFFF0000u);
+        z[i][2 * m] = __uint_as_float(vx[i][m] << 16);
+        z[i][2 * m + 1] = __uint_as_float(vx[i][m] & 0xFFFF0000u);
       }
-      kc = quantize_row8(y, &ks);
-      vc = quantize_row8(z, &vs);
-      *reinterpret_cast<uint2*>(kdst + static_cast<size_t>(p) * kD + lane * 8) = kc;
-    }
-    if (lane == 0) {
-      ksc[p] = ks;
-      vsc[p] = vs;
+    float inv[4];
+    const float q = row_scales4(z, lane, inv);
+    if (in_plane && (lane & 12) == 4) {
+      const int p = t0 + (lane & 3);
+      a.v_scale[pl * a.plane_len + p] = p < a.n_tok ? q : 0.f;
     }
 #pragma unroll
     for (int m = 0; m < 8; ++m)
-      vt[(lane * 8 + m) * kI8Stride + tok] = static_cast<uint8_t>((m < 4 ? vc.x : vc.y) >> (8 * (m & 3)));
+      *reinterpret_cast<uint32_t*>(&vt[(lane * 8 + m) * kI8Stride + 4 * grp]) =
+          low_bytes4(code_bits(z[0][m], inv[0]), code_bits(z[1][m], inv[1]),
+                     code_bits(z[2][m], inv[2]), code_bits(z[3][m], inv[3]));
   }
   __syncthreads();
   // V^T rows: dim d, tokens p0 + 16 q .. + 15 (16-byte runs)
