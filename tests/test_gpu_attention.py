@@ -385,6 +385,37 @@ def test_fp8_logits_far_above_the_first_tile(split):
     np.testing.assert_allclose(got_lse, wq_lse, rtol=2e-3, atol=0.05)
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_fp8_logits_a_few_units_above_the_first_tile(split):
+    """e4m3 cache, Q x 3: row maxima rise a few log2 units past their first
+    tile, so the kernel's overflow guard (some lane's sum of four scaled
+    probabilities above 2^8.5) fires on many steps and moves the running max by
+    small integer shifts. The counters show that it fired; the output is gated
+    like the far case, against the oracle with the kernel's query split."""
+    wl = _fp8_wl("fp8_mid", 2, 4, 6, 8, 24, 8)
+    s = Session(wl, seed=17, layer=0, session=0, q_scale=3.0)
+    print(f"fp8 moderate rises split={split}", flush=True)
+    ws = "auto" if split else None
+    if split:
+        assert sa.segment_attention_workspace(s.geom, [s.item()]) > 0
+    c = torch.zeros(3, dtype=torch.int32, device="cuda")
+    sa.segment_attention(s.geom, [s.item()], workspace=ws, counters=c)
+    torch.cuda.synchronize()
+    tiles, slow, resc = (int(x) for x in c.cpu())
+    print(f"fp8 moderate rises: work tiles {tiles}, renormalisations {slow}, rescale steps {resc}",
+          flush=True)
+    assert resc > 0
+    got, got_lse = s.gpu_out()
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(got_lse))
+    wq, wq_lse, bound = s.oracle_fp8_cache(split_q=True)
+    err = np.abs(got - wq)
+    worst = float(np.max(err / (bound + 5e-3)))
+    print(f"fp8 moderate rises split={split}: max_abs={err.max():.3e} "
+          f"max(err / (bound + 5e-3))={worst:.3f}", flush=True)
+    assert worst <= 1.0
+    np.testing.assert_allclose(got_lse, wq_lse, rtol=2e-3, atol=0.05)
+
+
 FP8_CASES = [
     # name, H, F, lat_h, lat_w, n_text, prior segments
     ("fp8_small", 2, 2, 4, 8, 16, 2),       # P = 32
