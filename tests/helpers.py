@@ -33,6 +33,21 @@ def kept_frames(wl, session):
     raise ValueError(wl.policy)
 
 
+def prob_rounding_bound(p, absv):
+    """Per-element bound of the error that rounding the probabilities to e4m3
+    adds to softmax(.) v: sum_j e_j |v_jd| / sum_j p_j, with p [M, N] the
+    probabilities relative to each row's max (exp(s - max)) and absv [N, D].
+    The e4m3 kernel weighs V by P' >= 2^5 p (its running max never passes the
+    row's max by a whole unit), so a key with p >= 2^-11 has a normal P' and
+    e = 2^-4 p (half a spacing at 3 mantissa bits); a smaller one may be
+    subnormal, where half a spacing is 2^-10 in P' units, at most 2^-15 in p
+    units, and rounding never moves a value by more than itself:
+    e = max(2^-4 p, min(p, 2^-15)). Hidden keys have p = 0."""
+    small = np.maximum(2.0 ** -4 * p, np.minimum(p, 2.0 ** -15))
+    e = np.where(p >= 2.0 ** -11, 2.0 ** -4 * p, small)
+    return (e @ absv) / p.sum(1)[:, None]
+
+
 class Session:
     """One session of one layer: raw inputs on the device plus its cache layer."""
 
@@ -222,23 +237,12 @@ class Session:
                                                   self.visibility(rows, hsel[h]))
         return out, lse
 
-    def oracle_fp8_cache(self, rows=None, heads=None, split_q=False):
-        """Oracle for an e4m3 cache: fp64 attention over the values the cache
-        stores -- the oracle's own quantised-then-dequantised K and V (per
-        (frame, head) planes, per head for text) -- and the fp64 rotated Q.
-        split_q=True is the diagnostic variant that also models the kernel's
-        query precision (split_query_fp8).
-
-        Returns (out, lse, bound): `bound` is the per-element error that rounding
-        the probabilities to e4m3 can add. The kernel multiplies V by e4m3
-        probabilities P' = 2^(x - m + 6) against its running max m, which never
-        passes the row's true max by a whole unit, so P' >= 2^5 p with p the
-        probability against the true max: the rounding is at most 2^-4 relative
-        for a normal P' and at most 2^-10 absolute in P' units (2^-15 in p units)
-        below the normal range, i.e. sum_j (2^-4 p_j + 2^-15) |v_jd| / sum_j p_j."""
+    def fp8_stored_kv(self, hs):
+        """The key set of heads hs as an e4m3 cache stores it, from the
+        oracle's own append (quantise, then decode times the plane scale):
+        rotated K [Lk, len(hs), D] and V [Lk, len(hs), D], float64."""
         from oracle import cache as ocache
         wl = self.wl
-        hs = list(range(wl.heads)) if heads is None else list(heads)
         F, P = wl.lat_t, wl.P
         raw = [(f, self.raw_k[f // F][(f % F) * P:(f % F + 1) * P].float().cpu().double().numpy(),
                 self.raw_v[f // F][(f % F) * P:(f % F + 1) * P].float().cpu().double().numpy())
@@ -249,8 +253,7 @@ class Session:
             kc, ksc, vc, vsc = ocache.append_fp8(kin, vin, f, wl.lat_h, wl.lat_w, wl.split,
                                                  self.geom.rope_theta)
             return (ocache.dequant(kc[0], ksc[0][:, None, None]).transpose(1, 0, 2)[:, hs],
-                    ocache.dequant(vc[0], vsc[0][:, None, None]).transpose(2, 0, 1)[:, hs],
-                    np.repeat(vsc[0][None, hs], P, axis=0))
+                    ocache.dequant(vc[0], vsc[0][:, None, None]).transpose(2, 0, 1)[:, hs])
 
         import concurrent.futures   # frames are independent: one per worker thread
         with concurrent.futures.ThreadPoolExecutor(max_workers=16) as ex:
@@ -258,17 +261,30 @@ class Session:
         del raw
         ks = [x[0] for x in per_frame]
         vs = [x[1] for x in per_frame]
-        vsc_key = [x[2] for x in per_frame]
         del per_frame
         tk = self.text_k.float().cpu().double().numpy()
         tv = self.text_v.float().cpu().double().numpy()
         kc, ksc, vc, vsc = ocache.append_text_fp8(tk, tv)
         ks.append(ocache.dequant(kc, ksc[:, None, None]).transpose(1, 0, 2)[:, hs])
         vs.append(ocache.dequant(vc, vsc[:, None, None]).transpose(2, 0, 1)[:, hs])
-        vsc_key.append(np.repeat(vsc[None, hs], wl.n_text, axis=0))
         k = np.concatenate(ks)          # already rotated
         v = np.concatenate(vs)
-        vsk = np.concatenate(vsc_key).astype(np.float64)     # [Lk, heads]
+        return k, v
+
+    def oracle_fp8_cache(self, rows=None, heads=None, split_q=False):
+        """Oracle for an e4m3 cache: fp64 attention over the values the cache
+        stores -- the oracle's own quantised-then-dequantised K and V (per
+        (frame, head) planes, per head for text) -- and the fp64 rotated Q.
+        split_q=True is the diagnostic variant that also models the kernel's
+        query precision (split_query_fp8).
+
+        Returns (out, lse, bound): `bound` is the per-element error that rounding
+        the probabilities to e4m3 can add (prob_rounding_bound: the kernel
+        multiplies V by e4m3 probabilities P' = 2^(x - m + 6) against its
+        running max m)."""
+        wl = self.wl
+        hs = list(range(wl.heads)) if heads is None else list(heads)
+        k, v = self.fp8_stored_kv(hs)
         q = self.q[:, hs].float().cpu().double().numpy()
         if rows is None:
             rows = np.arange(q.shape[0])
@@ -289,9 +305,7 @@ class Session:
             if vis is not None:
                 s_ = np.where(vis, s_, -np.inf)
             p_ = np.exp(s_ - s_.max(axis=1, keepdims=True))
-            floor = np.full(vsk.shape[0], 2.0 ** -15)
-            fl = floor[None, :] if vis is None else np.where(vis, floor[None, :], 0.0)
-            bound[:, j] = ((2.0 ** -4 * p_ + fl) @ np.abs(v[:, j])) / p_.sum(1)[:, None]
+            bound[:, j] = prob_rounding_bound(p_, np.abs(v[:, j]))
         return out, lse, bound
 
     def oracle_int8_cache(self, rows=None, heads=None):
@@ -366,6 +380,51 @@ def oracle_all_heads(s, rows=None, workers=16):
     with threadpool_limits(1):
         with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
             list(ex.map(one, range(wl.heads)))
+    return out, lse
+
+
+def oracle_fp8_cache_all_heads(s, rows=None, workers=16, chunk=256, with_bound=False):
+    """Session.oracle_fp8_cache's (out, lse) for every head: the oracle over
+    the values an e4m3 cache stores, one head per worker thread, query rows in
+    chunks of `chunk` so that a full-size output fits in memory. With
+    with_bound, also the e4m3 probability-rounding bound of
+    Session.oracle_fp8_cache and each row's largest probability (out, lse,
+    bound, pmax). Prints a line per finished head."""
+    import concurrent.futures
+    from threadpoolctl import threadpool_limits
+    wl = s.wl
+    k, v = s.fp8_stored_kv(list(range(wl.heads)))
+    q = s.q.float().cpu().double().numpy()
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    qr = orope.rope3d(q[rows], s.q_positions()[rows], wl.split, s.geom.rope_theta)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    out = np.zeros(qr.shape)
+    lse = np.zeros(qr.shape[:2])
+    bound = np.zeros(qr.shape) if with_bound else None
+    pmax = np.zeros(qr.shape[:2]) if with_bound else None
+
+    def one(h):
+        kh = np.ascontiguousarray(k[:, h])
+        vh = np.ascontiguousarray(v[:, h])
+        for c0 in range(0, len(rows), chunk):
+            vis = s.visibility(rows[c0:c0 + chunk], h)
+            o, l = oatt.attention(qr[c0:c0 + chunk, h], kh, vh, scale, vis)
+            out[c0:c0 + chunk, h] = o
+            lse[c0:c0 + chunk, h] = l
+            if with_bound:   # as Session.oracle_fp8_cache's bound
+                s_ = (qr[c0:c0 + chunk, h] @ kh.T) * scale
+                if vis is not None:
+                    s_ = np.where(vis, s_, -np.inf)
+                p_ = np.exp(s_ - s_.max(axis=1, keepdims=True))
+                bound[c0:c0 + chunk, h] = prob_rounding_bound(p_, np.abs(vh))
+                pmax[c0:c0 + chunk, h] = 1.0 / p_.sum(1)
+        print(f"  oracle head {h} done", flush=True)
+
+    with threadpool_limits(1):
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one, range(wl.heads)))
+    if with_bound:
+        return out, lse, bound, pmax
     return out, lse
 
 

@@ -133,8 +133,8 @@ def fp8seg8():
     """The fp8 workload run once: eight prior segments stored e4m3 with
     per-(frame, head) scales, values scaled by U[0.5, 2] per (frame, head);
     237,856 keys. Yields the session, its sampled rows (512, all 16 heads),
-    the kernel's output there and the oracle over the values the cache
-    stores."""
+    the kernel's output there, the oracle over the values the cache stores
+    and the e4m3 probability-rounding bound there."""
     wl = WL["fp8seg8"]
     print("workload fp8seg8: 26,656 queries x 237,856 keys x 16 heads", flush=True)
     s = Session(wl, 0, 0, 0)
@@ -142,8 +142,8 @@ def fp8seg8():
     torch.cuda.synchronize()
     rows = _rows(wl, 512, 3)
     got, got_lse = s.gpu_out(rows=rows)
-    want_c, want_c_lse, _ = s.oracle_fp8_cache(rows=rows)
-    yield s, rows, got, got_lse, want_c, want_c_lse
+    want_c, want_c_lse, bound = s.oracle_fp8_cache(rows=rows)
+    yield s, rows, got, got_lse, want_c, want_c_lse, bound
     del s
     gc.collect()
     torch.cuda.empty_cache()
@@ -153,10 +153,21 @@ def fp8seg8():
 def test_fp8_cache_eight_prior_segments(fp8seg8):
     """The cache bytes are bit-exact to the oracle's quantisation (append
     tests), so the kernel is gated against the oracle over the values the
-    cache stores: max-abs 2e-2, mean-abs 2e-3 (inside the fp8 bar of 5e-2 /
-    5e-3), relative L2 0.05, lse 2e-2, on 512 rows of all 16 heads."""
-    s, rows, got, got_lse, want_c, want_c_lse = fp8seg8
-    _, _, rel = compare(got, want_c, 2e-2, 2e-3, "fp8seg8 vs stored cache")
+    cache stores, on 512 rows of all 16 heads: every element within the
+    e4m3 probability-rounding bound plus 5e-3 (as the small e4m3 cases),
+    mean-abs 2e-3, relative L2 0.05, lse 2e-2. A flat max-abs bar does not
+    fit e4m3 probabilities: over the whole output (the full-coverage run)
+    the largest error is 5.5e-2, in a row where one key holds 29 % of the
+    weight, while rows where no key passes 10 % stay below 2.4e-2."""
+    s, rows, got, got_lse, want_c, want_c_lse, bound = fp8seg8
+    err = np.abs(got - want_c)
+    worst = float(np.max(err / (bound + 5e-3)))
+    rel = float(np.linalg.norm(got - want_c) / np.linalg.norm(want_c))
+    print(f"fp8seg8 vs stored cache: max_abs={err.max():.3e} mean_abs={err.mean():.3e} "
+          f"rel_l2={rel:.3e} max(err / (bound + 5e-3))={worst:.3f}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert worst <= 1.0
+    assert err.mean() <= 2e-3
     assert rel <= 0.05
     np.testing.assert_allclose(got_lse, want_c_lse, atol=2e-2, rtol=0)
 
@@ -175,7 +186,7 @@ def test_fp8_cache_against_exact_inputs(fp8seg8):
     and 5.7e-2 max-abs, 7.5e-4 and 8.1e-4 mean-abs, when written). The
     kernel's own error is gated against the stored values
     (test_fp8_cache_eight_prior_segments)."""
-    s, rows, got, got_lse, want_c, want_c_lse = fp8seg8
+    s, rows, got, got_lse, want_c, want_c_lse, _ = fp8seg8
     want, _ = s.oracle(rows=rows)
     storage = np.abs(want_c - want)
     print(f"fp8seg8: e4m3 storage error of the oracle itself: max {storage.max():.3e} "

@@ -114,3 +114,31 @@ def test_e4m3_encode_is_nearest_even_by_brute_force():
 def test_e4m3_nan_and_saturation():
     enc = numerics.e4m3_encode(np.array([np.nan, 1e9, -1e9, 448.0, 460.0]))
     assert list(enc) == [0x7F, 0x7E, 0xFE, 0x7E, 0x7E]
+
+
+
+def test_probability_rounding_bound_holds_for_the_kernels_scaling():
+    """The e4m3 error bound the GPU tests allow (helpers.prob_rounding_bound)
+    against brute force: probabilities scaled as the e4m3 kernel scales them,
+    P' = 2^(x - m + 6) with a running max m anywhere in [M - 2.5, M + 1) (it
+    never passes the row's max M by a whole unit, and the overflow guard keeps
+    every P' at or below 2^8.5, so m never lies more than 2.5 below a key the
+    row has seen), rounded by the oracle's e4m3 encoder and brought
+    back to units of p = 2^(x - M): every key's error is within its share of
+    the bound (the bound with a one-hot |v| column per key), the worst case
+    comes within 10 % of it, and the subnormal range is reached."""
+    from helpers import prob_rounding_bound
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.normal(0.0, 4.0, 2000), rng.uniform(-20.0, 0.0, 2000), [0.0]])
+    p = 2.0 ** (x - x.max())
+    e = prob_rounding_bound(p[None, :], np.eye(len(p)))[0] * p.sum()    # per key
+    worst = 0.0
+    saw_subnormal = False
+    for shift in np.linspace(-2.5, 0.999, 36):       # m - M
+        scale = 2.0 ** (6.0 - shift)                  # P' = scale * p
+        pq = p * scale
+        err = np.abs(numerics.e4m3_decode(numerics.e4m3_encode(pq)) / scale - p)
+        assert np.all(err <= e * (1 + 1e-12))
+        worst = max(worst, float(np.max(err / e)))
+        saw_subnormal |= bool(np.any((pq > 0) & (pq < 2.0 ** -6)))
+    assert worst > 0.9 and saw_subnormal
