@@ -226,7 +226,7 @@ def append_text_fp8(k_in, v_in):
 
 def dequant(codes, scale):
     """Real value of fp8 codes times their plane scale (float64)."""
-    return numerics.e4m3_decode(codes) * np.float64(scale)
+    return numerics.e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)
 
 
 # ------------------------------------------------------ expected append (int8)
