@@ -5,8 +5,11 @@ heads, latent grids from 2 x 4 to 9 x 16 (frames of 8 to 144 tokens, a
 multiple of 8 as the library requires; padded planes for the one-byte
 caches), 1-4 frames per segment, 0-257 text tokens,
 0-3 prior segments whose kept frames are a random subset in random order (or
-all of them, in order), timed text windows on half of the cases, and split
-tiles on half of the cases. The cache type cycles through bf16, e4m3 (values
+all of them, in order), timed text windows on half of the cases, split tiles
+on half of the cases, and block-sparse history (1, 25, 50 or 100 % kept) on
+some of the cases with a history: there the library's block lists are
+checked against the oracle's selection, and the attention runs with the
+oracle's lists. The cache type cycles through bf16, e4m3 (values
 scaled per (frame, head)) and int8. Each output is checked against the
 oracle for the same inputs with that cache type's bar: bf16 max-abs 2e-2,
 mean-abs 2e-3, relative L2 1e-2; e4m3 per element within the e4m3
@@ -21,12 +24,12 @@ import torch
 
 import diffusion_transformer_attention_segment_amd as sa
 import seeded_inputs as si
-from helpers import Session, compare
+from helpers import Session, check_block_lists, compare
 
 pytestmark = pytest.mark.gpu
 
 KINDS = ("bf16", "fp8", "int8")
-N_CASES = 30
+N_CASES = 48
 
 
 def _draw(case):
@@ -48,20 +51,33 @@ def _draw(case):
         history = [int(f) for f in g.choice(prior * F, size=n_keep, replace=False)]
     windows = n_text > 0 and g.random() < 0.5
     split = bool(g.random() < 0.5)
-    return wl, history, windows, split
+    # block-sparse history on some cases with a history: the kept percentage
+    sparse = int(g.choice([1, 25, 50, 100])) if prior > 0 and g.random() < 0.4 else 0
+    return wl, history, windows, split, sparse
 
 
 @pytest.mark.parametrize("case", range(N_CASES))
 def test_random_shape(case):
-    wl, history, windows, split = _draw(case)
+    wl, history, windows, split, sparse = _draw(case)
     label = (f"case {case}: {wl.kv_dtype} H={wl.heads} grid={wl.lat_h}x{wl.lat_w} F={wl.lat_t} "
              f"text={wl.n_text} prior={wl.prior_segments[0]} "
              f"history={'all' if history is None else len(history)} windows={windows} "
-             f"split={split}")
+             f"split={split} sparse={sparse or 'no'}")
     print(label, flush=True)
     s = Session(wl, seed=case, layer=0, session=0, history=history)
     if windows:
         s.set_windows(si.text_windows(wl, case, wl.prior_segments[0] * wl.lat_t))
+    if sparse:
+        # the library's lists against the oracle's selection; the attention
+        # then runs with the oracle's lists (neither half feeds the other)
+        n_hist = len(s.frames) - wl.lat_t
+        keep = sa.sparse_keep(n_hist * -(-wl.P // 64), sparse)
+        it = s.item()
+        it.n_hist_frames, it.keep_blocks = n_hist, keep
+        got_lists = sa.sparse_select(s.geom, it).cpu().numpy()
+        want_lists, scores = s.oracle_select(n_hist, keep)
+        check_block_lists(got_lists, want_lists, scores, 1e-4 if wl.kv_dtype == "bf16" else 1e-3)
+        s.set_sparse(want_lists, n_hist)
     sa.segment_attention(s.geom, [s.item()], workspace="auto" if split else None)
     torch.cuda.synchronize()
     got, got_lse = s.gpu_out()
