@@ -36,7 +36,8 @@ namespace {
 constexpr int kPoolWaves = 4;
 constexpr int kSelThreads = 512;
 constexpr int kQB = SA_SPARSE_QUERY_BLOCK;   // query rows per block list
-constexpr int kChunkRows = 64;               // query rows rotated per LDS pass
+constexpr int kRowGroups = kSelThreads / 8;  // query rows rotated at a time (8 threads each)
+constexpr int kSelLut = 2048;                // cos/sin entries of a query block's table
 constexpr int kPerThread = (kMaxCandidates + kSelThreads - 1) / kSelThreads;   // 16
 
 __global__ __launch_bounds__(64 * kPoolWaves) void pool_k_kernel(const SelectArgs a) {
@@ -121,8 +122,66 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
   return before + x - v;
 }
 
+// The rotation table of a query block: the t band of the frames its video
+// rows span (f_lo ..), the h band of every latent row and the w band of every
+// column, each entry from the same fp64-reduced angle as rope_cos_sin, so a
+// lookup and the direct evaluation agree bit for bit.
+struct QueryLut {
+  int nt, nh, nw;   // pairs per band
+  int f_lo, nf;     // first frame (within the segment) and frame count
+  int lat_h;
+  int size;         // entries: nf * nt + lat_h * nh + lat_w * nw
+};
+
+__device__ __forceinline__ QueryLut query_lut_shape(const AttnItemDev& I, const RopeParams& r,
+                                                    int q0, int nrows) {
+  QueryLut s;
+  s.nt = r.split0 / 2;
+  s.nh = r.split1 / 2;
+  s.nw = r.split2 / 2;
+  s.lat_h = r.P / r.lat_w;
+  const int v_end = min(q0 + nrows, I.n_q_video);
+  s.f_lo = q0 / r.P;
+  s.nf = v_end > q0 ? (v_end - 1) / r.P - s.f_lo + 1 : 0;
+  s.size = s.nf * s.nt + s.lat_h * s.nh + r.lat_w * s.nw;
+  return s;
+}
+
+__device__ void build_query_lut(float2* lut, const QueryLut& s, const AttnItemDev& I,
+                                const RopeParams& r) {
+  for (int i = threadIdx.x; i < s.size; i += kSelThreads) {
+    int pair, pos;
+    if (i < s.nf * s.nt) {
+      const int f = i / s.nt;
+      pair = i - f * s.nt;
+      pos = I.frame0_q + s.f_lo + f;
+    } else if (i < s.nf * s.nt + s.lat_h * s.nh) {
+      const int j = i - s.nf * s.nt;
+      pos = j / s.nh;
+      pair = s.nt + (j - pos * s.nh);
+    } else {
+      const int j = i - s.nf * s.nt - s.lat_h * s.nh;
+      pos = j / s.nw;
+      pair = s.nt + s.nh + (j - pos * s.nw);
+    }
+    int axis;
+    const double om = rope_omega(pair, r, &axis);
+    float c, sn;
+    rope_cos_sin(pos, om, &c, &sn);
+    lut[i] = make_float2(c, sn);
+  }
+}
+
+__device__ __forceinline__ float2 query_lut_get(const float2* lut, const QueryLut& s, int pair,
+                                                int f, int hh, int ww) {
+  if (pair < s.nt) return lut[(f - s.f_lo) * s.nt + pair];
+  if (pair < s.nt + s.nh) return lut[s.nf * s.nt + hh * s.nh + (pair - s.nt)];
+  return lut[s.nf * s.nt + s.lat_h * s.nh + ww * s.nw + (pair - s.nt - s.nh)];
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a) {
-  __shared__ float rot[kChunkRows][kD + 4];
+  __shared__ float2 lut[kSelLut];
+  __shared__ float wsum[kSelThreads / 64][kD];
   __shared__ double om[kD / 2];
   __shared__ int ax[kD / 2];
   __shared__ float pq[kD];
@@ -138,48 +197,74 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
   const int q0 = qt * kQB;
   const int nrows = min(kQB, I.n_q - q0);
 
-  if (tid < kD / 2) {
+  const QueryLut ls = query_lut_shape(I, a.rope, q0, nrows);
+  const bool use_lut = ls.size <= kSelLut;
+  if (use_lut) {
+    build_query_lut(lut, ls, I, a.rope);
+  } else if (tid < kD / 2) {
     int axis;
     om[tid] = rope_omega(tid, a.rope, &axis);
     ax[tid] = axis;
   }
   __syncthreads();
 
-  // ---- mean rotated query of the block: 64 rows per pass, 8 threads per row,
-  // 8 rotation pairs each; columns summed over rows in row order -------------
-  float acc = 0.f;   // column tid (tid < 128)
-  for (int c0 = 0; c0 < nrows; c0 += kChunkRows) {
-    const int rr = tid >> 3, part = tid & 7;
-    const int row = q0 + c0 + rr;
+  // ---- mean rotated query of the block: 8 threads per row, 8 rotation pairs
+  // (16 dims) each; every thread sums its dims over its rows (rr, rr + 64, ...)
+  // in registers, then the 64 row groups are reduced in a fixed order (lanes,
+  // then waves), so the mean is deterministic -------------------------------------
+  const int rr = tid >> 3, part = tid & 7;
+  float ps[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ps[i] = 0.f;
+  for (int c0 = 0; c0 < nrows; c0 += kRowGroups) {
     if (c0 + rr < nrows) {
+      const int row = q0 + c0 + rr;
       bool video;
       int tpos, hpos, wpos;
       query_position(I, a.rope, row, &video, &tpos, &hpos, &wpos);
       const uint16_t* src = I.q + (static_cast<size_t>(row) * H + h) * kD + 16 * part;
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(src);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + 8);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(src + 2 * m);
-        float xa = __uint_as_float(w << 16), xb = __uint_as_float(w & 0xFFFF0000u);
+        const uint32_t wd = m < 4 ? w0[m] : w1[m - 4];
+        float xa = __uint_as_float(wd << 16), xb = __uint_as_float(wd & 0xFFFF0000u);
         if (video) {
           const int pr = 8 * part + m;
-          const int axis = ax[pr];
-          const int pos = axis == 0 ? tpos : (axis == 1 ? hpos : wpos);
           float cs, sn;
-          rope_cos_sin(pos, om[pr], &cs, &sn);
+          if (use_lut) {
+            const float2 e = query_lut_get(lut, ls, pr, tpos - I.frame0_q, hpos, wpos);
+            cs = e.x;
+            sn = e.y;
+          } else {
+            const int axis = ax[pr];
+            rope_cos_sin(axis == 0 ? tpos : (axis == 1 ? hpos : wpos), om[pr], &cs, &sn);
+          }
           const float ya = xa * cs - xb * sn;
           xb = xa * sn + xb * cs;
           xa = ya;
         }
-        rot[rr][16 * part + 2 * m] = xa;
-        rot[rr][16 * part + 2 * m + 1] = xb;
+        ps[2 * m] += xa;
+        ps[2 * m + 1] += xb;
       }
     }
-    __syncthreads();
-    if (tid < kD) {
-      const int n = min(kChunkRows, nrows - c0);
-      for (int r = 0; r < n; ++r) acc += rot[r][tid];
-    }
-    __syncthreads();
+  }
+  // lanes of one wave with the same dims differ in lane bits 3-5 (rows)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ps[i] += __shfl_xor(ps[i], 8);
+    ps[i] += __shfl_xor(ps[i], 16);
+    ps[i] += __shfl_xor(ps[i], 32);
+  }
+  if ((tid & 63) < 8) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wsum[tid >> 6][16 * part + i] = ps[i];
+  }
+  __syncthreads();
+  float acc = 0.f;   // column tid (tid < 128), waves in order
+  if (tid < kD) {
+#pragma unroll
+    for (int i = 0; i < kSelThreads / 64; ++i) acc += wsum[i][tid];
   }
   if (tid < kD) pq[tid] = acc / static_cast<float>(nrows);
   __syncthreads();
@@ -220,16 +305,36 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
       if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
+    if (tid < 64) {
+      // the highest bin b whose keys from b up reach `need`: lane l holds bins
+      // 255 - 4 l .. 252 - 4 l; counts of the bins above come from a scan
+      // over the lanes, and the first lane that reaches `need` decides
       const int need = sel_need;
-      int above = 0, b = 255;
-      for (; b > 0; --b) {
-        if (above + static_cast<int>(hist[b]) >= need) break;
-        above += static_cast<int>(hist[b]);
+      int c[4], s = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = static_cast<int>(hist[255 - 4 * tid - i]);
+        s += c[i];
       }
-      sel_need = need - above;
-      sel_prefix = prefix | (static_cast<uint32_t>(b) << shift);
-      sel_mask = mask | (255u << shift);
+      int incl = s;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (tid >= o) incl += y;
+      }
+      const unsigned long long hit = __ballot(incl >= need);
+      if (tid == __ffsll(static_cast<long long>(hit)) - 1) {
+        int above = incl - s, b = 255 - 4 * tid;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          if (above + c[i] >= need) break;
+          above += c[i];
+          --b;
+        }
+        sel_need = need - above;
+        sel_prefix = prefix | (static_cast<uint32_t>(b) << shift);
+        sel_mask = mask | (255u << shift);
+      }
     }
     __syncthreads();
   }
