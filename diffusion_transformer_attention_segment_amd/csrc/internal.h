@@ -110,7 +110,7 @@ __host__ __device__ inline int window_row_words(int n_text) { return (n_text + 3
 __host__ __device__ inline int window_table_rows(int P, int block_m) { return (block_m - 1) / P + 3; }
 
 // ---- sparse history: block selection -------------------------------------------
-// pool_k: mean stored key of every candidate block, fp32 [H][n_cand][128].
+// pool_k: mean stored key of every candidate block, fp32 [H][128][n_cand].
 // select: per (head, query block) the keep best blocks by pooled q . pooled k.
 struct SelectArgs {
   AttnItemDev item;        // q, kv planes, frames, counts of the session
@@ -119,7 +119,7 @@ struct SelectArgs {
   int32_t int8;            // 1: int8 planes with per-token scales
   int32_t n_cand;          // n_hist_frames * ceil(P / 64)
   int32_t keep;
-  float* pooled;           // workspace [H][n_cand][128]
+  float* pooled;           // workspace [H][128][n_cand]
   int32_t* out;            // [H][q_tiles][keep]
   RopeParams rope;
 };

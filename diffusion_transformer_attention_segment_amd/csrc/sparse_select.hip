@@ -12,7 +12,7 @@
 //   pool_k_kernel  one wave per candidate block: the mean of its <= 64 stored
 //                  keys (e4m3 codes times the plane scale, int8 codes times
 //                  their token's scale), fp32, into the
-//                  workspace [H][n_cand][128]. Reads the history K once.
+//                  workspace [H][128][n_cand] (dim-major). Reads the history K once.
 //   select_kernel  one workgroup per (query block, head): the mean rotated
 //                  query (fp32, rows summed in a fixed order), one score per
 //                  candidate, then the keep-th largest score by a 4-pass
@@ -24,7 +24,7 @@
 
 #include "attention_common.h"
 
-// Pooled keys of sa_sparse_select_noalloc: [H][n_cand][128] fp32 in the
+// Pooled keys of sa_sparse_select_noalloc: [H][128][n_cand] fp32 in the
 // library's own device memory, one copy per GPU. Host code never passes this
 // name to a kernel (on the host it is only a stand-in for the symbol): the
 // device address comes from hipGetSymbolAddress, per device.
@@ -92,10 +92,11 @@ __global__ __launch_bounds__(64 * kPoolWaves) void pool_k_kernel(const SelectArg
     s1 *= sc;
   }
   const float inv = 1.0f / static_cast<float>(n);
-  float2 v;
-  v.x = s0 * inv;
-  v.y = s1 * inv;
-  reinterpret_cast<float2*>(a.pooled + (static_cast<size_t>(h) * a.n_cand + c) * kD)[lane] = v;
+  // dim-major [H][128][n_cand]: the scores read one dim of consecutive
+  // candidates per load
+  float* dst = a.pooled + (static_cast<size_t>(h) * kD + 2 * lane) * a.n_cand + c;
+  dst[0] = s0 * inv;
+  dst[a.n_cand] = s1 * inv;
 }
 
 // Exclusive prefix sum of v over the workgroup's threads (in thread order);
@@ -269,22 +270,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
   if (tid < kD) pq[tid] = acc / static_cast<float>(nrows);
   __syncthreads();
 
-  // ---- scores of this thread's contiguous run of candidates, as keys that
-  // order like the scores (larger score -> larger key) ---------------------------
-  const int per = (a.n_cand + kSelThreads - 1) / kSelThreads;
-  const int cb = tid * per, ce = min(a.n_cand, cb + per);
-  const float* pk = a.pooled + static_cast<size_t>(h) * a.n_cand * kD;
-  for (int c = cb; c < ce; ++c) {
-    const float4* row = reinterpret_cast<const float4*>(pk + static_cast<size_t>(c) * kD);
+  // ---- one score per candidate (candidates tid, tid + 512, ...: a load reads
+  // one dim of 64 consecutive candidates), as a key that orders like the score
+  // (larger score -> larger key); dims in order, so the score is the same
+  // fp32 chain whatever the layout ----------------------------------------------
+  const float* pk = a.pooled + static_cast<size_t>(h) * kD * a.n_cand;
+  for (int c = tid; c < a.n_cand; c += kSelThreads) {
     float s = 0.f;
-#pragma unroll 8
-    for (int d = 0; d < kD / 4; ++d) {
-      const float4 k4 = row[d];
-      s = fmaf(pq[4 * d], k4.x, s);
-      s = fmaf(pq[4 * d + 1], k4.y, s);
-      s = fmaf(pq[4 * d + 2], k4.z, s);
-      s = fmaf(pq[4 * d + 3], k4.w, s);
-    }
+#pragma unroll 16
+    for (int d = 0; d < kD; ++d) s = fmaf(pq[d], pk[static_cast<size_t>(d) * a.n_cand + c], s);
     const uint32_t u = __float_as_uint(s);
     keys[c] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   }
@@ -294,6 +288,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const SelectArgs a)
     sel_need = a.keep;
   }
   __syncthreads();
+  // from here on each thread owns a contiguous run of candidates (index order)
+  const int per = (a.n_cand + kSelThreads - 1) / kSelThreads;
+  const int cb = tid * per, ce = min(a.n_cand, cb + per);
 
   // ---- radix select of the keep-th largest key, 8 bits per pass from the top --
   for (int shift = 24; shift >= 0; shift -= 8) {
