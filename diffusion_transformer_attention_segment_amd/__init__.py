@@ -17,7 +17,8 @@ thin ctypes binding. The calls follow the method's hot path:
 from .binding import (  # noqa: F401
     AttnItem, Geom, KVLayer, SegAttnError, MAX_CAMERA_CHUNK, camera_attention, KV_BF16, KV_FP8,
     KV_INT8, SEL_ALL, SEL_RECENT, SEL_POWER,
-    SEL_ANCHOR_RECENT, MAX_ITEMS, HEAD_DIM, SIGNATURES, LIB_PATH, abi_version, cache_bytes,
+    SEL_ANCHOR_RECENT, MAX_ITEMS, MAX_FRAMES_KV, HEAD_DIM, SIGNATURES, LIB_PATH, abi_version,
+    cache_bytes,
     history_gather, history_select, kv_append, kv_dequant, last_error, lib, segment_attention,
     segment_attention_workspace, sparse_keep, sparse_select, sparse_select_noalloc,
     SPARSE_SCRATCH_BYTES, SPARSE_KEY_BLOCK, SPARSE_QUERY_BLOCK,

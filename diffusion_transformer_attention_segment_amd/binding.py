@@ -22,6 +22,7 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_E_ARG", 2: "SA_E_SHAPE", 3: "SA_E_ALIGN",
 KV_BF16, KV_FP8, KV_INT8 = 0, 1, 2
 SEL_ALL, SEL_RECENT, SEL_POWER, SEL_ANCHOR_RECENT = 0, 1, 2, 3
 MAX_ITEMS = 8
+MAX_FRAMES_KV = 65536
 HEAD_DIM = 128
 
 

@@ -57,6 +57,24 @@ def test_abi_version(lib):
     assert sa.abi_version() == 11
 
 
+def test_binding_constants_match_the_header():
+    """The Python binding's limits and sizes are the header's #defines."""
+    text = open(HEADER).read()
+    defs = {m.group(1): m.group(2) for m in re.finditer(r"#define (SA_[A-Z0-9_]+) +([^/\n]+)", text)}
+
+    def value(name):
+        return int(eval(defs[name].strip().replace("u", "")))   # integers and shifts only
+
+    assert value("SA_ABI_VERSION") == sa.abi_version()
+    assert value("SA_HEAD_DIM") == sa.HEAD_DIM
+    assert value("SA_MAX_ITEMS") == sa.MAX_ITEMS
+    assert value("SA_MAX_FRAMES_KV") == sa.MAX_FRAMES_KV
+    assert value("SA_MAX_CAMERA_CHUNK") == sa.MAX_CAMERA_CHUNK
+    assert value("SA_SPARSE_KEY_BLOCK") == sa.SPARSE_KEY_BLOCK
+    assert value("SA_SPARSE_QUERY_BLOCK") == sa.SPARSE_QUERY_BLOCK
+    assert value("SA_SPARSE_SCRATCH_BYTES") == sa.SPARSE_SCRATCH_BYTES
+
+
 def test_status_strings(lib):
     assert lib.sa_status_string(0) == b"SA_OK"
     assert lib.sa_status_string(7) == b"SA_E_HIP"

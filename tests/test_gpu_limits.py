@@ -7,7 +7,10 @@
   other history frames stay dense), and a single kept block;
 - timed text windows at the window-table bound: frames of 16 tokens with
   3,616 text keys fill (255 / 16 + 3) * ceil(3616 / 32) = 2,034 of the 2,048
-  table words (one more word is refused on the host: tests/test_abi_cpu.py).
+  table words (one more word is refused on the host: tests/test_abi_cpu.py);
+- a key set of SA_MAX_FRAMES_KV frames (65,536 frames of 8 tokens, the
+  history in a seeded random order), bf16 and e4m3, whole and split: one key
+  tile per frame, so the key walk enters a new frame on every tile.
 """
 
 import numpy as np
@@ -16,7 +19,10 @@ import torch
 
 import diffusion_transformer_attention_segment_amd as sa
 import seeded_inputs as si
-from helpers import Session, check_block_lists, compare
+from helpers import Session, check_block_lists, compare, prob_rounding_bound
+from oracle import attention as oatt
+from oracle import cache as ocache
+from oracle import rope as orope
 
 pytestmark = pytest.mark.gpu
 
@@ -84,3 +90,81 @@ def test_windows_at_the_table_bound():
     rows = np.concatenate([np.arange(64), si.sample_rows(wl.Lq, 128, 5, [64, 255, 256])])
     rows = np.unique(rows)
     _check(s, "windows at the table bound", rows=rows)
+
+
+def _fp8_stored(s):
+    """The e4m3 cache's K and V of the session's key set, [Lk, H, D] float64,
+    from the oracle's own append of each segment (quantise, then decode times
+    the plane scale), taken in key-set order."""
+    wl = s.wl
+    F, H, D = wl.lat_t, wl.heads, wl.head_dim
+    raw = [(seg, s.raw_k[seg].float().cpu().double().numpy(),
+            s.raw_v[seg].float().cpu().double().numpy()) for seg in range(s.S + 1)]
+
+    def one_segment(args):   # segments are independent: one per worker thread
+        seg, kin, vin = args
+        kc, ksc, vc, vsc = ocache.append_fp8(kin, vin, seg * F, wl.lat_h, wl.lat_w, wl.split,
+                                             s.geom.rope_theta)
+        return (ocache.dequant(kc, ksc[:, :, None, None]).transpose(0, 2, 1, 3),   # [F, P, H, D]
+                ocache.dequant(vc, vsc[:, :, None, None]).transpose(0, 3, 1, 2))
+
+    import concurrent.futures
+    with concurrent.futures.ThreadPoolExecutor(max_workers=16) as ex:
+        per_seg = list(ex.map(one_segment, raw))
+    del raw
+    fr = np.asarray(s.frames)
+    k = np.concatenate([x[0] for x in per_seg])[fr].reshape(-1, H, D)
+    v = np.concatenate([x[1] for x in per_seg])[fr].reshape(-1, H, D)
+    del per_seg
+    tk = s.text_k.float().cpu().double().numpy()
+    tv = s.text_v.float().cpu().double().numpy()
+    kc, ksc, vc, vsc = ocache.append_text_fp8(tk, tv)
+    k = np.concatenate([k, ocache.dequant(kc, ksc[:, None, None]).transpose(1, 0, 2)])
+    v = np.concatenate([v, ocache.dequant(vc, vsc[:, None, None]).transpose(2, 0, 1)])
+    return k, v
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_key_set_at_the_frame_bound(kv):
+    """65,536 frames in the key set (31 prior segments of 2,048 frames of
+    2 x 4 tokens, history shuffled, and the segment's own 2,048 frames), one
+    head, 16 text keys; sampled rows against the oracle, with the tiles run
+    whole and split."""
+    wl = si.Workload("maxframes", heads=1, lat_t=2048, lat_h=2, lat_w=4, n_text=16,
+                     prior_segments=(31,), kv_dtype=kv, scale_factors=(kv == "fp8"))
+    g = np.random.default_rng(si.derive_seed(127, "frame bound history"))
+    history = [int(f) for f in g.permutation(31 * 2048)]
+    print(f"{kv}: {len(history) + wl.lat_t} frames of {wl.P} tokens, one head", flush=True)
+    s = Session(wl, seed=127, layer=0, session=0, history=history)
+    assert len(s.frames) == sa.MAX_FRAMES_KV
+    rows = si.sample_rows(wl.Lq, 48, 7, [255, 256, wl.Lq - 17, wl.Lq - 16])
+    if kv == "bf16":
+        want, want_lse = s.oracle(rows=rows)
+    else:
+        k, v = _fp8_stored(s)
+        q = s.q.float().cpu().double().numpy()[rows]
+        qr = orope.rope3d(q, s.q_positions()[rows], wl.split, s.geom.rope_theta)
+        scale = 1.0 / np.sqrt(wl.head_dim)
+        want, want_lse = oatt.attention(qr[:, 0], k[:, 0], v[:, 0], scale, None)
+        sc = (qr[:, 0] @ k[:, 0].T) * scale
+        p = np.exp(sc - sc.max(axis=1, keepdims=True))
+        bound = prob_rounding_bound(p, np.abs(v[:, 0]))
+        del k, v, sc, p
+    for split in (False, True):
+        label = f"{kv} at {sa.MAX_FRAMES_KV} frames, {'split' if split else 'whole'} tiles"
+        print(label, flush=True)
+        sa.segment_attention(s.geom, [s.item()], workspace="auto" if split else None)
+        torch.cuda.synchronize()
+        got, got_lse = s.gpu_out(rows=rows)
+        if kv == "bf16":
+            _, _, rel = compare(got, want, MAX_ABS, MEAN_ABS, label)
+            assert rel <= REL_L2, label
+            np.testing.assert_allclose(got_lse, want_lse, atol=LSE_ATOL, rtol=0, err_msg=label)
+        else:
+            err = np.abs(got[:, 0] - want)
+            worst = float(np.max(err / (bound + 5e-3)))
+            rel = float(np.linalg.norm(got[:, 0] - want) / np.linalg.norm(want))
+            print(f"  max_abs={err.max():.3e} rel_l2={rel:.3e} max(err / (bound + 5e-3))={worst:.3f}",
+                  flush=True)
+            assert worst <= 1.0 and rel <= 0.05, label
+            np.testing.assert_allclose(got_lse[:, 0], want_lse, atol=2e-2, rtol=0, err_msg=label)
