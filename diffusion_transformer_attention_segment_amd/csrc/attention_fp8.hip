@@ -47,7 +47,9 @@
 // packing. S^T is computed in place: block 0 of tile t+1 replaces block 0 of
 // tile t once its words are packed, block 1 after the rescale check. Tiles go
 // HBM -> LDS directly (buffer loads with the LDS flag) two tiles ahead into a
-// 4-stage ring, one barrier per tile.
+// 4-stage ring, one barrier per tile. With block-sparse history, the kept
+// tiles' plane offsets and scales are staged in LDS before the key loop, so a
+// jump to the next kept tile reads no memory on the scalar path.
 #include "attention_common.h"
 
 namespace segattn {
@@ -206,6 +208,28 @@ __device__ __forceinline__ TileInfo tile_info(const TileCursor& c, int flag_fi) 
   t.ksc = e8m0_of(c.kscale);
   t.vsc = e8m0_of(c.vscale);
   return t;
+}
+
+// Block-sparse history: the kept tiles of a work tile are staged in LDS before
+// the key loop, one 16-byte entry per tile: the byte offset of the tile's
+// (frame, head) plane in the K and V caches (64 bits), and the tile's index in
+// its frame with the E8M0 bytes of the plane's K and V scales. A jump to a
+// kept tile then reads LDS instead of the chain of dependent scalar loads
+// (list entry, frame entry, plane scales) that would stall the wave.
+constexpr int kKeptTab = 4096;   // entries; later kept tiles take the scalar walk
+
+__device__ __forceinline__ void cursor_kept(TileCursor& c, const char* kbase, const char* vbase,
+                                            uint32_t off_lo, uint32_t off_hi, uint32_t w1, int P,
+                                            int PL) {
+  const size_t plane = (static_cast<size_t>(off_hi) << 32) | off_lo;
+  c.fi = 0;   // a history frame: never a text segment under timed windows
+  c.p0 = static_cast<int>(w1 & 0xFFFFu) * kKeyTile;
+  c.len = P;
+  c.vstride = PL;
+  c.kplane = kbase + plane;
+  c.vplane = vbase + plane;
+  c.kscale = __uint_as_float(((w1 >> 16) & 0xFFu) << 23);
+  c.vscale = __uint_as_float((w1 >> 24) << 23);
 }
 
 // Word w (0..3) of one 32-key block: keys 4w .. 4w+3 of the block (registers
@@ -390,6 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   // read one word past the table; their keys are all masked by the valid count)
   __shared__ uint32_t wtab[kWindowWords + 1];
   __shared__ int woff[kThreads];
+  __shared__ uint4 ktab[kSparse ? kKeptTab : 1];   // kept tiles of the work tile
 
   const WorkTile wt = map_workgroup(a, BM);
   const AttnItemDev& I = a.items[wt.item];
@@ -418,6 +443,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
     ax[tid] = axis;
   }
   stage_window_table(I, wtab, q0, BM, P, tid, kThreads);
+  int n_tab = 0;   // kept tiles staged (logical tiles kt0 .. kt0 + n_tab - 1)
+  if constexpr (kSparse) {
+    const int tpf = (P + kKeyTile - 1) / kKeyTile;
+    // (an entry holds the tile's index in its frame in 16 bits)
+    n_tab = tpf <= 0x10000 ? min(max(0, min(kt1, seq.keep) - kt0), kKeptTab) : 0;
+    for (int i = tid; i < n_tab; i += kThreads) {
+      const int tile = seq.list[kt0 + i];
+      const int fi = tile / tpf;
+      const int frame = I.frames[fi];
+      const size_t pl = static_cast<size_t>(frame) * H + h;
+      const size_t off = pl * static_cast<size_t>(PL) * kD;
+      const uint32_t ks = static_cast<uint32_t>(e8m0_of(I.k_scale[pl]));
+      const uint32_t vs = static_cast<uint32_t>(e8m0_of(I.v_scale[pl]));
+      ktab[i] = make_uint4(static_cast<uint32_t>(off), static_cast<uint32_t>(off >> 32),
+                           static_cast<uint32_t>(tile - fi * tpf) | (ks << 16) | (vs << 24), 0u);
+    }
+  }
   // Every stage starts as zeros (the V stage of "tile -1" is read once with
   // zero probabilities; stages of tiles past the end may be read, unused).
   for (int i = tid; i < kStages * KT8 / 16; i += kThreads)
@@ -570,6 +612,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
   // barrier of step t comes after its first two (PV) MFMAs; K of tile t+1
   // (loaded in step t-1) is read after it. Two steps per loop trip: the P
   // buffers swap roles without copies.
+  // The key walk's next tile: a staged kept tile (its entry read from LDS one
+  // step ahead, into ent), else the scalar walk.
+  const char* kbase = static_cast<const char*>(I.k);
+  const char* vbase = static_cast<const char*>(I.v);
+  uint4 ent = make_uint4(0u, 0u, 0u, 0u);   // entry of the kept tile the next advance takes
+  if constexpr (kSparse) {
+    if (n_tab > 2) ent = ktab[2];
+  }
+  auto advance = [&](int li) __attribute__((always_inline)) {
+    if constexpr (kSparse) {
+      const int i = li - kt0;   // >= 2: tiles kt0 and kt0 + 1 are loaded before the loop
+      if (i < n_tab) {
+        const uint32_t off_lo = __builtin_amdgcn_readfirstlane(ent.x);
+        const uint32_t off_hi = __builtin_amdgcn_readfirstlane(ent.y);
+        const uint32_t w1 = __builtin_amdgcn_readfirstlane(ent.z);
+        if (i + 1 < n_tab) ent = ktab[i + 1];
+        cursor_kept(lc, kbase, vbase, off_lo, off_hi, w1, P, PL);
+        return;
+      }
+    }
+    seq_next<kSparse, 1>(lc, I, h, H, P, seq, li);
+  };
   int pending = 0;   // lower bound of this wave's loads issued in the step before
   auto step = [&](int tt, const i32x8v& p_prev, i32x8v& p_cur) __attribute__((always_inline)) {
     const uint8_t* Vprev = Vs + ((tt + kStages - 1) & (kStages - 1)) * VT8 + voff;
@@ -589,7 +653,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fp8_kernel(const AttnArgs a)
       pending = 0;
       if (tt + 2 < ntiles) {
         const int s2 = (tt + 2) & (kStages - 1);
-        seq_next<kSparse, 1>(lc, I, h, H, P, seq, kt0 + tt + 2);
+        advance(kt0 + tt + 2);
         ti2 = tile_info(lc, flag_fi);
         dma_k8(lc, Ks + s2 * KT8, w, dmo);
         dma_v8(lc, Vs + s2 * VT8, w, PL, dmo);

@@ -168,3 +168,28 @@ def test_key_set_at_the_frame_bound(kv):
                   flush=True)
             assert worst <= 1.0 and rel <= 0.05, label
             np.testing.assert_allclose(got_lse[:, 0], want_lse, atol=2e-2, rtol=0, err_msg=label)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_full_list_past_the_staged_kept_tiles(kv):
+    """8,192 candidate tiles (128 prior segments of 64 one-tile frames), all
+    kept in order: the sparse walk visits the dense key order, so the result
+    is bitwise the dense one, whole and split. The e4m3 kernel stages at most
+    4,096 kept tiles of a work tile in LDS and walks the rest from the list."""
+    wl = si.Workload("fullkeep", heads=1, lat_t=64, lat_h=8, lat_w=8, n_text=16,
+                     prior_segments=(128,), kv_dtype=kv, scale_factors=(kv == "fp8"))
+    s = Session(wl, seed=129, layer=0, session=0)
+    n_hist = 128 * 64
+    nq = -(-wl.Lq // sa.SPARSE_QUERY_BLOCK)
+    lists = np.tile(np.arange(n_hist, dtype=np.int32), (wl.heads, nq, 1))
+    for ws in (None, "auto"):
+        print(f"{kv}: keep all {n_hist} candidates, {'split' if ws else 'whole'} tiles", flush=True)
+        s.clear_sparse()
+        sa.segment_attention(s.geom, [s.item()], workspace=ws)
+        torch.cuda.synchronize()
+        dense, dense_lse = s.gpu_out()
+        s.set_sparse(lists, n_hist)
+        sa.segment_attention(s.geom, [s.item()], workspace=ws)
+        torch.cuda.synchronize()
+        got, got_lse = s.gpu_out()
+        assert np.array_equal(got, dense) and np.array_equal(got_lse, dense_lse), ws
