@@ -53,6 +53,12 @@ constexpr int VT = kD * VS;      // elements of one V^T stage
 constexpr int kKChunks = BN * kD / 8 / kThreads;   // 16-byte K chunks per thread (2)
 constexpr int kVChunks = kD * BN / 8 / kThreads;   // 16-byte V chunks per thread (2)
 constexpr float kRescaleSum = 256.0f;   // a row's block sum above this moves the running max
+// Block-sparse history: up to this many kept tiles of a work tile are staged
+// in LDS before the key loop (8 bytes each: the tile's (frame, head) plane
+// index and its tile index in the frame), so a jump to a kept tile reads no
+// memory on the scalar path; later kept tiles take the scalar walk. (The LDS
+// ring leaves about 11 KB for it.)
+constexpr int kKeptTab = 1280;
 constexpr float kFastLimit = 1.8446744e19f;   // 2^64: a block sum above it sends the workgroup to the rescaling loop
 
 // Load tile c: K rows past the valid count and V^T bytes past the plane end
@@ -355,6 +361,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   // timed-window bits (+ 1 word: block 1 of the last text tile may read one
   // word past the table; its keys are all masked by the valid count)
   __shared__ uint32_t wtab[kWindowWords + 1];
+  __shared__ uint2 ktab[kSparse ? kKeptTab : 1];   // kept tiles of the work tile
 
   const WorkTile wt = map_workgroup(a, BM);
   const AttnItemDev& I = a.items[wt.item];
@@ -380,6 +387,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     ax[tid] = axis;
   }
   stage_window_table(I, wtab, q0, BM, P, tid, kThreads);
+  const int PL = plane_tokens(P, CK != kCkBf16);   // token slots of a frame plane
+  const uint64_t plane_bytes64 = static_cast<uint64_t>(PL) * kD * elem_bytes<CK>();
+  const uint32_t plane_bytes = static_cast<uint32_t>(plane_bytes64);
+  int n_tab = 0;   // kept tiles staged (logical tiles kt0 .. kt0 + n_tab - 1)
+  if constexpr (kSparse) {
+    const int tpf = (P + kKeyTile - 1) / kKeyTile;
+    // (a jump multiplies the plane index by a 32-bit plane size)
+    n_tab = plane_bytes64 <= 0xFFFFFFFFu ? min(max(0, min(kt1, seq.keep) - kt0), kKeptTab) : 0;
+    for (int i = tid; i < n_tab; i += kThreads) {
+      const int tile = seq.list[kt0 + i];
+      const int fi = tile / tpf;
+      const uint32_t pl = static_cast<uint32_t>(I.frames[fi] * H + h);
+      ktab[i] = make_uint2(pl, static_cast<uint32_t>(tile - fi * tpf));
+    }
+  }
   __syncthreads();
 
   // ---- Q fragments (B operand of S^T = K Q^T): rotated in fp32, times the
@@ -427,6 +449,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   f32x16 negm;
   float l_run;
   uint32_t n_resc = 0;   // this wave's rescale steps (diagnostic counters only)
+  const char* kbase = static_cast<const char*>(I.k);   // cache bases of the staged kept tiles
+  const char* vbase = static_cast<const char*>(I.v);
+  const float* kscb = I.k_scale;
+  const float* vscb = I.v_scale;
 
   // The whole key loop, run first without the rescale: the running max stays
   // at block 0's max, and a block sum above kFastLimit only raises a flag
@@ -441,6 +467,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     // the load cursor runs three tiles ahead of the compute tile; nv0..nv2
     // keep the valid-key counts of the tiles in between
     TileCursor lc;
+    // The next tile of the walk: a staged kept tile (its entry read from LDS
+    // one step ahead, into ent), else the scalar walk.
+    uint2 ent = make_uint2(0u, 0u);
+    if constexpr (kSparse) {
+      if (n_tab > 3) ent = ktab[3];
+    }
+    auto advance = [&](int li) __attribute__((always_inline)) {
+      if constexpr (kSparse) {
+        const int i = li - kt0;   // >= 3: tiles kt0 .. kt0 + 2 are loaded before the loop
+        if (i < n_tab) {
+          const uint32_t pl = __builtin_amdgcn_readfirstlane(ent.x);
+          const uint32_t tix = __builtin_amdgcn_readfirstlane(ent.y);
+          if (i + 1 < n_tab) ent = ktab[i + 1];
+          const size_t off = static_cast<size_t>(pl) * plane_bytes;
+          lc.fi = 0;   // a history frame: never a text segment under timed windows
+          lc.p0 = static_cast<int>(tix) * kKeyTile;
+          lc.len = P;
+          lc.vstride = PL;
+          lc.kplane = kbase + off;
+          lc.vplane = vbase + off;
+          if constexpr (kInt8) {
+            lc.kst = kscb + static_cast<size_t>(pl) * PL;
+            lc.vst = vscb + static_cast<size_t>(pl) * PL;
+          }
+          return;
+        }
+      }
+      seq_next<kSparse, CK>(lc, I, h, H, P, seq, li);
+    };
     seq_start<kSparse, CK>(lc, I, h, H, P, seq, kt0);
     Staged<kInt8> stg;
     int nv0 = cursor_mask_code(lc, flag_fi);
@@ -519,7 +574,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
           const int s2 = (t + 2) & (kStages - 1);
           stage_store<kInt8>(Ks + s2 * KT, Vs + s2 * VT, tid, stg);
           if (t + 3 < ntiles) {
-            seq_next<kSparse, CK>(lc, I, h, H, P, seq, kt0 + t + 3);
+            advance(kt0 + t + 3);
             nv3 = cursor_mask_code(lc, flag_fi);
             stage_load<kInt8>(lc, koff_ld, tid, stg);
           }
