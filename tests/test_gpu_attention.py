@@ -118,6 +118,83 @@ def test_logits_far_above_the_first_block():
     np.testing.assert_allclose(got_lse, wr_lse, rtol=2e-3, atol=0.05)
 
 
+def _rise_past_first_block(s, rows=None):
+    """Largest rise of a row's logit max (log2 units, oracle's fp64 logits)
+    past the max of the row's first 32 keys, over the given rows and all heads."""
+    from oracle import rope as orope
+    wl = s.wl
+    k, _, kpos = s.raw_keys()
+    q = s.q.float().cpu().double().numpy()
+    qr = orope.rope3d(q, s.q_positions(), wl.split, s.geom.rope_theta)
+    kr = orope.rope3d(k, kpos, wl.split, s.geom.rope_theta)
+    if rows is not None:
+        qr = qr[rows]
+    c2 = math.log2(math.e) / math.sqrt(wl.head_dim)
+    rise = 0.0
+    for hh in range(wl.heads):
+        lg = (qr[:, hh] @ kr[:, hh].T) * c2
+        rise = max(rise, float(np.max(lg.max(axis=1) - lg[:, :min(32, wl.P)].max(axis=1))))
+    return rise
+
+
+@pytest.mark.parametrize("n_text", [16, 256])
+def test_fast_pass_overflow_in_its_last_tiles(n_text):
+    """Text keys x 40: only the text tiles, which the key walk takes last,
+    hold logits far above every row's first block. With one text tile the
+    fast pass meets the overflow in its final tile, where only the vote at
+    the end of the pass sees it; with four the pass leaves its loop early.
+    Either way the workgroups redo the loop with the running max moving, and
+    the output matches the oracle."""
+    print(f"fast-pass overflow in the last tiles, n_text={n_text}", flush=True)
+    wl = _wl(f"late{n_text}", 2, 4, 6, 8, n_text, 2)
+    s = Session(wl, seed=21, layer=0, session=0)
+    s.text_k = (s.text_k.float() * 40.0).to(torch.bfloat16)
+    sa.text_append(s.geom, s.kv, s.text_k, s.text_v, wl.n_text)
+    rise = _rise_past_first_block(s)
+    print(f"largest rise past the first block: {rise:.1f} log2 units", flush=True)
+    assert rise > 80.0
+    c = torch.zeros(3, dtype=torch.int32, device="cuda")
+    sa.segment_attention(s.geom, [s.item()], workspace=None, counters=c)
+    torch.cuda.synchronize()
+    work, slow, _ = c.tolist()
+    print(f"work tiles {work}, slow-path events {slow}", flush=True)
+    assert slow >= 1
+    got, got_lse = s.gpu_out()
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(got_lse))
+    wr, wr_lse = s.oracle(round_rotated=True)
+    compare(got, wr, MAX_ABS, MEAN_ABS, f"text keys x40, n_text={n_text}")
+    np.testing.assert_allclose(got_lse, wr_lse, rtol=2e-3, atol=0.05)
+
+
+def test_fast_pass_overflow_in_one_wave():
+    """One query row of head 0 x 200 (row 100: the fourth wave of its
+    workgroup): only that wave's rows pass the fast loop's limit, so only it
+    raises the flag; all eight waves must leave the first pass at the same
+    tile and redo the loop together, while head 1's workgroup stays on the
+    fast path. The whole output matches the oracle."""
+    print("fast-pass overflow in one wave (row 100 of head 0 x 200)", flush=True)
+    wl = _wl("onerow", 2, 4, 6, 8, 24, 2)
+    s = Session(wl, seed=23, layer=0, session=0)
+    q = s.q.float()
+    q[100, 0] *= 200.0
+    s.q = q.to(torch.bfloat16)
+    s.out = torch.empty_like(s.q)
+    rise = _rise_past_first_block(s, rows=[100])
+    print(f"row 100: largest rise past the first block: {rise:.1f} log2 units", flush=True)
+    assert rise > 80.0
+    c = torch.zeros(3, dtype=torch.int32, device="cuda")
+    sa.segment_attention(s.geom, [s.item()], workspace=None, counters=c)
+    torch.cuda.synchronize()
+    work, slow, _ = c.tolist()
+    print(f"work tiles {work}, slow-path events {slow}", flush=True)
+    assert 1 <= slow < work
+    got, got_lse = s.gpu_out()
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(got_lse))
+    wr, wr_lse = s.oracle(round_rotated=True)
+    compare(got, wr, MAX_ABS, MEAN_ABS, "row 100 x200")
+    np.testing.assert_allclose(got_lse, wr_lse, rtol=2e-3, atol=0.05)
+
+
 @pytest.mark.parametrize("case", CASES[:3], ids=[c[0] for c in CASES[:3]])
 def test_kernel_error_against_rounded_inputs(case):
     """Against the oracle that rounds rotated Q and K to bf16, the kernel's own
