@@ -362,8 +362,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   // word past the table; its keys are all masked by the valid count)
   __shared__ uint32_t wtab[kWindowWords + 1];
   __shared__ uint2 ktab[kSparse ? kKeptTab : 1];   // kept tiles of the work tile
-  // overflow flags of the first pass, one per tile modulo 3 (see attend)
-  __shared__ int fast_stop[3];
 
   const WorkTile wt = map_workgroup(a, BM);
   const AttnItemDev& I = a.items[wt.item];
@@ -404,7 +402,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
       ktab[i] = make_uint2(pl, static_cast<uint32_t>(tile - fi * tpf));
     }
   }
-  if (tid < 3) fast_stop[tid] = 0;
   __syncthreads();
 
   // ---- Q fragments (B operand of S^T = K Q^T): rotated in fp32, times the
@@ -463,13 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
   // the flag is lost; the flag is raised long before anything could
   // overflow). Without rescale code in the loop the register allocator keeps
   // every block in place. If any row of the workgroup raised the flag, the
-  // whole loop runs again, rescaling in place. The first pass stops early once
-  // a flag is up: a wave whose rows raised it by the end of tile t sets
-  // fast_stop[t % 3]; every wave reads fast_stop[(t - 2) % 3] after the
-  // barrier of tile t and leaves the loop at the end of that tile if it is
-  // set. That slot was last written before the barrier of tile t - 1 and is
-  // next written after the barrier of tile t + 1, so all waves read the same
-  // value and leave after the same number of barriers.
+  // whole loop runs again, rescaling in place.
   auto attend = [&](auto safe_tag) __attribute__((always_inline)) {
     constexpr bool kSafe = decltype(safe_tag)::value;
     bool over = false;
@@ -553,8 +544,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
     }
     bf16x8 pa[2], pb[2];                      // P of block 2t-1 at the top; of 2t
     pa[0] = pa[1] = bf16x8{};
-    int s3 = 0;           // t % 3: the first pass's flag slot of this tile
-    int stop_seen = 0;    // fast_stop[(t - 2) % 3], read after the barrier of tile t
 
     // operands of step 0's first slots: V of "tile -1" (the zeroed last stage,
     // met by the zero probabilities pa) and block 1's K rows
@@ -581,7 +570,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if constexpr (!kSafe) stop_seen = fast_stop[s3 == 2 ? 0 : s3 + 1];
         if (t + 2 < ntiles) {
           const int s2 = (t + 2) & (kStages - 1);
           stage_store<kInt8>(Ks + s2 * KT, Vs + s2 * VT, tid, stg);
@@ -630,11 +618,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(const AttnArgs a
       nv0 = nv1;
       nv1 = nv2;
       nv2 = nv3;
-      if constexpr (!kSafe) {
-        if (over) fast_stop[s3] = 1;
-        s3 = s3 == 2 ? 0 : s3 + 1;
-        if (__builtin_amdgcn_readfirstlane(stop_seen) != 0) break;
-      }
     }
     {
       const uint16_t* Vlast = Vs + ((ntiles - 1) & (kStages - 1)) * VT;

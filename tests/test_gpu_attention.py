@@ -140,11 +140,10 @@ def _rise_past_first_block(s, rows=None):
 @pytest.mark.parametrize("n_text", [16, 256])
 def test_fast_pass_overflow_in_its_last_tiles(n_text):
     """Text keys x 40: only the text tiles, which the key walk takes last,
-    hold logits far above every row's first block. With one text tile the
-    fast pass meets the overflow in its final tile, where only the vote at
-    the end of the pass sees it; with four the pass leaves its loop early.
-    Either way the workgroups redo the loop with the running max moving, and
-    the output matches the oracle."""
+    hold logits far above every row's first block, so the fast pass raises
+    its flag only in its last one or four tiles. The vote at the end of the
+    pass still sends every workgroup through the loop again with the running
+    max moving, and the output matches the oracle."""
     print(f"fast-pass overflow in the last tiles, n_text={n_text}", flush=True)
     wl = _wl(f"late{n_text}", 2, 4, 6, 8, n_text, 2)
     s = Session(wl, seed=21, layer=0, session=0)
@@ -169,9 +168,9 @@ def test_fast_pass_overflow_in_its_last_tiles(n_text):
 def test_fast_pass_overflow_in_one_wave():
     """One query row of head 0 x 200 (row 100: the fourth wave of its
     workgroup): only that wave's rows pass the fast loop's limit, so only it
-    raises the flag; all eight waves must leave the first pass at the same
-    tile and redo the loop together, while head 1's workgroup stays on the
-    fast path. The whole output matches the oracle."""
+    raises the flag; the workgroup's vote makes all eight waves redo the loop
+    together, while head 1's workgroup stays on the fast path. The whole
+    output matches the oracle."""
     print("fast-pass overflow in one wave (row 100 of head 0 x 200)", flush=True)
     wl = _wl("onerow", 2, 4, 6, 8, 24, 2)
     s = Session(wl, seed=23, layer=0, session=0)
